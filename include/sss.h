@@ -1,0 +1,228 @@
+/*
+ * sss.h -- C ABI of the sparse self-speculative decode attention library
+ * (libsss.so, HIP for AMD MI355X / gfx950).
+ *
+ * The method (SparseSpec, "Accelerating Large-Scale Reasoning Model
+ * Inference: Self-Speculative Decoding with Sparse Attention", §4.1 PillarAttn
+ * and Fig. 7; SpecAttn, "SpecAttn: Co-Designing Sparse Attention with
+ * Self-Speculative Decoding", technical framework): one model drafts k tokens
+ * with attention restricted to a few critical KV blocks and verifies them with
+ * full attention.  The verification pass already computes the softmax
+ * probability of every cached token; its per-block mass, aggregated over the
+ * verify rows of one GQA group, picks the blocks the next k drafts read.
+ *
+ * Entry points:
+ *   sss_verify_attn  full causal attention of n_q = k+1 query tokens per
+ *                    request over the whole paged cache, plus per-block
+ *                    probability mass;
+ *   sss_block_topk   per (request, KV head) Top-N block list;
+ *   sss_draft_attn   single-query attention over the selected blocks plus a
+ *                    recent window;
+ *   sss_merge        log-sum-exp merge of split-KV partials.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument except `kv` itself and the host structs points to
+ *   DEVICE memory owned by the caller.  Inputs are read only; outputs must
+ *   not alias inputs or each other.  The library allocates nothing: callers
+ *   size the workspace with the matching *_workspace_size query.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *   enqueued asynchronously on it; the library never synchronises.
+ * - Arguments are validated on the host before anything is launched.  A
+ *   violated precondition returns SSS_ERR_INVALID_ARGUMENT or
+ *   SSS_ERR_UNSUPPORTED and launches nothing; sss_last_error() then holds a
+ *   message naming the argument.  SSS_ERR_HIP reports a failed launch.
+ *   Faults during execution surface at the caller's next synchronisation.
+ * - Device-resident values (seq_lens, budgets, selections) cannot be checked
+ *   on the host.  Kernels clamp every index they derive from them to the
+ *   buffers' stated sizes; a request whose seq_len exceeds
+ *   kv->max_seq_len, kv->max_pages_per_req * page_size, or falls below the
+ *   entry point's minimum gets NaN in its floating outputs.
+ * - Results are bitwise reproducible for equal arguments on one GPU.
+ * - Query head hq reads KV head hq / G with G = num_q_heads / num_kv_heads.
+ * - LSE values are natural-log log-sum-exp of the scaled logits.
+ */
+#ifndef SSS_H_
+#define SSS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSS_OK = 0,
+  SSS_ERR_INVALID_ARGUMENT = 1,
+  SSS_ERR_UNSUPPORTED = 2,
+  SSS_ERR_WORKSPACE_TOO_SMALL = 3,
+  SSS_ERR_HIP = 4
+} sss_status;
+
+typedef enum { SSS_F32 = 0, SSS_BF16 = 1 } sss_dtype;
+
+/*
+ * Paged KV cache (SparseSpec §4.2: the paged cache of PagedAttention).
+ *
+ * k, v        [num_pages][num_kv_heads][page_size][head_dim], dense, in
+ *             `dtype`; 16-byte aligned.  One (page, head) is a contiguous run
+ *             of page_size * head_dim elements.
+ * page_table  [batch][max_pages_per_req] int32: token t of request b lives in
+ *             page page_table[b][t / page_size], slot t % page_size.  Entries
+ *             past ceil(seq_lens[b] / page_size) are never read.
+ * seq_lens    [batch] int32: KV length of each request.  For verify it
+ *             counts the n_q new tokens, which occupy the last n_q positions.
+ * max_seq_len host-side upper bound of seq_lens, used to size grids.
+ *
+ * Supported: dtype F32 or BF16; head_dim 64 or 128; page_size >= 1;
+ * num_pages >= 1; max_pages_per_req >= ceil(max_seq_len / page_size).
+ */
+typedef struct {
+  const void* k;
+  const void* v;
+  int32_t dtype;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_pages_per_req;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int32_t max_seq_len;
+} sss_paged_kv;
+
+/*
+ * Verify attention with block importance.
+ *
+ * Definition (SparseSpec §4.1 and Fig. 7; SpecAttn technical framework):
+ * for request b, KV head h, query position i in [0, n_q) and group head g,
+ * row r = i*G + g at position pos = L_b - n_q + i attends to tokens
+ * t <= pos with logits s = sm_scale * <q, k_t>:
+ *     lse[b][i][hq] = log sum_{t<=pos} exp(s_t),
+ *     o[b][i][hq]   = sum_{t<=pos} exp(s_t - lse) v_t.
+ * The per-block importance is the probability mass the scored rows put on
+ * each block of `block_size` tokens, summed over the rows
+ * r >= score_row_start * G of the unit:
+ *     block_scores[b][h][j] = sum_r sum_{t in block j, t<=pos_r} exp(s_rt - lse_r).
+ * With score_row_start = 1 only the k draft positions are scored (the
+ * bonus row is skipped); 0 scores all k+1.  Blocks j >= ceil(L_b/block_size)
+ * (up to max_blocks) are written as 0.
+ *
+ * q     [batch][n_q][num_q_heads][head_dim] in kv->dtype, 16-byte aligned.
+ * o     same shape and dtype as q.
+ * lse   [batch][n_q][num_q_heads] float.
+ * block_scores [batch][num_kv_heads][max_blocks] float.
+ * num_splits  number of KV chunks for the longest request (0 = chosen by
+ *             the library); shorter requests use proportionally fewer.
+ * workspace   device scratch of at least sss_verify_workspace_size() bytes,
+ *             256-byte aligned; its contents on entry are irrelevant.
+ *
+ * Preconditions (host-checked): batch >= 0; 1 <= n_q <= 32;
+ * num_q_heads % num_kv_heads == 0; n_q * G <= 128; block_size >= 1;
+ * 0 <= score_row_start < n_q; max_blocks >= ceil(max_seq_len / block_size);
+ * max_seq_len >= n_q; num_splits >= 0.  Device-side:
+ * n_q <= seq_lens[b] <= max_seq_len.
+ * Path: BF16 caches with page_size and block_size multiples of 16 run the
+ * matrix-core (MFMA) kernel; every other supported case runs the vector-ALU
+ * kernel.  Both compute in fp32 and round o once to kv->dtype.
+ */
+sss_status sss_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch, int32_t n_q,
+                           int32_t num_q_heads, float sm_scale, int32_t block_size,
+                           int32_t score_row_start, int32_t num_splits, void* o, float* lse,
+                           float* block_scores, int32_t max_blocks, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sss_verify_attn needs for these arguments (0 on invalid
+ * arguments; call sss_last_error() to see why). */
+size_t sss_verify_workspace_size(const sss_paged_kv* kv, int32_t batch, int32_t n_q,
+                                 int32_t num_q_heads, int32_t block_size, int32_t max_blocks,
+                                 int32_t num_splits);
+
+/*
+ * Top-N block selection (SparseSpec §4.1: Top-K over the aggregated scores).
+ *
+ * For request b and KV head h with L = seq_lens[b] and window start
+ * ws = max(0, L - window) (ws = L when window == 0), the candidates are the
+ * blocks j < ceil(L/block_size) with j*block_size < ws.  The selection keeps
+ * N = min(budget[b], #candidates, max_sel) candidates, ranked by larger
+ * score first and lower index first among equal scores (-0.0 equals +0.0),
+ * and writes them in ascending order:
+ *     sel[b][h][0..N) ascending, sel[b][h][N..max_sel) = -1, sel_count[b][h] = N.
+ * Scores must not be NaN.
+ *
+ * block_scores [batch][num_kv_heads][max_blocks] float (fp32 compared
+ * exactly, so equal inputs give bit-identical selections);
+ * seq_lens [batch], budget [batch] int32 (budget < 0 counts as 0);
+ * sel [batch][num_kv_heads][max_sel] int32; sel_count [batch][num_kv_heads].
+ * Preconditions: block_size >= 1; window >= 0; max_sel >= 1;
+ * max_blocks >= 1.  Device-side: ceil(seq_lens[b]/block_size) <= max_blocks
+ * (blocks past max_blocks are ignored).
+ */
+sss_status sss_block_topk(const float* block_scores, int32_t batch, int32_t num_kv_heads,
+                          int32_t max_blocks, const int32_t* seq_lens, int32_t block_size,
+                          const int32_t* budget, int32_t window, int32_t* sel,
+                          int32_t* sel_count, int32_t max_sel, void* stream);
+
+/*
+ * Sparse draft attention (SpecAttn technical framework: drafting loads only
+ * the critical KV entries; SparseSpec §4.1/§4.2).
+ *
+ * One query per (request, query head) at position L-1 attends to
+ *     S = { t in block j : j in sel[b][h][0..sel_count), t < ws }  U  [ws, L)
+ * with ws = max(0, L - window) (ws = L when window == 0):
+ *     lse = log sum_{t in S} exp(s_t),  o = sum_{t in S} exp(s_t - lse) v_t.
+ * An empty S gives o = 0 and lse = -inf.  Entries of sel that are negative
+ * or past the sequence contribute no tokens; the listed entries must be
+ * distinct.  Their order does not matter.
+ *
+ * q, o [batch][1][num_q_heads][head_dim] in kv->dtype; lse [batch][1][num_q_heads].
+ * sel  [batch][num_kv_heads][max_sel] int32; sel_count [batch][num_kv_heads]
+ * (clamped to [0, max_sel]).
+ * num_splits number of chunks each unit's token list is cut into (0 = chosen
+ * by the library).
+ * Preconditions: num_q_heads % num_kv_heads == 0; G <= 128;
+ * block_size >= 1; window >= 0; max_sel >= 1; num_splits >= 0.
+ * Device-side: 1 <= seq_lens[b] <= max_seq_len.  Kernel choice as for
+ * sss_verify_attn.
+ */
+sss_status sss_draft_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
+                          int32_t num_q_heads, float sm_scale, int32_t block_size,
+                          const int32_t* sel, const int32_t* sel_count, int32_t max_sel,
+                          int32_t window, int32_t num_splits, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+size_t sss_draft_workspace_size(const sss_paged_kv* kv, int32_t batch, int32_t num_q_heads,
+                                int32_t block_size, int32_t max_sel, int32_t window,
+                                int32_t num_splits);
+
+/*
+ * Log-sum-exp merge of attention partials over disjoint KV subsets (the
+ * verification kernel keeps the log-sum-exp of the logits, SparseSpec §4.1,
+ * which is what makes partial results combinable):
+ *     lse[r] = log sum_s exp(lse_parts[s][r]),
+ *     o[r]   = sum_s exp(lse_parts[s][r] - lse[r]) * o_parts[s][r].
+ * Partials with lse -inf carry no weight; if every partial of a row is
+ * -inf, o = 0 and lse = -inf.
+ *
+ * o_parts [num_parts][rows][head_dim] float; lse_parts [num_parts][rows] float;
+ * o [rows][head_dim] in o_dtype (SSS_F32 or SSS_BF16); lse [rows] float (may
+ * be NULL).  Preconditions: num_parts >= 1; rows >= 0; 1 <= head_dim <= 1024.
+ */
+sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_parts, int32_t rows,
+                     int32_t head_dim, void* o, int32_t o_dtype, float* lse, void* stream);
+
+/* Static description of a status code. */
+const char* sss_status_string(sss_status status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* sss_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t sss_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSS_H_ */

@@ -1,0 +1,443 @@
+// C ABI of libsss: host-side validation, work planning and dispatch.  No
+// state survives a call except the per-thread error message.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "sss_common.h"
+
+namespace sss {
+int mfma_token_groups(int rows);  // attn_mfma.hip
+}
+
+namespace {
+
+using namespace sss;
+
+thread_local char g_err[512] = "";
+
+sss_status fail(sss_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sss_status ok() {
+  g_err[0] = '\0';
+  return SSS_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+long long lcm_ll(long long a, long long b) {
+  long long x = a, y = b;
+  while (y) {
+    const long long t = x % y;
+    x = y;
+    y = t;
+  }
+  return a / x * b;
+}
+
+// The library targets MI355X: 256 compute units, and the matrix-core kernels
+// keep up to 8 waves resident per compute unit.  Planning uses these fixed
+// figures so that the workspace query and the call always agree.
+constexpr long long kTargetWaves = 256 * 8;
+constexpr int kMinChunkTokens = 256;
+
+sss_status check_kv(const sss_paged_kv* kv, int batch) {
+  if (!kv) return fail(SSS_ERR_INVALID_ARGUMENT, "kv is NULL");
+  if (kv->dtype != SSS_F32 && kv->dtype != SSS_BF16)
+    return fail(SSS_ERR_UNSUPPORTED, "kv->dtype %d is neither SSS_F32 nor SSS_BF16", kv->dtype);
+  if (kv->head_dim != 64 && kv->head_dim != 128)
+    return fail(SSS_ERR_UNSUPPORTED, "kv->head_dim %d (supported: 64, 128)", kv->head_dim);
+  if (kv->page_size < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "kv->page_size %d < 1", kv->page_size);
+  if (kv->num_kv_heads < 1)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "kv->num_kv_heads %d < 1", kv->num_kv_heads);
+  if (kv->num_pages < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "kv->num_pages %d < 1", kv->num_pages);
+  if (kv->max_pages_per_req < 1)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "kv->max_pages_per_req %d < 1", kv->max_pages_per_req);
+  if (kv->max_seq_len < 1)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "kv->max_seq_len %d < 1", kv->max_seq_len);
+  if ((long long)kv->max_pages_per_req * kv->page_size < kv->max_seq_len)
+    return fail(SSS_ERR_INVALID_ARGUMENT,
+                "kv->max_pages_per_req * page_size = %lld < max_seq_len %d",
+                (long long)kv->max_pages_per_req * kv->page_size, kv->max_seq_len);
+  if (batch > 0) {
+    if (!kv->k || !kv->v) return fail(SSS_ERR_INVALID_ARGUMENT, "kv->k or kv->v is NULL");
+    if (!kv->page_table || !kv->seq_lens)
+      return fail(SSS_ERR_INVALID_ARGUMENT, "kv->page_table or kv->seq_lens is NULL");
+    if (!aligned(kv->k, 16) || !aligned(kv->v, 16))
+      return fail(SSS_ERR_INVALID_ARGUMENT, "kv->k and kv->v must be 16-byte aligned");
+    if (!aligned(kv->page_table, 4) || !aligned(kv->seq_lens, 4))
+      return fail(SSS_ERR_INVALID_ARGUMENT, "page_table and seq_lens must be 4-byte aligned");
+  }
+  return ok();
+}
+
+bool use_mfma(const sss_paged_kv* kv, int block_size) {
+  return kv->dtype == SSS_BF16 && kv->page_size % kSeg == 0 && block_size % kSeg == 0;
+}
+
+struct Plan {
+  bool mfma;
+  int rows, num_chunks, chunk;  // chunk: tokens (verify) or list entries (draft)
+  size_t ell_off, opart_off, lpart_off, bytes;
+};
+
+void layout(Plan& pl, long long units, int head_dim, long long ell_elems) {
+  size_t off = 0;
+  pl.ell_off = off;
+  off += align_up((size_t)ell_elems * 4, 256);
+  pl.opart_off = off;
+  pl.lpart_off = off;
+  if (pl.num_chunks > 1) {
+    off += align_up((size_t)units * pl.num_chunks * pl.rows * head_dim * 4, 256);
+    pl.lpart_off = off;
+    off += align_up((size_t)units * pl.num_chunks * pl.rows * 4, 256);
+  }
+  pl.bytes = off;
+}
+
+sss_status plan_verify(const sss_paged_kv* kv, int batch, int n_q, int hq, int block_size,
+                       int max_blocks, int num_splits, Plan& pl) {
+  sss_status st = check_kv(kv, batch);
+  if (st != SSS_OK) return st;
+  if (batch < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "batch %d < 0", batch);
+  if (n_q < 1 || n_q > 32) return fail(SSS_ERR_INVALID_ARGUMENT, "n_q %d outside [1, 32]", n_q);
+  if (hq < 1 || hq % kv->num_kv_heads != 0)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                hq, kv->num_kv_heads);
+  const int G = hq / kv->num_kv_heads;
+  if ((long long)n_q * G > 128)
+    return fail(SSS_ERR_UNSUPPORTED, "n_q * G = %lld rows per KV head exceeds 128", (long long)n_q * G);
+  if (block_size < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "block_size %d < 1", block_size);
+  if (kv->max_seq_len < n_q)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "kv->max_seq_len %d < n_q %d", kv->max_seq_len, n_q);
+  if (max_blocks < ceil_div(kv->max_seq_len, block_size))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "max_blocks %d < ceil(max_seq_len / block_size) = %d",
+                max_blocks, ceil_div(kv->max_seq_len, block_size));
+  if (num_splits < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "num_splits %d < 0", num_splits);
+
+  pl.mfma = use_mfma(kv, block_size);
+  pl.rows = n_q * G;
+  const long long units = (long long)batch * kv->num_kv_heads;
+  const int nwt = pl.mfma ? mfma_token_groups(pl.rows) : 1;
+  const int nwr = ceil_div(pl.rows, 32);
+  const long long align =
+      pl.mfma ? lcm_ll((long long)nwt * 32, (long long)nwt * block_size) : (long long)block_size;
+  const long long Lmax = kv->max_seq_len;
+  long long S = num_splits;
+  if (S == 0) {
+    if (pl.mfma) {
+      const long long wgs_target = kTargetWaves / ((long long)nwr * nwt);
+      S = units > 0 ? (wgs_target + units - 1) / units : 1;
+      const long long cap = (Lmax + kMinChunkTokens - 1) / kMinChunkTokens;
+      if (S > cap) S = cap;
+    } else {
+      S = 1;
+    }
+  }
+  if (S < 1) S = 1;
+  long long chunk = (Lmax + S - 1) / S;
+  chunk = (chunk + align - 1) / align * align;
+  if (chunk > (1LL << 30)) return fail(SSS_ERR_UNSUPPORTED, "chunk too large");
+  pl.chunk = (int)chunk;
+  pl.num_chunks = (int)((Lmax + chunk - 1) / chunk);
+  layout(pl, units, kv->head_dim, units * (long long)max_blocks * pl.rows);
+  return ok();
+}
+
+sss_status plan_draft(const sss_paged_kv* kv, int batch, int hq, int block_size, int max_sel,
+                      int window, int num_splits, Plan& pl) {
+  sss_status st = check_kv(kv, batch);
+  if (st != SSS_OK) return st;
+  if (batch < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "batch %d < 0", batch);
+  if (hq < 1 || hq % kv->num_kv_heads != 0)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                hq, kv->num_kv_heads);
+  const int G = hq / kv->num_kv_heads;
+  if (G > 128) return fail(SSS_ERR_UNSUPPORTED, "group size %d exceeds 128", G);
+  if (block_size < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "block_size %d < 1", block_size);
+  if (max_sel < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "max_sel %d < 1", max_sel);
+  if (window < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "window %d < 0", window);
+  if (num_splits < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "num_splits %d < 0", num_splits);
+
+  pl.mfma = use_mfma(kv, block_size);
+  pl.rows = G;
+  const long long units = (long long)batch * kv->num_kv_heads;
+  const int nwt = pl.mfma ? mfma_token_groups(G) : 1;
+  const int nwr = ceil_div(G, 32);
+  const long long Lmax = kv->max_seq_len;
+  const long long wtok = window > 0 ? (window < Lmax ? window : Lmax) : 0;
+  long long list_max, align;
+  if (pl.mfma) {
+    list_max = (long long)max_sel * (block_size / kSeg) + (wtok > 0 ? (wtok + kSeg - 1) / kSeg + 1 : 0);
+    align = 2LL * nwt;
+  } else {
+    list_max = (long long)max_sel * block_size + wtok;
+    align = 1;
+  }
+  if (list_max < 1) list_max = 1;
+  long long S = num_splits;
+  if (S == 0) {
+    if (pl.mfma) {
+      const long long wgs_target = kTargetWaves / ((long long)nwr * nwt);
+      S = units > 0 ? (wgs_target + units - 1) / units : 1;
+    } else {
+      S = 1;
+    }
+  }
+  if (S < 1) S = 1;
+  long long chunk = (list_max + S - 1) / S;
+  chunk = (chunk + align - 1) / align * align;
+  if (chunk > (1LL << 30)) return fail(SSS_ERR_UNSUPPORTED, "chunk too large");
+  pl.chunk = (int)chunk;
+  pl.num_chunks = (int)((list_max + chunk - 1) / chunk);
+  layout(pl, units, kv->head_dim, 0);
+  return ok();
+}
+
+AttnParams base_params(const sss_paged_kv* kv, const void* q, int batch, int n_q, int hq,
+                       float sm_scale, const Plan& pl) {
+  AttnParams p = {};
+  p.k = kv->k;
+  p.v = kv->v;
+  p.page_table = kv->page_table;
+  p.seq_lens = kv->seq_lens;
+  p.num_pages = kv->num_pages;
+  p.page_size = kv->page_size;
+  p.num_kv_heads = kv->num_kv_heads;
+  p.head_dim = kv->head_dim;
+  p.max_pages = kv->max_pages_per_req;
+  p.max_seq_len = kv->max_seq_len;
+  p.q = q;
+  p.batch = batch;
+  p.n_q = n_q;
+  p.num_q_heads = hq;
+  p.group = hq / kv->num_kv_heads;
+  p.rows = pl.rows;
+  p.scale_log2 = sm_scale * kLog2e;
+  p.num_chunks = pl.num_chunks;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sss_status_string(sss_status status) {
+  switch (status) {
+    case SSS_OK: return "SSS_OK";
+    case SSS_ERR_INVALID_ARGUMENT: return "SSS_ERR_INVALID_ARGUMENT";
+    case SSS_ERR_UNSUPPORTED: return "SSS_ERR_UNSUPPORTED";
+    case SSS_ERR_WORKSPACE_TOO_SMALL: return "SSS_ERR_WORKSPACE_TOO_SMALL";
+    case SSS_ERR_HIP: return "SSS_ERR_HIP";
+  }
+  return "unknown sss_status";
+}
+
+const char* sss_last_error(void) { return g_err; }
+
+int32_t sss_version(void) { return 100; }
+
+size_t sss_verify_workspace_size(const sss_paged_kv* kv, int32_t batch, int32_t n_q,
+                                 int32_t num_q_heads, int32_t block_size, int32_t max_blocks,
+                                 int32_t num_splits) {
+  Plan pl;
+  if (plan_verify(kv, batch, n_q, num_q_heads, block_size, max_blocks, num_splits, pl) != SSS_OK)
+    return 0;
+  return pl.bytes;
+}
+
+size_t sss_draft_workspace_size(const sss_paged_kv* kv, int32_t batch, int32_t num_q_heads,
+                                int32_t block_size, int32_t max_sel, int32_t window,
+                                int32_t num_splits) {
+  Plan pl;
+  if (plan_draft(kv, batch, num_q_heads, block_size, max_sel, window, num_splits, pl) != SSS_OK)
+    return 0;
+  return pl.bytes;
+}
+
+sss_status sss_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch, int32_t n_q,
+                           int32_t num_q_heads, float sm_scale, int32_t block_size,
+                           int32_t score_row_start, int32_t num_splits, void* o, float* lse,
+                           float* block_scores, int32_t max_blocks, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  Plan pl;
+  sss_status st = plan_verify(kv, batch, n_q, num_q_heads, block_size, max_blocks, num_splits, pl);
+  if (st != SSS_OK) return st;
+  if (!std::isfinite(sm_scale)) return fail(SSS_ERR_INVALID_ARGUMENT, "sm_scale is not finite");
+  if (score_row_start < 0 || score_row_start >= n_q)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "score_row_start %d outside [0, n_q)", score_row_start);
+  if (batch == 0) return ok();
+  if (!q || !o || !lse || !block_scores)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "q, o, lse and block_scores must be non-NULL");
+  if (!aligned(q, 16) || !aligned(o, 16))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "q and o must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(block_scores, 4))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "lse and block_scores must be 4-byte aligned");
+  if (workspace_bytes < pl.bytes)
+    return fail(SSS_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace_bytes,
+                pl.bytes);
+  if (pl.bytes > 0 && (!workspace || !aligned(workspace, 256)))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  AttnParams p = base_params(kv, q, batch, n_q, num_q_heads, sm_scale, pl);
+  p.chunk_tokens = pl.chunk;
+  p.chunk_items = 0;
+  p.o_part = reinterpret_cast<float*>(ws + pl.opart_off);
+  p.lse_part = reinterpret_cast<float*>(ws + pl.lpart_off);
+  p.o = o;
+  p.lse = lse;
+  p.block_size = block_size;
+  p.max_blocks = max_blocks;
+  p.ell = reinterpret_cast<float*>(ws + pl.ell_off);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = pl.mfma ? launch_verify_mfma(p, s) : launch_attn_simple(p, kv->dtype, false, s);
+  if (e != hipSuccess) return fail(SSS_ERR_HIP, "verify launch: %s", hipGetErrorString(e));
+
+  FinalizeParams f = {};
+  f.batch = batch;
+  f.num_kv_heads = kv->num_kv_heads;
+  f.n_q = n_q;
+  f.group = p.group;
+  f.rows = pl.rows;
+  f.head_dim = kv->head_dim;
+  f.num_chunks = pl.num_chunks;
+  f.chunk_tokens = pl.chunk;
+  f.dtype = kv->dtype;
+  f.seq_lens = kv->seq_lens;
+  f.max_seq_len = kv->max_seq_len;
+  f.max_pages = kv->max_pages_per_req;
+  f.page_size = kv->page_size;
+  f.o_part = p.o_part;
+  f.lse_part = p.lse_part;
+  f.o = o;
+  f.lse = lse;
+  f.ell = p.ell;
+  f.block_scores = block_scores;
+  f.block_size = block_size;
+  f.max_blocks = max_blocks;
+  f.score_row_start = score_row_start;
+  e = launch_finalize(f, s);
+  if (e != hipSuccess) return fail(SSS_ERR_HIP, "verify finalize launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sss_status sss_block_topk(const float* block_scores, int32_t batch, int32_t num_kv_heads,
+                          int32_t max_blocks, const int32_t* seq_lens, int32_t block_size,
+                          const int32_t* budget, int32_t window, int32_t* sel,
+                          int32_t* sel_count, int32_t max_sel, void* stream) {
+  if (batch < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "batch %d < 0", batch);
+  if (num_kv_heads < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "num_kv_heads %d < 1", num_kv_heads);
+  if (max_blocks < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "max_blocks %d < 1", max_blocks);
+  if (block_size < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "block_size %d < 1", block_size);
+  if (window < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "window %d < 0", window);
+  if (max_sel < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "max_sel %d < 1", max_sel);
+  if (batch == 0) return ok();
+  if (!block_scores || !seq_lens || !budget || !sel || !sel_count)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(block_scores, 4) || !aligned(seq_lens, 4) || !aligned(budget, 4) ||
+      !aligned(sel, 4) || !aligned(sel_count, 4))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "arrays must be 4-byte aligned");
+  hipError_t e = launch_topk(block_scores, batch, num_kv_heads, max_blocks, seq_lens, block_size,
+                             budget, window, sel, sel_count, max_sel,
+                             reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSS_ERR_HIP, "topk launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sss_status sss_draft_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
+                          int32_t num_q_heads, float sm_scale, int32_t block_size,
+                          const int32_t* sel, const int32_t* sel_count, int32_t max_sel,
+                          int32_t window, int32_t num_splits, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  sss_status st = plan_draft(kv, batch, num_q_heads, block_size, max_sel, window, num_splits, pl);
+  if (st != SSS_OK) return st;
+  if (!std::isfinite(sm_scale)) return fail(SSS_ERR_INVALID_ARGUMENT, "sm_scale is not finite");
+  if (batch == 0) return ok();
+  if (!q || !o || !lse || !sel || !sel_count)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "q, o, lse, sel and sel_count must be non-NULL");
+  if (!aligned(q, 16) || !aligned(o, 16))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "q and o must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(sel, 4) || !aligned(sel_count, 4))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "lse, sel and sel_count must be 4-byte aligned");
+  if (workspace_bytes < pl.bytes)
+    return fail(SSS_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace_bytes,
+                pl.bytes);
+  if (pl.bytes > 0 && (!workspace || !aligned(workspace, 256)))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  AttnParams p = base_params(kv, q, batch, 1, num_q_heads, sm_scale, pl);
+  p.chunk_tokens = 0;
+  p.chunk_items = pl.chunk;
+  p.o_part = reinterpret_cast<float*>(ws + pl.opart_off);
+  p.lse_part = reinterpret_cast<float*>(ws + pl.lpart_off);
+  p.o = o;
+  p.lse = lse;
+  p.block_size = block_size;
+  p.sel = sel;
+  p.sel_count = sel_count;
+  p.max_sel = max_sel;
+  p.window = window;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = pl.mfma ? launch_draft_mfma(p, s) : launch_attn_simple(p, kv->dtype, true, s);
+  if (e != hipSuccess) return fail(SSS_ERR_HIP, "draft launch: %s", hipGetErrorString(e));
+  if (pl.num_chunks > 1) {
+    FinalizeParams f = {};
+    f.batch = batch;
+    f.num_kv_heads = kv->num_kv_heads;
+    f.n_q = 1;
+    f.group = p.group;
+    f.rows = pl.rows;
+    f.head_dim = kv->head_dim;
+    f.num_chunks = pl.num_chunks;
+    f.chunk_items = pl.chunk;
+    f.dtype = kv->dtype;
+    f.seq_lens = kv->seq_lens;
+    f.max_seq_len = kv->max_seq_len;
+    f.max_pages = kv->max_pages_per_req;
+    f.page_size = kv->page_size;
+    f.o_part = p.o_part;
+    f.lse_part = p.lse_part;
+    f.o = o;
+    f.lse = lse;
+    f.ell = nullptr;
+    f.block_size = block_size;
+    f.sel_count = sel_count;
+    f.max_sel = max_sel;
+    f.window = window;
+    f.draft = 1;
+    f.simple_list = pl.mfma ? 0 : 1;
+    e = launch_finalize(f, s);
+    if (e != hipSuccess) return fail(SSS_ERR_HIP, "draft finalize launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_parts, int32_t rows,
+                     int32_t head_dim, void* o, int32_t o_dtype, float* lse, void* stream) {
+  if (num_parts < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "num_parts %d < 1", num_parts);
+  if (rows < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "rows %d < 0", rows);
+  if (head_dim < 1 || head_dim > 1024)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "head_dim %d outside [1, 1024]", head_dim);
+  if (o_dtype != SSS_F32 && o_dtype != SSS_BF16)
+    return fail(SSS_ERR_UNSUPPORTED, "o_dtype %d is neither SSS_F32 nor SSS_BF16", o_dtype);
+  if (rows == 0) return ok();
+  if (!o_parts || !lse_parts || !o) return fail(SSS_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(o_parts, 4) || !aligned(lse_parts, 4) || !aligned(o, o_dtype == SSS_F32 ? 4 : 2) ||
+      (lse && !aligned(lse, 4)))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "misaligned array");
+  hipError_t e = launch_merge(o_parts, lse_parts, num_parts, rows, head_dim, o, o_dtype, lse,
+                              reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSS_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,525 @@
+// Matrix-core (MFMA) paged attention for gfx950: verify (causal, k+1 query
+// positions x GQA group rows, per-block probability mass) and sparse draft
+// (one query over selected blocks plus the recent window).
+//
+// Work decomposition.  A unit is one (request, KV head).  Its rows are the
+// n_q * G query rows sharing that KV head, padded to 32-row tiles.  A
+// workgroup handles one chunk of one unit and holds NWT token groups of NWR
+// waves; wave (tg, rt) owns row tile rt of token group tg.  The waves of a
+// token group load each 32-token KV tile from HBM once (16-byte coalesced
+// loads of contiguous page runs) into LDS and all of them read it, so K and
+// V are fetched once for every row of the unit.  Token groups cover
+// contiguous sub-ranges of the chunk and are merged through LDS at the end.
+//
+// Per tile, with 32x32x16 bf16 MFMAs:
+//   S^T = K * Q^T   (M = 32 tokens, N = 32 rows, K = head_dim)
+//   O^T += V^T * P^T (M = 32 head dims, N = 32 rows, K = 16 tokens)
+// Both accumulators put row (lane % 32) in lane, so the online-softmax
+// rescale is lane-local and a row is shared by the lane pair (l, l ^ 32).
+// V is stored transposed in LDS in the token order that makes P^T the
+// lane's own softmax values (no shuffles between the two MFMAs).
+//
+// The kernel follows SparseSpec §4.1 (PillarAttn): the verify pass keeps,
+// next to the running LSE, the log of each KV block's probability mass
+// (ell, log2 domain, in the frame of the row max at that time), so the exact
+// per-block scores can be rematerialised once the row's final LSE is known.
+#include "sss_common.h"
+
+namespace sss {
+namespace {
+
+template <int D>
+struct Geo {
+  static constexpr int KS = D / 16;             // QK MFMA k-steps
+  static constexpr int MT = D / 32;             // PV M-tiles
+  static constexpr int CPT = D / 8;             // 16-byte chunks per token row
+  static constexpr int K_STRIDE = D * 2 + 16;   // LDS bytes per K row (padded)
+  static constexpr int K_BYTES = 32 * K_STRIDE;
+  static constexpr int V_BYTES = D * 64;        // V^T: D rows of 32 positions
+  static constexpr int GROUP_BYTES = K_BYTES + V_BYTES;
+  static constexpr int K_CHUNKS = 32 * CPT;
+  static constexpr int V_UNITS = 8 * CPT;       // 4 positions x one 16-byte chunk
+};
+
+struct Seg {
+  long long base;  // element offset of token t0 of this (page, head) run
+  int t0, lo, hi;  // 16-aligned start; valid tokens are [lo, hi)
+};
+
+__device__ __forceinline__ Seg empty_seg() {
+  Seg s;
+  s.base = 0;
+  s.t0 = 0;
+  s.lo = 0;
+  s.hi = 0;
+  return s;
+}
+
+__device__ __forceinline__ void locate(const AttnParams& p, int b, int h, Seg& s, int& bad) {
+  if (s.lo >= s.hi) return;
+  int pg = p.page_table[(long long)b * p.max_pages + s.t0 / p.page_size];
+  if (pg < 0 || pg >= p.num_pages) {
+    bad = 1;
+    pg = 0;
+  }
+  s.base = (((long long)pg * p.num_kv_heads + h) * p.page_size + (s.t0 % p.page_size)) *
+           (long long)p.head_dim;
+}
+
+// Segment s_idx (16 tokens) of a verify unit.
+__device__ __forceinline__ Seg verify_seg(const AttnParams& p, int b, int h, int s_idx, int L,
+                                          int& bad) {
+  Seg s;
+  s.t0 = s_idx * kSeg;
+  s.lo = s.t0;
+  s.hi = min(s.t0 + kSeg, L);
+  s.base = 0;
+  locate(p, b, h, s, bad);
+  return s;
+}
+
+// Entry k of a draft unit's segment list: first the segments of the selected
+// blocks (only their tokens before the window start), then the window.
+__device__ __forceinline__ Seg draft_seg(const AttnParams& p, int b, int h, int k, int nsel,
+                                         int L, int ws, int& bad) {
+  Seg s;
+  s.base = 0;
+  const int spb = p.block_size / kSeg;
+  if (k < nsel * spb) {
+    const int j = p.sel[((long long)b * p.num_kv_heads + h) * p.max_sel + k / spb];
+    const int nblk_ws = ceil_div(ws, p.block_size);
+    if (j < 0 || j >= nblk_ws) {
+      s.t0 = s.lo = s.hi = 0;
+    } else {
+      s.t0 = j * p.block_size + kSeg * (k % spb);
+      s.lo = s.t0;
+      s.hi = min(s.t0 + kSeg, ws);
+    }
+  } else {
+    const int w0 = (ws / kSeg) * kSeg;
+    s.t0 = w0 + kSeg * (k - nsel * spb);
+    s.lo = max(s.t0, ws);
+    s.hi = min(s.t0 + kSeg, L);
+  }
+  locate(p, b, h, s, bad);
+  return s;
+}
+
+// Swizzle of the 16-byte quads of a V^T row, chosen so that both the
+// transposing writes and the MFMA operand reads spread over the LDS banks.
+__device__ __forceinline__ int vq_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
+
+// Position p (0..31) of the V^T tile holds tile token tau(p): within each 16,
+// positions 4..7 and 8..11 are exchanged.  This is the K-order in which a
+// lane's own S^T accumulator values form the P^T operand of the PV MFMA.
+__device__ __forceinline__ int tau_group(int g4) {  // group of 4 positions -> group of 4 tokens
+  const int w = g4 & 3;
+  return (g4 & ~3) | (w == 1 ? 2 : (w == 2 ? 1 : w));
+}
+
+template <int D, int NWR>
+struct TileRegs {
+  static constexpr int NL = 64 * NWR;
+  static constexpr int KJ = (Geo<D>::K_CHUNKS + NL - 1) / NL;
+  static constexpr int VJ = (Geo<D>::V_UNITS + NL - 1) / NL;
+  bf16x8 k[KJ];
+  bf16x8 v[VJ][4];
+};
+
+template <int D, int NWR>
+__device__ __forceinline__ void load_tile(TileRegs<D, NWR>& r, const bf16* __restrict__ kc,
+                                          const bf16* __restrict__ vc, const Seg& sa,
+                                          const Seg& sb, int lig) {
+  typedef TileRegs<D, NWR> TR;
+  typedef Geo<D> G;
+  const bf16x8 zero = {};
+#pragma unroll
+  for (int j = 0; j < TR::KJ; ++j) {
+    const int ci = lig + TR::NL * j;
+    const int m = ci / G::CPT, c = ci % G::CPT;
+    const Seg& s = (m < kSeg) ? sa : sb;
+    const int t = s.t0 + (m % kSeg);
+    r.k[j] = zero;
+    if (ci < G::K_CHUNKS && t >= s.lo && t < s.hi)
+      r.k[j] = *reinterpret_cast<const bf16x8*>(kc + s.base + (long long)(m % kSeg) * D + 8 * c);
+  }
+#pragma unroll
+  for (int j = 0; j < TR::VJ; ++j) {
+    const int ui = lig + TR::NL * j;
+    const int g4 = ui / G::CPT, c = ui % G::CPT;
+    const int tok0 = 4 * tau_group(g4 & 7);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = tok0 + e;
+      const Seg& s = (m < kSeg) ? sa : sb;
+      const int t = s.t0 + (m % kSeg);
+      r.v[j][e] = zero;
+      if (ui < G::V_UNITS && t >= s.lo && t < s.hi)
+        r.v[j][e] =
+            *reinterpret_cast<const bf16x8*>(vc + s.base + (long long)(m % kSeg) * D + 8 * c);
+    }
+  }
+}
+
+template <int D, int NWR>
+__device__ __forceinline__ void store_tile(const TileRegs<D, NWR>& r, char* grp, int lig) {
+  typedef TileRegs<D, NWR> TR;
+  typedef Geo<D> G;
+#pragma unroll
+  for (int j = 0; j < TR::KJ; ++j) {
+    const int ci = lig + TR::NL * j;
+    if (ci < G::K_CHUNKS) {
+      const int m = ci / G::CPT, c = ci % G::CPT;
+      *reinterpret_cast<bf16x8*>(grp + m * G::K_STRIDE + 16 * c) = r.k[j];
+    }
+  }
+  char* vt = grp + G::K_BYTES;
+#pragma unroll
+  for (int j = 0; j < TR::VJ; ++j) {
+    const int ui = lig + TR::NL * j;
+    if (ui < G::V_UNITS) {
+      const int g4 = ui / G::CPT, c = ui % G::CPT;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const int d = 8 * c + dd;
+        bf16x4 w;
+        w[0] = r.v[j][0][dd];
+        w[1] = r.v[j][1][dd];
+        w[2] = r.v[j][2][dd];
+        w[3] = r.v[j][3][dd];
+        *reinterpret_cast<bf16x4*>(vt + d * 64 + 16 * ((g4 >> 1) ^ vq_swz(d)) + 8 * (g4 & 1)) = w;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+template <int D, int NWR, int NWT, bool DRAFT>
+__global__ void __launch_bounds__(64 * NWR * NWT)
+    attn_mfma_kernel(AttnParams p) {
+  typedef Geo<D> G;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int u = blockIdx.x / p.num_chunks;
+  const int c = blockIdx.x % p.num_chunks;
+  const int b = u / p.num_kv_heads, h = u % p.num_kv_heads;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int rt = w % NWR, tg = w / NWR;
+  const int lig = rt * 64 + lane;
+  const int hl = lane >> 5;   // half of the wave: K-half of operands
+  const int rl = lane & 31;   // row within the tile
+  const int R = p.rows;
+  const int r = rt * 32 + rl;  // unit row of this lane
+  const bool row_ok = r < R;
+  const int iq = row_ok ? r / p.group : 0;
+  const int hq = h * p.group + (row_ok ? r % p.group : 0);
+
+  const int L = p.seq_lens[b];
+  const int minL = DRAFT ? 1 : p.n_q;
+  const bool unit_ok =
+      L >= minL && L <= p.max_seq_len && (long long)L <= (long long)p.max_pages * p.page_size;
+  const bool final_out = p.num_chunks == 1;
+  if (!unit_ok) {
+    if (final_out && tg == 0 && row_ok) {
+      bf16* o = reinterpret_cast<bf16*>(p.o);
+      const long long orow = ((long long)b * p.n_q + iq) * p.num_q_heads + hq;
+      for (int d = hl; d < D; d += 2) o[orow * D + d] = from_f32<bf16>(qnan());
+      if (hl == 0) p.lse[orow] = qnan();
+    }
+    return;
+  }
+
+  // ---- this workgroup's segment range, split among token groups ----
+  int seg_lo, seg_hi, nsel = 0, ws = L;
+  if (!DRAFT) {
+    const int t_lo = c * p.chunk_tokens;
+    if (t_lo >= L) return;  // chunk past this request's length
+    const int t_hi = min(t_lo + p.chunk_tokens, L);
+    seg_lo = t_lo / kSeg;
+    seg_hi = ceil_div(t_hi, kSeg);
+  } else {
+    ws = window_start(L, p.window);
+    nsel = p.sel_count[(long long)b * p.num_kv_heads + h];
+    nsel = nsel < 0 ? 0 : (nsel > p.max_sel ? p.max_sel : nsel);
+    const int nseg = draft_list_len_mfma(nsel, p.block_size, L, ws);
+    seg_lo = c * p.chunk_items;
+    if (seg_lo >= nseg && c > 0) return;
+    seg_hi = min(seg_lo + p.chunk_items, nseg);
+  }
+  const int per_group = (DRAFT ? p.chunk_items : p.chunk_tokens / kSeg) / NWT;
+  const int g_lo = min(seg_lo + tg * per_group, seg_hi);
+  const int g_hi = min(g_lo + per_group, seg_hi);
+  const int n_tiles = ceil_div(min(per_group, seg_hi - seg_lo), 2);  // group 0 has the most
+
+  const bf16* __restrict__ kc = reinterpret_cast<const bf16*>(p.k);
+  const bf16* __restrict__ vc = reinterpret_cast<const bf16*>(p.v);
+  char* grp = smem + tg * G::GROUP_BYTES;
+
+  // ---- Q^T operand of this lane's row ----
+  bf16x8 qv[G::KS];
+  {
+    const bf16* q = reinterpret_cast<const bf16*>(p.q) +
+                    (((long long)b * p.n_q + iq) * p.num_q_heads + hq) * D + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+      bf16x8 z = {};
+      qv[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(q + 16 * ks) : z;
+    }
+  }
+  const int pos_r = DRAFT ? (L - 1) : (L - p.n_q + iq);
+
+  f32x16 oacc[G::MT];
+#pragma unroll
+  for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[mt][i] = 0.f;
+  float m_run = neg_inf(), l_run = 0.f, blk_run = 0.f;
+  int bad = 0;
+
+  auto seg_at = [&](int k) -> Seg {
+    if (k >= g_hi) return empty_seg();
+    if (DRAFT) return draft_seg(p, b, h, k, nsel, L, ws, bad);
+    return verify_seg(p, b, h, k, L, bad);
+  };
+
+  TileRegs<D, NWR> regs;
+  Seg sa = seg_at(g_lo), sb = seg_at(g_lo + 1);
+  load_tile<D, NWR>(regs, kc, vc, sa, sb, lig);
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int k0 = g_lo + 2 * t;
+    const bool tile_live = k0 < g_hi;
+    const Seg ca = sa, cb = sb;
+    store_tile<D, NWR>(regs, grp, lig);
+    __syncthreads();
+    if (t + 1 < n_tiles) {
+      sa = seg_at(k0 + 2);
+      sb = seg_at(k0 + 3);
+      load_tile<D, NWR>(regs, kc, vc, sa, sb, lig);
+    }
+    if (tile_live) {
+      // S^T = K Q^T
+      f32x16 sacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) {
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(grp + rl * G::K_STRIDE + 32 * ks + 16 * hl);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[ks], sacc, 0, 0, 0);
+      }
+      // masked online softmax (log2 domain)
+      float s[16];
+      float mx = neg_inf();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = (i >> 2) * 8 + 4 * hl + (i & 3);
+        const Seg& sg = (m < kSeg) ? ca : cb;
+        const int tok = sg.t0 + (m % kSeg);
+        const bool ok = tok >= sg.lo && tok < sg.hi && tok <= pos_r;
+        s[i] = ok ? sacc[i] * p.scale_log2 : neg_inf();
+        mx = fmaxf(mx, s[i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float pr[16];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pr[i] = fast_exp2(s[i] - m_use);
+        psum += pr[i];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
+      // O^T += V^T P^T
+      char* vt = grp + G::K_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[j] = static_cast<bf16>(pr[8 * kk + j]);
+        const int qd = 2 * kk + hl;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) {
+          const int d = 32 * mt + rl;
+          const bf16x8 va =
+              *reinterpret_cast<const bf16x8*>(vt + d * 64 + 16 * (qd ^ vq_swz(d)));
+          oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[mt], 0, 0, 0);
+        }
+      }
+      if (!DRAFT) {
+        // per-block log mass of this row, frame m_use
+        const int bs = p.block_size;
+        float* ell = p.ell + (long long)u * p.max_blocks * R;
+        if (bs == kSeg) {
+          float a = 0.f, bb = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a += pr[i];
+#pragma unroll
+          for (int i = 8; i < 16; ++i) bb += pr[i];
+          a += __shfl_xor(a, 32);
+          bb += __shfl_xor(bb, 32);
+          const Seg& mine = hl ? cb : ca;
+          if (row_ok && mine.lo < mine.hi)
+            ell[(long long)(mine.t0 / kSeg) * R + r] = m_use + fast_log2(hl ? bb : a);
+        } else {
+          blk_run = blk_run * alpha + psum;
+          const int tile_end = ca.t0 + 2 * kSeg;
+          const bool last = (tile_end % bs == 0) || (k0 + 2 >= g_hi);
+          if (last) {
+            const float tot = blk_run + __shfl_xor(blk_run, 32);
+            if (row_ok && hl == 0) ell[(long long)(ca.t0 / bs) * R + r] = m_use + fast_log2(tot);
+            blk_run = 0.f;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- combine the lane pair, then the token groups ----
+  l_run += __shfl_xor(l_run, 32);
+  bad = __syncthreads_or(bad);
+  if (NWT > 1) {
+    float* red = reinterpret_cast<float*>(smem);  // [NWT-1][NWR][32][D]
+    float* ml = red + (NWT - 1) * NWR * 32 * D;   // [NWT][NWR][32] max, then sum
+    if (hl == 0) {
+      ml[(tg * NWR + rt) * 32 + rl] = m_run;
+      ml[NWT * NWR * 32 + (tg * NWR + rt) * 32 + rl] = l_run;
+    }
+    if (tg > 0) {
+      float* dst = red + (((tg - 1) * NWR + rt) * 32 + rl) * D;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = oacc[mt][4 * q4 + e];
+          *reinterpret_cast<f32x4*>(dst + 32 * mt + 8 * q4 + 4 * hl) = v4;
+        }
+    }
+    __syncthreads();
+    if (tg > 0) return;
+    float mg = m_run;
+#pragma unroll
+    for (int g = 1; g < NWT; ++g) mg = fmaxf(mg, ml[(g * NWR + rt) * 32 + rl]);
+    const float mu = (mg == neg_inf()) ? 0.f : mg;
+    const float a0 = fast_exp2(m_run - mu);
+    float lsum = l_run * a0;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[mt][i] *= a0;
+#pragma unroll
+    for (int g = 1; g < NWT; ++g) {
+      const float ag = fast_exp2(ml[(g * NWR + rt) * 32 + rl] - mu);
+      lsum += ag * ml[NWT * NWR * 32 + (g * NWR + rt) * 32 + rl];
+      const float* src = red + (((g - 1) * NWR + rt) * 32 + rl) * D;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(src + 32 * mt + 8 * q4 + 4 * hl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[mt][4 * q4 + e] += ag * v4[e];
+        }
+    }
+    m_run = mg;
+    l_run = lsum;
+  }
+  if (!row_ok) return;
+
+  const bool empty = !(l_run > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_run;
+  const float lse2 = bad ? qnan() : (empty ? neg_inf() : m_run + fast_log2(l_run));
+  const float poison = bad ? qnan() : 1.f;
+  if (final_out) {
+    bf16* o = reinterpret_cast<bf16*>(p.o);
+    const long long orow = ((long long)b * p.n_q + iq) * p.num_q_heads + hq;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = from_f32<bf16>(oacc[mt][4 * q4 + e] * inv * poison);
+        *reinterpret_cast<bf16x4*>(o + orow * D + 32 * mt + 8 * q4 + 4 * hl) = v4;
+      }
+    if (hl == 0) p.lse[orow] = lse2 * kLn2;
+  } else {
+    const long long prow = ((long long)u * p.num_chunks + c) * R + r;
+    float* op = p.o_part + prow * D;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = oacc[mt][4 * q4 + e] * inv * poison;
+        *reinterpret_cast<f32x4*>(op + 32 * mt + 8 * q4 + 4 * hl) = v4;
+      }
+    if (hl == 0) p.lse_part[prow] = lse2;
+  }
+}
+
+template <int D, int NWR, int NWT, bool DRAFT>
+hipError_t launch_cfg(const AttnParams& p, hipStream_t s) {
+  typedef Geo<D> G;
+  const size_t tiles = (size_t)NWT * G::GROUP_BYTES;
+  const size_t merge = NWT > 1 ? ((size_t)(NWT - 1) * NWR * 32 * D + 2 * NWT * NWR * 32) * 4 : 0;
+  const size_t smem = tiles > merge ? tiles : merge;
+  const unsigned grid = (unsigned)((long long)p.batch * p.num_kv_heads * p.num_chunks);
+  if (grid == 0) return hipSuccess;
+  // dynamic LDS above 64 KiB must be opted into (once per instantiation)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&attn_mfma_kernel<D, NWR, NWT, DRAFT>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NWR, NWT, DRAFT>), dim3(grid), dim3(64 * NWR * NWT),
+                     smem, s, p);
+  return hipGetLastError();
+}
+
+template <bool DRAFT>
+hipError_t dispatch(const AttnParams& p, hipStream_t s) {
+  const int nwr = ceil_div(p.rows, 32);
+  if (p.head_dim == 128) {
+    switch (nwr) {
+      case 1: return launch_cfg<128, 1, 4, DRAFT>(p, s);
+      case 2: return launch_cfg<128, 2, 2, DRAFT>(p, s);
+      case 3: return launch_cfg<128, 3, 1, DRAFT>(p, s);
+      case 4: return launch_cfg<128, 4, 1, DRAFT>(p, s);
+    }
+  } else if (p.head_dim == 64) {
+    switch (nwr) {
+      case 1: return launch_cfg<64, 1, 4, DRAFT>(p, s);
+      case 2: return launch_cfg<64, 2, 2, DRAFT>(p, s);
+      case 3: return launch_cfg<64, 3, 1, DRAFT>(p, s);
+      case 4: return launch_cfg<64, 4, 1, DRAFT>(p, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// Token groups per workgroup for a given row count (must match dispatch).
+int mfma_token_groups(int rows) {
+  const int nwr = ceil_div(rows, 32);
+  return nwr == 1 ? 4 : (nwr == 2 ? 2 : 1);
+}
+
+hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s) { return dispatch<false>(p, s); }
+hipError_t launch_draft_mfma(const AttnParams& p, hipStream_t s) { return dispatch<true>(p, s); }
+
+}  // namespace sss

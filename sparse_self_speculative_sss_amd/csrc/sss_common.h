@@ -1,0 +1,124 @@
+// Internal definitions shared by the HIP sources of libsss (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sss.h"
+
+namespace sss {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kSeg = 16;  // tokens per segment of the matrix-core path
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+__device__ __forceinline__ float qnan() { return __builtin_nanf(""); }
+
+// Window start: first token of the recent window; L when there is no window.
+__host__ __device__ __forceinline__ int window_start(int L, int window) {
+  if (window <= 0) return L;
+  return L - window > 0 ? L - window : 0;
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ __forceinline__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Everything an attention launch needs.  One "unit" is a (request, KV head)
+// pair; its rows are the n_q * G query rows that share the KV head
+// (row r = i * G + g).  Logits are kept in the log2 domain internally
+// (scale_log2 = sm_scale * log2(e)); outputs use natural logs.
+struct AttnParams {
+  // paged cache
+  const void* k;
+  const void* v;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int32_t num_pages, page_size, num_kv_heads, head_dim, max_pages, max_seq_len;
+  // queries / rows
+  const void* q;  // [B][n_q][Hq][d]
+  int32_t batch, n_q, num_q_heads, group, rows;
+  float scale_log2;
+  // split-KV: `num_chunks` chunks per unit (grid dimension); verify chunks
+  // hold `chunk_tokens` tokens, draft chunks `chunk_items` list entries
+  int32_t num_chunks, chunk_tokens, chunk_items;
+  float* o_part;    // [U][num_chunks][rows][d] normalised partial O
+  float* lse_part;  // [U][num_chunks][rows]   log2-domain partial LSE
+  // final outputs (written directly when num_chunks == 1)
+  void* o;
+  float* lse;
+  // verify: block importance partials, log2 domain, [U][max_blocks][rows]
+  int32_t block_size, max_blocks;
+  float* ell;
+  // draft
+  const int32_t* sel;
+  const int32_t* sel_count;
+  int32_t max_sel, window;
+};
+
+// Finalize a verify or draft launch: merge split partials (if any) and, for
+// verify, turn the per-(block, row) partial log-masses into block scores.
+struct FinalizeParams {
+  int32_t batch, num_kv_heads, n_q, group, rows, head_dim;
+  int32_t num_chunks, chunk_tokens, chunk_items;  // as in AttnParams
+  int32_t dtype;  // sss_dtype of o
+  const int32_t* seq_lens;
+  int32_t max_seq_len, max_pages, page_size;
+  const float* o_part;
+  const float* lse_part;
+  void* o;
+  float* lse;
+  // verify only (ell == nullptr for draft)
+  const float* ell;
+  float* block_scores;
+  int32_t block_size, max_blocks, score_row_start;
+  // draft only: list length per unit is needed to know the chunk count
+  const int32_t* sel_count;
+  int32_t max_sel, window, draft;
+  int32_t simple_list;  // draft list enumerated token by token (vector-ALU path)
+};
+
+// Host-side launchers (each returns hipGetLastError() of its launches).
+hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s);
+hipError_t launch_draft_mfma(const AttnParams& p, hipStream_t s);
+hipError_t launch_attn_simple(const AttnParams& p, int dtype, bool draft, hipStream_t s);
+hipError_t launch_finalize(const FinalizeParams& p, hipStream_t s);
+hipError_t launch_topk(const float* scores, int batch, int hkv, int max_blocks,
+                       const int32_t* seq_lens, int block_size, const int32_t* budget,
+                       int window, int32_t* sel, int32_t* sel_count, int max_sel, hipStream_t s);
+hipError_t launch_merge(const float* o_parts, const float* lse_parts, int num_parts, int rows,
+                        int head_dim, void* o, int o_dtype, float* lse, hipStream_t s);
+
+// Number of list entries (tokens) of a draft unit's attention list as the
+// vector-ALU path enumerates it: selected blocks block by block, then the
+// window.  Shared definition for kernels and finalize.
+__host__ __device__ __forceinline__ int draft_list_len_simple(int nsel, int block_size, int L,
+                                                              int ws) {
+  return nsel * block_size + (L - ws);
+}
+
+// Matrix-core path: the list is made of 16-token segments.
+__host__ __device__ __forceinline__ int draft_list_len_mfma(int nsel, int block_size, int L,
+                                                            int ws) {
+  const int spb = block_size / kSeg;
+  const int w0 = (ws / kSeg) * kSeg;
+  return nsel * spb + (ws < L ? ceil_div(L - w0, kSeg) : 0);
+}
+
+}  // namespace sss

@@ -1,0 +1,179 @@
+"""Thin ctypes binding of libsss.so (C ABI in include/sss.h).
+
+Each function marshals torch tensors into the C call with the same name and
+launches on ``torch.cuda.current_stream()``.  All arithmetic runs in the HIP
+library; if it is missing this module raises on import.  Workspaces are
+allocated here as plain device byte tensors (the library never allocates).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsss.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is missing: build it with `python -m sparse_self_speculative_sss_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+SSS_OK, SSS_ERR_INVALID_ARGUMENT, SSS_ERR_UNSUPPORTED, SSS_ERR_WORKSPACE_TOO_SMALL, SSS_ERR_HIP = range(5)
+SSS_F32, SSS_BF16 = 0, 1
+
+_c_int = ctypes.c_int32
+_vp = ctypes.c_void_p
+_fp = ctypes.c_void_p
+
+
+class PagedKV(ctypes.Structure):
+    _fields_ = [
+        ("k", _vp), ("v", _vp), ("dtype", _c_int), ("num_pages", _c_int),
+        ("page_size", _c_int), ("num_kv_heads", _c_int), ("head_dim", _c_int),
+        ("max_pages_per_req", _c_int), ("page_table", _vp), ("seq_lens", _vp),
+        ("max_seq_len", _c_int),
+    ]
+
+
+_lib.sss_verify_attn.restype = _c_int
+_lib.sss_verify_attn.argtypes = [ctypes.POINTER(PagedKV), _vp, _c_int, _c_int, _c_int,
+                                 ctypes.c_float, _c_int, _c_int, _c_int, _vp, _fp, _fp, _c_int,
+                                 _vp, ctypes.c_size_t, _vp]
+_lib.sss_verify_workspace_size.restype = ctypes.c_size_t
+_lib.sss_verify_workspace_size.argtypes = [ctypes.POINTER(PagedKV), _c_int, _c_int, _c_int,
+                                           _c_int, _c_int, _c_int]
+_lib.sss_block_topk.restype = _c_int
+_lib.sss_block_topk.argtypes = [_fp, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp, _vp,
+                                _c_int, _vp]
+_lib.sss_draft_attn.restype = _c_int
+_lib.sss_draft_attn.argtypes = [ctypes.POINTER(PagedKV), _vp, _c_int, _c_int, ctypes.c_float,
+                                _c_int, _vp, _vp, _c_int, _c_int, _c_int, _vp, _fp, _vp,
+                                ctypes.c_size_t, _vp]
+_lib.sss_draft_workspace_size.restype = ctypes.c_size_t
+_lib.sss_draft_workspace_size.argtypes = [ctypes.POINTER(PagedKV), _c_int, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int]
+_lib.sss_merge.restype = _c_int
+_lib.sss_merge.argtypes = [_fp, _fp, _c_int, _c_int, _c_int, _vp, _c_int, _fp, _vp]
+_lib.sss_status_string.restype = ctypes.c_char_p
+_lib.sss_status_string.argtypes = [_c_int]
+_lib.sss_last_error.restype = ctypes.c_char_p
+_lib.sss_last_error.argtypes = []
+_lib.sss_version.restype = _c_int
+_lib.sss_version.argtypes = []
+
+EXPORTED = ["sss_verify_attn", "sss_verify_workspace_size", "sss_block_topk", "sss_draft_attn",
+            "sss_draft_workspace_size", "sss_merge", "sss_status_string", "sss_last_error",
+            "sss_version"]
+
+
+class SSSError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.sss_last_error().decode()
+        super().__init__(f"{where}: {_lib.sss_status_string(status).decode()}: {msg}")
+
+
+def _check(status: int, where: str):
+    if status != SSS_OK:
+        raise SSSError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SSS_F32
+    if t.dtype == torch.bfloat16:
+        return SSS_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def paged_kv(k_cache, v_cache, page_table, seq_lens, max_seq_len: int) -> PagedKV:
+    """Describe a paged cache [num_pages][Hkv][page_size][d] to the library."""
+    return PagedKV(k=k_cache.data_ptr(), v=v_cache.data_ptr(), dtype=_dtype_code(k_cache),
+                   num_pages=k_cache.shape[0], page_size=k_cache.shape[2],
+                   num_kv_heads=k_cache.shape[1], head_dim=k_cache.shape[3],
+                   max_pages_per_req=page_table.shape[1], page_table=page_table.data_ptr(),
+                   seq_lens=seq_lens.data_ptr(), max_seq_len=int(max_seq_len))
+
+
+def verify_workspace_size(kv: PagedKV, batch, n_q, num_q_heads, block_size, max_blocks,
+                          num_splits=0) -> int:
+    n = _lib.sss_verify_workspace_size(ctypes.byref(kv), batch, n_q, num_q_heads, block_size,
+                                       max_blocks, num_splits)
+    if n == 0 and _lib.sss_last_error():
+        raise SSSError(SSS_ERR_INVALID_ARGUMENT, "sss_verify_workspace_size")
+    return n
+
+
+def draft_workspace_size(kv: PagedKV, batch, num_q_heads, block_size, max_sel, window,
+                         num_splits=0) -> int:
+    n = _lib.sss_draft_workspace_size(ctypes.byref(kv), batch, num_q_heads, block_size, max_sel,
+                                      window, num_splits)
+    if n == 0 and _lib.sss_last_error():
+        raise SSSError(SSS_ERR_INVALID_ARGUMENT, "sss_draft_workspace_size")
+    return n
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def verify_attn(kv: PagedKV, q, sm_scale, block_size, max_blocks, o, lse, block_scores,
+                ws=None, score_row_start=0, num_splits=0):
+    """sss_verify_attn on tensors: q/o [B][n_q][Hq][d], lse [B][n_q][Hq],
+    block_scores [B][Hkv][max_blocks]."""
+    B, n_q, hq, _ = q.shape
+    if ws is None:
+        ws = workspace(verify_workspace_size(kv, B, n_q, hq, block_size, max_blocks, num_splits),
+                       q.device)
+    _check(_lib.sss_verify_attn(ctypes.byref(kv), _ptr(q), B, n_q, hq, float(sm_scale), block_size,
+                                score_row_start, num_splits, _ptr(o), _ptr(lse),
+                                _ptr(block_scores), max_blocks, _ptr(ws), ws.numel(), _stream()),
+           "sss_verify_attn")
+    return o, lse, block_scores
+
+
+def block_topk(block_scores, seq_lens, block_size, budget, window, sel, sel_count):
+    """sss_block_topk: sel [B][Hkv][max_sel], sel_count [B][Hkv]."""
+    B, hkv, max_blocks = block_scores.shape
+    _check(_lib.sss_block_topk(_ptr(block_scores), B, hkv, max_blocks, _ptr(seq_lens), block_size,
+                               _ptr(budget), window, _ptr(sel), _ptr(sel_count), sel.shape[2],
+                               _stream()),
+           "sss_block_topk")
+    return sel, sel_count
+
+
+def draft_attn(kv: PagedKV, q, sm_scale, block_size, sel, sel_count, window, o, lse, ws=None,
+               num_splits=0):
+    """sss_draft_attn: q/o [B][1][Hq][d], lse [B][1][Hq]."""
+    B, _, hq, _ = q.shape
+    max_sel = sel.shape[2]
+    if ws is None:
+        ws = workspace(draft_workspace_size(kv, B, hq, block_size, max_sel, window, num_splits),
+                       q.device)
+    _check(_lib.sss_draft_attn(ctypes.byref(kv), _ptr(q), B, hq, float(sm_scale), block_size,
+                               _ptr(sel), _ptr(sel_count), max_sel, window, num_splits, _ptr(o),
+                               _ptr(lse), _ptr(ws), ws.numel(), _stream()),
+           "sss_draft_attn")
+    return o, lse
+
+
+def merge(o_parts, lse_parts, o, lse=None):
+    """sss_merge: o_parts [S][rows][d] fp32, lse_parts [S][rows] -> o [rows][d]."""
+    S, rows, d = o_parts.shape
+    _check(_lib.sss_merge(_ptr(o_parts), _ptr(lse_parts), S, rows, d, _ptr(o), _dtype_code(o),
+                          _ptr(lse), _stream()),
+           "sss_merge")
+    return o, lse
+
+
+def raw():
+    """The ctypes library handle (tests call entry points with raw values)."""
+    return _lib

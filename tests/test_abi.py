@@ -1,0 +1,112 @@
+"""The C-ABI library loads without a GPU, exports every declared entry point,
+and rejects invalid arguments on the host before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "sparse_self_speculative_sss_amd", "libsss.so")
+HDR = os.path.join(ROOT, "include", "sss.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libsss.so not built")
+
+
+def declared():
+    text = open(HDR).read()
+    return sorted(set(re.findall(r"\b(sss_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    names = declared()
+    assert {"sss_verify_attn", "sss_block_topk", "sss_draft_attn", "sss_merge"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {LIB}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def _binding():
+    from sparse_self_speculative_sss_amd import sss
+    return sss
+
+
+def good_kv(sss, **kw):
+    base = dict(k=256, v=512, dtype=sss.SSS_BF16, num_pages=64, page_size=16, num_kv_heads=2,
+                head_dim=128, max_pages_per_req=8, page_table=1024, seq_lens=2048,
+                max_seq_len=128)
+    base.update(kw)
+    return sss.PagedKV(**base)
+
+
+def call_verify(sss, kv, **kw):
+    a = dict(q=4096, batch=2, n_q=5, hq=8, scale=0.1, bs=16, r0=0, splits=0, o=8192, lse=16384,
+             sc=32768, mb=8, ws=65536, wsb=1 << 30)
+    a.update(kw)
+    return sss.raw().sss_verify_attn(ctypes.byref(kv), a["q"], a["batch"], a["n_q"], a["hq"],
+                                     a["scale"], a["bs"], a["r0"], a["splits"], a["o"], a["lse"],
+                                     a["sc"], a["mb"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kvkw,callkw,status", [
+    (dict(head_dim=96), {}, 2),
+    (dict(dtype=7), {}, 2),
+    (dict(page_size=0), {}, 1),
+    (dict(max_pages_per_req=4), {}, 1),          # 4 * 16 < 128
+    (dict(k=258), {}, 1),                        # misaligned cache
+    ({}, dict(n_q=0), 1),
+    ({}, dict(n_q=33), 1),
+    ({}, dict(hq=7), 1),                         # not a multiple of Hkv
+    ({}, dict(hq=128, n_q=5), 2),                # 5 * 64 rows > 128
+    ({}, dict(bs=0), 1),
+    ({}, dict(mb=7), 1),                         # < ceil(128 / 16)
+    ({}, dict(r0=5), 1),
+    ({}, dict(splits=-1), 1),
+    ({}, dict(scale=float("inf")), 1),
+    ({}, dict(q=4100), 1),                       # misaligned q
+    ({}, dict(o=0), 1),
+    ({}, dict(wsb=16), 3),                       # workspace too small
+    ({}, dict(ws=65537), 1),                     # misaligned workspace
+])
+def test_verify_rejects_bad_arguments(kvkw, callkw, status):
+    sss = _binding()
+    kv = good_kv(sss, **kvkw)
+    assert call_verify(sss, kv, **callkw) == status
+    assert sss.raw().sss_last_error()
+
+
+def test_workspace_queries():
+    sss = _binding()
+    kv = good_kv(sss)
+    n = sss.verify_workspace_size(kv, 2, 5, 8, 16, 8, 0)
+    assert n > 0 and n % 256 == 0
+    assert sss.verify_workspace_size(kv, 2, 5, 8, 16, 8, 4) >= n
+    assert sss.draft_workspace_size(kv, 2, 8, 16, 4, 64, 1) >= 0
+    with pytest.raises(sss.SSSError):
+        sss.verify_workspace_size(good_kv(sss, head_dim=65), 2, 5, 8, 16, 8, 0)
+
+
+def test_other_entry_points_reject_bad_arguments():
+    sss = _binding()
+    lib = sss.raw()
+    assert lib.sss_block_topk(256, 1, 0, 8, 256, 16, 256, 0, 256, 256, 4, None) == 1
+    assert lib.sss_block_topk(256, 1, 2, 8, 256, 16, 256, -1, 256, 256, 4, None) == 1
+    assert lib.sss_block_topk(256, 1, 2, 8, 256, 16, 256, 0, 256, 256, 0, None) == 1
+    assert lib.sss_block_topk(None, 1, 2, 8, 256, 16, 256, 0, 256, 256, 4, None) == 1
+    kv = good_kv(sss)
+    d = lib.sss_draft_attn
+    assert d(ctypes.byref(kv), 4096, 2, 8, 0.1, 16, 256, 256, 0, 64, 0, 8192, 256, 65536, 1 << 20, None) == 1
+    assert d(ctypes.byref(kv), 4096, 2, 8, 0.1, 16, 256, 256, 4, -1, 0, 8192, 256, 65536, 1 << 20, None) == 1
+    assert d(ctypes.byref(kv), 4096, 2, 7, 0.1, 16, 256, 256, 4, 64, 0, 8192, 256, 65536, 1 << 20, None) == 1
+    m = lib.sss_merge
+    assert m(256, 256, 0, 4, 128, 256, 0, 256, None) == 1
+    assert m(256, 256, 2, 4, 0, 256, 0, 256, None) == 1
+    assert m(256, 256, 2, 4, 128, 256, 9, 256, None) == 2
+    # zero-size work is a successful no-op (nothing to launch)
+    assert m(256, 256, 2, 0, 128, 256, 0, 256, None) == 0
+    assert call_verify(sss, kv, batch=0) == 0
+    for st in range(5):
+        assert lib.sss_status_string(st).startswith(b"SSS_")

@@ -1,0 +1,255 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Reduced shapes compare every unit; the full-size workloads (in the launch
+configuration the benchmark times) compare a seeded sample of units.  Block
+indices are compared bit-exactly when both selectors read the same
+oracle-supplied fp32 scores; the draft is compared on a shared selection.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import harness as H
+import oracle
+from sparse_self_speculative_sss_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def mk(name, seed=0, **kw):
+    return W.make(name, seed=seed, device=DEV, **kw)
+
+
+# reduced shapes: (id, shape name, overrides, num_splits list)
+SMALL = [
+    ("tiny_fp32", "tiny_fp32_b1_l512", {}, [0, 2]),
+    ("qwen_ragged", "qwen3_8b_layer_b16_l4096", dict(B=2, L=300), [0, 1, 3]),
+    ("qwen_sigma1", "qwen3_8b_layer_b16_l4096", dict(B=2, L=517, sigma="one"), [0, 2]),
+    ("d64_bf16", "decode_b128_l8192", dict(B=2, L=200, d=64, sigma="one"), [0, 1]),
+    ("mha_nq3", "qwen3_8b_layer_b16_l4096", dict(B=2, L=130, Hq=8, Hkv=8, n_q=3, sigma="one"), [0]),
+    ("decode_nq1", "qwen3_8b_layer_b16_l4096", dict(B=3, L=77, n_q=1, sigma="one"), [0, 2]),
+    ("L_eq_nq", "qwen3_8b_layer_b16_l4096", dict(B=2, L=5, window=0, sigma="one"), [0]),
+    ("page64_blk64", "longctx_b4_l128k", dict(B=1, L=2000, sigma="one"), [0, 3]),
+    ("page32_blk16", "qwen3_8b_layer_b16_l4096", dict(B=2, L=700, page_size=32, sigma="one"), [0]),
+    ("page16_blk64", "qwen3_8b_layer_b16_l4096", dict(B=2, L=700, block_size=64, sigma="one"), [0, 2]),
+    ("bf16_page8_simple", "qwen3_8b_layer_b16_l4096",
+     dict(B=2, L=150, page_size=8, block_size=8, Hq=8, Hkv=2, sigma="one"), [0, 2]),
+    ("f32_d128", "qwen3_8b_layer_b16_l4096", dict(B=1, L=100, dtype="f32", Hq=8, Hkv=2), [0]),
+    ("rows80", "longctx_b4_l128k", dict(B=1, L=3000, sigma="one"), [0, 4]),
+    ("rows128", "qwen3_8b_layer_b16_l4096", dict(B=1, L=400, Hq=32, Hkv=1, n_q=4), [0, 2]),
+    ("rows40", "qwen3_8b_layer_b16_l4096", dict(B=2, L=333, Hq=16, Hkv=2, sigma="one"), [0, 2]),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_verify_small(case):
+    cid, name, kw, splits = case
+    wl = mk(name, seed=11, **kw)
+    vb = wl.verify
+    units = H.all_units(vb, wl.shape.Hkv)
+    for ns in splits:
+        print(f"[verify] {cid} num_splits={ns}", flush=True)
+        out = H.gpu_verify(wl, vb, num_splits=ns)
+        torch.cuda.synchronize()
+        st = H.compare_verify(wl, vb, out, units)
+        st.check(f"{cid} splits={ns}")
+        sc = out[2].cpu().numpy()
+        for b in range(vb.B):
+            nblk = -(-int(vb.seq_lens[b]) // wl.shape.block_size)
+            assert np.all(sc[b, :, nblk:] == 0.0)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_draft_small(case):
+    cid, name, kw, splits = case
+    wl = mk(name, seed=12, **kw)
+    vb, db = wl.verify, wl.draft
+    units = H.all_units(db, wl.shape.Hkv)
+    _, sel, cnt = H.oracle_selection(wl, vb, units)
+    sel_t = torch.from_numpy(sel).to(DEV)
+    cnt_t = torch.from_numpy(cnt).to(DEV)
+    for ns in splits:
+        for window in sorted({wl.shape.window, 0}):
+            print(f"[draft] {cid} num_splits={ns} window={window}", flush=True)
+            out = H.gpu_draft(wl, db, sel_t, cnt_t, num_splits=ns, window=window)
+            torch.cuda.synchronize()
+            H.compare_draft(wl, db, out, sel, cnt, units, window=window).check(
+                f"draft {cid} splits={ns} W={window}")
+
+
+def test_score_row_start_one():
+    wl = mk("qwen3_8b_layer_b16_l4096", seed=3, B=2, L=260, sigma="one")
+    vb = wl.verify
+    out = H.gpu_verify(wl, vb, score_row_start=1)
+    torch.cuda.synchronize()
+    H.compare_verify(wl, vb, out, H.all_units(vb, wl.shape.Hkv), score_row_start=1).check("r0=1")
+    G = wl.shape.Hq // wl.shape.Hkv
+    assert np.allclose(out[2].cpu().numpy().sum(-1), (wl.shape.n_q - 1) * G, atol=1e-3)
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, launch configuration of the benchmark
+# --------------------------------------------------------------------------
+FULL = [("qwen3_8b_layer_b16_l4096", 128), ("decode_b128_l8192", 6),
+        ("mixed_b96_l1k_32k", 6), ("longctx_b4_l128k", 2)]
+
+
+@pytest.mark.parametrize("name,n_units", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(name, n_units):
+    wl = mk(name, seed=0)
+    hkv = wl.shape.Hkv
+    vb, db = wl.verify, wl.draft
+    print(f"[full] {name} verify", flush=True)
+    v_out = H.gpu_verify(wl, vb)
+    torch.cuda.synchronize()
+    units = H.sample_units(vb, hkv, n_units, seed=1)
+    H.compare_verify(wl, vb, v_out, units).check(f"{name} verify")
+    # per-row mass invariant on every unit
+    G = wl.shape.Hq // hkv
+    tot = v_out[2].sum(-1).cpu().numpy()
+    assert np.abs(tot - wl.shape.n_q * G).max() < 5e-3
+    # draft on a shared selection
+    if db.sel is None:
+        d_units = H.sample_units(db, hkv, n_units, seed=2)
+        _, sel, cnt = H.oracle_selection(wl, vb, d_units)
+    else:
+        d_units = H.sample_units(db, hkv, n_units, seed=2)
+        sel, cnt = db.sel.cpu().numpy(), db.sel_count.cpu().numpy()
+    print(f"[full] {name} draft", flush=True)
+    d_out = H.gpu_draft(wl, db, torch.from_numpy(sel).to(DEV), torch.from_numpy(cnt).to(DEV))
+    torch.cuda.synchronize()
+    H.compare_draft(wl, db, d_out, sel, cnt, d_units).check(f"{name} draft")
+
+
+# --------------------------------------------------------------------------
+# Top-N: bit-exact on oracle-supplied scores
+# --------------------------------------------------------------------------
+TOPK_CASES = [
+    # B, Hkv, max_blocks, L range, block, window, budget range, max_sel, score levels
+    (3, 2, 40, (1, 600), 16, 64, (0, 12), 8, 3),
+    (4, 3, 300, (100, 4800), 16, 0, (0, 30), 20, 1000),
+    (2, 2, 2048, (64 * 1500, 64 * 2048), 64, 128, (16, 16), 16, 7),
+    (5, 1, 64, (1, 64 * 4), 4, 5, (0, 70), 80, 2),
+    (2, 8, 512, (8000, 8192), 16, 64, (26, 26), 26, 0),   # 0 levels: continuous scores
+    (3, 2, 33, (1, 33), 1, 0, (0, 40), 33, 2),
+]
+
+
+@pytest.mark.parametrize("case", TOPK_CASES)
+def test_topk_bit_exact(case):
+    B, hkv, mb, (lo, hi), bs, window, (blo, bhi), max_sel, levels = case
+    g = np.random.default_rng(hash(case) % (2 ** 32))
+    for trial in range(4):
+        lens = g.integers(lo, hi + 1, B).astype(np.int32)
+        lens = np.minimum(lens, mb * bs).astype(np.int32)
+        budget = g.integers(blo, bhi + 1, B).astype(np.int32)
+        if levels:
+            scores = (g.integers(0, levels, (B, hkv, mb)) / levels).astype(np.float32)
+        else:
+            scores = g.random((B, hkv, mb)).astype(np.float32)
+        if trial == 3:
+            scores[..., ::3] = -0.0      # -0.0 must tie with +0.0
+            scores[..., 1::3] = 0.0
+        ref_sel, ref_cnt = oracle.block_topk(scores, lens, bs, budget, window, max_sel)
+        st = torch.from_numpy(scores).to(DEV)
+        lt = torch.from_numpy(lens).to(DEV)
+        bt = torch.from_numpy(budget).to(DEV)
+        sel = torch.full((B, hkv, max_sel), 999, dtype=torch.int32, device=DEV)
+        cnt = torch.full((B, hkv), -5, dtype=torch.int32, device=DEV)
+        H.sss().block_topk(st, lt, bs, bt, window, sel, cnt)
+        torch.cuda.synchronize()
+        assert np.array_equal(cnt.cpu().numpy(), ref_cnt), (case, trial)
+        assert np.array_equal(sel.cpu().numpy(), ref_sel), (case, trial)
+
+
+def test_topk_on_oracle_verify_scores():
+    wl = mk("qwen3_8b_layer_b16_l4096", seed=5, B=3, L=1000)
+    vb = wl.verify
+    units = H.all_units(vb, wl.shape.Hkv)
+    scores, ref_sel, ref_cnt = H.oracle_selection(wl, vb, units)
+    sel, cnt = H.gpu_topk(wl, vb, torch.from_numpy(scores).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), ref_sel)
+    assert np.array_equal(cnt.cpu().numpy(), ref_cnt)
+
+
+def test_pipeline_selection_overlap():
+    """verify -> top-N -> draft entirely on the GPU.  The GPU-score selection
+    can differ from the oracle-score selection only between blocks whose
+    scores agree to within the score tolerance; the check is that it captures
+    as much oracle probability mass."""
+    wl = mk("qwen3_8b_layer_b16_l4096", seed=6, B=4, L=2048)
+    vb = wl.verify
+    _, _, sc = H.gpu_verify(wl, vb)
+    sel, cnt = H.gpu_topk(wl, vb, sc)
+    torch.cuda.synchronize()
+    units = H.all_units(vb, wl.shape.Hkv)
+    scores, ref_sel, ref_cnt = H.oracle_selection(wl, vb, units)
+    sel_np, cnt_np = sel.cpu().numpy(), cnt.cpu().numpy()
+    assert np.array_equal(cnt_np, ref_cnt)
+    overlap = []
+    for b, h in units:
+        a = set(sel_np[b, h, :cnt_np[b, h]].tolist())
+        r = set(ref_sel[b, h, :ref_cnt[b, h]].tolist())
+        overlap.append(len(a & r) / max(1, len(r)))
+        mass_gpu = sum(float(scores[b, h, j]) for j in a)
+        mass_ref = sum(float(scores[b, h, j]) for j in r)
+        assert mass_gpu >= mass_ref - 2 * H.SCORE_ABS * len(r)
+    print(f"mean selection overlap {np.mean(overlap):.4f}", flush=True)
+    assert np.mean(overlap) > 0.9
+
+
+def test_bitwise_determinism():
+    wl = mk("qwen3_8b_layer_b16_l4096", seed=7, B=4, L=1500)
+    vb, db = wl.verify, wl.draft
+    runs = []
+    for _ in range(2):
+        o, lse, sc = H.gpu_verify(wl, vb, num_splits=3)
+        sel, cnt = H.gpu_topk(wl, vb, sc)
+        od, lsed = H.gpu_draft(wl, db, sel, cnt, num_splits=2)
+        torch.cuda.synchronize()
+        runs.append([t.cpu() for t in (o, lse, sc, sel, cnt, od, lsed)])
+    for a, b in zip(*runs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+def test_merge_matches_oracle():
+    g = np.random.default_rng(21)
+    S, rows, d = 5, 37, 128
+    o_parts = g.normal(size=(S, rows, d)).astype(np.float32)
+    lse_parts = g.normal(size=(S, rows)).astype(np.float32) * 3
+    lse_parts[1, 3] = -np.inf
+    lse_parts[:, 7] = -np.inf           # an all-empty row
+    ref_o, ref_l = oracle.merge(o_parts, lse_parts)
+    for dtype, tol in ((torch.float32, 1e-5), (torch.bfloat16, 1e-2)):
+        o = torch.full((rows, d), float("nan"), dtype=dtype, device=DEV)
+        lse = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV)
+        H.sss().merge(torch.from_numpy(o_parts).to(DEV), torch.from_numpy(lse_parts).to(DEV), o, lse)
+        torch.cuda.synchronize()
+        go = o.float().cpu().numpy()
+        gl = lse.cpu().numpy()
+        assert np.abs(go - ref_o).max() < tol
+        fin = np.isfinite(ref_l)
+        assert np.array_equal(np.isfinite(gl), fin)
+        assert np.abs(gl[fin] - ref_l[fin]).max() < 1e-5
+        assert np.all(go[7] == 0)
+
+
+def test_invalid_seq_len_poisons_outputs():
+    wl = mk("qwen3_8b_layer_b16_l4096", seed=8, B=2, L=200)
+    vb = wl.verify
+    bad = W.Batch(q=vb.q, page_table=vb.page_table, seq_lens=vb.seq_lens.clone(),
+                  budget=vb.budget, req_ids=vb.req_ids)
+    bad.seq_lens[1] = 100000          # above max_seq_len
+    kv = H.sss().paged_kv(wl.k_cache, wl.v_cache, bad.page_table, bad.seq_lens, 200)
+    o = torch.zeros_like(vb.q)
+    lse = torch.zeros(vb.q.shape[:3], device=DEV)
+    sc = torch.zeros((2, wl.shape.Hkv, wl.max_blocks), device=DEV)
+    H.sss().verify_attn(kv, vb.q, wl.sm_scale, 16, wl.max_blocks, o, lse, sc)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[1].float()).all() and torch.isnan(lse[1]).all() and torch.isnan(sc[1]).all()
+    assert torch.isfinite(o[0].float()).all() and torch.isfinite(lse[0]).all()
