@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse self-speculative decode attention hot path on one
+MI355X.
+
+One step = one pass of the whole path over one batch:
+  sss_verify_attn (k+1 queries per request over the full paged KV, block
+  scores) -> sss_block_topk (critical-block lists) -> sss_draft_attn (one
+  query per request over the selected blocks plus the recent window).
+Default workload: batch 128, 8192-token contexts, Qwen3-8B attention shape
+(32 query heads, 8 KV heads, head dim 128), k = 4, 16-token blocks and pages,
+5% block budget plus a 64-token window, bf16 -- the batch-128 x 8K decode
+configuration on which the bandwidth target is stated.  Inputs are seeded
+synthetic tensors, resident in HBM before timing starts.
+
+Prints one JSON line (metric, value = query tokens/s, roofline of the verify
+kernel, CPU-oracle baseline on a bounded sample).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify+draft attn tokens/s and KV HBM GB/s (% of MI355X peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_b128_l8192")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample", type=int, default=24,
+                    help="requests the CPU oracle processes for the baseline (0 = skip)")
+    ap.add_argument("--verify-splits", type=int, default=-1,
+                    help="override num_splits of the verify call (-1: workload default)")
+    ap.add_argument("--draft-splits", type=int, default=0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one device copy of this size (for counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(wl, sel_np, cnt_np):
+    """Bytes the method must move per step (K/V read once, inputs, outputs)."""
+    s = wl.shape
+    vb, db = wl.verify, wl.draft
+    el = 2 if s.dtype == "bf16" else 4
+    lens = vb.seq_lens.cpu().numpy()
+    kv_verify = int(sum(int(L) for L in lens)) * s.Hkv * s.d * el * 2
+    B, n_q = vb.B, s.n_q
+    q_bytes = B * n_q * s.Hq * s.d * el
+    verify = (kv_verify + 2 * q_bytes + B * n_q * s.Hq * 4 + B * s.Hkv * wl.max_blocks * 4
+              + sum(-(-int(L) // s.page_size) for L in lens) * 4 + B * 4)
+    topk = B * s.Hkv * wl.max_blocks * 4 + B * s.Hkv * wl.max_sel * 4 + B * s.Hkv * 4 + 2 * B * 4
+    # draft: distinct tokens of each unit's attention set
+    toks = 0
+    dl = db.seq_lens.cpu().numpy()
+    for b in range(db.B):
+        L = int(dl[b])
+        ws = L if s.window <= 0 else max(0, L - s.window)
+        for h in range(s.Hkv):
+            n = 0
+            for j in sel_np[b, h, :cnt_np[b, h]]:
+                n += max(0, min((int(j) + 1) * s.block_size, ws) - int(j) * s.block_size)
+            toks += n + (L - ws)
+    draft = (toks * s.d * el * 2 + 2 * db.B * s.Hq * s.d * el + db.B * s.Hq * 4
+             + db.B * s.Hkv * (wl.max_sel + 1) * 4)
+    return {"verify": verify, "verify_kv": kv_verify, "topk": topk, "draft": draft,
+            "draft_kv": toks * s.d * el * 2, "total": verify + topk + draft}
+
+
+def cpu_baseline(wl, n_req):
+    """Time the fp64 oracle (as it stands) on the first n_req requests:
+    verify + block scores, Top-N, draft.  Returns query tokens/s."""
+    import numpy as np
+    import torch
+    import oracle
+    from threadpoolctl import threadpool_info
+    from sparse_self_speculative_sss_amd import workload as W
+    s = wl.shape
+    vb, db = wl.verify, wl.draft
+    n_req = min(n_req, vb.B)
+    q = W.to_numpy64(vb.q[:n_req])
+    qd = W.to_numpy64(db.q[:n_req])
+    elapsed = 0.0
+    for b in range(n_req):
+        L = int(vb.seq_lens[b])
+        n = -(-L // s.page_size)
+        pages = vb.page_table[b, :n].long().to(wl.k_cache.device)
+        k = W.to_numpy64(wl.k_cache[pages])
+        v = W.to_numpy64(wl.v_cache[pages])
+        table = np.arange(n, dtype=np.int32)[None]
+        lens = np.array([L], dtype=np.int32)
+        t0 = time.perf_counter()
+        _, _, sc = oracle.verify_with_scores(q[b:b + 1], k, v, table, lens, wl.sm_scale,
+                                             s.block_size, wl.max_blocks)
+        sel, cnt = oracle.block_topk(sc.astype(np.float32), lens, s.block_size,
+                                     vb.budget[b:b + 1].cpu().numpy(), s.window, wl.max_sel)
+        oracle.draft(qd[b:b + 1], k, v, table, lens, sel, cnt, s.block_size, s.window,
+                     wl.sm_scale)
+        elapsed += time.perf_counter() - t0
+        del k, v
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    tokens = n_req * (s.n_q + 1)
+    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{n_req} of {vb.B} requests (all {s.Hkv} KV heads each): fp64 verify + "
+                       f"block scores, Top-N and draft, {elapsed:.1f} s wall on the host")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by request and KV head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from sparse_self_speculative_sss_amd import workload as W
+    from sparse_self_speculative_sss_amd import sss
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {args.workload} seed={args.seed}", file=sys.stderr, flush=True)
+    wl = W.make(args.workload, seed=args.seed, device=dev)
+    s = wl.shape
+    if s.p_verify is not None:
+        print("bench.py times the single-phase workloads; use the tests for the mixed batch",
+              file=sys.stderr)
+        sys.exit(2)
+    vb, db = wl.verify, wl.draft
+    B, n_q = vb.B, s.n_q
+    kv_v = sss.paged_kv(wl.k_cache, wl.v_cache, vb.page_table, vb.seq_lens, vb.max_seq_len)
+    kv_d = sss.paged_kv(wl.k_cache, wl.v_cache, db.page_table, db.seq_lens, db.max_seq_len)
+    vsplits = s.num_splits if args.verify_splits < 0 else args.verify_splits
+    o = torch.empty_like(vb.q)
+    lse = torch.empty((B, n_q, s.Hq), dtype=torch.float32, device=dev)
+    sc = torch.empty((B, s.Hkv, wl.max_blocks), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, s.Hkv, wl.max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, s.Hkv), dtype=torch.int32, device=dev)
+    od = torch.empty_like(db.q)
+    lsed = torch.empty((B, 1, s.Hq), dtype=torch.float32, device=dev)
+    ws_v = sss.workspace(sss.verify_workspace_size(kv_v, B, n_q, s.Hq, s.block_size,
+                                                   wl.max_blocks, vsplits), dev)
+    ws_d = sss.workspace(sss.draft_workspace_size(kv_d, B, s.Hq, s.block_size, wl.max_sel,
+                                                  s.window, args.draft_splits), dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        sss.verify_attn(kv_v, vb.q, wl.sm_scale, s.block_size, wl.max_blocks, o, lse, sc, ws=ws_v,
+                        num_splits=vsplits)
+        if ev is not None:
+            ev[1].record()
+        sss.block_topk(sc, vb.seq_lens, s.block_size, vb.budget, s.window, sel, cnt)
+        if ev is not None:
+            ev[2].record()
+        sss.draft_attn(kv_d, db.q, wl.sm_scale, s.block_size, sel, cnt, s.window, od, lsed,
+                       ws=ws_d, num_splits=args.draft_splits)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nbytes = algorithmic_bytes(wl, sel.cpu().numpy(), cnt.cpu().numpy())
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    v_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    d_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    tokens = B * n_q + db.B
+    value = tokens / (ms_step / 1e3)
+
+    v_gbs = nbytes["verify"] / (v_ms * 1e-3) / 1e9
+    unit_gbs = nbytes["total"] / (ms_step * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic (seeded; Qwen3-8B attention shape, planted heavy-hitter keys)",
+        "config": {
+            "workload": s.name, "batch": B, "context": int(vb.max_seq_len), "q_heads": s.Hq,
+            "kv_heads": s.Hkv, "head_dim": s.d, "k_plus_1": n_q, "block": s.block_size,
+            "page": s.page_size, "budget_blocks": int(vb.budget[0]), "window": s.window,
+            "verify_splits": vsplits, "draft_splits": args.draft_splits,
+        },
+        "roofline": {
+            "kernel": "sss_verify_attn (verify attention + block-score finalize)",
+            "bound": "hbm",
+            "achieved": round(v_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(v_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": nbytes["verify"],
+            "ms": round(v_ms, 4),
+        },
+        "step_hbm": {
+            "algorithmic_bytes": nbytes["total"],
+            "GB/s": round(unit_gbs, 1),
+            "frac": round(unit_gbs / HBM_PEAK_GBS, 4),
+            "verify_ms": round(v_ms, 4), "topk_ms": round(t_ms, 4), "draft_ms": round(d_ms, 4),
+            "draft_GB/s": round(nbytes["draft"] / (d_ms * 1e-3) / 1e9, 1),
+        },
+    }
+    if args.cpu_sample > 0:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
