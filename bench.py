@@ -44,7 +44,8 @@ def parse():
                     help="override num_splits of the verify call (-1: workload default)")
     ap.add_argument("--draft-splits", type=int, default=0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="also run one device copy of this size (for counter calibration)")
+                    help="only run device copies of this size (calibrates HBM byte counters "
+                         "against a transfer of known size) and exit")
     return ap.parse_args()
 
 
@@ -130,6 +131,16 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read": n * 4, "bytes_written": n * 4,
+                                               "copies": 3}}), flush=True)
+        return
     print(f"[bench] generating {args.workload} seed={args.seed}", file=sys.stderr, flush=True)
     wl = W.make(args.workload, seed=args.seed, device=dev)
     s = wl.shape
@@ -173,14 +184,6 @@ def main():
         step()
     torch.cuda.synchronize()
     nbytes = algorithmic_bytes(wl, sel.cpu().numpy(), cnt.cpu().numpy())
-
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()

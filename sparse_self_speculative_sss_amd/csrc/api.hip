@@ -84,6 +84,8 @@ bool use_mfma(const sss_paged_kv* kv, int block_size) {
 struct Plan {
   bool mfma;
   int rows, num_chunks, chunk;  // chunk: tokens (verify) or list entries (draft)
+  bool ell_in_lds = false;
+  long long ell_lds_floats = 0;
   size_t ell_off, opart_off, lpart_off, bytes;
 };
 
@@ -146,7 +148,11 @@ sss_status plan_verify(const sss_paged_kv* kv, int batch, int n_q, int hq, int b
   if (chunk > (1LL << 30)) return fail(SSS_ERR_UNSUPPORTED, "chunk too large");
   pl.chunk = (int)chunk;
   pl.num_chunks = (int)((Lmax + chunk - 1) / chunk);
-  layout(pl, units, kv->head_dim, units * (long long)max_blocks * pl.rows);
+  // an unsplit unit keeps its block log masses in LDS when they fit
+  pl.ell_lds_floats = (long long)ceil_div(pl.chunk, block_size) * pl.rows;
+  pl.ell_in_lds = pl.mfma && pl.num_chunks == 1 &&
+                  mfma_smem_bytes(kv->head_dim, nwr, nwt, pl.ell_lds_floats) <= kMaxLds;
+  layout(pl, units, kv->head_dim, pl.ell_in_lds ? 0 : units * (long long)max_blocks * pl.rows);
   return ok();
 }
 
@@ -295,10 +301,16 @@ sss_status sss_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
   p.lse = lse;
   p.block_size = block_size;
   p.max_blocks = max_blocks;
+  p.score_row_start = score_row_start;
   p.ell = reinterpret_cast<float*>(ws + pl.ell_off);
+  p.block_scores = block_scores;
+  p.ell_in_lds = pl.ell_in_lds ? 1 : 0;
+  p.ell_lds_floats = (int32_t)pl.ell_lds_floats;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = pl.mfma ? launch_verify_mfma(p, s) : launch_attn_simple(p, kv->dtype, false, s);
   if (e != hipSuccess) return fail(SSS_ERR_HIP, "verify launch: %s", hipGetErrorString(e));
+  // an unsplit matrix-core launch finalises the block scores itself
+  if (pl.mfma && pl.num_chunks == 1) return ok();
 
   FinalizeParams f = {};
   f.batch = batch;

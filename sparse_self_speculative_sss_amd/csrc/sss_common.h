@@ -18,6 +18,12 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kSeg = 16;  // tokens per segment of the matrix-core path
+// dynamic LDS a workgroup may request: the 160 KiB of a gfx950 compute unit
+// minus a reserve for the kernels' static LDS (barrier reductions)
+constexpr size_t kMaxLds = 159 * 1024;
+
+// LDS bytes of one matrix-core workgroup (attn_mfma.hip).
+size_t mfma_smem_bytes(int head_dim, int nwr, int nwt, long long ell_floats);
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
@@ -63,9 +69,13 @@ struct AttnParams {
   // final outputs (written directly when num_chunks == 1)
   void* o;
   float* lse;
-  // verify: block importance partials, log2 domain, [U][max_blocks][rows]
-  int32_t block_size, max_blocks;
+  // verify: block importance partials, log2 domain, [U][max_blocks][rows];
+  // when num_chunks == 1 the matrix-core kernel also writes block_scores
+  int32_t block_size, max_blocks, score_row_start;
   float* ell;
+  float* block_scores;
+  int32_t ell_in_lds;      // unsplit matrix-core verify: log masses stay in LDS
+  int32_t ell_lds_floats;  // their count (blocks of the chunk x rows)
   // draft
   const int32_t* sel;
   const int32_t* sel_count;
