@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_b128_l8192")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample", type=int, default=24,
+    ap.add_argument("--cpu-sample", type=int, default=128,
                     help="requests the CPU oracle processes for the baseline (0 = skip)")
     ap.add_argument("--verify-splits", type=int, default=-1,
                     help="override num_splits of the verify call (-1: workload default)")
@@ -49,78 +49,137 @@ def parse():
     return ap.parse_args()
 
 
+COUNTERS = os.path.join(ROOT, "profiles", "verify_decode_b128_l8192_counters.json")
+KERNEL_SOURCES = ["sparse_self_speculative_sss_amd/csrc/attn_mfma.hip",
+                  "sparse_self_speculative_sss_amd/csrc/sss_common.h",
+                  "sparse_self_speculative_sss_amd/csrc/api.hip"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per verify launch from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a copy of known size), or None
+    when the kernel sources changed since the counters were taken."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
 def algorithmic_bytes(wl, sel_np, cnt_np):
-    """Bytes the method must move per step (K/V read once, inputs, outputs)."""
+    """Bytes the method must move per step: K and V of every attended token
+    read once, plus queries, outputs, LSEs, scores, selections, page tables."""
     s = wl.shape
     vb, db = wl.verify, wl.draft
     el = 2 if s.dtype == "bf16" else 4
-    lens = vb.seq_lens.cpu().numpy()
-    kv_verify = int(sum(int(L) for L in lens)) * s.Hkv * s.d * el * 2
-    B, n_q = vb.B, s.n_q
-    q_bytes = B * n_q * s.Hq * s.d * el
-    verify = (kv_verify + 2 * q_bytes + B * n_q * s.Hq * 4 + B * s.Hkv * wl.max_blocks * 4
-              + sum(-(-int(L) // s.page_size) for L in lens) * 4 + B * 4)
-    topk = B * s.Hkv * wl.max_blocks * 4 + B * s.Hkv * wl.max_sel * 4 + B * s.Hkv * 4 + 2 * B * 4
-    # draft: distinct tokens of each unit's attention set
-    toks = 0
-    dl = db.seq_lens.cpu().numpy()
-    for b in range(db.B):
-        L = int(dl[b])
-        ws = L if s.window <= 0 else max(0, L - s.window)
-        for h in range(s.Hkv):
-            n = 0
-            for j in sel_np[b, h, :cnt_np[b, h]]:
-                n += max(0, min((int(j) + 1) * s.block_size, ws) - int(j) * s.block_size)
-            toks += n + (L - ws)
-    draft = (toks * s.d * el * 2 + 2 * db.B * s.Hq * s.d * el + db.B * s.Hq * 4
-             + db.B * s.Hkv * (wl.max_sel + 1) * 4)
+    verify = kv_verify = topk = 0
+    if vb is not None:
+        lens = vb.seq_lens.cpu().numpy()
+        kv_verify = int(sum(int(L) for L in lens)) * s.Hkv * s.d * el * 2
+        B, n_q = vb.B, s.n_q
+        q_bytes = B * n_q * s.Hq * s.d * el
+        verify = (kv_verify + 2 * q_bytes + B * n_q * s.Hq * 4 + B * s.Hkv * wl.max_blocks * 4
+                  + sum(-(-int(L) // s.page_size) for L in lens) * 4 + B * 4)
+        topk = (B * s.Hkv * wl.max_blocks * 4 + B * s.Hkv * wl.max_sel * 4 + B * s.Hkv * 4
+                + 2 * B * 4)
+    toks = draft = 0
+    if db is not None:
+        dl = db.seq_lens.cpu().numpy()
+        for b in range(db.B):
+            L = int(dl[b])
+            ws = L if s.window <= 0 else max(0, L - s.window)
+            for h in range(s.Hkv):
+                n = 0
+                for j in sel_np[b, h, :cnt_np[b, h]]:
+                    n += max(0, min((int(j) + 1) * s.block_size, ws) - int(j) * s.block_size)
+                toks += n + (L - ws)
+        draft = (toks * s.d * el * 2 + 2 * db.B * s.Hq * s.d * el + db.B * s.Hq * 4
+                 + db.B * s.Hkv * (wl.max_sel + 1) * 4
+                 + sum(-(-int(L) // s.page_size) for L in dl) * 4)
     return {"verify": verify, "verify_kv": kv_verify, "topk": topk, "draft": draft,
             "draft_kv": toks * s.d * el * 2, "total": verify + topk + draft}
 
 
-def cpu_baseline(wl, n_req):
-    """Time the fp64 oracle (as it stands) on the first n_req requests:
-    verify + block scores, Top-N, draft.  Returns query tokens/s."""
+def _request_copy(wl, batch, b):
+    """Host fp64 copy of request b's pages (all KV heads), page table remapped."""
     import numpy as np
-    import torch
+    from sparse_self_speculative_sss_amd import workload as W
+    P = wl.shape.page_size
+    L = int(batch.seq_lens[b])
+    n = -(-L // P)
+    pages = batch.page_table[b, :n].long().to(wl.k_cache.device)
+    k = W.to_numpy64(wl.k_cache[pages])
+    v = W.to_numpy64(wl.v_cache[pages])
+    return k, v, np.arange(n, dtype=np.int32)[None], np.array([L], dtype=np.int32)
+
+
+def cpu_baseline(wl, n_req):
+    """Time the fp64 oracle (as it stands) on up to n_req verify requests
+    (verify + block scores + Top-N) and up to n_req draft requests (draft over
+    the selection: the oracle's own for verify->draft workloads, the given
+    lists for the mixed batch).  Returns query tokens/s."""
+    import numpy as np
     import oracle
     from threadpoolctl import threadpool_info
     from sparse_self_speculative_sss_amd import workload as W
     s = wl.shape
     vb, db = wl.verify, wl.draft
-    n_req = min(n_req, vb.B)
-    q = W.to_numpy64(vb.q[:n_req])
-    qd = W.to_numpy64(db.q[:n_req])
-    elapsed = 0.0
-    for b in range(n_req):
-        L = int(vb.seq_lens[b])
-        n = -(-L // s.page_size)
-        pages = vb.page_table[b, :n].long().to(wl.k_cache.device)
-        k = W.to_numpy64(wl.k_cache[pages])
-        v = W.to_numpy64(wl.v_cache[pages])
-        table = np.arange(n, dtype=np.int32)[None]
-        lens = np.array([L], dtype=np.int32)
-        t0 = time.perf_counter()
-        _, _, sc = oracle.verify_with_scores(q[b:b + 1], k, v, table, lens, wl.sm_scale,
-                                             s.block_size, wl.max_blocks)
-        sel, cnt = oracle.block_topk(sc.astype(np.float32), lens, s.block_size,
-                                     vb.budget[b:b + 1].cpu().numpy(), s.window, wl.max_sel)
-        oracle.draft(qd[b:b + 1], k, v, table, lens, sel, cnt, s.block_size, s.window,
-                     wl.sm_scale)
-        elapsed += time.perf_counter() - t0
-        del k, v
+    shared = s.p_verify is None
+    elapsed, tokens, nv, nd = 0.0, 0, 0, 0
+    if vb is not None:
+        nv = min(n_req, vb.B)
+        q = W.to_numpy64(vb.q[:nv])
+        qd = W.to_numpy64(db.q[:nv]) if shared else None
+        for b in range(nv):
+            k, v, table, lens = _request_copy(wl, vb, b)
+            t0 = time.perf_counter()
+            _, _, sc = oracle.verify_with_scores(q[b:b + 1], k, v, table, lens, wl.sm_scale,
+                                                 s.block_size, wl.max_blocks)
+            sel, cnt = oracle.block_topk(sc.astype(np.float32), lens, s.block_size,
+                                         vb.budget[b:b + 1].cpu().numpy(), s.window, wl.max_sel)
+            if shared:
+                oracle.draft(qd[b:b + 1], k, v, table, lens, sel, cnt, s.block_size, s.window,
+                             wl.sm_scale)
+            elapsed += time.perf_counter() - t0
+            tokens += s.n_q + (1 if shared else 0)
+            del k, v
+    if not shared and db is not None:
+        nd = min(n_req, db.B)
+        qd = W.to_numpy64(db.q[:nd])
+        sel_all, cnt_all = db.sel.cpu().numpy(), db.sel_count.cpu().numpy()
+        for b in range(nd):
+            k, v, table, lens = _request_copy(wl, db, b)
+            t0 = time.perf_counter()
+            oracle.draft(qd[b:b + 1], k, v, table, lens, sel_all[b:b + 1], cnt_all[b:b + 1],
+                         s.block_size, s.window, wl.sm_scale)
+            elapsed += time.perf_counter() - t0
+            tokens += 1
+            del k, v
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    tokens = n_req * (s.n_q + 1)
+    what = (f"{nv} of {vb.B if vb else 0} verify requests" +
+            ("" if shared else f" and {nd} of {db.B if db else 0} draft requests"))
     return {"value": tokens / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"{n_req} of {vb.B} requests (all {s.Hkv} KV heads each): fp64 verify + "
-                       f"block scores, Top-N and draft, {elapsed:.1f} s wall on the host")}
+            "sample": (f"{what} (all {s.Hkv} KV heads each): fp64 verify + block scores, Top-N "
+                       f"and draft, {elapsed:.1f} s wall on the host")}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by request and KV head with no exchange; see DESIGN.md)",
+              "(attention units shard by request and KV head with no exchange; only the one-GPU share is measured)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -144,46 +203,58 @@ def main():
     print(f"[bench] generating {args.workload} seed={args.seed}", file=sys.stderr, flush=True)
     wl = W.make(args.workload, seed=args.seed, device=dev)
     s = wl.shape
-    if s.p_verify is not None:
-        print("bench.py times the single-phase workloads; use the tests for the mixed batch",
-              file=sys.stderr)
-        sys.exit(2)
     vb, db = wl.verify, wl.draft
-    B, n_q = vb.B, s.n_q
-    kv_v = sss.paged_kv(wl.k_cache, wl.v_cache, vb.page_table, vb.seq_lens, vb.max_seq_len)
-    kv_d = sss.paged_kv(wl.k_cache, wl.v_cache, db.page_table, db.seq_lens, db.max_seq_len)
+    shared = s.p_verify is None      # draft reads the selection this step's verify made
+    n_q = s.n_q
+    Bv = vb.B if vb is not None else 0
+    Bd = db.B if db is not None else 0
     vsplits = s.num_splits if args.verify_splits < 0 else args.verify_splits
-    o = torch.empty_like(vb.q)
-    lse = torch.empty((B, n_q, s.Hq), dtype=torch.float32, device=dev)
-    sc = torch.empty((B, s.Hkv, wl.max_blocks), dtype=torch.float32, device=dev)
-    sel = torch.empty((B, s.Hkv, wl.max_sel), dtype=torch.int32, device=dev)
-    cnt = torch.empty((B, s.Hkv), dtype=torch.int32, device=dev)
-    od = torch.empty_like(db.q)
-    lsed = torch.empty((B, 1, s.Hq), dtype=torch.float32, device=dev)
-    ws_v = sss.workspace(sss.verify_workspace_size(kv_v, B, n_q, s.Hq, s.block_size,
-                                                   wl.max_blocks, vsplits), dev)
-    ws_d = sss.workspace(sss.draft_workspace_size(kv_d, B, s.Hq, s.block_size, wl.max_sel,
-                                                  s.window, args.draft_splits), dev)
+    if Bv:
+        kv_v = sss.paged_kv(wl.k_cache, wl.v_cache, vb.page_table, vb.seq_lens, vb.max_seq_len)
+        o = torch.empty_like(vb.q)
+        lse = torch.empty((Bv, n_q, s.Hq), dtype=torch.float32, device=dev)
+        sc = torch.empty((Bv, s.Hkv, wl.max_blocks), dtype=torch.float32, device=dev)
+        sel = torch.empty((Bv, s.Hkv, wl.max_sel), dtype=torch.int32, device=dev)
+        cnt = torch.empty((Bv, s.Hkv), dtype=torch.int32, device=dev)
+        ws_v = sss.workspace(sss.verify_workspace_size(kv_v, Bv, n_q, s.Hq, s.block_size,
+                                                       wl.max_blocks, vsplits), dev)
+        # the verify call is a single kernel launch when its plan leaves units unsplit
+        verify_launches = 1 if sss.verify_workspace_size(kv_v, Bv, n_q, s.Hq, s.block_size,
+                                                         wl.max_blocks, vsplits) == 0 else 2
+    else:
+        verify_launches = 0
+    if Bd:
+        kv_d = sss.paged_kv(wl.k_cache, wl.v_cache, db.page_table, db.seq_lens, db.max_seq_len)
+        od = torch.empty_like(db.q)
+        lsed = torch.empty((Bd, 1, s.Hq), dtype=torch.float32, device=dev)
+        sel_d = sel if shared else db.sel
+        cnt_d = cnt if shared else db.sel_count
+        ws_d = sss.workspace(sss.draft_workspace_size(kv_d, Bd, s.Hq, s.block_size, wl.max_sel,
+                                                      s.window, args.draft_splits), dev)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        sss.verify_attn(kv_v, vb.q, wl.sm_scale, s.block_size, wl.max_blocks, o, lse, sc, ws=ws_v,
-                        num_splits=vsplits)
+        if Bv:
+            sss.verify_attn(kv_v, vb.q, wl.sm_scale, s.block_size, wl.max_blocks, o, lse, sc,
+                            ws=ws_v, num_splits=vsplits)
         if ev is not None:
             ev[1].record()
-        sss.block_topk(sc, vb.seq_lens, s.block_size, vb.budget, s.window, sel, cnt)
+        if Bv:
+            sss.block_topk(sc, vb.seq_lens, s.block_size, vb.budget, s.window, sel, cnt)
         if ev is not None:
             ev[2].record()
-        sss.draft_attn(kv_d, db.q, wl.sm_scale, s.block_size, sel, cnt, s.window, od, lsed,
-                       ws=ws_d, num_splits=args.draft_splits)
+        if Bd:
+            sss.draft_attn(kv_d, db.q, wl.sm_scale, s.block_size, sel_d, cnt_d, s.window, od,
+                           lsed, ws=ws_d, num_splits=args.draft_splits)
         if ev is not None:
             ev[3].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    nbytes = algorithmic_bytes(wl, sel.cpu().numpy(), cnt.cpu().numpy())
+    nbytes = algorithmic_bytes(wl, sel_d.cpu().numpy() if Bd else None,
+                               cnt_d.cpu().numpy() if Bd else None)
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -196,11 +267,12 @@ def main():
     v_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     t_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     d_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    tokens = B * n_q + db.B
+    tokens = Bv * n_q + Bd
     value = tokens / (ms_step / 1e3)
 
-    v_gbs = nbytes["verify"] / (v_ms * 1e-3) / 1e9
+    v_gbs = nbytes["verify"] / (v_ms * 1e-3) / 1e9 if Bv else 0.0
     unit_gbs = nbytes["total"] / (ms_step * 1e-3) / 1e9
+    lens = vb.seq_lens if Bv else db.seq_lens
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -215,19 +287,25 @@ def main():
         "dtype": s.dtype,
         "data": "synthetic (seeded; Qwen3-8B attention shape, planted heavy-hitter keys)",
         "config": {
-            "workload": s.name, "batch": B, "context": int(vb.max_seq_len), "q_heads": s.Hq,
-            "kv_heads": s.Hkv, "head_dim": s.d, "k_plus_1": n_q, "block": s.block_size,
-            "page": s.page_size, "budget_blocks": int(vb.budget[0]), "window": s.window,
+            "workload": s.name, "batch": s.B, "verify_requests": Bv, "draft_requests": Bd,
+            "context": (int(lens.max()) if s.p_verify is None
+                        else f"{int(lens.min())}..{int(lens.max())}"),
+            "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.d, "k_plus_1": n_q,
+            "block": s.block_size, "page": s.page_size, "window": s.window,
+            "budget_blocks": (int(vb.budget[0]) if s.budget_frac is None or s.p_verify is None
+                              else f"ceil({s.budget_frac} * blocks)"),
             "verify_splits": vsplits, "draft_splits": args.draft_splits,
         },
         "roofline": {
-            "kernel": "sss_verify_attn (verify attention + block-score finalize)",
+            "kernel": ("attn_mfma_kernel<verify> (the one launch of sss_verify_attn when units "
+                       "run unsplit)" if verify_launches == 1 else
+                       "sss_verify_attn (attention + split merge/score finalize launches)"),
             "bound": "hbm",
             "achieved": round(v_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(v_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(s.name) if verify_launches == 1 else None,
             "algorithmic_bytes": nbytes["verify"],
             "ms": round(v_ms, 4),
         },
@@ -236,7 +314,7 @@ def main():
             "GB/s": round(unit_gbs, 1),
             "frac": round(unit_gbs / HBM_PEAK_GBS, 4),
             "verify_ms": round(v_ms, 4), "topk_ms": round(t_ms, 4), "draft_ms": round(d_ms, 4),
-            "draft_GB/s": round(nbytes["draft"] / (d_ms * 1e-3) / 1e9, 1),
+            "draft_GB/s": round(nbytes["draft"] / (d_ms * 1e-3) / 1e9, 1) if Bd else None,
         },
     }
     if args.cpu_sample > 0:

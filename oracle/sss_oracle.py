@@ -21,7 +21,7 @@ Every step below is the plain mathematical definition written out with numpy
 (matrix products, exp/log, Python sorting).  No blocking, online softmax,
 splitting or fusion is used anywhere here.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * Causal alignment: ``seq_lens[b]`` counts every KV token of request b,
   including the n_q new query tokens, which sit at the tail; verify row i sits

@@ -68,8 +68,9 @@ def call_verify(sss, kv, **kw):
     ({}, dict(scale=float("inf")), 1),
     ({}, dict(q=4100), 1),                       # misaligned q
     ({}, dict(o=0), 1),
-    ({}, dict(wsb=16), 3),                       # workspace too small
-    ({}, dict(ws=65537), 1),                     # misaligned workspace
+    (dict(max_seq_len=1024, max_pages_per_req=64), dict(mb=64, wsb=16, splits=4), 3),
+    # (split units need a workspace for their partials: too small, misaligned)
+    (dict(max_seq_len=1024, max_pages_per_req=64), dict(mb=64, ws=65537, splits=4), 1),
 ])
 def test_verify_rejects_bad_arguments(kvkw, callkw, status):
     sss = _binding()
@@ -82,8 +83,10 @@ def test_workspace_queries():
     sss = _binding()
     kv = good_kv(sss)
     n = sss.verify_workspace_size(kv, 2, 5, 8, 16, 8, 0)
-    assert n > 0 and n % 256 == 0
-    assert sss.verify_workspace_size(kv, 2, 5, 8, 16, 8, 4) >= n
+    assert n >= 0 and n % 256 == 0
+    long_kv = good_kv(sss, max_seq_len=1024, max_pages_per_req=64)
+    n4 = sss.verify_workspace_size(long_kv, 2, 5, 8, 16, 64, 4)
+    assert n4 > 0 and n4 % 256 == 0
     assert sss.draft_workspace_size(kv, 2, 8, 16, 4, 64, 1) >= 0
     with pytest.raises(sss.SSSError):
         sss.verify_workspace_size(good_kv(sss, head_dim=65), 2, 5, 8, 16, 8, 0)
