@@ -24,9 +24,13 @@ __device__ __forceinline__ void store_out(void* o, int dtype, long long idx, flo
     reinterpret_cast<float*>(o)[idx] = v;
 }
 
+// Grid: (unit, part).  Every workgroup of a unit recomputes the unit's row
+// LSEs (S values per row, cheap) and then merges its share of the rows and
+// scores its share of the blocks, so small batches still fill the GPU.
 __global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinalizeParams p) {
   __shared__ float lse2[kMaxRows];
   const int u = blockIdx.x;
+  const int part = blockIdx.y, nparts = gridDim.y;
   const int b = u / p.num_kv_heads, h = u % p.num_kv_heads;
   const int R = p.rows, D = p.head_dim, G = p.group;
   const int L = p.seq_lens[b];
@@ -39,12 +43,18 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinalizeParams p)
     return ((long long)b * p.n_q + iq) * (p.num_kv_heads * G) + h * G + g;
   };
 
+  // this workgroup's rows and blocks
+  const int rows_per = ceil_div(R, nparts);
+  const int r_lo = min(part * rows_per, R), r_hi = min(r_lo + rows_per, R);
+  const int blk_per = ceil_div(p.max_blocks, nparts);
+  const int j_lo = min(part * blk_per, p.max_blocks), j_hi = min(j_lo + blk_per, p.max_blocks);
+
   if (!ok) {
-    for (int idx = threadIdx.x; idx < R * D; idx += kFinThreads)
+    for (int idx = r_lo * D + threadIdx.x; idx < r_hi * D; idx += kFinThreads)
       store_out(p.o, p.dtype, out_row(idx / D) * D + idx % D, qnan());
-    for (int r = threadIdx.x; r < R; r += kFinThreads) p.lse[out_row(r)] = qnan();
+    for (int r = r_lo + threadIdx.x; r < r_hi; r += kFinThreads) p.lse[out_row(r)] = qnan();
     if (p.ell)
-      for (int j = threadIdx.x; j < p.max_blocks; j += kFinThreads)
+      for (int j = j_lo + threadIdx.x; j < j_hi; j += kFinThreads)
         p.block_scores[(long long)u * p.max_blocks + j] = qnan();
     return;
   }
@@ -82,11 +92,11 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinalizeParams p)
         out = m + flog2(sum);
       }
       lse2[r] = out;
-      p.lse[out_row(r)] = out * kLn2;
+      if (r >= r_lo && r < r_hi) p.lse[out_row(r)] = out * kLn2;
     }
     __syncthreads();
     const float* op = p.o_part + (long long)u * p.num_chunks * R * D;
-    for (int idx = threadIdx.x; idx < R * D; idx += kFinThreads) {
+    for (int idx = r_lo * D + threadIdx.x; idx < r_hi * D; idx += kFinThreads) {
       const int r = idx / D, d = idx % D;
       const float tot = lse2[r];
       float acc = 0.f;
@@ -108,7 +118,7 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinalizeParams p)
   const int nblk = ceil_div(L, p.block_size);
   const float* ell = p.ell + (long long)u * p.max_blocks * R;
   const int r0 = p.score_row_start * G;
-  for (int j = threadIdx.x; j < p.max_blocks; j += kFinThreads) {
+  for (int j = j_lo + threadIdx.x; j < j_hi; j += kFinThreads) {
     float sc = 0.f;
     if (j < nblk) {
       const float* e = ell + (long long)j * R;
@@ -152,9 +162,17 @@ __global__ void merge_kernel(const float* __restrict__ o_parts, const float* __r
 }  // namespace
 
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t s) {
-  const unsigned grid = (unsigned)((long long)p.batch * p.num_kv_heads);
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(finalize_kernel, dim3(grid), dim3(kFinThreads), 0, s, p);
+  const long long units = (long long)p.batch * p.num_kv_heads;
+  if (units == 0) return hipSuccess;
+  // enough workgroups to cover the GPU: about 2048 in total, at most one
+  // per 64 blocks (scores) or per row (merge) of a unit
+  long long parts = (2048 + units - 1) / units;
+  const long long cap = (p.max_blocks + 63) / 64 > p.rows ? (p.max_blocks + 63) / 64 : p.rows;
+  if (parts > cap) parts = cap;
+  if (parts > 64) parts = 64;
+  if (parts < 1) parts = 1;
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)units, (unsigned)parts), dim3(kFinThreads), 0,
+                     s, p);
   return hipGetLastError();
 }
 
