@@ -148,11 +148,13 @@ sss_status plan_verify(const sss_paged_kv* kv, int batch, int n_q, int hq, int b
   if (chunk > (1LL << 30)) return fail(SSS_ERR_UNSUPPORTED, "chunk too large");
   pl.chunk = (int)chunk;
   pl.num_chunks = (int)((Lmax + chunk - 1) / chunk);
-  // an unsplit unit keeps its block log masses in LDS when they fit
+  // a unit that fits in one chunk keeps its block log masses in LDS when
+  // they fit; units spread over several chunks spill them to the workspace
   pl.ell_lds_floats = (long long)ceil_div(pl.chunk, block_size) * pl.rows;
-  pl.ell_in_lds = pl.mfma && pl.num_chunks == 1 &&
-                  mfma_smem_bytes(kv->head_dim, nwr, nwt, pl.ell_lds_floats) <= kMaxLds;
-  layout(pl, units, kv->head_dim, pl.ell_in_lds ? 0 : units * (long long)max_blocks * pl.rows);
+  pl.ell_in_lds =
+      pl.mfma && mfma_smem_bytes(kv->head_dim, nwr, nwt, pl.ell_lds_floats) <= kMaxLds;
+  const bool ell_global = !pl.ell_in_lds || pl.num_chunks > 1;
+  layout(pl, units, kv->head_dim, ell_global ? units * (long long)max_blocks * pl.rows : 0);
   return ok();
 }
 
@@ -335,6 +337,7 @@ sss_status sss_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
   f.block_size = block_size;
   f.max_blocks = max_blocks;
   f.score_row_start = score_row_start;
+  f.single_done = pl.mfma ? 1 : 0;
   e = launch_finalize(f, s);
   if (e != hipSuccess) return fail(SSS_ERR_HIP, "verify finalize launch: %s", hipGetErrorString(e));
   return ok();
@@ -427,6 +430,7 @@ sss_status sss_draft_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
     f.window = window;
     f.draft = 1;
     f.simple_list = pl.mfma ? 0 : 1;
+    f.single_done = pl.mfma ? 1 : 0;
     e = launch_finalize(f, s);
     if (e != hipSuccess) return fail(SSS_ERR_HIP, "draft finalize launch: %s", hipGetErrorString(e));
   }

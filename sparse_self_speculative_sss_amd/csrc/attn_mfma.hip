@@ -251,11 +251,19 @@ __device__ __forceinline__ void store_tile(const TileRegs<D, NWR>& r, char* grp,
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Largest lead (log2 units) of a row's logits over the softmax reference
+// before the reference moves: terms stay <= 256, exact in fp32 and bf16 range.
+constexpr float kRescaleSlack = 8.f;
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// PD: tiles in flight per token group (register prefetch depth).  A tile
+// shared by several row waves costs each of them only a fraction of its
+// registers, so those configurations keep two tiles in flight.
 template <int D, int NWR, int NWT, bool DRAFT>
 __global__ void __launch_bounds__(64 * NWR * NWT, 2)
     attn_mfma_kernel(AttnParams p) {
+  constexpr int PD = NWR >= 2 ? 2 : 1;
   typedef Geo<D> G;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -274,17 +282,16 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
   const int iq = row_ok ? r / p.group : 0;
   const int hq = h * p.group + (row_ok ? r % p.group : 0);
   float* lse2s = reinterpret_cast<float*>(smem + NWT * G::GROUP_BYTES + NWR * G::Q_BYTES);
-  // block log masses of the whole unit, when the unit runs unsplit in this
-  // workgroup and they fit: [block][rows]
+  // block log masses of the whole unit when it fits in this workgroup's
+  // chunk and LDS holds them: [block][rows]
   float* ell_s = lse2s + 128;
 
   const int L = p.seq_lens[b];
   const int minL = DRAFT ? 1 : p.n_q;
   const bool unit_ok =
       L >= minL && L <= p.max_seq_len && (long long)L <= (long long)p.max_pages * p.page_size;
-  const bool final_out = p.num_chunks == 1;
   if (!unit_ok) {
-    if (final_out) {
+    if (p.num_chunks == 1) {
       if (tg == 0 && row_ok) {
         bf16* o = reinterpret_cast<bf16*>(p.o);
         const long long orow = ((long long)b * p.n_q + iq) * p.num_q_heads + hq;
@@ -299,7 +306,7 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
   }
 
   // ---- this workgroup's segment range, split among token groups ----
-  int seg_lo, seg_hi, nsel = 0, ws = L;
+  int seg_lo, seg_hi, nsel = 0, ws = L, nseg = 0;
   if (!DRAFT) {
     const int t_lo = c * p.chunk_tokens;
     if (t_lo >= L) return;  // chunk past this request's length
@@ -310,11 +317,16 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
     ws = window_start(L, p.window);
     nsel = p.sel_count[(long long)b * p.num_kv_heads + h];
     nsel = nsel < 0 ? 0 : (nsel > p.max_sel ? p.max_sel : nsel);
-    const int nseg = draft_list_len_mfma(nsel, p.block_size, L, ws);
+    nseg = draft_list_len_mfma(nsel, p.block_size, L, ws);
     seg_lo = c * p.chunk_items;
     if (seg_lo >= nseg && c > 0) return;
     seg_hi = min(seg_lo + p.chunk_items, nseg);
   }
+  // a unit that fits in its first chunk is finished here (outputs, scores)
+  const bool final_out =
+      p.num_chunks == 1 || (DRAFT ? (c == 0 && nseg <= p.chunk_items)
+                                  : (c == 0 && L <= p.chunk_tokens));
+  const bool ell_lds = !DRAFT && p.ell_in_lds && final_out;
   const int per_group = (DRAFT ? p.chunk_items : p.chunk_tokens / kSeg) / NWT;
   const int g_lo = min(seg_lo + tg * per_group, seg_hi);
   const int g_hi = min(g_lo + per_group, seg_hi);
@@ -365,18 +377,27 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
   long long ell_at = -1;
   float* ell_u = p.ell + (long long)u * p.max_blocks * R;
 
-  TileRegs<D, NWR> regs;
-  Seg sa = seg_of(p, h, cur, nxt, false, 0), sb = seg_of(p, h, cur, nxt, false, 1);
-  if (seg_full(sa) && seg_full(sb))
-    load_tile<D, NWR, true>(regs, kc, vc, sa, sb, lig);
-  else
-    load_tile<D, NWR, false>(regs, kc, vc, sa, sb, lig);
+  TileRegs<D, NWR> regs[PD];
+  Seg sa[PD], sb[PD];
+#pragma unroll
+  for (int q = 0; q < PD; ++q) {
+    sa[q] = seg_of(p, h, cur, nxt, false, 2 * q);
+    sb[q] = seg_of(p, h, cur, nxt, false, 2 * q + 1);
+    if (seg_full(sa[q]) && seg_full(sb[q]))
+      load_tile<D, NWR, true>(regs[q], kc, vc, sa[q], sb[q], lig);
+    else
+      load_tile<D, NWR, false>(regs[q], kc, vc, sa[q], sb[q], lig);
+  }
 
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int t0 = 0; t0 < n_tiles; t0 += PD)
+#pragma unroll
+  for (int q = 0; q < PD; ++q) {
+    const int t = t0 + q;
+    if (t >= n_tiles) break;
     const int rel0 = 2 * t;
     const bool tile_live = g_lo + rel0 < g_hi;
-    const Seg ca = sa, cb = sb;
-    store_tile<D, NWR>(regs, grp, lig);
+    const Seg ca = sa[q], cb = sb[q];
+    store_tile<D, NWR>(regs[q], grp, lig);
     if (rel0 > 0 && (rel0 & 63) == 0) {
       // move to the next batch of descriptors; fetch the one after it
       cur = nxt;
@@ -384,19 +405,19 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
       nxt = seg_lane<DRAFT>(p, b, h, g_lo + 64 * (cur_batch + 1) + lane, g_hi, nsel, L, ws, bad);
     }
     group_sync<NWR>();
-    if (!DRAFT && !p.ell_in_lds) {
+    if (!DRAFT && !ell_lds) {
       if (ell_at >= 0) ell_u[ell_at] = ell_val;
       ell_at = -1;
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (t + 1 < n_tiles) {
-      const int ra = rel0 + 2, rb = rel0 + 3;
-      sa = seg_of(p, h, cur, nxt, (ra >> 6) != cur_batch, ra & 63);
-      sb = seg_of(p, h, cur, nxt, (rb >> 6) != cur_batch, rb & 63);
-      if (seg_full(sa) && seg_full(sb))
-        load_tile<D, NWR, true>(regs, kc, vc, sa, sb, lig);
+    if (t + PD < n_tiles) {
+      const int ra = rel0 + 2 * PD, rb = ra + 1;
+      sa[q] = seg_of(p, h, cur, nxt, (ra >> 6) != cur_batch, ra & 63);
+      sb[q] = seg_of(p, h, cur, nxt, (rb >> 6) != cur_batch, rb & 63);
+      if (seg_full(sa[q]) && seg_full(sb[q]))
+        load_tile<D, NWR, true>(regs[q], kc, vc, sa[q], sb[q], lig);
       else
-        load_tile<D, NWR, false>(regs, kc, vc, sa, sb, lig);
+        load_tile<D, NWR, false>(regs[q], kc, vc, sa[q], sb[q], lig);
     }
     if (tile_live) {
       // S^T = K Q^T
@@ -433,9 +454,23 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // lazy rescaling: the reference max m_run moves only when a row's max
+      // exceeds it by more than kRescaleSlack (log2 units), so softmax terms
+      // stay <= 2^kRescaleSlack and most tiles skip the O rescale entirely
       const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+      const bool move = (m_run == neg_inf()) || (m_new > m_run + kRescaleSlack);
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float m_tgt = move ? m_new : m_run;
+        const float alpha = (m_tgt == neg_inf()) ? 1.f : fast_exp2(m_run - m_tgt);
+        l_run *= alpha;
+        blk_run *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
+        m_run = m_tgt;
+      }
+      const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
       float pr[16];
       float psum = 0.f;
 #pragma unroll
@@ -443,12 +478,7 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
         pr[i] = fast_exp2(s[i] - m_use);
         psum += pr[i];
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
+      l_run += psum;
       // O^T += V^T P^T
       char* vt = grp + G::K_BYTES;
 #pragma unroll
@@ -479,7 +509,7 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
           const Seg& mine = hl ? cb : ca;
           if (row_ok && mine.lo < mine.hi) {
             const float v = m_use + fast_log2(hl ? bb : a);
-            if (p.ell_in_lds) {
+            if (ell_lds) {
               ell_s[(mine.t0 / kSeg) * R + r] = v;
             } else {
               ell_at = (long long)(mine.t0 / kSeg) * R + r;
@@ -487,14 +517,14 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
             }
           }
         } else {
-          blk_run = blk_run * alpha + psum;
+          blk_run += psum;
           const int tile_end = ca.t0 + 2 * kSeg;
           const bool last = (tile_end % bs == 0) || (g_lo + rel0 + 2 >= g_hi);
           if (last) {
             const float tot = blk_run + __shfl_xor(blk_run, 32);
             if (row_ok && hl == 0) {
               const float v = m_use + fast_log2(tot);
-              if (p.ell_in_lds) {
+              if (ell_lds) {
                 ell_s[(ca.t0 / bs) * R + r] = v;
               } else {
                 ell_at = (long long)(ca.t0 / bs) * R + r;
@@ -608,7 +638,7 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
     __threadfence_block();
     __syncthreads();
     const int nblk = ceil_div(L, p.block_size);
-    const float* ell = p.ell_in_lds ? ell_s : p.ell + (long long)u * p.max_blocks * R;
+    const float* ell = ell_lds ? ell_s : p.ell + (long long)u * p.max_blocks * R;
     const int r0 = p.score_row_start * p.group;
     for (int j = threadIdx.x; j < p.max_blocks; j += 64 * NWR * NWT) {
       float sc = 0.f;

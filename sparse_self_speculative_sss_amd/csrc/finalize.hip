@@ -13,6 +13,8 @@ namespace {
 
 constexpr int kFinThreads = 256;
 constexpr int kMaxRows = 128;
+constexpr int kMaxWeights = 2048;
+constexpr int kMaxStage = 8192;
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
@@ -29,6 +31,8 @@ __device__ __forceinline__ void store_out(void* o, int dtype, long long idx, flo
 // scores its share of the blocks, so small batches still fill the GPU.
 __global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinalizeParams p) {
   __shared__ float lse2[kMaxRows];
+  __shared__ float wts[kMaxWeights];  // merge weights [partial][row of this workgroup]
+  __shared__ float stage[kMaxStage];  // partial LSEs [partial][row]
   const int u = blockIdx.x;
   const int part = blockIdx.y, nparts = gridDim.y;
   const int b = u / p.num_kv_heads, h = u % p.num_kv_heads;
@@ -72,28 +76,41 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinalizeParams p)
       S = n > 0 ? ceil_div(n, p.chunk_items) : 1;
     }
     if (S > p.num_chunks) S = p.num_chunks;
+    if (S == 1 && p.single_done) return;  // the attention kernel finished this unit
     const float* lp = p.lse_part + (long long)u * p.num_chunks * R;
+    // all partial LSEs of the unit -> LDS with independent coalesced loads,
+    // then one thread per row reduces them
+    const bool staged = S * R <= kMaxStage;
+    if (staged)
+      for (int i = threadIdx.x; i < S * R; i += kFinThreads) stage[i] = lp[i];
+    __syncthreads();
     for (int r = threadIdx.x; r < R; r += kFinThreads) {
       float m = neg_inf();
       bool nan = false;
-      for (int s = 0; s < S; ++s) {
-        const float x = lp[(long long)s * R + r];
+      for (int s0 = 0; s0 < S; ++s0) {
+        const float x = staged ? stage[s0 * R + r] : lp[(long long)s0 * R + r];
         nan |= (x != x);
         m = fmaxf(m, x);
       }
-      float out;
-      if (nan) {
-        out = qnan();
-      } else if (m == neg_inf()) {
-        out = neg_inf();
-      } else {
-        float sum = 0.f;
-        for (int s = 0; s < S; ++s) sum += fexp2(lp[(long long)s * R + r] - m);
-        out = m + flog2(sum);
-      }
+      float sum = 0.f;
+      if (!nan && m != neg_inf())
+        for (int s0 = 0; s0 < S; ++s0)
+          sum += fexp2((staged ? stage[s0 * R + r] : lp[(long long)s0 * R + r]) - m);
+      const float out = nan ? qnan() : (m == neg_inf() ? neg_inf() : m + flog2(sum));
       lse2[r] = out;
       if (r >= r_lo && r < r_hi) p.lse[out_row(r)] = out * kLn2;
     }
+    __syncthreads();
+    // merge weights of this workgroup's rows, then coalesced weighted sums
+    const int nr = r_hi - r_lo;
+    const bool wfit = S * nr <= kMaxWeights;
+    if (wfit)
+      for (int i = threadIdx.x; i < S * nr; i += kFinThreads) {
+        const int s0 = i / nr, r = r_lo + i % nr;
+        const float tot = lse2[r];
+        const float x = staged ? stage[s0 * R + r] : lp[(long long)s0 * R + r];
+        wts[i] = (tot == neg_inf() || tot != tot) ? 0.f : fexp2(x - tot);
+      }
     __syncthreads();
     const float* op = p.o_part + (long long)u * p.num_chunks * R * D;
     for (int idx = r_lo * D + threadIdx.x; idx < r_hi * D; idx += kFinThreads) {
@@ -101,9 +118,10 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinalizeParams p)
       const float tot = lse2[r];
       float acc = 0.f;
       if (tot != neg_inf()) {
-        for (int s = 0; s < S; ++s) {
-          const float w = fexp2(lp[(long long)s * R + r] - tot);
-          acc += w * op[((long long)s * R + r) * D + d];
+#pragma unroll 8
+        for (int s0 = 0; s0 < S; ++s0) {
+          const float w = wfit ? wts[s0 * nr + (r - r_lo)] : fexp2(lp[(long long)s0 * R + r] - tot);
+          acc += w * op[((long long)s0 * R + r) * D + d];
         }
       }
       if (tot != tot) acc = qnan();
@@ -122,6 +140,7 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinalizeParams p)
     float sc = 0.f;
     if (j < nblk) {
       const float* e = ell + (long long)j * R;
+#pragma unroll 8
       for (int r = r0; r < R; ++r) sc += fexp2(e[r] - lse2[r]);
     }
     p.block_scores[(long long)u * p.max_blocks + j] = sc;

@@ -74,8 +74,8 @@ struct AttnParams {
   int32_t block_size, max_blocks, score_row_start;
   float* ell;
   float* block_scores;
-  int32_t ell_in_lds;      // unsplit matrix-core verify: log masses stay in LDS
-  int32_t ell_lds_floats;  // their count (blocks of the chunk x rows)
+  int32_t ell_in_lds;      // LDS holds the log masses of a unit that fits in one chunk
+  int32_t ell_lds_floats;  // their count (blocks of a chunk x rows)
   // draft
   const int32_t* sel;
   const int32_t* sel_count;
@@ -102,6 +102,7 @@ struct FinalizeParams {
   const int32_t* sel_count;
   int32_t max_sel, window, draft;
   int32_t simple_list;  // draft list enumerated token by token (vector-ALU path)
+  int32_t single_done;  // units that fit in one chunk were finished by the attention kernel
 };
 
 // Host-side launchers (each returns hipGetLastError() of its launches).
