@@ -148,11 +148,12 @@ sss_status plan_verify(const sss_paged_kv* kv, int batch, int n_q, int hq, int b
   if (chunk > (1LL << 30)) return fail(SSS_ERR_UNSUPPORTED, "chunk too large");
   pl.chunk = (int)chunk;
   pl.num_chunks = (int)((Lmax + chunk - 1) / chunk);
-  // a unit that fits in one chunk keeps its block log masses in LDS when
-  // they fit; units spread over several chunks spill them to the workspace
+  // unsplit units keep their block log masses in LDS when they fit; split
+  // units store them to the workspace (LDS room for them would cost
+  // resident workgroups)
   pl.ell_lds_floats = (long long)ceil_div(pl.chunk, block_size) * pl.rows;
-  pl.ell_in_lds =
-      pl.mfma && mfma_smem_bytes(kv->head_dim, nwr, nwt, pl.ell_lds_floats) <= kMaxLds;
+  pl.ell_in_lds = pl.mfma && pl.num_chunks == 1 &&
+                  mfma_smem_bytes(kv->head_dim, nwr, nwt, pl.ell_lds_floats) <= kMaxLds;
   const bool ell_global = !pl.ell_in_lds || pl.num_chunks > 1;
   layout(pl, units, kv->head_dim, ell_global ? units * (long long)max_blocks * pl.rows : 0);
   return ok();

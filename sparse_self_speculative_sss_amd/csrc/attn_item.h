@@ -1,0 +1,704 @@
+// Matrix-core (MFMA) paged attention for gfx950, as a workgroup-level device
+// routine: one work item = one chunk of one (request, KV head) unit, verify
+// (causal, k+1 query positions x GQA group rows, per-block probability mass)
+// or sparse draft (one query over selected blocks plus the recent window).
+// The one-item-per-workgroup kernels (attn_mfma.hip) and the persistent
+// fused step kernel (fused.hip) both run items through attn_item().
+//
+// Work decomposition.  A unit is one (request, KV head).  Its rows are the
+// n_q * G query rows sharing that KV head, padded to 32-row tiles.  A
+// workgroup holds NWT token groups of NWR waves; wave (tg, rt) owns row tile
+// rt of token group tg.  The waves of a token group load each 32-token KV
+// tile from HBM once (16-byte coalesced loads of contiguous page runs) into
+// LDS and all of them read it, so K and V are fetched once for every row of
+// the unit.  Token groups cover contiguous sub-ranges of the chunk and are
+// merged through LDS at the end.
+//
+// Per tile, with 32x32x16 bf16 MFMAs:
+//   S^T = K * Q^T   (M = 32 tokens, N = 32 rows, K = head_dim)
+//   O^T += V^T * P^T (M = 32 head dims, N = 32 rows, K = 16 tokens)
+// Both accumulators put row (lane % 32) in lane, so the online-softmax
+// rescale is lane-local and a row is shared by the lane pair (l, l ^ 32).
+// V is stored transposed in LDS in the token order that makes P^T the
+// lane's own softmax values (no shuffles between the two MFMAs).
+//
+// The routine follows SparseSpec §4.1 (PillarAttn): the verify pass keeps,
+// next to the running LSE, the log of each KV block's probability mass
+// (ell, log2 domain, in the frame of the row max at that time), so the exact
+// per-block scores can be rematerialised once the row's final LSE is known.
+#pragma once
+
+#include "sss_common.h"
+
+namespace sss {
+
+template <int D>
+struct Geo {
+  static constexpr int KS = D / 16;             // QK MFMA k-steps
+  static constexpr int MT = D / 32;             // PV M-tiles
+  static constexpr int CPT = D / 8;             // 16-byte chunks per token row
+  static constexpr int K_STRIDE = D * 2 + 16;   // LDS bytes per K row (padded)
+  static constexpr int K_BYTES = 32 * K_STRIDE;
+  static constexpr int V_BYTES = D * 64;        // V^T: D rows of 32 positions
+  static constexpr int GROUP_BYTES = K_BYTES + V_BYTES;
+  static constexpr int K_CHUNKS = 32 * CPT;
+  static constexpr int V_UNITS = 8 * CPT;       // 4 positions x one 16-byte chunk
+  static constexpr int Q_BYTES = 32 * K_STRIDE;  // Q rows of one row tile (padded)
+  static constexpr int LSE_BYTES = 128 * 4;      // final row log2-LSEs (block scores)
+};
+
+// Token groups per workgroup for a given number of 32-row tiles.
+__host__ __device__ constexpr int token_groups_for(int nwr) { return nwr == 1 ? 4 : (nwr == 2 ? 2 : 1); }
+
+// LDS bytes attn_item<D, NWR, NWT, *> uses from the start of its LDS area:
+// K/V tiles (or the token-group merge scratch, which reuses them), Q tiles,
+// row LSEs.
+__host__ __device__ constexpr size_t item_lds_bytes(int D, int nwr, int nwt) {
+  return (size_t)nwt * ((size_t)32 * (D * 2 + 16) + (size_t)D * 64) +
+         (size_t)nwr * 32 * (D * 2 + 16) + 128 * 4;
+}
+
+// What attn_item left behind.
+enum ItemStatus { kItemNone = 0, kItemFinal = 1, kItemPartial = 2 };
+
+// One work item: chunk c of unit u.
+struct Item {
+  int u, c;
+  int chunk;             // tokens (verify) or list entries (draft) per chunk
+  int single;            // every unit is one chunk (outputs are final)
+  long long part_row0;   // partial-output row of chunk 0, row 0 of the unit
+  int ell_off;           // verify: LDS byte offset of the chunk's block log
+                         // masses (-1: stored to p.ell as blocks complete)
+  int sel_off;           // draft: LDS byte offset of the unit's selection
+                         // (-1: read from p.sel / p.sel_count)
+  int nsel_s;            // the selection's length when sel_off >= 0
+};
+
+// Orders LDS writes before reads among the waves sharing a tile: a plain
+// wave-local ordering point when a token group is a single wave (LDS
+// operations of one wave complete in issue order), a workgroup barrier
+// otherwise.
+template <int NWR>
+__device__ __forceinline__ void group_sync() {
+  if (NWR == 1) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
+}
+
+struct Seg {
+  long long base;  // element offset of token t0 of this (page, head) run
+  int t0, lo, hi;  // 16-aligned start; valid tokens are [lo, hi)
+};
+
+// Descriptor of one 16-token segment, held by one lane: 64 consecutive
+// segments of a token group live in one register set, and each tile reads
+// its two descriptors with readlane, so page-table lookups are issued a whole
+// batch ahead instead of once per tile.
+struct SegLane {
+  int t0;
+  int lohi;  // (lo - t0) | ((hi - t0) << 8)
+  int pg;    // page id (0 for an empty segment)
+};
+
+// Segment k of a verify unit (16 tokens starting at 16k), or entry k of a
+// draft unit's list: first the segments of the selected blocks (only their
+// tokens before the window start), then the window.
+// The page id is loaded for every lane (the table index is clamped into the
+// request's row) and only checked when a tile reads the descriptor, so the
+// load is never waited for here.
+template <bool DRAFT>
+__device__ __forceinline__ SegLane seg_lane(const AttnParams& p, const int32_t* sel_s, int b,
+                                            int h, int k, int k_end, int nsel, int L, int ws) {
+  int t0 = 0, lo = 0, hi = 0;
+  if (k < k_end) {
+    if (!DRAFT) {
+      t0 = k * kSeg;
+      lo = t0;
+      hi = min(t0 + kSeg, L);
+    } else {
+      const int spb = p.block_size / kSeg;
+      if (k < nsel * spb) {
+        const int j = sel_s ? sel_s[k / spb]
+                            : p.sel[((long long)b * p.num_kv_heads + h) * p.max_sel + k / spb];
+        if (j >= 0 && j < ceil_div(ws, p.block_size)) {
+          t0 = j * p.block_size + kSeg * (k % spb);
+          lo = t0;
+          hi = min(t0 + kSeg, ws);
+        }
+      } else {
+        t0 = (ws / kSeg) * kSeg + kSeg * (k - nsel * spb);
+        lo = max(t0, ws);
+        hi = min(t0 + kSeg, L);
+      }
+    }
+  }
+  SegLane d;
+  d.t0 = t0;
+  d.lohi = lo < hi ? ((lo - t0) | ((hi - t0) << 8)) : 0;
+  d.pg = p.page_table[(long long)b * p.max_pages + min(t0 / p.page_size, p.max_pages - 1)];
+  return d;
+}
+
+// Descriptor idx of the current (or next) batch as uniform values.  An
+// empty segment reads page 0; a page id outside [0, num_pages) also reads
+// page 0 and sets `bad` (the unit's outputs become NaN).
+__device__ __forceinline__ Seg seg_of(const AttnParams& p, int h, const SegLane& cur,
+                                      const SegLane& nxt, bool use_nxt, int idx, int& bad) {
+  Seg s;
+  const int t0c = __builtin_amdgcn_readlane(cur.t0, idx);
+  const int t0n = __builtin_amdgcn_readlane(nxt.t0, idx);
+  const int lhc = __builtin_amdgcn_readlane(cur.lohi, idx);
+  const int lhn = __builtin_amdgcn_readlane(nxt.lohi, idx);
+  const int pgc = __builtin_amdgcn_readlane(cur.pg, idx);
+  const int pgn = __builtin_amdgcn_readlane(nxt.pg, idx);
+  s.t0 = use_nxt ? t0n : t0c;
+  const int lh = use_nxt ? lhn : lhc;
+  int pg = use_nxt ? pgn : pgc;
+  if (lh == 0) {
+    pg = 0;
+  } else if (pg < 0 || pg >= p.num_pages) {
+    bad = 1;
+    pg = 0;
+  }
+  s.lo = s.t0 + (lh & 255);
+  s.hi = s.t0 + (lh >> 8);
+  s.base = (((long long)pg * p.num_kv_heads + h) * p.page_size + (s.t0 % p.page_size)) *
+           (long long)p.head_dim;
+  return s;
+}
+
+__device__ __forceinline__ bool seg_full(const Seg& s) { return s.lo == s.t0 && s.hi == s.t0 + kSeg; }
+
+// Swizzle of the 16-byte quads of a V^T row and permutation of the rows,
+// chosen so that the transposing writes (16 lanes: 8 positions x 2 rows
+// eight apart) and the MFMA operand reads (8 lanes: 8 consecutive rows)
+// both spread over the LDS banks.
+__device__ __forceinline__ int vq_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
+__device__ __forceinline__ int vrow(int d) { return d ^ ((d >> 3) & 1); }
+
+// Position p (0..31) of the V^T tile holds tile token tau(p): within each 16,
+// positions 4..7 and 8..11 are exchanged.  This is the K-order in which a
+// lane's own S^T accumulator values form the P^T operand of the PV MFMA.
+__device__ __forceinline__ int tau_group(int g4) {  // group of 4 positions -> group of 4 tokens
+  const int w = g4 & 3;
+  return (g4 & ~3) | (w == 1 ? 2 : (w == 2 ? 1 : w));
+}
+
+template <int D, int NWR>
+struct TileRegs {
+  static constexpr int NL = 64 * NWR;
+  static constexpr int KJ = (Geo<D>::K_CHUNKS + NL - 1) / NL;
+  static constexpr int VJ = (Geo<D>::V_UNITS + NL - 1) / NL;
+  static constexpr bool K_CHUNKS_EXACT = Geo<D>::K_CHUNKS % NL == 0;
+  static constexpr bool V_UNITS_EXACT = Geo<D>::V_UNITS % NL == 0;
+  bf16x8 k[KJ];
+  bf16x8 v[VJ][4];
+};
+
+// KV bytes are read exactly once: non-temporal loads keep them from evicting
+// the lines this kernel writes and re-reads (outputs, block log masses).
+__device__ __forceinline__ bf16x8 stream_load(const bf16x8* ptr) {
+  return __builtin_nontemporal_load(ptr);
+}
+
+// K chunk ci: token ci / CPT, 16-byte column ci % CPT.  V unit ui: 4 tokens
+// (positions 4*g4 .. 4*g4+3, g4 = ui % 8) x one 16-byte column ui / 8.
+// Every load is issued unconditionally: tokens outside [lo, hi) still lie in
+// an allocated page slot (a segment's page is valid, or page 0 for an empty
+// segment), lanes past the tile's chunk count re-read the last chunk, and
+// invalid tokens are dealt with when the tile is stored (V zeroed) and
+// scored (logits masked).  Conditional loads would make the compiler wait
+// for them before the next tile's loads are issued.
+template <int D, int NWR>
+__device__ __forceinline__ void load_tile(TileRegs<D, NWR>& r, const bf16* __restrict__ kc,
+                                          const bf16* __restrict__ vc, const Seg& sa,
+                                          const Seg& sb, int lig) {
+  typedef TileRegs<D, NWR> TR;
+  typedef Geo<D> G;
+#pragma unroll
+  for (int j = 0; j < TR::KJ; ++j) {
+    int ci = lig + TR::NL * j;
+    if (!TR::K_CHUNKS_EXACT) ci = min(ci, G::K_CHUNKS - 1);
+    const int m = ci / G::CPT, c = ci % G::CPT;
+    const long long base = m < kSeg ? sa.base : sb.base;
+    r.k[j] = stream_load(reinterpret_cast<const bf16x8*>(kc + base + (long long)(m % kSeg) * D + 8 * c));
+  }
+#pragma unroll
+  for (int j = 0; j < TR::VJ; ++j) {
+    int ui = lig + TR::NL * j;
+    if (!TR::V_UNITS_EXACT) ui = min(ui, G::V_UNITS - 1);
+    const int g4 = ui & 7, c = (ui >> 3) % G::CPT;
+    const int tok0 = 4 * tau_group(g4);
+    const long long base = (tok0 < kSeg ? sa.base : sb.base) + (long long)(tok0 % kSeg) * D + 8 * c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      r.v[j][e] = stream_load(reinterpret_cast<const bf16x8*>(vc + base + (long long)e * D));
+  }
+}
+
+// Tile registers -> LDS: K rows as loaded, V transposed.  Unless both
+// segments are full, V rows of tokens outside their segment's [lo, hi) are
+// zeroed (their probabilities are 0, but the cache slots may hold non-finite
+// values).
+template <int D, int NWR>
+__device__ __forceinline__ void store_tile(TileRegs<D, NWR>& r, char* grp, int lig, const Seg& sa,
+                                           const Seg& sb, bool full) {
+  typedef TileRegs<D, NWR> TR;
+  typedef Geo<D> G;
+#pragma unroll
+  for (int j = 0; j < TR::KJ; ++j) {
+    const int ci = lig + TR::NL * j;
+    if (TR::K_CHUNKS_EXACT || ci < G::K_CHUNKS) {
+      const int m = ci / G::CPT, c = ci % G::CPT;
+      *reinterpret_cast<bf16x8*>(grp + m * G::K_STRIDE + 16 * c) = r.k[j];
+    }
+  }
+  char* vt = grp + G::K_BYTES;
+#pragma unroll
+  for (int j = 0; j < TR::VJ; ++j) {
+    const int ui = lig + TR::NL * j;
+    if (TR::V_UNITS_EXACT || ui < G::V_UNITS) {
+      const int g4 = ui & 7, c = (ui >> 3) % G::CPT;
+      if (!full) {
+        const int tok0 = 4 * tau_group(g4);
+        const Seg& sg = tok0 < kSeg ? sa : sb;
+        const bf16x8 zero = {};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = sg.t0 + tok0 % kSeg + e;
+          if (t < sg.lo || t >= sg.hi) r.v[j][e] = zero;
+        }
+      }
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const int d = 8 * c + dd;
+        bf16x4 w;
+        w[0] = r.v[j][0][dd];
+        w[1] = r.v[j][1][dd];
+        w[2] = r.v[j][2][dd];
+        w[3] = r.v[j][3][dd];
+        *reinterpret_cast<bf16x4*>(vt + vrow(d) * 64 + 16 * ((g4 >> 1) ^ vq_swz(d)) +
+                                   8 * (g4 & 1)) = w;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Largest lead (log2 units) of a row's logits over the softmax reference
+// before the reference moves: terms stay <= 256, exact in fp32 and bf16 range.
+constexpr float kRescaleSlack = 8.f;
+
+// Runs one item with all 64 * NWR * NWT threads of the workgroup over the
+// LDS area `smem` (item_lds_bytes(D, NWR, NWT) bytes; with ELL_LDS, also
+// the chunk's block log masses, chunk-blocks x rows floats at byte offset
+// it.ell_off).  Final outputs (o, lse and, for
+// verify, block_scores) are written when the unit fits in this chunk or
+// it.single is set; otherwise the normalised partial O and log2 LSE of the
+// chunk go to p.o_part / p.lse_part row it.part_row0 + c * rows, and the
+// chunk's block log masses to p.ell.  Returns the ItemStatus.
+//
+// PD: tiles in flight per token group (register prefetch depth).  A tile
+// shared by several row waves costs each of them only a fraction of its
+// registers, so those configurations keep two tiles in flight.
+template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS>
+__device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
+  constexpr int PD = NWR >= 2 ? 2 : 1;
+  constexpr int NT = 64 * NWR * NWT;
+  typedef Geo<D> G;
+
+  const int u = it.u, c = it.c;
+  const int b = u / p.num_kv_heads, h = u % p.num_kv_heads;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rt = w % NWR, tg = w / NWR;
+  const int lig = rt * 64 + lane;
+  const int hl = lane >> 5;   // half of the wave: K-half of operands
+  const int rl = lane & 31;   // row within the tile
+  const int R = p.rows;
+  const int r = rt * 32 + rl;  // unit row of this lane
+  const bool row_ok = r < R;
+  const int iq = row_ok ? r / p.group : 0;
+  const int hq = h * p.group + (row_ok ? r % p.group : 0);
+  float* lse2s = reinterpret_cast<float*>(smem + NWT * G::GROUP_BYTES + NWR * G::Q_BYTES);
+
+  const int L = p.seq_lens[b];
+  const int minL = DRAFT ? 1 : p.n_q;
+  const bool unit_ok =
+      L >= minL && L <= p.max_seq_len && (long long)L <= (long long)p.max_pages * p.page_size;
+  if (!unit_ok) {
+    // chunk 0 owns the unit's (NaN) outputs
+    if (c != 0) return kItemNone;
+    if (tg == 0 && row_ok) {
+      bf16* o = reinterpret_cast<bf16*>(p.o);
+      const long long orow = ((long long)b * p.n_q + iq) * p.num_q_heads + hq;
+      for (int d = hl; d < D; d += 2) o[orow * D + d] = from_f32<bf16>(qnan());
+      if (hl == 0) p.lse[orow] = qnan();
+    }
+    if (!DRAFT)
+      for (int j = threadIdx.x; j < p.max_blocks; j += NT)
+        p.block_scores[(long long)u * p.max_blocks + j] = qnan();
+    return kItemFinal;
+  }
+
+  // ---- this item's segment range, split among token groups ----
+  int seg_lo, seg_hi, nsel = 0, ws = L, nseg = 0;
+  if (!DRAFT) {
+    const int t_lo = c * it.chunk;
+    if (t_lo >= L) return kItemNone;  // chunk past this request's length
+    const int t_hi = min(t_lo + it.chunk, L);
+    seg_lo = t_lo / kSeg;
+    seg_hi = ceil_div(t_hi, kSeg);
+  } else {
+    ws = window_start(L, p.window);
+    nsel = it.sel_off >= 0 ? it.nsel_s : p.sel_count[(long long)b * p.num_kv_heads + h];
+    nsel = nsel < 0 ? 0 : (nsel > p.max_sel ? p.max_sel : nsel);
+    nseg = draft_list_len_mfma(nsel, p.block_size, L, ws);
+    seg_lo = c * it.chunk;
+    if (seg_lo >= nseg && c > 0) return kItemNone;
+    seg_hi = min(seg_lo + it.chunk, nseg);
+  }
+  // a unit that fits in its first chunk is finished here (outputs, scores)
+  const bool final_out =
+      it.single || (DRAFT ? (c == 0 && nseg <= it.chunk) : (c == 0 && L <= it.chunk));
+  constexpr bool ell_lds = !DRAFT && ELL_LDS;
+  // first block of the chunk (chunks hold whole blocks); the LDS copy of the
+  // block log masses holds the chunk's blocks only and is addressed by
+  // absolute block index through an offset base
+  const int blk0 = DRAFT ? 0 : c * (it.chunk / p.block_size);
+  float* const ell_s = reinterpret_cast<float*>(smem + it.ell_off) - (ptrdiff_t)blk0 * p.rows;
+  const int32_t* const sel_s =
+      (DRAFT && it.sel_off >= 0) ? reinterpret_cast<const int32_t*>(smem + it.sel_off) : nullptr;
+  const int per_group = (DRAFT ? it.chunk : it.chunk / kSeg) / NWT;
+  const int g_lo = min(seg_lo + tg * per_group, seg_hi);
+  const int g_hi = min(g_lo + per_group, seg_hi);
+  const int n_tiles = ceil_div(min(per_group, seg_hi - seg_lo), 2);  // group 0 has the most
+
+  const bf16* __restrict__ kc = reinterpret_cast<const bf16*>(p.k);
+  const bf16* __restrict__ vc = reinterpret_cast<const bf16*>(p.v);
+  char* grp = smem + tg * G::GROUP_BYTES;
+
+  int bad = 0;
+  // segment descriptors of the first two batches of 64
+  SegLane cur = seg_lane<DRAFT>(p, sel_s, b, h, g_lo + lane, g_hi, nsel, L, ws);
+  SegLane nxt = seg_lane<DRAFT>(p, sel_s, b, h, g_lo + 64 + lane, g_hi, nsel, L, ws);
+  int cur_batch = 0;
+
+  // ---- Q rows of each row tile -> LDS (the Q^T operand is read from there) ----
+  char* qtile = smem + NWT * G::GROUP_BYTES + rt * G::Q_BYTES;
+  if (tg == 0) {
+#pragma unroll
+    for (int j = 0; j < (32 * G::CPT) / 64; ++j) {
+      const int ci = lane + 64 * j;
+      const int row = ci / G::CPT, cc = ci % G::CPT;
+      const int rr = rt * 32 + row;
+      bf16x8 v = {};
+      if (rr < R) {
+        const int qi = rr / p.group, qh = h * p.group + rr % p.group;
+        v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(p.q) +
+                                             (((long long)b * p.n_q + qi) * p.num_q_heads + qh) * D +
+                                             8 * cc);
+      }
+      *reinterpret_cast<bf16x8*>(qtile + row * G::K_STRIDE + 16 * cc) = v;
+    }
+  }
+  __syncthreads();
+  const int pos_r = DRAFT ? (L - 1) : (L - p.n_q + iq);
+  const int pos_min = DRAFT ? (L - 1) : (L - p.n_q);  // smallest causal limit of the unit's rows
+
+  f32x16 oacc[G::MT];
+#pragma unroll
+  for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[mt][i] = 0.f;
+  float m_run = neg_inf(), l_run = 0.f, blk_run = 0.f;
+  // without LDS room the block log mass of a tile is stored one iteration
+  // later, ahead of the next tile's loads: stores count in the same in-order
+  // counter as loads, so a store issued after the loads would lengthen the
+  // wait for them
+  float ell_val = 0.f;
+  long long ell_at = -1;
+  float* ell_u = p.ell + (long long)u * p.max_blocks * R;
+
+  TileRegs<D, NWR> regs[PD];
+  Seg sa[PD], sb[PD];
+#pragma unroll
+  for (int q = 0; q < PD; ++q) {
+    sa[q] = seg_of(p, h, cur, nxt, false, 2 * q, bad);
+    sb[q] = seg_of(p, h, cur, nxt, false, 2 * q + 1, bad);
+    load_tile<D, NWR>(regs[q], kc, vc, sa[q], sb[q], lig);
+  }
+
+  for (int t0 = 0; t0 < n_tiles; t0 += PD)
+#pragma unroll
+  for (int q = 0; q < PD; ++q) {
+    const int t = t0 + q;
+    if (t >= n_tiles) break;
+    const int rel0 = 2 * t;
+    const bool tile_live = g_lo + rel0 < g_hi;
+    const Seg ca = sa[q], cb = sb[q];
+    const bool full = seg_full(ca) && seg_full(cb);
+    store_tile<D, NWR>(regs[q], grp, lig, ca, cb, full);
+    if (rel0 > 0 && (rel0 & 63) == 0) {
+      // move to the next batch of descriptors; fetch the one after it
+      cur = nxt;
+      ++cur_batch;
+      nxt = seg_lane<DRAFT>(p, sel_s, b, h, g_lo + 64 * (cur_batch + 1) + lane, g_hi, nsel, L, ws);
+    }
+    group_sync<NWR>();
+    if (!DRAFT && !ell_lds) {
+      if (ell_at >= 0) ell_u[ell_at] = ell_val;
+      ell_at = -1;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (t + PD < n_tiles) {
+      const int ra = rel0 + 2 * PD, rb = ra + 1;
+      sa[q] = seg_of(p, h, cur, nxt, (ra >> 6) != cur_batch, ra & 63, bad);
+      sb[q] = seg_of(p, h, cur, nxt, (rb >> 6) != cur_batch, rb & 63, bad);
+      load_tile<D, NWR>(regs[q], kc, vc, sa[q], sb[q], lig);
+    }
+    if (tile_live) {
+      // S^T = K Q^T
+      f32x16 sacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) {
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(grp + rl * G::K_STRIDE + 32 * ks + 16 * hl);
+        const bf16x8 qb =
+            *reinterpret_cast<const bf16x8*>(qtile + rl * G::K_STRIDE + 32 * ks + 16 * hl);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb, sacc, 0, 0, 0);
+      }
+      // online softmax (log2 domain); interior tiles need no mask
+      float s[16];
+      float mx = neg_inf();
+      const bool interior = full && cb.t0 + kSeg - 1 <= pos_min;
+      if (interior) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[i] = sacc[i] * p.scale_log2;
+          mx = fmaxf(mx, s[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = (i >> 2) * 8 + 4 * hl + (i & 3);
+          const Seg& sg = (m < kSeg) ? ca : cb;
+          const int tok = sg.t0 + (m % kSeg);
+          const bool ok = tok >= sg.lo && tok < sg.hi && tok <= pos_r;
+          s[i] = ok ? sacc[i] * p.scale_log2 : neg_inf();
+          mx = fmaxf(mx, s[i]);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // lazy rescaling: the reference max m_run moves only when a row's max
+      // exceeds it by more than kRescaleSlack (log2 units), so softmax terms
+      // stay <= 2^kRescaleSlack and most tiles skip the O rescale entirely
+      const float m_new = fmaxf(m_run, mx);
+      const bool move = (m_run == neg_inf()) || (m_new > m_run + kRescaleSlack);
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float m_tgt = move ? m_new : m_run;
+        const float alpha = (m_tgt == neg_inf()) ? 1.f : fast_exp2(m_run - m_tgt);
+        l_run *= alpha;
+        blk_run *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
+        m_run = m_tgt;
+      }
+      const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
+      float pr[16];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pr[i] = fast_exp2(s[i] - m_use);
+        psum += pr[i];
+      }
+      l_run += psum;
+      // O^T += V^T P^T
+      char* vt = grp + G::K_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[j] = static_cast<bf16>(pr[8 * kk + j]);
+        const int qd = 2 * kk + hl;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) {
+          const int d = 32 * mt + rl;
+          const bf16x8 va =
+              *reinterpret_cast<const bf16x8*>(vt + vrow(d) * 64 + 16 * (qd ^ vq_swz(d)));
+          oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[mt], 0, 0, 0);
+        }
+      }
+      if (!DRAFT) {
+        // per-block log mass of this row, frame m_use
+        const int bs = p.block_size;
+        if (bs == kSeg) {
+          float a = 0.f, bb = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a += pr[i];
+#pragma unroll
+          for (int i = 8; i < 16; ++i) bb += pr[i];
+          a += __shfl_xor(a, 32);
+          bb += __shfl_xor(bb, 32);
+          const Seg& mine = hl ? cb : ca;
+          if (row_ok && mine.lo < mine.hi) {
+            const float v = m_use + fast_log2(hl ? bb : a);
+            if (ell_lds) {
+              ell_s[(mine.t0 / kSeg) * R + r] = v;
+            } else {
+              ell_at = (long long)(mine.t0 / kSeg) * R + r;
+              ell_val = v;
+            }
+          }
+        } else {
+          blk_run += psum;
+          const int tile_end = ca.t0 + 2 * kSeg;
+          const bool last = (tile_end % bs == 0) || (g_lo + rel0 + 2 >= g_hi);
+          if (last) {
+            const float tot = blk_run + __shfl_xor(blk_run, 32);
+            if (row_ok && hl == 0) {
+              const float v = m_use + fast_log2(tot);
+              if (ell_lds) {
+                ell_s[(ca.t0 / bs) * R + r] = v;
+              } else {
+                ell_at = (long long)(ca.t0 / bs) * R + r;
+                ell_val = v;
+              }
+            }
+            blk_run = 0.f;
+          }
+        }
+      }
+    }
+    group_sync<NWR>();
+  }
+
+  if (!DRAFT && ell_at >= 0) ell_u[ell_at] = ell_val;
+
+  // ---- combine the lane pair, then the token groups ----
+  l_run += __shfl_xor(l_run, 32);
+  bad = __syncthreads_or(bad);
+  if (!DRAFT && ell_lds && !final_out) {
+    // the chunk's block log masses -> workspace, for the split merge
+    const int blk_end = ceil_div(min((c + 1) * it.chunk, L), p.block_size);
+    for (int i = blk0 * R + threadIdx.x; i < blk_end * R; i += NT) ell_u[i] = ell_s[i];
+  }
+  if (NWT > 1) {
+    float* red = reinterpret_cast<float*>(smem);  // [NWT-1][NWR][32][D]
+    float* ml = red + (NWT - 1) * NWR * 32 * D;   // [NWT][NWR][32] max, then sum
+    if (hl == 0) {
+      ml[(tg * NWR + rt) * 32 + rl] = m_run;
+      ml[NWT * NWR * 32 + (tg * NWR + rt) * 32 + rl] = l_run;
+    }
+    if (tg > 0) {
+      float* dst = red + (((tg - 1) * NWR + rt) * 32 + rl) * D;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = oacc[mt][4 * q4 + e];
+          *reinterpret_cast<f32x4*>(dst + 32 * mt + 8 * q4 + 4 * hl) = v4;
+        }
+    }
+    __syncthreads();
+    if (tg == 0) {
+      float mg = m_run;
+#pragma unroll
+      for (int g = 1; g < NWT; ++g) mg = fmaxf(mg, ml[(g * NWR + rt) * 32 + rl]);
+      const float mu = (mg == neg_inf()) ? 0.f : mg;
+      const float a0 = fast_exp2(m_run - mu);
+      float lsum = l_run * a0;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[mt][i] *= a0;
+#pragma unroll
+      for (int g = 1; g < NWT; ++g) {
+        const float ag = fast_exp2(ml[(g * NWR + rt) * 32 + rl] - mu);
+        lsum += ag * ml[NWT * NWR * 32 + (g * NWR + rt) * 32 + rl];
+        const float* src = red + (((g - 1) * NWR + rt) * 32 + rl) * D;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 v4 = *reinterpret_cast<const f32x4*>(src + 32 * mt + 8 * q4 + 4 * hl);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[mt][4 * q4 + e] += ag * v4[e];
+          }
+      }
+      m_run = mg;
+      l_run = lsum;
+    }
+  }
+
+  if (tg == 0 && row_ok) {
+    const bool empty = !(l_run > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_run;
+    const float lse2 = bad ? qnan() : (empty ? neg_inf() : m_run + fast_log2(l_run));
+    const float poison = bad ? qnan() : 1.f;
+    if (final_out) {
+      bf16* o = reinterpret_cast<bf16*>(p.o);
+      const long long orow = ((long long)b * p.n_q + iq) * p.num_q_heads + hq;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v4[e] = from_f32<bf16>(oacc[mt][4 * q4 + e] * inv * poison);
+          *reinterpret_cast<bf16x4*>(o + orow * D + 32 * mt + 8 * q4 + 4 * hl) = v4;
+        }
+      if (hl == 0) {
+        p.lse[orow] = lse2 * kLn2;
+        if (!DRAFT) lse2s[r] = lse2;
+      }
+    } else {
+      const long long prow = it.part_row0 + (long long)c * R + r;
+      float* op = p.o_part + prow * D;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = oacc[mt][4 * q4 + e] * inv * poison;
+          *reinterpret_cast<f32x4*>(op + 32 * mt + 8 * q4 + 4 * hl) = v4;
+        }
+      if (hl == 0) p.lse_part[prow] = lse2;
+    }
+  }
+
+  if (!DRAFT && final_out) {
+    // the whole unit ran in this item: block scores from its block log
+    // masses (LDS, or read back from L2) and the final row LSEs
+    __threadfence_block();
+    __syncthreads();
+    const int nblk = ceil_div(L, p.block_size);
+    const float* ell = ell_lds ? ell_s : ell_u;
+    const int r0 = p.score_row_start * p.group;
+    for (int j = threadIdx.x; j < p.max_blocks; j += NT) {
+      float sc = 0.f;
+      if (j < nblk) {
+        const float* e = ell + (long long)j * R;
+        for (int rr = r0; rr < R; ++rr) sc += fast_exp2(e[rr] - lse2s[rr]);
+      }
+      p.block_scores[(long long)u * p.max_blocks + j] = bad ? qnan() : sc;
+    }
+  }
+  return final_out ? kItemFinal : kItemPartial;
+}
+
+}  // namespace sss
