@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--verify-splits", type=int, default=-1,
                     help="override num_splits of the verify call (-1: workload default)")
     ap.add_argument("--draft-splits", type=int, default=0)
+    ap.add_argument("--path", choices=("auto", "separate", "fused"), default="auto",
+                    help="separate: one call per stage (verify, top-N, draft); fused: "
+                         "sss_fused_step (one work-list launch, plus merge launches for "
+                         "split units); auto: fused for mixed batches, separate otherwise "
+                         "(the faster of the two on each benchmark workload)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run device copies of this size (calibrates HBM byte counters "
                          "against a transfer of known size) and exit")
@@ -205,6 +210,8 @@ def main():
     s = wl.shape
     vb, db = wl.verify, wl.draft
     shared = s.p_verify is None      # draft reads the selection this step's verify made
+    if args.path == "auto":
+        args.path = "separate" if shared else "fused"
     n_q = s.n_q
     Bv = vb.B if vb is not None else 0
     Bd = db.B if db is not None else 0
@@ -232,7 +239,28 @@ def main():
         ws_d = sss.workspace(sss.draft_workspace_size(kv_d, Bd, s.Hq, s.block_size, wl.max_sel,
                                                       s.window, args.draft_splits), dev)
 
+    if args.path == "fused":
+        v_step = d_step = None
+        if Bv:
+            v_step = sss.verify_step(kv_v, vb.q, wl.sm_scale, s.block_size, wl.max_blocks, o, lse,
+                                     sc, budget=vb.budget, window=s.window, sel=sel,
+                                     sel_count=cnt)
+        if Bd:
+            # a shared workload drafts the verify requests over this step's
+            # selection (same cache description); a mixed one its own
+            d_step = sss.draft_step(kv_v if shared else kv_d, db.q, wl.sm_scale, s.block_size,
+                                    sel_d, cnt_d, s.window, od, lsed)
+        ws_f = sss.workspace(sss.fused_workspace_size(v_step, d_step, shared), dev)
+
     def step(ev=None):
+        if args.path == "fused":
+            if ev is not None:
+                ev[0].record()
+            sss.fused_step(v_step, d_step, chained=shared, ws=ws_f)
+            if ev is not None:
+                for e in ev[1:]:
+                    e.record()
+            return
         if ev is not None:
             ev[0].record()
         if Bv:
@@ -272,6 +300,34 @@ def main():
 
     v_gbs = nbytes["verify"] / (v_ms * 1e-3) / 1e9 if Bv else 0.0
     unit_gbs = nbytes["total"] / (ms_step * 1e-3) / 1e9
+    if args.path == "fused":
+        # one call does the whole step: its bytes are the step's bytes
+        roofline = {
+            "kernel": "sss_fused_step (fused_kernel work-list launch; plan and split-merge "
+                      "launches included in the time)",
+            "bound": "hbm",
+            "achieved": round(nbytes["total"] / (v_ms * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(nbytes["total"] / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": nbytes["total"],
+            "ms": round(v_ms, 4),
+        }
+    else:
+        roofline = {
+            "kernel": ("attn_mfma_kernel<verify> (the one launch of sss_verify_attn when units "
+                       "run unsplit)" if verify_launches == 1 else
+                       "sss_verify_attn (attention + split merge/score finalize launches)"),
+            "bound": "hbm",
+            "achieved": round(v_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(v_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(s.name) if verify_launches == 1 else None,
+            "algorithmic_bytes": nbytes["verify"],
+            "ms": round(v_ms, 4),
+        }
     lens = vb.seq_lens if Bv else db.seq_lens
     rec = {
         "metric": METRIC,
@@ -294,27 +350,16 @@ def main():
             "block": s.block_size, "page": s.page_size, "window": s.window,
             "budget_blocks": (int(vb.budget[0]) if s.budget_frac is None or s.p_verify is None
                               else f"ceil({s.budget_frac} * blocks)"),
-            "verify_splits": vsplits, "draft_splits": args.draft_splits,
+            "verify_splits": vsplits, "draft_splits": args.draft_splits, "path": args.path,
         },
-        "roofline": {
-            "kernel": ("attn_mfma_kernel<verify> (the one launch of sss_verify_attn when units "
-                       "run unsplit)" if verify_launches == 1 else
-                       "sss_verify_attn (attention + split merge/score finalize launches)"),
-            "bound": "hbm",
-            "achieved": round(v_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(v_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(s.name) if verify_launches == 1 else None,
-            "algorithmic_bytes": nbytes["verify"],
-            "ms": round(v_ms, 4),
-        },
+        "roofline": roofline,
         "step_hbm": {
             "algorithmic_bytes": nbytes["total"],
             "GB/s": round(unit_gbs, 1),
             "frac": round(unit_gbs / HBM_PEAK_GBS, 4),
             "verify_ms": round(v_ms, 4), "topk_ms": round(t_ms, 4), "draft_ms": round(d_ms, 4),
-            "draft_GB/s": round(nbytes["draft"] / (d_ms * 1e-3) / 1e9, 1) if Bd else None,
+            "draft_GB/s": (round(nbytes["draft"] / (d_ms * 1e-3) / 1e9, 1)
+                           if Bd and args.path == "separate" else None),
         },
     }
     if args.cpu_sample > 0:

@@ -18,7 +18,9 @@
  *   sss_block_topk   per (request, KV head) Top-N block list;
  *   sss_draft_attn   single-query attention over the selected blocks plus a
  *                    recent window;
- *   sss_merge        log-sum-exp merge of split-KV partials.
+ *   sss_merge        log-sum-exp merge of split-KV partials;
+ *   sss_fused_step   all of the above for a (mixed or chained) batch in one
+ *                    work-list launch.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -211,6 +213,83 @@ size_t sss_draft_workspace_size(const sss_paged_kv* kv, int32_t batch, int32_t n
  */
 sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_parts, int32_t rows,
                      int32_t head_dim, void* o, int32_t o_dtype, float* lse, void* stream);
+
+/*
+ * Fused decode step: verify, block scores, Top-N and sparse draft in one
+ * work-list launch (SparseSpec §4.2, unified batch scheduler and fused
+ * sparse/full attention: drafting and verifying requests share one
+ * balanced launch instead of running as separate kernels).
+ *
+ * The verify half computes exactly what sss_verify_attn does for its
+ * requests (o, lse, block_scores) and, when `sel` is non-NULL, what
+ * sss_block_topk does on those scores (sel, sel_count, with `budget`,
+ * `window`, `max_sel`).  The draft half computes what sss_draft_attn does
+ * for its requests.  Either half may be NULL or have batch 0.
+ *
+ * chained == 0: the halves are independent request sets (a mixed batch in
+ *   which some requests verify and the others draft).  Draft selections
+ *   are inputs and must not alias the verify half's outputs.
+ * chained != 0: the draft half drafts the verify half's own requests right
+ *   after their selection: draft->kv must describe the same cache, page
+ *   table and lengths as verify->kv, draft->batch == verify->batch,
+ *   draft->block_size == verify->block_size, draft->max_sel ==
+ *   verify->max_sel, and draft->sel / draft->sel_count must be
+ *   verify->sel / verify->sel_count (written by this call, then read).
+ *
+ * Work decomposition: one launch with a slot per possible chunk -- every
+ * verify unit (request, KV head) has ceil(max_seq_len / C) slots, every
+ * unchained draft unit ceil(longest list / C') -- verify slots first, so
+ * the small draft items fill the tail; slots past a unit's actual length
+ * exit at once.  A unit that fits in one chunk is finished inside the
+ * launch (outputs, scores, selection and, when chained, its draft).  Split
+ * units are finished by follow-up launches on the same stream (merge and
+ * scoring, selection, draft), which touch only those units.
+ *
+ * Requirements beyond those of the separate entry points: both halves use
+ * the matrix-core path (BF16 cache, page_size and block_size multiples of
+ * 16) and the same head_dim; the draft group size G <= 32; otherwise
+ * SSS_ERR_UNSUPPORTED.  workspace: at least sss_fused_workspace_size()
+ * bytes (0 when no unit can be split: NULL is then allowed), 256-byte
+ * aligned, contents irrelevant on entry.  Results equal the separate entry
+ * points' up to the rounding of split merges (bitwise for requests that
+ * run unsplit in both).
+ */
+typedef struct {
+  sss_paged_kv kv;
+  const void* q;          /* [batch][n_q][num_q_heads][head_dim] */
+  int32_t batch, n_q, num_q_heads;
+  float sm_scale;
+  int32_t block_size, score_row_start, max_blocks;
+  void* o;                /* like q */
+  float* lse;             /* [batch][n_q][num_q_heads] */
+  float* block_scores;    /* [batch][num_kv_heads][max_blocks] */
+  /* Top-N of the scores (sel == NULL: none) */
+  const int32_t* budget;  /* [batch] */
+  int32_t window;
+  int32_t* sel;           /* [batch][num_kv_heads][max_sel] */
+  int32_t* sel_count;     /* [batch][num_kv_heads] */
+  int32_t max_sel;
+} sss_verify_step;
+
+typedef struct {
+  sss_paged_kv kv;
+  const void* q;          /* [batch][1][num_q_heads][head_dim] */
+  int32_t batch, num_q_heads;
+  float sm_scale;
+  int32_t block_size;
+  const int32_t* sel;     /* [batch][num_kv_heads][max_sel] */
+  const int32_t* sel_count;
+  int32_t max_sel, window;
+  void* o;                /* like q */
+  float* lse;             /* [batch][1][num_q_heads] */
+} sss_draft_step;
+
+sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* draft,
+                          int32_t chained, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sss_fused_step needs (0 on invalid arguments). */
+size_t sss_fused_workspace_size(const sss_verify_step* verify, const sss_draft_step* draft,
+                                int32_t chained);
 
 /* Static description of a status code. */
 const char* sss_status_string(sss_status status);

@@ -1,5 +1,6 @@
 // C ABI of libsss: host-side validation, work planning and dispatch.  No
 // state survives a call except the per-thread error message.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -230,7 +231,195 @@ AttnParams base_params(const sss_paged_kv* kv, const void* q, int batch, int n_q
   p.rows = pl.rows;
   p.scale_log2 = sm_scale * kLog2e;
   p.num_chunks = pl.num_chunks;
+  p.skip_len = -1;
   return p;
+}
+
+bool same_cache(const sss_paged_kv& a, const sss_paged_kv& b) {
+  return a.k == b.k && a.v == b.v && a.dtype == b.dtype && a.num_pages == b.num_pages &&
+         a.page_size == b.page_size && a.num_kv_heads == b.num_kv_heads &&
+         a.head_dim == b.head_dim && a.max_pages_per_req == b.max_pages_per_req &&
+         a.page_table == b.page_table && a.seq_lens == b.seq_lens && a.max_seq_len == b.max_seq_len;
+}
+
+// Everything sss_fused_step derives from its arguments on the host.
+struct FusedSetup {
+  bool has_v = false, has_d = false, split_v = false, split_d = false;
+  int rows_v = 0, group_d = 0, head_dim = 0;
+  long long nv = 0, nd = 0;
+  FusedPlan pl = {};
+  Plan chain_draft = {};  // chained draft of split units (one-launch-per-stage kernels)
+  size_t ell_off = 0, opv_off = 0, lpv_off = 0, opd_off = 0,
+         lpd_off = 0, chain_off = 0, bytes = 0;
+};
+
+sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int chained,
+                       FusedSetup& fs) {
+  fs = FusedSetup();
+  fs.has_v = v && v->batch > 0;
+  fs.has_d = d && d->batch > 0;
+  if (v) {
+    Plan pv;
+    sss_status st = plan_verify(&v->kv, v->batch, v->n_q, v->num_q_heads, v->block_size,
+                                v->max_blocks, 0, pv);
+    if (st != SSS_OK) return st;
+    if (!std::isfinite(v->sm_scale)) return fail(SSS_ERR_INVALID_ARGUMENT, "verify sm_scale is not finite");
+    if (v->score_row_start < 0 || v->score_row_start >= v->n_q)
+      return fail(SSS_ERR_INVALID_ARGUMENT, "verify score_row_start %d outside [0, n_q)",
+                  v->score_row_start);
+    if (v->sel) {
+      if (v->window < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "verify window %d < 0", v->window);
+      if (v->max_sel < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "verify max_sel %d < 1", v->max_sel);
+    }
+    if (fs.has_v) {
+      if (!pv.mfma)
+        return fail(SSS_ERR_UNSUPPORTED,
+                    "fused step needs a BF16 cache with page_size and block_size multiples of 16");
+      if (!v->q || !v->o || !v->lse || !v->block_scores)
+        return fail(SSS_ERR_INVALID_ARGUMENT, "verify q, o, lse and block_scores must be non-NULL");
+      if (!aligned(v->q, 16) || !aligned(v->o, 16))
+        return fail(SSS_ERR_INVALID_ARGUMENT, "verify q and o must be 16-byte aligned");
+      if (!aligned(v->lse, 4) || !aligned(v->block_scores, 4))
+        return fail(SSS_ERR_INVALID_ARGUMENT, "verify lse and block_scores must be 4-byte aligned");
+      if (v->sel && (!v->budget || !v->sel_count || !aligned(v->sel, 4) ||
+                     !aligned(v->sel_count, 4) || !aligned(v->budget, 4)))
+        return fail(SSS_ERR_INVALID_ARGUMENT,
+                    "verify budget, sel and sel_count must be non-NULL and 4-byte aligned");
+      fs.rows_v = pv.rows;
+      fs.nv = (long long)v->batch * v->kv.num_kv_heads;
+      fs.head_dim = v->kv.head_dim;
+    }
+  }
+  int list_max_d = 0;
+  if (d) {
+    Plan pd;
+    sss_status st = plan_draft(&d->kv, d->batch, d->num_q_heads, d->block_size, d->max_sel,
+                               d->window, 0, pd);
+    if (st != SSS_OK) return st;
+    if (!std::isfinite(d->sm_scale)) return fail(SSS_ERR_INVALID_ARGUMENT, "draft sm_scale is not finite");
+    if (fs.has_d) {
+      if (!pd.mfma)
+        return fail(SSS_ERR_UNSUPPORTED,
+                    "fused step needs a BF16 cache with page_size and block_size multiples of 16");
+      if (pd.rows > 32)
+        return fail(SSS_ERR_UNSUPPORTED, "fused step drafts groups of at most 32 heads (G = %d)",
+                    pd.rows);
+      if (!d->q || !d->o || !d->lse || !d->sel || !d->sel_count)
+        return fail(SSS_ERR_INVALID_ARGUMENT, "draft q, o, lse, sel and sel_count must be non-NULL");
+      if (!aligned(d->q, 16) || !aligned(d->o, 16))
+        return fail(SSS_ERR_INVALID_ARGUMENT, "draft q and o must be 16-byte aligned");
+      if (!aligned(d->lse, 4) || !aligned(d->sel, 4) || !aligned(d->sel_count, 4))
+        return fail(SSS_ERR_INVALID_ARGUMENT, "draft lse, sel and sel_count must be 4-byte aligned");
+      if (fs.has_v && d->kv.head_dim != v->kv.head_dim)
+        return fail(SSS_ERR_UNSUPPORTED, "verify and draft head_dim differ (%d, %d)",
+                    v->kv.head_dim, d->kv.head_dim);
+      fs.group_d = pd.rows;
+      fs.head_dim = d->kv.head_dim;
+      const long long wtok = d->window > 0 ? std::min<long long>(d->window, d->kv.max_seq_len) : 0;
+      const long long lm = (long long)d->max_sel * (d->block_size / kSeg) +
+                           (wtok > 0 ? (wtok + kSeg - 1) / kSeg + 1 : 0);
+      if (lm > (1 << 28)) return fail(SSS_ERR_UNSUPPORTED, "draft list too long");
+      list_max_d = (int)lm;
+    }
+  }
+  if (chained) {
+    if (!fs.has_v || !fs.has_d)
+      return fail(SSS_ERR_INVALID_ARGUMENT, "a chained step needs both halves with batch > 0");
+    if (!v->sel) return fail(SSS_ERR_INVALID_ARGUMENT, "a chained step needs verify->sel");
+    if (d->batch != v->batch || !same_cache(d->kv, v->kv))
+      return fail(SSS_ERR_INVALID_ARGUMENT,
+                  "a chained step drafts the verify requests: batch and kv must be equal");
+    if (d->sel != v->sel || d->sel_count != v->sel_count || d->max_sel != v->max_sel ||
+        d->block_size != v->block_size)
+      return fail(SSS_ERR_INVALID_ARGUMENT,
+                  "a chained step reads the selection it writes: draft sel, sel_count, max_sel "
+                  "and block_size must equal the verify half's");
+  } else if (fs.has_v && fs.has_d && v->sel &&
+             (v->sel == d->sel || v->sel_count == d->sel_count)) {
+    return fail(SSS_ERR_INVALID_ARGUMENT,
+                "the verify half's selection output aliases the draft half's input");
+  }
+  if (!fs.has_v && !fs.has_d) return ok();
+
+  FusedPlanIn in = {};
+  in.head_dim = fs.head_dim;
+  in.rows_v = fs.has_v ? fs.rows_v : 0;
+  in.nv = fs.nv;
+  in.max_len_v = fs.has_v ? v->kv.max_seq_len : 0;
+  in.block_size_v = fs.has_v ? v->block_size : kSeg;
+  in.nd = (fs.has_d && !chained) ? (long long)d->batch * d->kv.num_kv_heads : 0;
+  in.list_max_d = list_max_d;
+  in.chained = chained ? 1 : 0;
+  in.max_sel = chained ? v->max_sel : 0;
+  fused_plan(in, fs.pl);
+  fs.nd = in.nd;
+  if (fs.has_v && fs.pl.chunk_v <= 0)
+    return fail(SSS_ERR_UNSUPPORTED, "fused step: block masses of one chunk do not fit in LDS");
+  if (fs.pl.lds_bytes > kMaxLds)
+    return fail(SSS_ERR_UNSUPPORTED, "fused step needs %zu bytes of LDS (max_sel too large?)",
+                fs.pl.lds_bytes);
+  if (fs.pl.max_items > (1LL << 30))
+    return fail(SSS_ERR_UNSUPPORTED, "fused step: too many work items");
+  fs.split_v = fs.has_v && fs.pl.maxch_v > 1;
+  fs.split_d = fs.nd > 0 && fs.pl.maxch_d > 1;
+  if (chained && fs.split_v) {
+    // split units draft after their selection, with the one-launch kernels
+    sss_status st = plan_draft(&d->kv, d->batch, d->num_q_heads, d->block_size, d->max_sel,
+                               d->window, 0, fs.chain_draft);
+    if (st != SSS_OK) return st;
+  }
+
+  const int D = fs.head_dim;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t at = off;
+    off += align_up(n, 256);
+    return at;
+  };
+  fs.ell_off = take(fs.split_v ? (size_t)fs.nv * v->max_blocks * fs.rows_v * 4 : 0);
+  fs.opv_off = take(fs.split_v ? (size_t)fs.nv * fs.pl.maxch_v * fs.rows_v * D * 4 : 0);
+  fs.lpv_off = take(fs.split_v ? (size_t)fs.nv * fs.pl.maxch_v * fs.rows_v * 4 : 0);
+  fs.opd_off = take(fs.split_d ? (size_t)fs.nd * fs.pl.maxch_d * fs.group_d * D * 4 : 0);
+  fs.lpd_off = take(fs.split_d ? (size_t)fs.nd * fs.pl.maxch_d * fs.group_d * 4 : 0);
+  fs.chain_off = take(fs.chain_draft.bytes);
+  fs.bytes = off;
+  return ok();
+}
+
+FinalizeParams finalize_of(const AttnParams& p, int dtype, bool draft, int num_chunks, int chunk,
+                           int skip_len) {
+  FinalizeParams f = {};
+  f.batch = p.batch;
+  f.num_kv_heads = p.num_kv_heads;
+  f.n_q = p.n_q;
+  f.group = p.group;
+  f.rows = p.rows;
+  f.head_dim = p.head_dim;
+  f.num_chunks = num_chunks;
+  f.chunk_tokens = draft ? 0 : chunk;
+  f.chunk_items = draft ? chunk : 0;
+  f.dtype = dtype;
+  f.seq_lens = p.seq_lens;
+  f.max_seq_len = p.max_seq_len;
+  f.max_pages = p.max_pages;
+  f.page_size = p.page_size;
+  f.o_part = p.o_part;
+  f.lse_part = p.lse_part;
+  f.o = p.o;
+  f.lse = p.lse;
+  f.ell = draft ? nullptr : p.ell;
+  f.block_scores = draft ? nullptr : p.block_scores;
+  f.block_size = p.block_size;
+  f.max_blocks = p.max_blocks;
+  f.score_row_start = p.score_row_start;
+  f.sel_count = p.sel_count;
+  f.max_sel = p.max_sel;
+  f.window = p.window;
+  f.draft = draft ? 1 : 0;
+  f.simple_list = 0;
+  f.single_done = 1;
+  f.skip_len = skip_len;
+  return f;
 }
 
 }  // namespace
@@ -339,6 +528,7 @@ sss_status sss_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
   f.max_blocks = max_blocks;
   f.score_row_start = score_row_start;
   f.single_done = pl.mfma ? 1 : 0;
+  f.skip_len = -1;
   e = launch_finalize(f, s);
   if (e != hipSuccess) return fail(SSS_ERR_HIP, "verify finalize launch: %s", hipGetErrorString(e));
   return ok();
@@ -361,7 +551,7 @@ sss_status sss_block_topk(const float* block_scores, int32_t batch, int32_t num_
       !aligned(sel, 4) || !aligned(sel_count, 4))
     return fail(SSS_ERR_INVALID_ARGUMENT, "arrays must be 4-byte aligned");
   hipError_t e = launch_topk(block_scores, batch, num_kv_heads, max_blocks, seq_lens, block_size,
-                             budget, window, sel, sel_count, max_sel,
+                             budget, window, sel, sel_count, max_sel, -1,
                              reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSS_ERR_HIP, "topk launch: %s", hipGetErrorString(e));
   return ok();
@@ -432,6 +622,7 @@ sss_status sss_draft_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
     f.draft = 1;
     f.simple_list = pl.mfma ? 0 : 1;
     f.single_done = pl.mfma ? 1 : 0;
+    f.skip_len = -1;
     e = launch_finalize(f, s);
     if (e != hipSuccess) return fail(SSS_ERR_HIP, "draft finalize launch: %s", hipGetErrorString(e));
   }
@@ -454,6 +645,130 @@ sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_p
   hipError_t e = launch_merge(o_parts, lse_parts, num_parts, rows, head_dim, o, o_dtype, lse,
                               reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSS_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t sss_fused_workspace_size(const sss_verify_step* verify, const sss_draft_step* draft,
+                                int32_t chained) {
+  FusedSetup fs;
+  if (setup_fused(verify, draft, chained, fs) != SSS_OK) return 0;
+  return fs.bytes;
+}
+
+sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* draft,
+                          int32_t chained, void* workspace, size_t workspace_bytes, void* stream) {
+  FusedSetup fs;
+  sss_status st = setup_fused(verify, draft, chained, fs);
+  if (st != SSS_OK) return st;
+  if (!fs.has_v && !fs.has_d) return ok();
+  if (workspace_bytes < fs.bytes)
+    return fail(SSS_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace_bytes,
+                fs.bytes);
+  if (fs.bytes > 0 && (!workspace || !aligned(workspace, 256)))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  AttnParams pv = {};
+  pv.skip_len = -1;
+  if (fs.has_v) {
+    const sss_verify_step* v = verify;
+    Plan pl = {};
+    pl.rows = fs.rows_v;
+    pl.num_chunks = fs.pl.maxch_v;
+    pv = base_params(&v->kv, v->q, v->batch, v->n_q, v->num_q_heads, v->sm_scale, pl);
+    pv.chunk_tokens = fs.pl.chunk_v;
+    pv.o_part = reinterpret_cast<float*>(ws + fs.opv_off);
+    pv.lse_part = reinterpret_cast<float*>(ws + fs.lpv_off);
+    pv.o = v->o;
+    pv.lse = v->lse;
+    pv.block_size = v->block_size;
+    pv.max_blocks = v->max_blocks;
+    pv.score_row_start = v->score_row_start;
+    pv.ell = reinterpret_cast<float*>(ws + fs.ell_off);
+    pv.block_scores = v->block_scores;
+  }
+  AttnParams pd = {};
+  pd.skip_len = -1;
+  if (fs.has_d) {
+    const sss_draft_step* d = draft;
+    Plan pl = {};
+    pl.rows = fs.group_d;
+    pl.num_chunks = std::max(fs.pl.maxch_d, 1);
+    pd = base_params(&d->kv, d->q, d->batch, 1, d->num_q_heads, d->sm_scale, pl);
+    pd.chunk_items = fs.pl.chunk_d;
+    pd.o_part = reinterpret_cast<float*>(ws + fs.opd_off);
+    pd.lse_part = reinterpret_cast<float*>(ws + fs.lpd_off);
+    pd.o = d->o;
+    pd.lse = d->lse;
+    pd.block_size = d->block_size;
+    pd.sel = d->sel;
+    pd.sel_count = d->sel_count;
+    pd.max_sel = d->max_sel;
+    pd.window = d->window;
+  }
+  FusedParams f = {};
+  f.nv_units = (int32_t)fs.nv;
+  f.nd_units = (int32_t)fs.nd;
+  f.chunk_v = fs.pl.chunk_v;
+  f.maxch_v = fs.pl.maxch_v;
+  f.chunk_d = fs.pl.chunk_d;
+  f.maxch_d = fs.pl.maxch_d;
+  const bool topk = fs.has_v && verify->sel;
+  f.topk = topk ? 1 : 0;
+  if (topk) {
+    f.topk_window = verify->window;
+    f.max_sel = verify->max_sel;
+    f.budget = verify->budget;
+    f.sel = verify->sel;
+    f.sel_count = verify->sel_count;
+  }
+  f.chained = chained ? 1 : 0;
+  f.off_ell = fs.pl.off_ell;
+  f.off_sel = fs.pl.off_sel;
+  hipError_t e = launch_fused(f, pv, pd, fs.pl, fs.head_dim, s);
+  if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step launch: %s", hipGetErrorString(e));
+
+  // units split over several chunks: merge and score, select, then draft
+  if (fs.split_v) {
+    // a unit's partials small enough for one workgroup: merge, score and
+    // select in one launch; otherwise spread the merge, then select
+    const size_t unit_partials = (size_t)fs.pl.maxch_v * fs.rows_v * fs.head_dim * 4;
+    if (unit_partials <= ((size_t)1 << 20)) {
+      e = launch_fused_finish(f, pv, s);
+      if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step finish launch: %s", hipGetErrorString(e));
+    } else {
+      e = launch_finalize(finalize_of(pv, SSS_BF16, false, fs.pl.maxch_v, fs.pl.chunk_v,
+                                      fs.pl.chunk_v), s);
+      if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step merge launch: %s", hipGetErrorString(e));
+      if (topk) {
+        e = launch_topk(verify->block_scores, verify->batch, verify->kv.num_kv_heads,
+                        verify->max_blocks, verify->kv.seq_lens, verify->block_size,
+                        verify->budget, verify->window, verify->sel, verify->sel_count,
+                        verify->max_sel, fs.pl.chunk_v, s);
+        if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step topk launch: %s", hipGetErrorString(e));
+      }
+    }
+    if (chained) {
+      const Plan& cp = fs.chain_draft;
+      AttnParams q = pd;
+      q.num_chunks = cp.num_chunks;
+      q.chunk_tokens = 0;
+      q.chunk_items = cp.chunk;
+      q.o_part = reinterpret_cast<float*>(ws + fs.chain_off + cp.opart_off);
+      q.lse_part = reinterpret_cast<float*>(ws + fs.chain_off + cp.lpart_off);
+      q.skip_len = fs.pl.chunk_v;
+      e = launch_draft_mfma(q, s);
+      if (e == hipSuccess && cp.num_chunks > 1)
+        e = launch_finalize(finalize_of(q, SSS_BF16, true, cp.num_chunks, cp.chunk, fs.pl.chunk_v),
+                            s);
+      if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step draft launch: %s", hipGetErrorString(e));
+    }
+  }
+  if (fs.split_d) {
+    e = launch_finalize(finalize_of(pd, SSS_BF16, true, fs.pl.maxch_d, fs.pl.chunk_d, -1), s);
+    if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step merge launch: %s", hipGetErrorString(e));
+  }
   return ok();
 }
 

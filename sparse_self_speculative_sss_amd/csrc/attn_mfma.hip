@@ -9,6 +9,8 @@ namespace {
 template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS>
 __global__ void __launch_bounds__(64 * NWR * NWT, 2) attn_mfma_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  if (p.skip_len >= 0 && p.seq_lens[(blockIdx.x / p.num_chunks) / p.num_kv_heads] <= p.skip_len)
+    return;
   Item it;
   it.u = blockIdx.x / p.num_chunks;
   it.c = blockIdx.x % p.num_chunks;

@@ -38,6 +38,7 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinalizeParams p)
   const int b = u / p.num_kv_heads, h = u % p.num_kv_heads;
   const int R = p.rows, D = p.head_dim, G = p.group;
   const int L = p.seq_lens[b];
+  if (p.skip_len >= 0 && L <= p.skip_len) return;
   const int minL = p.draft ? 1 : p.n_q;
   const bool ok =
       L >= minL && L <= p.max_seq_len && (long long)L <= (long long)p.max_pages * p.page_size;

@@ -80,6 +80,9 @@ struct AttnParams {
   const int32_t* sel;
   const int32_t* sel_count;
   int32_t max_sel, window;
+  // >= 0: units whose request length is <= skip_len were finished by the
+  // fused step kernel and are skipped; -1: none
+  int32_t skip_len;
 };
 
 // Finalize a verify or draft launch: merge split partials (if any) and, for
@@ -103,16 +106,63 @@ struct FinalizeParams {
   int32_t max_sel, window, draft;
   int32_t simple_list;  // draft list enumerated token by token (vector-ALU path)
   int32_t single_done;  // units that fit in one chunk were finished by the attention kernel
+  int32_t skip_len;     // as in AttnParams
 };
 
+// Fused step (fused.hip): work-list shape and in-kernel selection state.  The
+// verify and draft halves use their own AttnParams; unit indices are
+// (request, KV head) of each half.  Split units keep the partial layout of
+// the one-launch-per-stage path ([unit][maxch][rows]...), so the same merge
+// and selection kernels finish them.
+struct FusedParams {
+  int32_t nv_units;    // verify units (0: no verify half)
+  int32_t nd_units;    // draft units run as separate items (0: none / chained)
+  int32_t chunk_v, maxch_v;  // tokens per verify chunk; chunks of the longest unit
+  int32_t chunk_d, maxch_d;  // list entries per draft chunk; chunks of the longest list
+  // Top-N of the verify units (topk == 0: scores only)
+  int32_t topk, topk_window, max_sel, chained;
+  const int32_t* budget;
+  int32_t* sel;
+  int32_t* sel_count;
+  // LDS byte offsets: block log masses of a verify chunk, the selection
+  int32_t off_ell, off_sel;
+};
+
+struct FusedPlanIn {
+  int32_t head_dim;
+  int32_t rows_v;        // n_q * G of the verify half (0: none)
+  long long nv;          // verify units
+  int32_t max_len_v, block_size_v;
+  long long nd;          // draft units run as items
+  int32_t list_max_d;    // longest draft list (16-token entries)
+  int32_t chained, max_sel;
+};
+
+struct FusedPlan {
+  int32_t nwr, nwt;
+  int32_t chunk_v, maxch_v, chunk_d, maxch_d;
+  int32_t off_ell, off_sel;
+  size_t lds_bytes;
+  long long max_items;
+};
+
+void fused_plan(const FusedPlanIn& in, FusedPlan& pl);
+
 // Host-side launchers (each returns hipGetLastError() of its launches).
+hipError_t launch_fused(const FusedParams& f, const AttnParams& pv, const AttnParams& pd,
+                        const FusedPlan& pl, int head_dim, hipStream_t s);
+// One workgroup per split verify unit: merge, scores and selection.
+hipError_t launch_fused_finish(const FusedParams& f, const AttnParams& pv, hipStream_t s);
 hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s);
 hipError_t launch_draft_mfma(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_simple(const AttnParams& p, int dtype, bool draft, hipStream_t s);
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t s);
+// skip_len >= 0: units whose request length is <= skip_len are left alone
+// (the fused step kernel finished them); -1: every unit.
 hipError_t launch_topk(const float* scores, int batch, int hkv, int max_blocks,
                        const int32_t* seq_lens, int block_size, const int32_t* budget,
-                       int window, int32_t* sel, int32_t* sel_count, int max_sel, hipStream_t s);
+                       int window, int32_t* sel, int32_t* sel_count, int max_sel, int skip_len,
+                       hipStream_t s);
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, int num_parts, int rows,
                         int head_dim, void* o, int o_dtype, float* lse, hipStream_t s);
 

@@ -11,10 +11,12 @@ __global__ void __launch_bounds__(kTopkThreads)
     topk_kernel(const float* __restrict__ scores, int hkv, int max_blocks,
                 const int32_t* __restrict__ seq_lens, int bs, const int32_t* __restrict__ budget,
                 int window, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
-                int max_sel) {
+                int max_sel, int skip_len) {
   __shared__ int lds[kTopkLdsWords];
   const int u = blockIdx.x;
   const int b = u / hkv;
+  // units no longer than skip_len were selected by the fused step kernel
+  if (skip_len >= 0 && seq_lens[b] <= skip_len) return;
   int ncand, n;
   topk_bounds(seq_lens[b], bs, window, max_blocks, budget[b], max_sel, ncand, n);
   if (threadIdx.x == 0) sel_count[u] = n;
@@ -26,11 +28,12 @@ __global__ void __launch_bounds__(kTopkThreads)
 
 hipError_t launch_topk(const float* scores, int batch, int hkv, int max_blocks,
                        const int32_t* seq_lens, int block_size, const int32_t* budget, int window,
-                       int32_t* sel, int32_t* sel_count, int max_sel, hipStream_t s) {
+                       int32_t* sel, int32_t* sel_count, int max_sel, int skip_len,
+                       hipStream_t s) {
   const unsigned grid = (unsigned)((long long)batch * hkv);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(topk_kernel, dim3(grid), dim3(kTopkThreads), 0, s, scores, hkv, max_blocks,
-                     seq_lens, block_size, budget, window, sel, sel_count, max_sel);
+                     seq_lens, block_size, budget, window, sel, sel_count, max_sel, skip_len);
   return hipGetLastError();
 }
 

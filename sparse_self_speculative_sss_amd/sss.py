@@ -54,6 +54,33 @@ _lib.sss_draft_workspace_size.argtypes = [ctypes.POINTER(PagedKV), _c_int, _c_in
                                           _c_int, _c_int]
 _lib.sss_merge.restype = _c_int
 _lib.sss_merge.argtypes = [_fp, _fp, _c_int, _c_int, _c_int, _vp, _c_int, _fp, _vp]
+
+
+class VerifyStep(ctypes.Structure):
+    """sss_verify_step (include/sss.h)."""
+    _fields_ = [
+        ("kv", PagedKV), ("q", _vp), ("batch", _c_int), ("n_q", _c_int), ("num_q_heads", _c_int),
+        ("sm_scale", ctypes.c_float), ("block_size", _c_int), ("score_row_start", _c_int),
+        ("max_blocks", _c_int), ("o", _vp), ("lse", _vp), ("block_scores", _vp), ("budget", _vp),
+        ("window", _c_int), ("sel", _vp), ("sel_count", _vp), ("max_sel", _c_int),
+    ]
+
+
+class DraftStep(ctypes.Structure):
+    """sss_draft_step (include/sss.h)."""
+    _fields_ = [
+        ("kv", PagedKV), ("q", _vp), ("batch", _c_int), ("num_q_heads", _c_int),
+        ("sm_scale", ctypes.c_float), ("block_size", _c_int), ("sel", _vp), ("sel_count", _vp),
+        ("max_sel", _c_int), ("window", _c_int), ("o", _vp), ("lse", _vp),
+    ]
+
+
+_lib.sss_fused_step.restype = _c_int
+_lib.sss_fused_step.argtypes = [ctypes.POINTER(VerifyStep), ctypes.POINTER(DraftStep), _c_int,
+                                _vp, ctypes.c_size_t, _vp]
+_lib.sss_fused_workspace_size.restype = ctypes.c_size_t
+_lib.sss_fused_workspace_size.argtypes = [ctypes.POINTER(VerifyStep), ctypes.POINTER(DraftStep),
+                                          _c_int]
 _lib.sss_status_string.restype = ctypes.c_char_p
 _lib.sss_status_string.argtypes = [_c_int]
 _lib.sss_last_error.restype = ctypes.c_char_p
@@ -62,8 +89,8 @@ _lib.sss_version.restype = _c_int
 _lib.sss_version.argtypes = []
 
 EXPORTED = ["sss_verify_attn", "sss_verify_workspace_size", "sss_block_topk", "sss_draft_attn",
-            "sss_draft_workspace_size", "sss_merge", "sss_status_string", "sss_last_error",
-            "sss_version"]
+            "sss_draft_workspace_size", "sss_merge", "sss_fused_step", "sss_fused_workspace_size",
+            "sss_status_string", "sss_last_error", "sss_version"]
 
 
 class SSSError(RuntimeError):
@@ -172,6 +199,52 @@ def merge(o_parts, lse_parts, o, lse=None):
                           _ptr(lse), _stream()),
            "sss_merge")
     return o, lse
+
+
+def verify_step(kv: PagedKV, q, sm_scale, block_size, max_blocks, o, lse, block_scores,
+                score_row_start=0, budget=None, window=0, sel=None, sel_count=None) -> VerifyStep:
+    """Verify half of a fused step (tensors as for verify_attn; with sel /
+    sel_count / budget, the step also selects, as block_topk does)."""
+    B, n_q, hq, _ = q.shape
+    return VerifyStep(kv=kv, q=q.data_ptr(), batch=B, n_q=n_q, num_q_heads=hq,
+                      sm_scale=float(sm_scale), block_size=block_size,
+                      score_row_start=score_row_start, max_blocks=max_blocks, o=o.data_ptr(),
+                      lse=lse.data_ptr(), block_scores=block_scores.data_ptr(),
+                      budget=None if budget is None else budget.data_ptr(), window=int(window),
+                      sel=None if sel is None else sel.data_ptr(),
+                      sel_count=None if sel_count is None else sel_count.data_ptr(),
+                      max_sel=0 if sel is None else sel.shape[2])
+
+
+def draft_step(kv: PagedKV, q, sm_scale, block_size, sel, sel_count, window, o, lse) -> DraftStep:
+    """Draft half of a fused step (tensors as for draft_attn)."""
+    B, _, hq, _ = q.shape
+    return DraftStep(kv=kv, q=q.data_ptr(), batch=B, num_q_heads=hq, sm_scale=float(sm_scale),
+                     block_size=block_size, sel=sel.data_ptr(), sel_count=sel_count.data_ptr(),
+                     max_sel=sel.shape[2], window=int(window), o=o.data_ptr(), lse=lse.data_ptr())
+
+
+def _byref_or_null(x, ctype):
+    return ctypes.byref(x) if x is not None else ctypes.POINTER(ctype)()
+
+
+def fused_workspace_size(verify=None, draft=None, chained=False) -> int:
+    n = _lib.sss_fused_workspace_size(_byref_or_null(verify, VerifyStep),
+                                      _byref_or_null(draft, DraftStep), int(bool(chained)))
+    if n == 0 and _lib.sss_last_error():
+        raise SSSError(SSS_ERR_INVALID_ARGUMENT, "sss_fused_workspace_size")
+    return n
+
+
+def fused_step(verify=None, draft=None, chained=False, ws=None, device=None):
+    """sss_fused_step: one work-list launch for a verify half and a draft
+    half (chained: the draft half drafts the verify requests over the
+    selection this call makes)."""
+    if ws is None:
+        ws = workspace(fused_workspace_size(verify, draft, chained), device or "cuda")
+    _check(_lib.sss_fused_step(_byref_or_null(verify, VerifyStep), _byref_or_null(draft, DraftStep),
+                               int(bool(chained)), _ptr(ws), ws.numel(), _stream()),
+           "sss_fused_step")
 
 
 def raw():

@@ -113,3 +113,114 @@ def test_other_entry_points_reject_bad_arguments():
     assert call_verify(sss, kv, batch=0) == 0
     for st in range(5):
         assert lib.sss_status_string(st).startswith(b"SSS_")
+
+
+# --------------------------------------------------------------------------
+# fused step: struct layout and host-side validation (nothing is launched)
+# --------------------------------------------------------------------------
+LAYOUT_C = r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "sss.h"
+#define F(T, f) printf(#T " " #f " %zu\n", offsetof(T, f));
+int main(void) {
+  printf("sss_paged_kv size %zu\n", sizeof(sss_paged_kv));
+  printf("sss_verify_step size %zu\n", sizeof(sss_verify_step));
+  printf("sss_draft_step size %zu\n", sizeof(sss_draft_step));
+  F(sss_paged_kv, k) F(sss_paged_kv, v) F(sss_paged_kv, dtype) F(sss_paged_kv, num_pages)
+  F(sss_paged_kv, page_size) F(sss_paged_kv, num_kv_heads) F(sss_paged_kv, head_dim)
+  F(sss_paged_kv, max_pages_per_req) F(sss_paged_kv, page_table) F(sss_paged_kv, seq_lens)
+  F(sss_paged_kv, max_seq_len)
+  F(sss_verify_step, kv) F(sss_verify_step, q) F(sss_verify_step, batch) F(sss_verify_step, n_q)
+  F(sss_verify_step, num_q_heads) F(sss_verify_step, sm_scale) F(sss_verify_step, block_size)
+  F(sss_verify_step, score_row_start) F(sss_verify_step, max_blocks) F(sss_verify_step, o)
+  F(sss_verify_step, lse) F(sss_verify_step, block_scores) F(sss_verify_step, budget)
+  F(sss_verify_step, window) F(sss_verify_step, sel) F(sss_verify_step, sel_count)
+  F(sss_verify_step, max_sel)
+  F(sss_draft_step, kv) F(sss_draft_step, q) F(sss_draft_step, batch) F(sss_draft_step, num_q_heads)
+  F(sss_draft_step, sm_scale) F(sss_draft_step, block_size) F(sss_draft_step, sel)
+  F(sss_draft_step, sel_count) F(sss_draft_step, max_sel) F(sss_draft_step, window)
+  F(sss_draft_step, o) F(sss_draft_step, lse)
+  return 0;
+}
+'''
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """The binding's ctypes structures have the C header's field offsets."""
+    import shutil
+    import subprocess
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not available")
+    src = tmp_path / "layout.c"
+    exe = tmp_path / "layout"
+    src.write_text(LAYOUT_C)
+    subprocess.run(["gcc", "-I", os.path.dirname(HDR), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    sss = _binding()
+    types = {"sss_paged_kv": sss.PagedKV, "sss_verify_step": sss.VerifyStep,
+             "sss_draft_step": sss.DraftStep}
+    for line in out.splitlines():
+        t, f, n = line.split()
+        if f == "size":
+            assert ctypes.sizeof(types[t]) == int(n), line
+        else:
+            assert getattr(types[t], f).offset == int(n), line
+
+
+def fused_args(sss, vkw=None, dkw=None, kvkw=None):
+    kv = good_kv(sss, **(kvkw or {}))
+    v = dict(kv=kv, q=4096, batch=2, n_q=5, num_q_heads=8, sm_scale=0.1, block_size=16,
+             score_row_start=0, max_blocks=8, o=8192, lse=16384, block_scores=32768, budget=256,
+             window=64, sel=1 << 20, sel_count=1 << 21, max_sel=4)
+    v.update(vkw or {})
+    d = dict(kv=kv, q=12288, batch=2, num_q_heads=8, sm_scale=0.1, block_size=16, sel=1 << 20,
+             sel_count=1 << 21, max_sel=4, window=64, o=20480, lse=24576)
+    d.update(dkw or {})
+    return sss.VerifyStep(**v), sss.DraftStep(**d)
+
+
+def call_fused(sss, v, d, chained, wsb=1 << 30):
+    return sss.raw().sss_fused_step(None if v is None else ctypes.byref(v),
+                                    None if d is None else ctypes.byref(d), chained, 1 << 22, wsb,
+                                    None)
+
+
+@pytest.mark.parametrize("vkw,dkw,kvkw,chained,status", [
+    ({}, dict(sel=1 << 23), {}, 1, 1),                  # chained draft must read verify's selection
+    ({}, dict(batch=1), {}, 1, 1),                      # chained batches differ
+    ({}, dict(max_sel=3), {}, 1, 1),
+    (dict(sel=None), {}, {}, 1, 1),                     # chained step needs a selection
+    ({}, {}, {}, 0, 1),                                 # unchained: output aliases input
+    ({}, {}, dict(dtype=0), 0, 2),                      # fp32 cache: no matrix-core path
+    (dict(n_q=0), {}, {}, 0, 1),
+    (dict(window=-1), dict(sel=1 << 23, sel_count=1 << 24), {}, 0, 1),
+    ({}, dict(sel=1 << 23, sel_count=1 << 24, num_q_heads=2 * 64), {}, 0, 2),   # draft G = 64
+])
+def test_fused_rejects_bad_arguments(vkw, dkw, kvkw, chained, status):
+    sss = _binding()
+    v, d = fused_args(sss, vkw, dkw, kvkw)
+    assert call_fused(sss, v, d, chained) == status
+    assert sss.raw().sss_last_error()
+
+
+def test_fused_workspace_query_and_size_check():
+    sss = _binding()
+    # short requests: every unit fits in one chunk, nothing to stage
+    v, d = fused_args(sss)
+    assert sss.fused_workspace_size(v, d, True) == 0
+    # long requests: units split, partials and block masses are staged
+    long_kv = dict(max_seq_len=8192, max_pages_per_req=512)
+    v, d = fused_args(sss, vkw=dict(max_blocks=512), kvkw=long_kv)
+    n = sss.fused_workspace_size(v, d, True)
+    assert n > 0 and n % 256 == 0
+    assert call_fused(sss, v, d, 1, wsb=n - 1) == 3
+    v2, d2 = fused_args(sss, vkw=dict(max_blocks=512), dkw=dict(sel=1 << 23, sel_count=1 << 24),
+                        kvkw=long_kv)
+    assert sss.fused_workspace_size(v2, d2, False) > 0
+    d3 = fused_args(sss, dkw=dict(max_sel=600), kvkw=long_kv)[1]
+    assert sss.fused_workspace_size(None, d3, False) > 0
+    # nothing to do: a successful no-op
+    assert call_fused(sss, None, None, 0) == 0
+    v0, d0 = fused_args(sss, vkw=dict(batch=0), dkw=dict(batch=0))
+    assert call_fused(sss, v0, d0, 0) == 0

@@ -1,0 +1,260 @@
+"""GPU parity of the fused step (sss_fused_step) against the fp64 oracle,
+through the C ABI.
+
+Chained steps (verify -> block scores -> Top-N -> draft of the same
+requests) are checked stage by stage: verify outputs and scores against the
+oracle; the selection bit-exactly against the oracle's Top-N run on the
+step's own fp32 scores; the draft against the oracle's draft over the
+step's own selection.  Mixed steps (some requests verify, the others draft
+over given selections) are checked the same way.  Small lengths force the
+work list to split units into many chunks, so the last-arrival merge runs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import harness as H
+import oracle
+from sparse_self_speculative_sss_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def mk(name, seed=0, **kw):
+    return W.make(name, seed=seed, device=DEV, **kw)
+
+
+def verify_outputs(wl, vb, with_sel=True):
+    B, n_q, hq, _ = vb.q.shape
+    hkv = wl.shape.Hkv
+    o = torch.full_like(vb.q, float("nan"))
+    lse = torch.full((B, n_q, hq), float("nan"), device=DEV)
+    sc = torch.full((B, hkv, wl.max_blocks), float("nan"), device=DEV)
+    sel = torch.full((B, hkv, wl.max_sel), 777, dtype=torch.int32, device=DEV) if with_sel else None
+    cnt = torch.full((B, hkv), -9, dtype=torch.int32, device=DEV) if with_sel else None
+    return o, lse, sc, sel, cnt
+
+
+def run_chained(wl, score_row_start=0, ws=None):
+    s = H.sss()
+    vb, db = wl.verify, wl.draft
+    o, lse, sc, sel, cnt = verify_outputs(wl, vb)
+    od = torch.full_like(db.q, float("nan"))
+    lsed = torch.full(db.q.shape[:3], float("nan"), device=DEV)
+    kv = H.kv_of(wl, vb)
+    v = s.verify_step(kv, vb.q, wl.sm_scale, wl.shape.block_size, wl.max_blocks, o, lse, sc,
+                      score_row_start=score_row_start, budget=vb.budget, window=wl.shape.window,
+                      sel=sel, sel_count=cnt)
+    d = s.draft_step(kv, db.q, wl.sm_scale, wl.shape.block_size, sel, cnt, wl.shape.window, od,
+                     lsed)
+    s.fused_step(v, d, chained=True, ws=ws)
+    torch.cuda.synchronize()
+    return (o, lse, sc), (sel, cnt), (od, lsed)
+
+
+def check_selection(wl, batch, sc, sel, cnt, units=None):
+    """Selection == oracle Top-N of the step's own fp32 scores (bit-exact)."""
+    scores = sc.cpu().numpy().astype(np.float32)
+    ref_sel, ref_cnt = oracle.block_topk(scores, batch.seq_lens.cpu().numpy(), wl.shape.block_size,
+                                         batch.budget.cpu().numpy(), wl.shape.window, wl.max_sel)
+    assert np.array_equal(cnt.cpu().numpy(), ref_cnt)
+    assert np.array_equal(sel.cpu().numpy(), ref_sel)
+    return sel.cpu().numpy(), cnt.cpu().numpy()
+
+
+CHAINED = [
+    ("qwen_ragged", "qwen3_8b_layer_b16_l4096", dict(B=3, L=300)),
+    ("decode_small", "decode_b128_l8192", dict(B=4, L=1000, sigma="one")),
+    ("decode_nq1", "qwen3_8b_layer_b16_l4096", dict(B=3, L=77, n_q=1, sigma="one")),
+    ("L_eq_nq", "qwen3_8b_layer_b16_l4096", dict(B=2, L=5, window=0, sigma="one")),
+    ("d64", "decode_b128_l8192", dict(B=2, L=200, d=64, sigma="one")),
+    ("page16_blk64", "qwen3_8b_layer_b16_l4096", dict(B=2, L=700, block_size=64, sigma="one")),
+    ("page64_blk64_rows80", "longctx_b4_l128k", dict(B=1, L=2000, sigma="one")),
+    ("rows40", "qwen3_8b_layer_b16_l4096", dict(B=2, L=333, Hq=16, Hkv=2, sigma="one")),
+    ("rows128", "qwen3_8b_layer_b16_l4096", dict(B=1, L=400, Hq=32, Hkv=1, n_q=4)),
+]
+
+
+@pytest.mark.parametrize("case", CHAINED, ids=[c[0] for c in CHAINED])
+def test_fused_chained(case):
+    cid, name, kw = case
+    wl = mk(name, seed=31, **kw)
+    vb, db = wl.verify, wl.draft
+    hkv = wl.shape.Hkv
+    print(f"[fused chained] {cid}", flush=True)
+    v_out, (sel, cnt), d_out = run_chained(wl)
+    units = H.all_units(vb, hkv)
+    H.compare_verify(wl, vb, v_out, units).check(f"fused {cid} verify")
+    sc = v_out[2].cpu().numpy()
+    for b in range(vb.B):
+        nblk = -(-int(vb.seq_lens[b]) // wl.shape.block_size)
+        assert np.all(sc[b, :, nblk:] == 0.0)
+    sel_np, cnt_np = check_selection(wl, vb, v_out[2], sel, cnt)
+    H.compare_draft(wl, db, d_out, sel_np, cnt_np, H.all_units(db, hkv)).check(
+        f"fused {cid} draft")
+
+
+def test_fused_chained_matches_separate_calls():
+    """Unsplit units run the same routine as the one-launch-per-stage path:
+    verify outputs, scores and selection are bitwise equal.  (A batch of
+    1024 units keeps every unit in one chunk; smaller batches are split to
+    fill the GPU.)"""
+    wl = mk("decode_b128_l8192", seed=32, B=128, L=512)
+    vb = wl.verify
+    v_out, (sel, cnt), _ = run_chained(wl)
+    o, lse, sc = H.gpu_verify(wl, vb, num_splits=1)
+    sel2, cnt2 = H.gpu_topk(wl, vb, sc)
+    torch.cuda.synchronize()
+    assert torch.equal(v_out[0].view(torch.uint8), o.view(torch.uint8))
+    assert torch.equal(v_out[1], lse)
+    assert torch.equal(v_out[2], sc)
+    assert torch.equal(sel, sel2) and torch.equal(cnt, cnt2)
+
+
+def test_fused_score_row_start_one():
+    wl = mk("qwen3_8b_layer_b16_l4096", seed=33, B=2, L=260, sigma="one")
+    vb = wl.verify
+    v_out, (sel, cnt), _ = run_chained(wl, score_row_start=1)
+    H.compare_verify(wl, vb, v_out, H.all_units(vb, wl.shape.Hkv), score_row_start=1).check(
+        "fused r0=1")
+    G = wl.shape.Hq // wl.shape.Hkv
+    assert np.allclose(v_out[2].cpu().numpy().sum(-1), (wl.shape.n_q - 1) * G, atol=1e-3)
+
+
+def run_mixed(wl, with_sel=True):
+    s = H.sss()
+    vb, db = wl.verify, wl.draft
+    v = d = None
+    v_out = d_out = None
+    if vb is not None:
+        o, lse, sc, sel, cnt = verify_outputs(wl, vb, with_sel)
+        v = s.verify_step(H.kv_of(wl, vb), vb.q, wl.sm_scale, wl.shape.block_size, wl.max_blocks,
+                          o, lse, sc, budget=vb.budget if with_sel else None,
+                          window=wl.shape.window, sel=sel, sel_count=cnt)
+        v_out = (o, lse, sc, sel, cnt)
+    if db is not None:
+        od = torch.full_like(db.q, float("nan"))
+        lsed = torch.full(db.q.shape[:3], float("nan"), device=DEV)
+        d = s.draft_step(H.kv_of(wl, db), db.q, wl.sm_scale, wl.shape.block_size, db.sel,
+                         db.sel_count, wl.shape.window, od, lsed)
+        d_out = (od, lsed)
+    s.fused_step(v, d, chained=False)
+    torch.cuda.synchronize()
+    return v_out, d_out
+
+
+MIXED = [
+    ("mixed_small", dict(B=12, L=(200, 3000), sigma="one"), True),
+    ("mixed_scores_only", dict(B=10, L=(50, 1500)), False),
+    ("mixed_long", dict(B=6, L=(3000, 9000)), True),
+]
+
+
+@pytest.mark.parametrize("case", MIXED, ids=[c[0] for c in MIXED])
+def test_fused_mixed(case):
+    cid, kw, with_sel = case
+    wl = mk("mixed_b96_l1k_32k", seed=34, p_verify=0.4, **kw)
+    vb, db = wl.verify, wl.draft
+    hkv = wl.shape.Hkv
+    print(f"[fused mixed] {cid} verify={vb.B if vb else 0} draft={db.B if db else 0}", flush=True)
+    v_out, d_out = run_mixed(wl, with_sel)
+    if vb is not None:
+        H.compare_verify(wl, vb, v_out[:3], H.all_units(vb, hkv)).check(f"fused {cid} verify")
+        if with_sel:
+            check_selection(wl, vb, v_out[2], v_out[3], v_out[4])
+    if db is not None:
+        H.compare_draft(wl, db, d_out, db.sel.cpu().numpy(), db.sel_count.cpu().numpy(),
+                        H.all_units(db, hkv)).check(f"fused {cid} draft")
+
+
+def test_fused_draft_only_split_lists():
+    """Draft-only step with long lists: each unit's list is cut into several
+    chunks and merged by the last arriving chunk."""
+    wl = mk("qwen3_8b_layer_b16_l4096", seed=35, B=3, L=2900, sigma="one")
+    db = wl.draft
+    hkv = wl.shape.Hkv
+    bs, win = wl.shape.block_size, wl.shape.window
+    lens = db.seq_lens.cpu().numpy()
+    max_sel = wl.max_blocks
+    sel = np.full((db.B, hkv, max_sel), -1, np.int32)
+    cnt = np.zeros((db.B, hkv), np.int32)
+    g = np.random.default_rng(5)
+    for b in range(db.B):
+        ncand = -(-max(0, int(lens[b]) - win) // bs)
+        for h in range(hkv):
+            n = int(g.integers(ncand // 2, ncand + 1))
+            pick = np.sort(g.choice(ncand, n, replace=False))
+            sel[b, h, :n] = pick
+            cnt[b, h] = n
+    sel_t, cnt_t = torch.from_numpy(sel).to(DEV), torch.from_numpy(cnt).to(DEV)
+    od = torch.full_like(db.q, float("nan"))
+    lsed = torch.full(db.q.shape[:3], float("nan"), device=DEV)
+    s = H.sss()
+    d = s.draft_step(H.kv_of(wl, db), db.q, wl.sm_scale, bs, sel_t, cnt_t, win, od, lsed)
+    s.fused_step(None, d, chained=False)
+    torch.cuda.synchronize()
+    H.compare_draft(wl, db, (od, lsed), sel, cnt, H.all_units(db, hkv)).check("fused draft split")
+
+
+def test_fused_determinism():
+    wl = mk("mixed_b96_l1k_32k", seed=36, p_verify=0.5, B=10, L=(100, 4000))
+    runs = []
+    for _ in range(2):
+        v_out, d_out = run_mixed(wl)
+        runs.append([t.cpu() for t in (*v_out, *d_out)])
+    wl2 = mk("qwen3_8b_layer_b16_l4096", seed=37, B=3, L=1500)
+    for _ in range(2):
+        v_out, sel_out, d_out = run_chained(wl2)
+        runs.append([t.cpu() for t in (*v_out, *sel_out, *d_out)])
+    for i, j in ((0, 1), (2, 3)):
+        for a, b in zip(runs[i], runs[j]):
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.uint8), b.view(torch.uint8)
+            assert torch.equal(a, b)
+
+
+def test_fused_invalid_seq_len_poisons_outputs():
+    wl = mk("qwen3_8b_layer_b16_l4096", seed=38, B=3, L=200)
+    vb, db = wl.verify, wl.draft
+    lens = vb.seq_lens.clone()
+    lens[1] = 100000                 # above max_seq_len
+    s = H.sss()
+    kv = s.paged_kv(wl.k_cache, wl.v_cache, vb.page_table, lens, 200)
+    o, lse, sc, sel, cnt = verify_outputs(wl, vb)
+    od = torch.zeros_like(db.q)
+    lsed = torch.zeros(db.q.shape[:3], device=DEV)
+    v = s.verify_step(kv, vb.q, wl.sm_scale, 16, wl.max_blocks, o, lse, sc, budget=vb.budget,
+                      window=wl.shape.window, sel=sel, sel_count=cnt)
+    d = s.draft_step(kv, db.q, wl.sm_scale, 16, sel, cnt, wl.shape.window, od, lsed)
+    s.fused_step(v, d, chained=True)
+    torch.cuda.synchronize()
+    for t in (o[1].float(), lse[1], sc[1], od[1].float(), lsed[1]):
+        assert torch.isnan(t).all()
+    for t in (o[0].float(), lse[0], sc[0], od[2].float(), lsed[2]):
+        assert torch.isfinite(t).all()
+
+
+def test_fused_full_size_sampled():
+    """Both benchmark workloads in the benchmark's launch configuration, on a
+    seeded sample of units."""
+    for name in ("decode_b128_l8192", "mixed_b96_l1k_32k"):
+        wl = mk(name, seed=0)
+        hkv = wl.shape.Hkv
+        vb, db = wl.verify, wl.draft
+        print(f"[fused full] {name}", flush=True)
+        if wl.shape.p_verify is None:
+            v_out, (sel, cnt), d_out = run_chained(wl)
+            sel_np, cnt_np = sel.cpu().numpy(), cnt.cpu().numpy()
+            vo = v_out
+        else:
+            v_out, d_out = run_mixed(wl)
+            vo = v_out[:3]
+            sel_np, cnt_np = db.sel.cpu().numpy(), db.sel_count.cpu().numpy()
+        units = H.sample_units(vb, hkv, 6, seed=1)
+        H.compare_verify(wl, vb, vo, units).check(f"fused {name} verify")
+        G = wl.shape.Hq // hkv
+        tot = vo[2].sum(-1).cpu().numpy()
+        assert np.abs(tot - wl.shape.n_q * G).max() < 5e-3
+        d_units = H.sample_units(db, hkv, 6, seed=2)
+        H.compare_draft(wl, db, d_out, sel_np, cnt_np, d_units).check(f"fused {name} draft")
