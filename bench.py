@@ -55,7 +55,8 @@ def parse():
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "verify_decode_b128_l8192_counters.json")
-KERNEL_SOURCES = ["sparse_self_speculative_sss_amd/csrc/attn_mfma.hip",
+KERNEL_SOURCES = ["sparse_self_speculative_sss_amd/csrc/attn_item.h",
+                  "sparse_self_speculative_sss_amd/csrc/attn_mfma.hip",
                   "sparse_self_speculative_sss_amd/csrc/sss_common.h",
                   "sparse_self_speculative_sss_amd/csrc/api.hip"]
 
