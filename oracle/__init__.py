@@ -10,6 +10,8 @@ from .sss_oracle import (  # noqa: F401
     draft,
     draft_token_set,
     gather_unit,
+    kv_commit,
+    kv_write,
     merge,
     topk_unit,
     verify,

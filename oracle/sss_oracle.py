@@ -17,6 +17,12 @@ What it computes (the pages it follows):
   Decoding", 方法详解 (technical framework): the critical KV entries are a
   by-product of verification and drafting loads only those entries.
 
+* SpecSA -- "SpecSA：融合推测解码与稀疏注意力的高效LLM推理框架", 核心创新 /
+  刷新/复用NSA内核融合 (refresh / reuse): the KV of accepted speculative
+  tokens is kept for later queries, the KV of rejected ones is refreshed.
+  Here: writing the new positions' K/V into the paged cache (kv_write) and
+  shortening each request to the positions it keeps (kv_commit).
+
 Every step below is the plain mathematical definition written out with numpy
 (matrix products, exp/log, Python sorting).  No blocking, online softmax,
 splitting or fusion is used anywhere here.
@@ -304,3 +310,43 @@ def attention_partial(q_rows, K, V, sm_scale: float, positions, token_ids):
     lse, P = _softmax_rows(S)
     O = P @ V[idx] if len(idx) else np.zeros((q.shape[0], K.shape[1]))
     return O, lse
+
+
+# ---------------------------------------------------------------------------
+# KV update for the speculative positions (SpecSA 核心创新, 刷新/复用: KV of
+# accepted tokens is reused, KV of rejected tokens is refreshed)
+# ---------------------------------------------------------------------------
+def kv_write(k_cache, v_cache, page_table, k_new, v_new, pos0):
+    """Copies of the caches with token ``pos0[b] + i`` of request b set to
+    ``k_new[b, i]`` / ``v_new[b, i]`` (all KV heads), through the page table:
+    page ``page_table[b][t // page_size]``, slot ``t % page_size``.  A
+    position outside the request's table row, or a page id outside the pool,
+    leaves the cache unchanged for that token (nothing is written)."""
+    k = np.array(k_cache, copy=True)
+    v = np.array(v_cache, copy=True)
+    num_pages, _, page_size, _ = k.shape
+    B, n_new = k_new.shape[0], k_new.shape[1]
+    max_pages = page_table.shape[1]
+    for b in range(B):
+        for i in range(n_new):
+            t = int(pos0[b]) + i
+            if t < 0 or t // page_size >= max_pages:
+                continue
+            page = int(page_table[b][t // page_size])
+            if page < 0 or page >= num_pages:
+                continue
+            k[page, :, t % page_size, :] = k_new[b, i]
+            v[page, :, t % page_size, :] = v_new[b, i]
+    return k, v
+
+
+def kv_commit(seq_lens, keep, n_q: int):
+    """New lengths after verification: the request's last n_q positions were
+    the speculative ones; the first ``keep[b]`` of them (clamped to
+    [0, n_q]) stay, the rest are dropped.  Their cache slots are not touched:
+    a position at or past the length is never read."""
+    out = []
+    for L, kp in zip(seq_lens, keep):
+        kp = min(max(int(kp), 0), n_q)
+        out.append(max(int(L) - n_q + kp, 0))
+    return np.array(out, dtype=np.int32)

@@ -12,7 +12,11 @@
 * draft: SDPA with the boolean mask of the token set; dense and sliding
   window as special cases;
 * merge: partials of a partition computed by SDPA merge to the unsplit
-  result; identity, associativity and the empty case.
+  result; identity, associativity and the empty case;
+* KV update: a write equals slicing the logical per-request sequence (built
+  by torch indexing, not page arithmetic); out-of-range writes change
+  nothing; after a commit, verify equals SDPA on the explicitly truncated
+  sequence.
 
 The mutation tests at the end plant plausible mistakes in copies of oracle
 functions and check that the pins above reject them.
@@ -435,6 +439,96 @@ def _mut_verify_head_map(q, kc, vc, table, lens, scale):
     return O, LSE
 
 
+def _logical(kc, table, L, Hkv):
+    """[L][Hkv][d] view of one request through torch indexing."""
+    return torch.stack([contiguous(kc, table, L, h) for h in range(Hkv)], dim=1).numpy()
+
+
+def test_kv_write_equals_logical_slice_assignment():
+    g = np.random.default_rng(17)
+    B, Hkv, d, P, n_new = 3, 2, 8, 4, 5
+    q, kc, vc, table, lens = paged_case(B=B, Ls=(37, 20, 29), Hkv=Hkv, d=d, P=P, seed=4)
+    pos0 = np.array([32, 15, 24], dtype=np.int32)      # the last n_new positions
+    k_new = g.normal(size=(B, n_new, Hkv, d))
+    v_new = g.normal(size=(B, n_new, Hkv, d))
+    k2, v2 = oracle.kv_write(kc, vc, table, k_new, v_new, pos0)
+    for b in range(B):
+        L = int(lens[b])
+        want_k = _logical(kc, table[b], L, Hkv)
+        want_v = _logical(vc, table[b], L, Hkv)
+        want_k[pos0[b]:pos0[b] + n_new] = k_new[b]
+        want_v[pos0[b]:pos0[b] + n_new] = v_new[b]
+        assert np.array_equal(_logical(k2, table[b], L, Hkv), want_k)
+        assert np.array_equal(_logical(v2, table[b], L, Hkv), want_v)
+    # pages no request uses are untouched
+    used = {int(x) for b in range(B) for x in table[b, :-(-int(lens[b]) // P)]}
+    for pg in range(kc.shape[0]):
+        if pg not in used:
+            assert np.array_equal(k2[pg], kc[pg])
+
+
+def test_kv_write_out_of_range_and_identity():
+    g = np.random.default_rng(18)
+    q, kc, vc, table, lens = paged_case(B=2, Ls=(16, 16), P=4, seed=5)
+    Hkv, d = kc.shape[1], kc.shape[3]
+    bad_table = table.copy()
+    bad_table[1, 1] = 10 ** 6                     # page id outside the pool
+    k_new = g.normal(size=(2, 3, Hkv, d))
+    pos0 = np.array([-3, 4], dtype=np.int32)      # request 0 entirely before 0
+    k2, v2 = oracle.kv_write(kc, vc, bad_table, k_new, k_new, pos0)
+    assert np.array_equal(k2, kc) and np.array_equal(v2, vc)
+    far = np.array([4 * table.shape[1], 4 * table.shape[1] + 7], dtype=np.int32)
+    k3, _ = oracle.kv_write(kc, vc, table, k_new, k_new, far)
+    assert np.array_equal(k3, kc)
+    # writing back what is there changes nothing
+    cur = np.stack([_logical(kc, table[b], 16, Hkv)[5:8] for b in range(2)])
+    k4, _ = oracle.kv_write(kc, vc, table, cur, cur, np.array([5, 5], dtype=np.int32))
+    assert np.array_equal(k4, kc)
+
+
+def test_kv_commit_closed_forms():
+    lens = np.array([40, 17, 5, 9], dtype=np.int32)
+    assert np.array_equal(oracle.kv_commit(lens, [5, 5, 5, 5], 5), lens)
+    assert np.array_equal(oracle.kv_commit(lens, [0, 0, 0, 0], 5), lens - 5)
+    assert np.array_equal(oracle.kv_commit(lens, [9, -2, 3, 1], 5), [40, 12, 3, 5])
+
+
+def test_verify_after_commit_equals_truncated_sdpa():
+    """Rolled-back positions are never read: verify on the committed length
+    equals SDPA over the explicitly truncated logical sequence."""
+    g = np.random.default_rng(19)
+    n_q, Hkv, Hq, d, P = 4, 2, 4, 8, 4
+    # pages allocated for 8 more tokens than the current lengths
+    q, kc, vc, table, alloc = paged_case(B=2, Ls=(41, 34), Hq=Hq, Hkv=Hkv, d=d, P=P, n_q=n_q,
+                                         seed=6)
+    lens = alloc - 8
+    keep = np.array([2, 4], dtype=np.int32)
+    new_lens = oracle.kv_commit(lens, keep, n_q)
+    # the next step's verify: n_q fresh positions on top of the kept prefix
+    pos0 = new_lens.copy()
+    k_new = g.normal(size=(2, n_q, Hkv, d))
+    v_new = g.normal(size=(2, n_q, Hkv, d))
+    k2, v2 = oracle.kv_write(kc, vc, table, k_new, v_new, pos0)
+    L2 = new_lens + n_q
+    O, LSE = oracle.verify(q, k2, v2, table, L2, 0.37)
+    G = Hq // Hkv
+    for b in range(2):
+        L = int(L2[b])
+        K = np.concatenate([_logical(kc, table[b], int(new_lens[b]), Hkv), k_new[b]])
+        V = np.concatenate([_logical(vc, table[b], int(new_lens[b]), Hkv), v_new[b]])
+        for hq in range(Hq):
+            h = hq // G
+            qt = torch.as_tensor(q[b, :, hq])[None, None]
+            kt = torch.as_tensor(K[:, h])[None, None]
+            vt = torch.as_tensor(V[:, h])[None, None]
+            mask = torch.ones(n_q, L, dtype=torch.bool).tril(L - n_q)
+            ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.37)[0, 0]
+            s_ = (qt[0, 0] @ kt[0, 0].T) * 0.37
+            lse = torch.logsumexp(s_.masked_fill(~mask, -math.inf), dim=-1)
+            assert np.abs(O[b, :, hq] - ref.numpy()).max() < 1e-12
+            assert np.abs(LSE[b, :, hq] - lse.numpy()).max() < 1e-12
+
+
 def test_mutations_are_caught():
     assert verify_err(_mut_verify_off_by_one) > 1e-3
     assert verify_err(_mut_verify_head_map, Hq=4, Hkv=2) > 1e-3
@@ -456,3 +550,27 @@ def test_mutations_are_caught():
     bad = oracle.block_mass_unit(P, 40, 3, 2, 4, 0, 10)
     ref = softmax_block_scores(q, kc, vc, table, lens, 0.25, 4, 10, 0)[0, 0]
     assert np.abs(bad - ref).max() > 1e-3
+
+
+def test_kv_write_mutation_is_caught():
+    """An off-by-one write position, or a write into the wrong KV head, fails
+    the logical-slice pin."""
+    g = np.random.default_rng(20)
+    q, kc, vc, table, lens = paged_case(B=1, Ls=(30,), Hkv=2, P=4, seed=7)
+    Hkv, d = kc.shape[1], kc.shape[3]
+    k_new = g.normal(size=(1, 3, Hkv, d))
+    pos0 = np.array([27], dtype=np.int32)
+
+    def mut_shift(kc_, vc_, table_, kn, vn, p0):
+        return oracle.kv_write(kc_, vc_, table_, kn, vn, np.asarray(p0) + 1)
+
+    def mut_heads(kc_, vc_, table_, kn, vn, p0):
+        return oracle.kv_write(kc_, vc_, table_, kn[:, :, ::-1], vn[:, :, ::-1], p0)
+
+    want = _logical(kc, table[0], 30, Hkv)
+    want[27:30] = k_new[0]
+    for fn in (mut_shift, mut_heads):
+        k2, _ = fn(kc, vc, table, k_new, k_new, pos0)
+        assert not np.array_equal(_logical(k2, table[0], 30, Hkv), want)
+    k2, _ = oracle.kv_write(kc, vc, table, k_new, k_new, pos0)
+    assert np.array_equal(_logical(k2, table[0], 30, Hkv), want)
