@@ -48,6 +48,9 @@ def parse():
                          "sss_fused_step (one work-list launch, plus merge launches for "
                          "split units); auto: fused for mixed batches, separate otherwise "
                          "(the faster of the two on each benchmark workload)")
+    ap.add_argument("--kv-update", action="store_true",
+                    help="also time sss_kv_write (the k+1 speculative positions of every "
+                         "request) and sss_kv_commit, outside the timed step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run device copies of this size (calibrates HBM byte counters "
                          "against a transfer of known size) and exit")
@@ -179,6 +182,44 @@ def cpu_baseline(wl, n_req):
     return {"value": tokens / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"{what} (all {s.Hkv} KV heads each): fp64 verify + block scores, Top-N "
                        f"and draft, {elapsed:.1f} s wall on the host")}
+
+
+def time_kv_update(wl, kv, vb, dev, steps):
+    """sss_kv_write of the last n_q positions of every verify request (the
+    values already there, so the cache is unchanged) and sss_kv_commit keeping
+    all of them (lengths unchanged); mean times over `steps` calls each."""
+    import torch
+    from sparse_self_speculative_sss_amd import sss
+    s = wl.shape
+    B, n_q = vb.B, s.n_q
+    lens = vb.seq_lens
+    pos0 = (lens - n_q).to(torch.int32)
+    # the rows currently stored at those positions
+    P = s.page_size
+    t = pos0[:, None].long() + torch.arange(n_q, device=dev)[None]
+    pages = torch.gather(vb.page_table.long(), 1, t // P)
+    k_new = wl.k_cache[pages, :, t % P].contiguous()        # [B][n_q][Hkv][d]
+    v_new = wl.v_cache[pages, :, t % P].contiguous()
+    keep = torch.full((B,), n_q, dtype=torch.int32, device=dev)
+    out = torch.empty_like(lens)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for _ in range(3):
+        sss.kv_write(kv, k_new, v_new, pos0)
+        sss.kv_commit(lens, keep, n_q, out)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        sss.kv_write(kv, k_new, v_new, pos0)
+    ev[1].record()
+    for _ in range(steps):
+        sss.kv_commit(lens, keep, n_q, out)
+    ev[2].record()
+    torch.cuda.synchronize()
+    w_ms = ev[0].elapsed_time(ev[1]) / steps
+    c_ms = ev[1].elapsed_time(ev[2]) / steps
+    moved = 2 * k_new.numel() * k_new.element_size() * 2      # K and V, read + written
+    return {"write_ms": round(w_ms, 4), "write_bytes": moved,
+            "write_GB/s": round(moved / (w_ms * 1e-3) / 1e9, 1), "commit_ms": round(c_ms, 4)}
 
 
 def main():
@@ -363,6 +404,8 @@ def main():
                            if Bd and args.path == "separate" else None),
         },
     }
+    if args.kv_update and Bv:
+        rec["kv_update"] = time_kv_update(wl, kv_v, vb, dev, args.steps)
     if args.cpu_sample > 0:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)

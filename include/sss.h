@@ -20,7 +20,9 @@
  *                    recent window;
  *   sss_merge        log-sum-exp merge of split-KV partials;
  *   sss_fused_step   all of the above for a (mixed or chained) batch in one
- *                    work-list launch.
+ *                    work-list launch;
+ *   sss_kv_write     K/V of new token positions into the paged cache;
+ *   sss_kv_commit    lengths after acceptance (drops rejected positions).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -290,6 +292,40 @@ sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* d
 /* Workspace bytes sss_fused_step needs (0 on invalid arguments). */
 size_t sss_fused_workspace_size(const sss_verify_step* verify, const sss_draft_step* draft,
                                 int32_t chained);
+
+/*
+ * KV write for new token positions (SpecSA, 核心创新 / 刷新/复用NSA内核融合:
+ * the KV of the speculative positions is written before verification and
+ * refreshed -- overwritten -- when it is recomputed; the KV of accepted
+ * tokens is then reused by later queries).
+ *
+ * For request b and i in [0, n_new), token t = pos0[b] + i gets
+ *     k[page_table[b][t / page_size]][h][t % page_size][:] = k_new[b][i][h][:]
+ * (and likewise v) for every KV head h.  Rows whose position lies outside
+ * [0, max_pages_per_req * page_size) or whose page id lies outside
+ * [0, num_pages) are skipped (nothing is written for them).  kv->seq_lens is
+ * not read; the caller owns the lengths (see sss_kv_commit).
+ *
+ * k_new, v_new [batch][n_new][num_kv_heads][head_dim] in kv->dtype, 16-byte
+ * aligned; pos0 [batch] int32.  THE CACHE PAGES kv->k / kv->v ARE WRITTEN
+ * (the one exception to "inputs are read only").  Two rows of one call
+ * must not map to the same slot.  Preconditions: batch >= 0, n_new >= 0.
+ */
+sss_status sss_kv_write(const sss_paged_kv* kv, const void* k_new, const void* v_new,
+                        int32_t batch, int32_t n_new, const int32_t* pos0, void* stream);
+
+/*
+ * Commit after acceptance (SpecSA, 刷新/复用: rejected speculative positions
+ * are dropped).  The last n_q positions of each request were speculative;
+ * the first keep[b] of them (clamped to [0, n_q]) stay:
+ *     new_seq_lens[b] = max(0, seq_lens[b] - n_q + clamp(keep[b], 0, n_q)).
+ * Dropped positions are not touched in the cache: a position at or past a
+ * request's length is never read, and the next sss_kv_write overwrites it.
+ * seq_lens, keep, new_seq_lens [batch] int32; new_seq_lens may equal
+ * seq_lens (in place).  Preconditions: batch >= 0, n_q >= 1.
+ */
+sss_status sss_kv_commit(const int32_t* seq_lens, const int32_t* keep, int32_t batch, int32_t n_q,
+                         int32_t* new_seq_lens, void* stream);
 
 /* Static description of a status code. */
 const char* sss_status_string(sss_status status);

@@ -629,6 +629,52 @@ sss_status sss_draft_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
   return ok();
 }
 
+sss_status sss_kv_write(const sss_paged_kv* kv, const void* k_new, const void* v_new,
+                        int32_t batch, int32_t n_new, const int32_t* pos0, void* stream) {
+  sss_status st = check_kv(kv, batch);
+  if (st != SSS_OK) return st;
+  if (batch < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "batch %d < 0", batch);
+  if (n_new < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "n_new %d < 0", n_new);
+  if (batch == 0 || n_new == 0) return ok();
+  if (!k_new || !v_new || !pos0)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "k_new, v_new and pos0 must be non-NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos0, 4))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "k_new and v_new must be 16-byte aligned, pos0 4-byte");
+  KvWriteParams p = {};
+  p.k = const_cast<void*>(kv->k);
+  p.v = const_cast<void*>(kv->v);
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.page_table = kv->page_table;
+  p.pos0 = pos0;
+  p.num_pages = kv->num_pages;
+  p.page_size = kv->page_size;
+  p.num_kv_heads = kv->num_kv_heads;
+  p.head_dim = kv->head_dim;
+  p.max_pages = kv->max_pages_per_req;
+  p.elem_bytes = kv->dtype == SSS_BF16 ? 2 : 4;
+  p.batch = batch;
+  p.n_new = n_new;
+  hipError_t e = launch_kv_write(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSS_ERR_HIP, "kv write launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sss_status sss_kv_commit(const int32_t* seq_lens, const int32_t* keep, int32_t batch, int32_t n_q,
+                         int32_t* new_seq_lens, void* stream) {
+  if (batch < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "batch %d < 0", batch);
+  if (n_q < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "n_q %d < 1", n_q);
+  if (batch == 0) return ok();
+  if (!seq_lens || !keep || !new_seq_lens)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "seq_lens, keep and new_seq_lens must be non-NULL");
+  if (!aligned(seq_lens, 4) || !aligned(keep, 4) || !aligned(new_seq_lens, 4))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "arrays must be 4-byte aligned");
+  hipError_t e = launch_kv_commit(seq_lens, keep, batch, n_q, new_seq_lens,
+                                  reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSS_ERR_HIP, "kv commit launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_parts, int32_t rows,
                      int32_t head_dim, void* o, int32_t o_dtype, float* lse, void* stream) {
   if (num_parts < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "num_parts %d < 1", num_parts);

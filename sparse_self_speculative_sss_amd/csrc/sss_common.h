@@ -148,6 +148,23 @@ struct FusedPlan {
 
 void fused_plan(const FusedPlanIn& in, FusedPlan& pl);
 
+// KV write (kv_update.hip): rows [batch][n_new][num_kv_heads][head_dim] of
+// k_new / v_new go to token pos0[b] + i of each request's paged cache.
+struct KvWriteParams {
+  void* k;
+  void* v;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* page_table;
+  const int32_t* pos0;
+  int32_t num_pages, page_size, num_kv_heads, head_dim, max_pages, elem_bytes;
+  int32_t batch, n_new;
+};
+
+hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t s);
+hipError_t launch_kv_commit(const int32_t* seq_lens, const int32_t* keep, int batch, int n_q,
+                            int32_t* out, hipStream_t s);
+
 // Host-side launchers (each returns hipGetLastError() of its launches).
 hipError_t launch_fused(const FusedParams& f, const AttnParams& pv, const AttnParams& pd,
                         const FusedPlan& pl, int head_dim, hipStream_t s);

@@ -81,6 +81,10 @@ _lib.sss_fused_step.argtypes = [ctypes.POINTER(VerifyStep), ctypes.POINTER(Draft
 _lib.sss_fused_workspace_size.restype = ctypes.c_size_t
 _lib.sss_fused_workspace_size.argtypes = [ctypes.POINTER(VerifyStep), ctypes.POINTER(DraftStep),
                                           _c_int]
+_lib.sss_kv_write.restype = _c_int
+_lib.sss_kv_write.argtypes = [ctypes.POINTER(PagedKV), _vp, _vp, _c_int, _c_int, _vp, _vp]
+_lib.sss_kv_commit.restype = _c_int
+_lib.sss_kv_commit.argtypes = [_vp, _vp, _c_int, _c_int, _vp, _vp]
 _lib.sss_status_string.restype = ctypes.c_char_p
 _lib.sss_status_string.argtypes = [_c_int]
 _lib.sss_last_error.restype = ctypes.c_char_p
@@ -90,7 +94,7 @@ _lib.sss_version.argtypes = []
 
 EXPORTED = ["sss_verify_attn", "sss_verify_workspace_size", "sss_block_topk", "sss_draft_attn",
             "sss_draft_workspace_size", "sss_merge", "sss_fused_step", "sss_fused_workspace_size",
-            "sss_status_string", "sss_last_error", "sss_version"]
+            "sss_kv_write", "sss_kv_commit", "sss_status_string", "sss_last_error", "sss_version"]
 
 
 class SSSError(RuntimeError):
@@ -245,6 +249,25 @@ def fused_step(verify=None, draft=None, chained=False, ws=None, device=None):
     _check(_lib.sss_fused_step(_byref_or_null(verify, VerifyStep), _byref_or_null(draft, DraftStep),
                                int(bool(chained)), _ptr(ws), ws.numel(), _stream()),
            "sss_fused_step")
+
+
+def kv_write(kv: PagedKV, k_new, v_new, pos0):
+    """sss_kv_write: rows k_new / v_new [B][n_new][Hkv][d] to positions
+    pos0[b] + i of the paged cache kv describes (the cache is written)."""
+    B, n_new = k_new.shape[0], k_new.shape[1]
+    _check(_lib.sss_kv_write(ctypes.byref(kv), _ptr(k_new), _ptr(v_new), B, n_new, _ptr(pos0),
+                             _stream()),
+           "sss_kv_write")
+
+
+def kv_commit(seq_lens, keep, n_q, out=None):
+    """sss_kv_commit: lengths after keeping keep[b] of the last n_q positions
+    (in place when out is None)."""
+    out = seq_lens if out is None else out
+    _check(_lib.sss_kv_commit(_ptr(seq_lens), _ptr(keep), seq_lens.shape[0], int(n_q), _ptr(out),
+                              _stream()),
+           "sss_kv_commit")
+    return out
 
 
 def raw():

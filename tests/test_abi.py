@@ -224,3 +224,21 @@ def test_fused_workspace_query_and_size_check():
     assert call_fused(sss, None, None, 0) == 0
     v0, d0 = fused_args(sss, vkw=dict(batch=0), dkw=dict(batch=0))
     assert call_fused(sss, v0, d0, 0) == 0
+
+
+def test_kv_update_rejects_bad_arguments():
+    sss = _binding()
+    lib = sss.raw()
+    kv = good_kv(sss)
+    w = lib.sss_kv_write
+    assert w(ctypes.byref(kv), 4096, 8192, -1, 2, 256, None) == 1
+    assert w(ctypes.byref(kv), 4096, 8192, 2, -1, 256, None) == 1
+    assert w(ctypes.byref(kv), 4100, 8192, 2, 2, 256, None) == 1      # misaligned rows
+    assert w(ctypes.byref(kv), None, 8192, 2, 2, 256, None) == 1
+    assert w(ctypes.byref(good_kv(sss, head_dim=96)), 4096, 8192, 2, 2, 256, None) == 2
+    assert w(ctypes.byref(kv), 4096, 8192, 2, 0, 256, None) == 0      # nothing to write
+    c = lib.sss_kv_commit
+    assert c(256, 512, 2, 0, 256, None) == 1
+    assert c(256, 512, -1, 5, 256, None) == 1
+    assert c(None, 512, 2, 5, 256, None) == 1
+    assert c(256, 512, 0, 5, 256, None) == 0
