@@ -127,9 +127,11 @@ typedef struct {
  * 0 <= score_row_start < n_q; max_blocks >= ceil(max_seq_len / block_size);
  * max_seq_len >= n_q; num_splits >= 0.  Device-side:
  * n_q <= seq_lens[b] <= max_seq_len.
- * Path: BF16 caches with page_size and block_size multiples of 16 run the
- * matrix-core (MFMA) kernel; every other supported case runs the vector-ALU
- * kernel.  Both compute in fp32 and round o once to kv->dtype.
+ * Path: BF16 caches with page_size a multiple of 16 and block_size a
+ * multiple of 16, or block_size == 1 (single tokens, the page-size-1
+ * selection of SparseSpec §4.1), run the matrix-core (MFMA) kernel; every
+ * other supported case runs the vector-ALU kernel.  Both compute in fp32
+ * and round o once to kv->dtype.
  */
 sss_status sss_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch, int32_t n_q,
                            int32_t num_q_heads, float sm_scale, int32_t block_size,
@@ -187,8 +189,11 @@ sss_status sss_block_topk(const float* block_scores, int32_t batch, int32_t num_
  * by the library).
  * Preconditions: num_q_heads % num_kv_heads == 0; G <= 128;
  * block_size >= 1; window >= 0; max_sel >= 1; num_splits >= 0.
- * Device-side: 1 <= seq_lens[b] <= max_seq_len.  Kernel choice as for
- * sss_verify_attn.
+ * Device-side: 1 <= seq_lens[b] <= max_seq_len.  Path: BF16 caches with
+ * page_size and block_size multiples of 16 run the matrix-core kernel over
+ * 16-token page runs; BF16 caches with block_size == 1 and G <= 32 run it
+ * over single tokens gathered from the list; every other case runs the
+ * vector-ALU kernel.
  */
 sss_status sss_draft_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
                           int32_t num_q_heads, float sm_scale, int32_t block_size,

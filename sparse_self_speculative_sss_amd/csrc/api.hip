@@ -8,7 +8,7 @@
 #include "sss_common.h"
 
 namespace sss {
-int mfma_token_groups(int rows);  // attn_mfma.hip
+int mfma_token_groups(int rows, bool draft);  // attn_mfma.hip
 }
 
 namespace {
@@ -78,8 +78,19 @@ sss_status check_kv(const sss_paged_kv* kv, int batch) {
   return ok();
 }
 
-bool use_mfma(const sss_paged_kv* kv, int block_size) {
-  return kv->dtype == SSS_BF16 && kv->page_size % kSeg == 0 && block_size % kSeg == 0;
+// Matrix-core path: BF16 caches.  Verify reads 16-token page runs (pages of
+// a multiple of 16 tokens) and scores blocks of a multiple of 16 tokens, or
+// single tokens.  Draft reads blocks of a multiple of 16 tokens as page runs
+// (same page rule), or single selected tokens gathered one row at a time
+// (one row tile: G <= 32).
+bool use_mfma_verify(const sss_paged_kv* kv, int block_size) {
+  return kv->dtype == SSS_BF16 && kv->page_size % kSeg == 0 &&
+         (block_size % kSeg == 0 || block_size == 1);
+}
+bool use_mfma_draft(const sss_paged_kv* kv, int block_size, int group) {
+  if (kv->dtype != SSS_BF16) return false;
+  if (block_size == 1) return group <= 32;
+  return kv->page_size % kSeg == 0 && block_size % kSeg == 0;
 }
 
 struct Plan {
@@ -124,10 +135,10 @@ sss_status plan_verify(const sss_paged_kv* kv, int batch, int n_q, int hq, int b
                 max_blocks, ceil_div(kv->max_seq_len, block_size));
   if (num_splits < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "num_splits %d < 0", num_splits);
 
-  pl.mfma = use_mfma(kv, block_size);
+  pl.mfma = use_mfma_verify(kv, block_size);
   pl.rows = n_q * G;
   const long long units = (long long)batch * kv->num_kv_heads;
-  const int nwt = pl.mfma ? mfma_token_groups(pl.rows) : 1;
+  const int nwt = pl.mfma ? mfma_token_groups(pl.rows, false) : 1;
   const int nwr = ceil_div(pl.rows, 32);
   const long long align =
       pl.mfma ? lcm_ll((long long)nwt * 32, (long long)nwt * block_size) : (long long)block_size;
@@ -153,7 +164,7 @@ sss_status plan_verify(const sss_paged_kv* kv, int batch, int n_q, int hq, int b
   // units store them to the workspace (LDS room for them would cost
   // resident workgroups)
   pl.ell_lds_floats = (long long)ceil_div(pl.chunk, block_size) * pl.rows;
-  pl.ell_in_lds = pl.mfma && pl.num_chunks == 1 &&
+  pl.ell_in_lds = pl.mfma && pl.num_chunks == 1 && block_size != 1 &&
                   mfma_smem_bytes(kv->head_dim, nwr, nwt, pl.ell_lds_floats) <= kMaxLds;
   const bool ell_global = !pl.ell_in_lds || pl.num_chunks > 1;
   layout(pl, units, kv->head_dim, ell_global ? units * (long long)max_blocks * pl.rows : 0);
@@ -175,15 +186,19 @@ sss_status plan_draft(const sss_paged_kv* kv, int batch, int hq, int block_size,
   if (window < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "window %d < 0", window);
   if (num_splits < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "num_splits %d < 0", num_splits);
 
-  pl.mfma = use_mfma(kv, block_size);
+  pl.mfma = use_mfma_draft(kv, block_size, G);
   pl.rows = G;
   const long long units = (long long)batch * kv->num_kv_heads;
-  const int nwt = pl.mfma ? mfma_token_groups(G) : 1;
+  const int nwt = pl.mfma ? mfma_token_groups(G, true) : 1;
   const int nwr = ceil_div(G, 32);
   const long long Lmax = kv->max_seq_len;
   const long long wtok = window > 0 ? (window < Lmax ? window : Lmax) : 0;
   long long list_max, align;
-  if (pl.mfma) {
+  if (pl.mfma && block_size == 1) {
+    // single tokens: the list holds tokens, tiles take 32 of them
+    list_max = (long long)max_sel + wtok;
+    align = 32LL * nwt;
+  } else if (pl.mfma) {
     list_max = (long long)max_sel * (block_size / kSeg) + (wtok > 0 ? (wtok + kSeg - 1) / kSeg + 1 : 0);
     align = 2LL * nwt;
   } else {
@@ -203,6 +218,14 @@ sss_status plan_draft(const sss_paged_kv* kv, int batch, int hq, int block_size,
   if (S < 1) S = 1;
   long long chunk = (list_max + S - 1) / S;
   chunk = (chunk + align - 1) / align * align;
+  if (pl.mfma && block_size == 1) {
+    // the chunk's token list (4 bytes per entry) sits in LDS after the tiles
+    const long long room =
+        ((long long)kMaxLds - (long long)mfma_smem_bytes(kv->head_dim, nwr, nwt, 0)) / 4;
+    const long long cap = room / align * align;
+    if (cap < align) return fail(SSS_ERR_UNSUPPORTED, "no LDS room for a token list");
+    if (chunk > cap) chunk = cap;
+  }
   if (chunk > (1LL << 30)) return fail(SSS_ERR_UNSUPPORTED, "chunk too large");
   pl.chunk = (int)chunk;
   pl.num_chunks = (int)((list_max + chunk - 1) / chunk);
@@ -285,6 +308,8 @@ sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int ch
                      !aligned(v->sel_count, 4) || !aligned(v->budget, 4)))
         return fail(SSS_ERR_INVALID_ARGUMENT,
                     "verify budget, sel and sel_count must be non-NULL and 4-byte aligned");
+      if (v->block_size % kSeg != 0)
+        return fail(SSS_ERR_UNSUPPORTED, "fused step needs block_size a multiple of 16");
       fs.rows_v = pv.rows;
       fs.nv = (long long)v->batch * v->kv.num_kv_heads;
       fs.head_dim = v->kv.head_dim;
@@ -304,6 +329,8 @@ sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int ch
       if (pd.rows > 32)
         return fail(SSS_ERR_UNSUPPORTED, "fused step drafts groups of at most 32 heads (G = %d)",
                     pd.rows);
+      if (d->block_size % kSeg != 0)
+        return fail(SSS_ERR_UNSUPPORTED, "fused step needs block_size a multiple of 16");
       if (!d->q || !d->o || !d->lse || !d->sel || !d->sel_count)
         return fail(SSS_ERR_INVALID_ARGUMENT, "draft q, o, lse, sel and sel_count must be non-NULL");
       if (!aligned(d->q, 16) || !aligned(d->o, 16))
@@ -620,7 +647,8 @@ sss_status sss_draft_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
     f.max_sel = max_sel;
     f.window = window;
     f.draft = 1;
-    f.simple_list = pl.mfma ? 0 : 1;
+    // lists counted in 16-token segments, or token by token
+    f.simple_list = (pl.mfma && block_size % kSeg == 0) ? 0 : 1;
     f.single_done = pl.mfma ? 1 : 0;
     f.skip_len = -1;
     e = launch_finalize(f, s);

@@ -72,6 +72,10 @@ struct Item {
   int sel_off;           // draft: LDS byte offset of the unit's selection
                          // (-1: read from p.sel / p.sel_count)
   int nsel_s;            // the selection's length when sel_off >= 0
+  int list_off;          // single tokens: LDS byte offset of a draft chunk's
+                         // token list (cache row per entry, -1 = none), or
+                         // of a verify's logit staging slots (4 KiB per
+                         // wave; used with several row tiles)
 };
 
 // Orders LDS writes before reads among the waves sharing a tile: a plain
@@ -288,6 +292,92 @@ __device__ __forceinline__ void store_tile(TileRegs<D, NWR>& r, char* grp, int l
   }
 }
 
+// ---- single-token draft lists (block size 1): a tile is 32 arbitrary
+// tokens, each a row (page, head, slot) of the cache, read from a list
+// staged in LDS for the whole chunk ----
+
+// Bit m of the result: tile token m (list entry rel + m) is a real token of
+// this token group.  Lanes 0..31 test one entry each.
+__device__ __forceinline__ uint32_t gather_mask(const int32_t* rows_s, int rel, int n_left) {
+  const int lane = threadIdx.x & 63;
+  const bool v = lane < 32 && lane < n_left && rows_s[rel + lane] >= 0;
+  return (uint32_t)__ballot(v);
+}
+
+// Same chunk and unit assignment as load_tile; each token's row comes from
+// the list, an invalid token reads row 0 (allocated memory; masked later).
+template <int D, int NWR>
+__device__ __forceinline__ void load_tile_gather(TileRegs<D, NWR>& r, const bf16* __restrict__ kc,
+                                                 const bf16* __restrict__ vc,
+                                                 const int32_t* rows_s, int rel, uint32_t vm,
+                                                 int lig) {
+  typedef TileRegs<D, NWR> TR;
+  typedef Geo<D> G;
+#pragma unroll
+  for (int j = 0; j < TR::KJ; ++j) {
+    int ci = lig + TR::NL * j;
+    if (!TR::K_CHUNKS_EXACT) ci = min(ci, G::K_CHUNKS - 1);
+    const int m = ci / G::CPT, c = ci % G::CPT;
+    const int row = ((vm >> m) & 1u) ? rows_s[rel + m] : 0;
+    r.k[j] = stream_load(reinterpret_cast<const bf16x8*>(kc + (long long)row * D + 8 * c));
+  }
+#pragma unroll
+  for (int j = 0; j < TR::VJ; ++j) {
+    int ui = lig + TR::NL * j;
+    if (!TR::V_UNITS_EXACT) ui = min(ui, G::V_UNITS - 1);
+    const int g4 = ui & 7, c = (ui >> 3) % G::CPT;
+    const int tok0 = 4 * tau_group(g4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = tok0 + e;
+      const int row = ((vm >> m) & 1u) ? rows_s[rel + m] : 0;
+      r.v[j][e] = stream_load(reinterpret_cast<const bf16x8*>(vc + (long long)row * D + 8 * c));
+    }
+  }
+}
+
+// store_tile for a gathered tile: V rows of tokens outside the mask zeroed.
+template <int D, int NWR>
+__device__ __forceinline__ void store_tile_gather(TileRegs<D, NWR>& r, char* grp, int lig,
+                                                  uint32_t vm) {
+  typedef TileRegs<D, NWR> TR;
+  typedef Geo<D> G;
+#pragma unroll
+  for (int j = 0; j < TR::KJ; ++j) {
+    const int ci = lig + TR::NL * j;
+    if (TR::K_CHUNKS_EXACT || ci < G::K_CHUNKS) {
+      const int m = ci / G::CPT, c = ci % G::CPT;
+      *reinterpret_cast<bf16x8*>(grp + m * G::K_STRIDE + 16 * c) = r.k[j];
+    }
+  }
+  char* vt = grp + G::K_BYTES;
+#pragma unroll
+  for (int j = 0; j < TR::VJ; ++j) {
+    const int ui = lig + TR::NL * j;
+    if (TR::V_UNITS_EXACT || ui < G::V_UNITS) {
+      const int g4 = ui & 7, c = (ui >> 3) % G::CPT;
+      if (vm != 0xffffffffu) {
+        const int tok0 = 4 * tau_group(g4);
+        const bf16x8 zero = {};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (!((vm >> (tok0 + e)) & 1u)) r.v[j][e] = zero;
+      }
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const int d = 8 * c + dd;
+        bf16x4 w;
+        w[0] = r.v[j][0][dd];
+        w[1] = r.v[j][1][dd];
+        w[2] = r.v[j][2][dd];
+        w[3] = r.v[j][3][dd];
+        *reinterpret_cast<bf16x4*>(vt + vrow(d) * 64 + 16 * ((g4 >> 1) ^ vq_swz(d)) +
+                                   8 * (g4 & 1)) = w;
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -307,8 +397,13 @@ constexpr float kRescaleSlack = 8.f;
 // PD: tiles in flight per token group (register prefetch depth).  A tile
 // shared by several row waves costs each of them only a fraction of its
 // registers, so those configurations keep two tiles in flight.
-template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS>
+// TOKENS: blocks of one token.  A draft then gathers its tiles token by
+// token from a list (one row tile only); a verify stores each token's logit
+// as its log mass.
+template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS = false>
 __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
+  constexpr bool GATHER = DRAFT && TOKENS;
+  static_assert(!GATHER || NWR == 1, "token lists serve one-row-tile drafts");
   constexpr int PD = NWR >= 2 ? 2 : 1;
   constexpr int NT = 64 * NWR * NWT;
   typedef Geo<D> G;
@@ -359,7 +454,8 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
     ws = window_start(L, p.window);
     nsel = it.sel_off >= 0 ? it.nsel_s : p.sel_count[(long long)b * p.num_kv_heads + h];
     nsel = nsel < 0 ? 0 : (nsel > p.max_sel ? p.max_sel : nsel);
-    nseg = draft_list_len_mfma(nsel, p.block_size, L, ws);
+    nseg = GATHER ? draft_list_len_simple(nsel, 1, L, ws)
+                  : draft_list_len_mfma(nsel, p.block_size, L, ws);
     seg_lo = c * it.chunk;
     if (seg_lo >= nseg && c > 0) return kItemNone;
     seg_hi = min(seg_lo + it.chunk, nseg);
@@ -378,7 +474,11 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   const int per_group = (DRAFT ? it.chunk : it.chunk / kSeg) / NWT;
   const int g_lo = min(seg_lo + tg * per_group, seg_hi);
   const int g_hi = min(g_lo + per_group, seg_hi);
-  const int n_tiles = ceil_div(min(per_group, seg_hi - seg_lo), 2);  // group 0 has the most
+  // list entries per tile: two 16-token segments, or 32 single tokens
+  constexpr int kTileEntries = GATHER ? 32 : 2;
+  const int n_tiles = ceil_div(min(per_group, seg_hi - seg_lo), kTileEntries);  // group 0 has the most
+  // token list of a single-token draft chunk: cache row of each entry
+  int32_t* const rows_s = reinterpret_cast<int32_t*>(smem + (GATHER ? it.list_off : 0));
 
   const bf16* __restrict__ kc = reinterpret_cast<const bf16*>(p.k);
   const bf16* __restrict__ vc = reinterpret_cast<const bf16*>(p.v);
@@ -386,9 +486,42 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
 
   int bad = 0;
   // segment descriptors of the first two batches of 64
-  SegLane cur = seg_lane<DRAFT>(p, sel_s, b, h, g_lo + lane, g_hi, nsel, L, ws);
-  SegLane nxt = seg_lane<DRAFT>(p, sel_s, b, h, g_lo + 64 + lane, g_hi, nsel, L, ws);
+  SegLane cur = {}, nxt = {};
+  if constexpr (!GATHER) {
+    cur = seg_lane<DRAFT>(p, sel_s, b, h, g_lo + lane, g_hi, nsel, L, ws);
+    nxt = seg_lane<DRAFT>(p, sel_s, b, h, g_lo + 64 + lane, g_hi, nsel, L, ws);
+  }
   int cur_batch = 0;
+  // gathered tiles: list entry of the token group's first token, relative
+  // to the chunk's list, and the tokens left from there
+  const int g_rel = g_lo - seg_lo, g_len = g_hi - g_lo;
+
+  if constexpr (GATHER) {
+    // the chunk's token list: selected tokens before the window, then the
+    // window; entries past the list are -1
+    for (int e = threadIdx.x; e < it.chunk; e += NT) {
+      const int k = seg_lo + e;
+      int row = -1;
+      if (k < seg_hi) {
+        int t = -1;
+        if (k < nsel) {
+          const int j = sel_s ? sel_s[k]
+                              : p.sel[((long long)b * p.num_kv_heads + h) * p.max_sel + k];
+          if (j >= 0 && j < ws) t = j;
+        } else {
+          t = ws + (k - nsel);
+        }
+        if (t >= 0) {
+          const int pg = p.page_table[(long long)b * p.max_pages + t / p.page_size];
+          if (pg < 0 || pg >= p.num_pages)
+            bad = 1;
+          else
+            row = (pg * p.num_kv_heads + h) * p.page_size + t % p.page_size;
+        }
+      }
+      rows_s[e] = row;
+    }
+  }
 
   // ---- Q rows of each row tile -> LDS (the Q^T operand is read from there) ----
   char* qtile = smem + NWT * G::GROUP_BYTES + rt * G::Q_BYTES;
@@ -426,13 +559,23 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   long long ell_at = -1;
   float* ell_u = p.ell + (long long)u * p.max_blocks * R;
 
+  // single-token verify: this wave's logit parking area
+  float* const tok_stage = NWR == 1 ? reinterpret_cast<float*>(grp)
+                                    : reinterpret_cast<float*>(smem + it.list_off) + w * 32 * 32;
+
   TileRegs<D, NWR> regs[PD];
   Seg sa[PD], sb[PD];
+  uint32_t vm[PD];
 #pragma unroll
   for (int q = 0; q < PD; ++q) {
-    sa[q] = seg_of(p, h, cur, nxt, false, 2 * q, bad);
-    sb[q] = seg_of(p, h, cur, nxt, false, 2 * q + 1, bad);
-    load_tile<D, NWR>(regs[q], kc, vc, sa[q], sb[q], lig);
+    if constexpr (GATHER) {
+      vm[q] = gather_mask(rows_s, g_rel + 32 * q, g_len - 32 * q);
+      load_tile_gather<D, NWR>(regs[q], kc, vc, rows_s, g_rel + 32 * q, vm[q], lig);
+    } else {
+      sa[q] = seg_of(p, h, cur, nxt, false, 2 * q, bad);
+      sb[q] = seg_of(p, h, cur, nxt, false, 2 * q + 1, bad);
+      load_tile<D, NWR>(regs[q], kc, vc, sa[q], sb[q], lig);
+    }
   }
 
   for (int t0 = 0; t0 < n_tiles; t0 += PD)
@@ -440,12 +583,19 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   for (int q = 0; q < PD; ++q) {
     const int t = t0 + q;
     if (t >= n_tiles) break;
-    const int rel0 = 2 * t;
+    const int rel0 = kTileEntries * t;
     const bool tile_live = g_lo + rel0 < g_hi;
     const Seg ca = sa[q], cb = sb[q];
-    const bool full = seg_full(ca) && seg_full(cb);
-    store_tile<D, NWR>(regs[q], grp, lig, ca, cb, full);
-    if (rel0 > 0 && (rel0 & 63) == 0) {
+    const uint32_t vmq = GATHER ? vm[q] : 0u;
+    bool full;
+    if constexpr (GATHER) {
+      full = vmq == 0xffffffffu;
+      store_tile_gather<D, NWR>(regs[q], grp, lig, vmq);
+    } else {
+      full = seg_full(ca) && seg_full(cb);
+      store_tile<D, NWR>(regs[q], grp, lig, ca, cb, full);
+    }
+    if (!GATHER && rel0 > 0 && (rel0 & 63) == 0) {
       // move to the next batch of descriptors; fetch the one after it
       cur = nxt;
       ++cur_batch;
@@ -458,10 +608,16 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if (t + PD < n_tiles) {
-      const int ra = rel0 + 2 * PD, rb = ra + 1;
-      sa[q] = seg_of(p, h, cur, nxt, (ra >> 6) != cur_batch, ra & 63, bad);
-      sb[q] = seg_of(p, h, cur, nxt, (rb >> 6) != cur_batch, rb & 63, bad);
-      load_tile<D, NWR>(regs[q], kc, vc, sa[q], sb[q], lig);
+      if constexpr (GATHER) {
+        const int rn = rel0 + 32 * PD;
+        vm[q] = gather_mask(rows_s, g_rel + rn, g_len - rn);
+        load_tile_gather<D, NWR>(regs[q], kc, vc, rows_s, g_rel + rn, vm[q], lig);
+      } else {
+        const int ra = rel0 + 2 * PD, rb = ra + 1;
+        sa[q] = seg_of(p, h, cur, nxt, (ra >> 6) != cur_batch, ra & 63, bad);
+        sb[q] = seg_of(p, h, cur, nxt, (rb >> 6) != cur_batch, rb & 63, bad);
+        load_tile<D, NWR>(regs[q], kc, vc, sa[q], sb[q], lig);
+      }
     }
     if (tile_live) {
       // S^T = K Q^T
@@ -479,11 +635,19 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       // online softmax (log2 domain); interior tiles need no mask
       float s[16];
       float mx = neg_inf();
-      const bool interior = full && cb.t0 + kSeg - 1 <= pos_min;
+      const bool interior = full && (GATHER || cb.t0 + kSeg - 1 <= pos_min);
       if (interior) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           s[i] = sacc[i] * p.scale_log2;
+          mx = fmaxf(mx, s[i]);
+        }
+      } else if constexpr (GATHER) {
+        // every listed token precedes the query: only the mask applies
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = (i >> 2) * 8 + 4 * hl + (i & 3);
+          s[i] = ((vmq >> m) & 1u) ? sacc[i] * p.scale_log2 : neg_inf();
           mx = fmaxf(mx, s[i]);
         }
       } else {
@@ -496,6 +660,15 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
           s[i] = ok ? sacc[i] * p.scale_log2 : neg_inf();
           mx = fmaxf(mx, s[i]);
         }
+      }
+      if constexpr (!DRAFT && TOKENS) {
+        // single-token blocks: the log mass of token t in row r is the
+        // (masked) logit itself, whatever the frame.  The wave parks its
+        // 32 tokens x 32 rows in 4 KiB of LDS of its own (one row tile: the
+        // tile's K rows, which S has consumed; else a slot at it.list_off)
+        // and stores them once the tile is done
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tok_stage[((i >> 2) * 8 + 4 * hl + (i & 3)) * 32 + rl] = s[i];
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // lazy rescaling: the reference max m_run moves only when a row's max
@@ -542,7 +715,31 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       if (!DRAFT) {
         // per-block log mass of this row, frame m_use
         const int bs = p.block_size;
-        if (bs == kSeg) {
+        if (TOKENS) {
+          // the parked logits, token-major: token ca.t0 + m, row r at
+          // ell_u[(ca.t0 + m) * R + r], for the tokens of the request only;
+          // each token's run of rows with 16-byte stores, 8 lanes per token
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int n_tok = min(32, L - ca.t0);
+          const int rw = min(32, R - rt * 32);  // rows of this wave
+          float* dst = ell_u + (long long)ca.t0 * R + rt * 32;
+          // (offsets stay 32-bit and are formed in the loop: hoisting 64-bit
+          // addresses out of the tile loop costs more registers than exist)
+          if ((rw & 3) == 0 && (R & 3) == 0) {
+            const int q = lane & 7;
+            if (4 * q < rw) {
+#pragma unroll 1
+              for (int m = lane >> 3; m < n_tok; m += 8)
+                *reinterpret_cast<f32x4*>(dst + (m * R + 4 * q)) =
+                    *reinterpret_cast<const f32x4*>(tok_stage + m * 32 + 4 * q);
+            }
+          } else if (rl < rw) {
+#pragma unroll 1
+            for (int m = hl; m < n_tok; m += 2) dst[m * R + rl] = tok_stage[m * 32 + rl];
+          }
+        } else if (bs == kSeg) {
           float a = 0.f, bb = 0.f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) a += pr[i];
@@ -689,13 +886,39 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
     const int nblk = ceil_div(L, p.block_size);
     const float* ell = ell_lds ? ell_s : ell_u;
     const int r0 = p.score_row_start * p.group;
-    for (int j = threadIdx.x; j < p.max_blocks; j += NT) {
-      float sc = 0.f;
-      if (j < nblk) {
-        const float* e = ell + (long long)j * R;
-        for (int rr = r0; rr < R; ++rr) sc += fast_exp2(e[rr] - lse2s[rr]);
+    if (TOKENS && (R & 3) == 0 && (r0 & 3) == 0) {
+      // one token per thread, its rows as 16-byte loads issued 8 at a time
+      // (the log masses come back from L2 / HBM, so loads are batched)
+      const int nq = (R - r0) >> 2;
+      for (int j = threadIdx.x; j < p.max_blocks; j += NT) {
+        float sc = 0.f;
+        if (j < nblk) {
+          const f32x4* e = reinterpret_cast<const f32x4*>(ell + (long long)j * R + r0);
+          for (int q0 = 0; q0 < nq; q0 += 8) {
+            f32x4 x[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              if (q0 + k < nq) x[k] = e[q0 + k];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              if (q0 + k < nq) {
+                const float* l2 = lse2s + r0 + 4 * (q0 + k);
+                sc += fast_exp2(x[k][0] - l2[0]) + fast_exp2(x[k][1] - l2[1]) +
+                      fast_exp2(x[k][2] - l2[2]) + fast_exp2(x[k][3] - l2[3]);
+              }
+          }
+        }
+        p.block_scores[(long long)u * p.max_blocks + j] = bad ? qnan() : sc;
       }
-      p.block_scores[(long long)u * p.max_blocks + j] = bad ? qnan() : sc;
+    } else {
+      for (int j = threadIdx.x; j < p.max_blocks; j += NT) {
+        float sc = 0.f;
+        if (j < nblk) {
+          const float* e = ell + (long long)j * R;
+          for (int rr = r0; rr < R; ++rr) sc += fast_exp2(e[rr] - lse2s[rr]);
+        }
+        p.block_scores[(long long)u * p.max_blocks + j] = bad ? qnan() : sc;
+      }
     }
   }
   return final_out ? kItemFinal : kItemPartial;

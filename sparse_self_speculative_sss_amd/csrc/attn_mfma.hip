@@ -6,7 +6,7 @@
 namespace sss {
 namespace {
 
-template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS>
+template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS>
 __global__ void __launch_bounds__(64 * NWR * NWT, 2) attn_mfma_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   if (p.skip_len >= 0 && p.seq_lens[(blockIdx.x / p.num_chunks) / p.num_kv_heads] <= p.skip_len)
@@ -21,7 +21,10 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2) attn_mfma_kernel(AttnParams
   it.ell_off = (int)item_lds_bytes(D, NWR, NWT);
   it.sel_off = -1;
   it.nsel_s = 0;
-  attn_item<D, NWR, NWT, DRAFT, ELL_LDS>(p, it, smem);
+  // after the tiles: a single-token draft's token list, or the logit
+  // staging slots of a single-token verify with several row tiles
+  it.list_off = (int)item_lds_bytes(D, NWR, NWT);
+  attn_item<D, NWR, NWT, DRAFT, ELL_LDS, TOKENS>(p, it, smem);
 }
 
 }  // namespace
@@ -34,54 +37,73 @@ size_t mfma_smem_bytes(int D, int nwr, int nwt, long long ell_floats) {
 
 namespace {
 
+template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS>
+hipError_t launch_one(const AttnParams& p, size_t smem, unsigned grid, hipStream_t s) {
+  auto kern = attn_mfma_kernel<D, NWR, NWT, DRAFT, ELL_LDS, TOKENS>;
+  // dynamic LDS above 64 KiB must be opted into; allow the whole LDS once
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)kMaxLds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NWR * NWT), smem, s, p);
+  return hipGetLastError();
+}
+
 template <int D, int NWR, int NWT, bool DRAFT>
 hipError_t launch_cfg(const AttnParams& p, hipStream_t s) {
   typedef Geo<D> G;
   static_assert((size_t)NWT * G::GROUP_BYTES >=
                     (NWT > 1 ? ((size_t)(NWT - 1) * NWR * 32 * D + 2 * NWT * NWR * 32) * 4 : 0),
                 "merge scratch must fit below the Q tiles");
-  const size_t smem = mfma_smem_bytes(D, NWR, NWT, p.ell_in_lds ? p.ell_lds_floats : 0);
   const unsigned grid = (unsigned)((long long)p.batch * p.num_kv_heads * p.num_chunks);
   if (grid == 0) return hipSuccess;
-  // dynamic LDS above 64 KiB must be opted into; allow the whole LDS once
-  if (smem > kMaxLds) return hipErrorInvalidValue;
-  // block log masses in LDS (verify chunks whose masses fit) or stored to
-  // the workspace as blocks complete
-  if constexpr (!DRAFT) {
-    if (p.ell_in_lds) {
-      static const hipError_t attr = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&attn_mfma_kernel<D, NWR, NWT, DRAFT, true>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
-      if (attr != hipSuccess) return attr;
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NWR, NWT, DRAFT, true>), dim3(grid),
-                         dim3(64 * NWR * NWT), smem, s, p);
-      return hipGetLastError();
+  if constexpr (DRAFT) {
+    if (p.block_size == 1) {
+      // single-token selection: gathered tiles, token list in LDS
+      if constexpr (NWR == 1) {
+        const size_t smem = mfma_smem_bytes(D, NWR, NWT, 0) + (size_t)p.chunk_items * 4;
+        if (smem > kMaxLds) return hipErrorInvalidValue;
+        return launch_one<D, NWR, NWT, true, false, true>(p, smem, grid, s);
+      } else {
+        return hipErrorInvalidValue;
+      }
     }
+    const size_t smem = mfma_smem_bytes(D, NWR, NWT, 0);
+    return launch_one<D, NWR, NWT, true, false, false>(p, smem, grid, s);
+  } else {
+    // block log masses in LDS (verify units that fit in one chunk, when they
+    // fit) or stored to the workspace as blocks complete
+    const size_t smem = mfma_smem_bytes(D, NWR, NWT, p.ell_in_lds ? p.ell_lds_floats : 0);
+    if (smem > kMaxLds) return hipErrorInvalidValue;
+    // single-token blocks: every token's logit is stored (never in LDS),
+    // staged per wave in the tile's K rows (one row tile) or in a 4 KiB
+    // slot after the tiles
+    if (p.block_size == 1) {
+      const size_t smem_t = mfma_smem_bytes(D, NWR, NWT, 0) + (NWR > 1 ? (size_t)NWR * NWT * 4096 : 0);
+      if (smem_t > kMaxLds) return hipErrorInvalidValue;
+      return launch_one<D, NWR, NWT, false, false, true>(p, smem_t, grid, s);
+    }
+    if (p.ell_in_lds) return launch_one<D, NWR, NWT, false, true, false>(p, smem, grid, s);
+    return launch_one<D, NWR, NWT, false, false, false>(p, smem, grid, s);
   }
-  {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&attn_mfma_kernel<D, NWR, NWT, DRAFT, false>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((attn_mfma_kernel<D, NWR, NWT, DRAFT, false>), dim3(grid),
-                       dim3(64 * NWR * NWT), smem, s, p);
-  }
-  return hipGetLastError();
 }
+
+// Token groups of a one-row-tile draft workgroup.
+constexpr int kDraftNwt = 4;
 
 template <bool DRAFT>
 hipError_t dispatch(const AttnParams& p, hipStream_t s) {
   const int nwr = ceil_div(p.rows, 32);
   if (p.head_dim == 128) {
     switch (nwr) {
-      case 1: return launch_cfg<128, 1, 4, DRAFT>(p, s);
+      case 1: return launch_cfg<128, 1, DRAFT ? kDraftNwt : 4, DRAFT>(p, s);
       case 2: return launch_cfg<128, 2, 2, DRAFT>(p, s);
       case 3: return launch_cfg<128, 3, 1, DRAFT>(p, s);
       case 4: return launch_cfg<128, 4, 1, DRAFT>(p, s);
     }
   } else if (p.head_dim == 64) {
     switch (nwr) {
-      case 1: return launch_cfg<64, 1, 4, DRAFT>(p, s);
+      case 1: return launch_cfg<64, 1, DRAFT ? kDraftNwt : 4, DRAFT>(p, s);
       case 2: return launch_cfg<64, 2, 2, DRAFT>(p, s);
       case 3: return launch_cfg<64, 3, 1, DRAFT>(p, s);
       case 4: return launch_cfg<64, 4, 1, DRAFT>(p, s);
@@ -93,7 +115,10 @@ hipError_t dispatch(const AttnParams& p, hipStream_t s) {
 }  // namespace
 
 // Token groups per workgroup for a given row count (must match dispatch).
-int mfma_token_groups(int rows) { return token_groups_for(ceil_div(rows, 32)); }
+int mfma_token_groups(int rows, bool draft) {
+  const int nwr = ceil_div(rows, 32);
+  return (draft && nwr == 1) ? kDraftNwt : token_groups_for(nwr);
+}
 
 hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s) { return dispatch<false>(p, s); }
 hipError_t launch_draft_mfma(const AttnParams& p, hipStream_t s) { return dispatch<true>(p, s); }

@@ -135,8 +135,8 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinalizeParams p)
   if (!p.ell) return;
 
   const int nblk = ceil_div(L, p.block_size);
-  const float* ell = p.ell + (long long)u * p.max_blocks * R;
   const int r0 = p.score_row_start * G;
+  const float* ell = p.ell + (long long)u * p.max_blocks * R;
   for (int j = j_lo + threadIdx.x; j < j_hi; j += kFinThreads) {
     float sc = 0.f;
     if (j < nblk) {

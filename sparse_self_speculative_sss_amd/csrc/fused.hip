@@ -101,6 +101,8 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
     topk_bounds(L, pv.block_size, f.topk_window, pv.max_blocks, f.budget[b], f.max_sel, ncand, n);
     if (tid == 0) f.sel_count[u] = n;
     int32_t* sel_s = reinterpret_cast<int32_t*>(smem + f.off_sel);
+    static_assert(kTopkLdsWords * 4 <= NWT * Geo<D>::GROUP_BYTES,
+                  "selection scratch must fit in the tile area");
     topk_select<NT>(pv.block_scores + (long long)u * pv.max_blocks, ncand, n,
                     f.sel + (long long)u * f.max_sel, f.max_sel, f.chained ? sel_s : nullptr,
                     reinterpret_cast<int*>(smem));

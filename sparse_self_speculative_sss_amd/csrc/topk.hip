@@ -6,6 +6,8 @@ namespace sss {
 namespace {
 
 constexpr int kTopkThreads = 256;
+// keys parked in LDS up to this many candidates (64 KiB)
+constexpr int kTopkMaxKeys = 16384;
 
 __global__ void __launch_bounds__(kTopkThreads)
     topk_kernel(const float* __restrict__ scores, int hkv, int max_blocks,
@@ -13,6 +15,8 @@ __global__ void __launch_bounds__(kTopkThreads)
                 int window, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
                 int max_sel, int skip_len) {
   __shared__ int lds[kTopkLdsWords];
+  // the unit's keys, when max_blocks of them fit (dynamic LDS)
+  extern __shared__ uint32_t keys[];
   const int u = blockIdx.x;
   const int b = u / hkv;
   // units no longer than skip_len were selected by the fused step kernel
@@ -21,7 +25,8 @@ __global__ void __launch_bounds__(kTopkThreads)
   topk_bounds(seq_lens[b], bs, window, max_blocks, budget[b], max_sel, ncand, n);
   if (threadIdx.x == 0) sel_count[u] = n;
   topk_select<kTopkThreads>(scores + (long long)u * max_blocks, ncand, n,
-                            sel + (long long)u * max_sel, max_sel, nullptr, lds);
+                            sel + (long long)u * max_sel, max_sel, nullptr, lds, keys,
+                            max_blocks <= kTopkMaxKeys ? max_blocks : 0);
 }
 
 }  // namespace
@@ -32,7 +37,13 @@ hipError_t launch_topk(const float* scores, int batch, int hkv, int max_blocks,
                        hipStream_t s) {
   const unsigned grid = (unsigned)((long long)batch * hkv);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(grid), dim3(kTopkThreads), 0, s, scores, hkv, max_blocks,
+  const size_t smem = max_blocks <= kTopkMaxKeys ? (size_t)max_blocks * 4 : 0;
+  // dynamic LDS above 64 KiB (with the static part) must be opted into
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(topk_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+      kTopkMaxKeys * 4);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(topk_kernel, dim3(grid), dim3(kTopkThreads), smem, s, scores, hkv, max_blocks,
                      seq_lens, block_size, budget, window, sel, sel_count, max_sel, skip_len);
   return hipGetLastError();
 }

@@ -6,8 +6,10 @@
 // four 8-bit MSB-first histogram passes find the N-th largest key T; the
 // blocks with key > T are taken, plus the lowest-index blocks with key == T
 // until N are taken.  Histograms count with LDS integer atomics (order
-// independent), ranks come from ballot prefix sums in index order, so the
-// selection is bit-exact and deterministic.  Output is ascending.
+// independent), ranks come from prefix sums in index order, so the
+// selection is bit-exact and deterministic.  Output is ascending: each
+// thread emits a contiguous range of candidates at offsets from two
+// workgroup prefix sums (ties before it, selections before it).
 #pragma once
 
 #include "sss_common.h"
@@ -38,18 +40,26 @@ __device__ __forceinline__ void topk_bounds(int L, int bs, int window, int max_b
   if (n > max_sel) n = max_sel;
 }
 
+// histogram bins of a radix digit (8 bits)
+constexpr int kTopkBins = 256;
 // LDS words topk_select needs.
-constexpr int kTopkLdsWords = 256 + 16 + 2;
+constexpr int kTopkLdsWords = kTopkBins + 16 + 2;
+// scores loaded per thread before they are used
+constexpr int kTopkBatch = 8;
 
-// Exclusive prefix count of `flag` over the workgroup in thread order, and
-// the workgroup total.  `scratch` holds NT / 64 ints.
+// Exclusive prefix sum of v over the workgroup in thread order, and the
+// total.  `scratch` holds NT / 64 ints.
 template <int NT>
-__device__ __forceinline__ int wg_exclusive_count(bool flag, int* scratch, int& total) {
+__device__ __forceinline__ int wg_exclusive_sum(int v, int* scratch, int& total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long m = __ballot(flag);
-  const int below = __popcll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) scratch[wave] = __popcll(m);
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) scratch[wave] = incl;
   __syncthreads();
   int before = 0;
   total = 0;
@@ -60,25 +70,159 @@ __device__ __forceinline__ int wg_exclusive_count(bool flag, int* scratch, int& 
     total += c;
   }
   __syncthreads();
-  return before + below;
+  return before + incl - v;
+}
+
+// hist[bin] += 1 for every lane with `act`.  Scores crowd into few bins
+// (one histogram bin spans two binades in the first pass), and LDS atomics
+// to one address serialise lane by lane, so the two most common bins among
+// the wave's first active lanes are counted with one atomic each and only
+// the remaining lanes add one by one.
+__device__ __forceinline__ void hist_count(int* hist, bool act, uint32_t bin) {
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const unsigned long long am = __ballot(act);
+    if (am == 0) return;
+    const int leader = __builtin_ctzll(am);
+    const uint32_t b0 = __builtin_amdgcn_readlane(bin, leader);
+    const bool same = act && bin == b0;
+    const unsigned long long sm = __ballot(same);
+    if ((threadIdx.x & 63) == leader) atomicAdd(&hist[b0], (int)__popcll(sm));
+    act = act && !same;
+  }
+  if (act) atomicAdd(&hist[bin], 1);
+}
+
+// Where the selection reads its keys: the fp32 scores themselves, or their
+// keys parked in LDS.
+struct ScoreSrc {
+  const float* sc;
+  __device__ __forceinline__ uint32_t operator()(int j) const { return score_key(sc[j]); }
+};
+struct KeySrc {
+  const uint32_t* k;
+  __device__ __forceinline__ uint32_t operator()(int j) const { return k[j]; }
+};
+
+// Radix select and ascending emission over keys key(0 .. ncand-1), with
+// 0 < n < ncand.  `B` keys are read per thread before they are used.
+template <int NT, int B, typename Src>
+__device__ void topk_core(Src key, int ncand, int n, int32_t* __restrict__ out, int32_t* out_lds,
+                          int* lds) {
+  int* hist = lds;
+  int* scan_scratch = lds + kTopkBins;
+  int* s_digit = lds + kTopkBins + 16;
+  int* s_rem = lds + kTopkBins + 17;
+  const int tid = threadIdx.x;
+  constexpr int PT = (kTopkBins + NT - 1) / NT;  // bins per thread in the digit search
+
+  // ---- radix select of the n-th largest key: four 8-bit digits ----
+  uint32_t prefix = 0, pmask = 0;
+  int rem = n;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t dmask = 255u;
+    for (int i = tid; i < kTopkBins; i += NT) hist[i] = 0;
+    __syncthreads();
+    // indices past the end re-read the last key and count nothing
+    for (int j0 = tid; j0 < ncand; j0 += B * NT) {
+      uint32_t k[B];
+#pragma unroll
+      for (int e = 0; e < B; ++e) k[e] = key(min(j0 + e * NT, ncand - 1));
+#pragma unroll
+      for (int e = 0; e < B; ++e)
+        hist_count(hist, j0 + e * NT < ncand && (k[e] & pmask) == prefix, (k[e] >> shift) & dmask);
+    }
+    __syncthreads();
+    // the digit holding the rem-th largest key: bins in descending order,
+    // PT consecutive ones per thread
+    int c[PT], local = 0;
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int bin = kTopkBins - 1 - (tid * PT + i);
+      c[i] = bin >= 0 ? hist[bin] : 0;
+      local += c[i];
+    }
+    int tot;
+    const int excl = wg_exclusive_sum<NT>(local, scan_scratch, tot);
+    if (excl < rem && rem <= excl + local) {
+      int cum = excl;
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        if (cum + c[i] >= rem) {
+          *s_digit = kTopkBins - 1 - (tid * PT + i);
+          *s_rem = rem - cum;
+          break;
+        }
+        cum += c[i];
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)*s_digit << shift;
+    pmask |= dmask << shift;
+    rem = *s_rem;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const int need_eq = rem;
+
+  // ---- ascending emission: thread t owns candidates [t*per, (t+1)*per);
+  // an odd `per` keeps the lanes of a wave on distinct LDS banks ----
+  const int per = ((ncand + NT - 1) / NT) | 1;
+  const int j0 = min(tid * per, ncand), j1 = min(j0 + per, ncand);
+  int n_gt = 0, n_eq = 0;
+  for (int jb = j0; jb < j1; jb += B) {
+    uint32_t k[B];
+#pragma unroll
+    for (int e = 0; e < B; ++e) k[e] = key(min(jb + e, j1 - 1));
+#pragma unroll
+    for (int e = 0; e < B; ++e)
+      if (jb + e < j1) {
+        n_gt += k[e] > T;
+        n_eq += k[e] == T;
+      }
+  }
+  int tot;
+  const int eq_before = wg_exclusive_sum<NT>(n_eq, scan_scratch, tot);
+  // ties are taken lowest index first: this thread's share of the need_eq
+  const int eq_take = min(max(need_eq - eq_before, 0), n_eq);
+  int pos = wg_exclusive_sum<NT>(n_gt + eq_take, scan_scratch, tot);
+  int eq_seen = 0;
+  for (int jb = j0; jb < j1; jb += B) {
+    uint32_t k[B];
+#pragma unroll
+    for (int e = 0; e < B; ++e) k[e] = key(min(jb + e, j1 - 1));
+#pragma unroll
+    for (int e = 0; e < B; ++e) {
+      const int j = jb + e;
+      if (j >= j1) break;
+      bool take = k[e] > T;
+      if (k[e] == T) take = eq_seen++ < eq_take;
+      if (take) {
+        out[pos] = j;
+        if (out_lds) out_lds[pos] = j;
+        ++pos;
+      }
+    }
+  }
+  __syncthreads();
 }
 
 // The n largest of sc[0, ncand) (ties to the lower index), ascending, into
 // out[0, n); out[n, max_sel) = -1.  When out_lds is given, out_lds[0, n)
-// receives the same list.  `lds` holds kTopkLdsWords ints.  All NT threads
+// receives the same list.  `lds` holds kTopkLdsWords ints.  With `keys`
+// (LDS room for keys_cap words) and ncand <= keys_cap, the keys are read
+// from global memory once and parked there for the passes.  All NT threads
 // of the workgroup call it; it ends with a barrier.
 template <int NT>
 __device__ void topk_select(const float* sc, int ncand, int n, int32_t* __restrict__ out,
-                            int max_sel, int32_t* out_lds, int* lds) {
+                            int max_sel, int32_t* out_lds, int* lds, uint32_t* keys = nullptr,
+                            int keys_cap = 0) {
   static_assert(NT % 64 == 0 && NT >= 64 && NT <= 1024, "workgroup of whole waves");
-  int* hist = lds;
-  int* scan_scratch = lds + 256;
-  int* s_digit = lds + 272;
-  int* s_rem = lds + 273;
   const int tid = threadIdx.x;
 
   // every candidate kept, or none: the list is 0..n-1; otherwise positions
-  // [0, n) are written by the emission below
+  // [0, n) are written by the emission
   for (int j = tid; j < max_sel; j += NT) {
     if (n == ncand)
       out[j] = j < n ? j : -1;
@@ -91,77 +235,20 @@ __device__ void topk_select(const float* sc, int ncand, int n, int32_t* __restri
     __syncthreads();
     return;
   }
-
-  // ---- radix select of the n-th largest key ----
-  uint32_t prefix = 0, pmask = 0;
-  int rem = n;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
-    __syncthreads();
-    for (int j = tid; j < ncand; j += NT) {
-      const uint32_t k = score_key(sc[j]);
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+  if (keys && ncand <= keys_cap) {
+    for (int j0 = tid; j0 < ncand; j0 += kTopkBatch * NT) {
+      float x[kTopkBatch];
+#pragma unroll
+      for (int e = 0; e < kTopkBatch; ++e) x[e] = sc[min(j0 + e * NT, ncand - 1)];
+#pragma unroll
+      for (int e = 0; e < kTopkBatch; ++e)
+        if (j0 + e * NT < ncand) keys[j0 + e * NT] = score_key(x[e]);
     }
     __syncthreads();
-    if (tid < 64) {
-      const int lane = tid;
-      int c[4], local = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c[e] = hist[255 - (4 * lane + e)];  // descending digit order
-        local += c[e];
-      }
-      int incl = local;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      const int excl = incl - local;
-      if (excl < rem && rem <= incl) {
-        int cum = excl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (cum + c[e] >= rem) {
-            *s_digit = 255 - (4 * lane + e);
-            *s_rem = rem - cum;
-            break;
-          }
-          cum += c[e];
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= (uint32_t)*s_digit << shift;
-    pmask |= 255u << shift;
-    rem = *s_rem;
-    __syncthreads();
+    topk_core<NT, 4>(KeySrc{keys}, ncand, n, out, out_lds, lds);
+  } else {
+    topk_core<NT, kTopkBatch>(ScoreSrc{sc}, ncand, n, out, out_lds, lds);
   }
-  const uint32_t T = prefix;
-  const int need_eq = rem;
-
-  // ---- ascending emission ----
-  int taken = 0, ties = 0;
-  for (int base = 0; base < ncand; base += NT) {
-    const int j = base + tid;
-    const bool valid = j < ncand;
-    const uint32_t k = valid ? score_key(sc[j]) : 0u;
-    const bool gt = valid && k > T;
-    const bool eq = valid && k == T;
-    int tie_total;
-    const int tie_rank = ties + wg_exclusive_count<NT>(eq, scan_scratch, tie_total);
-    const bool take = gt || (eq && tie_rank < need_eq);
-    int take_total;
-    const int pos = taken + wg_exclusive_count<NT>(take, scan_scratch, take_total);
-    if (take) {
-      out[pos] = j;
-      if (out_lds) out_lds[pos] = j;
-    }
-    ties += tie_total;
-    taken += take_total;
-  }
-  __syncthreads();
 }
 
 }  // namespace sss

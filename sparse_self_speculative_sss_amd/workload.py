@@ -74,6 +74,10 @@ SHAPES = {
         Shape("longctx_b4_l128k", B=4, L=131072, Hq=32, Hkv=2, d=128, dtype="bf16", n_q=5,
               block_size=64, page_size=64, window=128, budget=16,
               planted=("block_clusters", 0.005, 2), num_splits=64),
+        # single-token selection (PillarAttn's own granularity): the decode
+        # shape with blocks of one token, 5% of the tokens selected
+        Shape("tokensel_b128_l8192", B=128, L=8192, Hq=32, Hkv=8, d=128, dtype="bf16", n_q=5,
+              block_size=1, page_size=16, window=64, budget_frac=0.05),
     ]
 }
 SHAPE_ORDER = list(SHAPES)

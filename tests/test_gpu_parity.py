@@ -41,6 +41,20 @@ SMALL = [
     ("rows80", "longctx_b4_l128k", dict(B=1, L=3000, sigma="one"), [0, 4]),
     ("rows128", "qwen3_8b_layer_b16_l4096", dict(B=1, L=400, Hq=32, Hkv=1, n_q=4), [0, 2]),
     ("rows40", "qwen3_8b_layer_b16_l4096", dict(B=2, L=333, Hq=16, Hkv=2, sigma="one"), [0, 2]),
+    # single-token blocks: logits as token masses, gathered draft tiles
+    ("tok_blk1", "qwen3_8b_layer_b16_l4096", dict(B=2, L=300, block_size=1), [0, 1, 3]),
+    ("tok_blk1_sigma1", "tokensel_b128_l8192", dict(B=2, L=517, sigma="one"), [0, 2]),
+    ("tok_blk1_d64", "decode_b128_l8192", dict(B=2, L=200, d=64, block_size=1, sigma="one"), [0]),
+    ("tok_blk1_rows80", "longctx_b4_l128k", dict(B=1, L=700, block_size=1, page_size=16,
+                                                 budget=40, sigma="one"), [0, 2]),
+    ("tok_blk1_page8", "qwen3_8b_layer_b16_l4096", dict(B=2, L=150, page_size=8, block_size=1,
+                                                        Hq=8, Hkv=2, sigma="one"), [0, 2]),
+    ("tok_blk1_rows40_d64", "decode_b128_l8192", dict(B=2, L=260, d=64, Hq=16, Hkv=2,
+                                                      block_size=1, sigma="one"), [0, 2]),
+    ("tok_blk1_rows3", "qwen3_8b_layer_b16_l4096", dict(B=2, L=130, Hq=8, Hkv=8, n_q=3,
+                                                        block_size=1, sigma="one"), [0, 2]),
+    ("tok_blk1_rows128", "qwen3_8b_layer_b16_l4096", dict(B=1, L=400, Hq=32, Hkv=1, n_q=4,
+                                                          block_size=1), [0, 2]),
 ]
 
 
@@ -94,7 +108,7 @@ def test_score_row_start_one():
 # full-size workloads, launch configuration of the benchmark
 # --------------------------------------------------------------------------
 FULL = [("qwen3_8b_layer_b16_l4096", 128), ("decode_b128_l8192", 6),
-        ("mixed_b96_l1k_32k", 6), ("longctx_b4_l128k", 2)]
+        ("mixed_b96_l1k_32k", 6), ("longctx_b4_l128k", 2), ("tokensel_b128_l8192", 4)]
 
 
 @pytest.mark.parametrize("name,n_units", FULL, ids=[f[0] for f in FULL])
@@ -135,6 +149,10 @@ TOPK_CASES = [
     (5, 1, 64, (1, 64 * 4), 4, 5, (0, 70), 80, 2),
     (2, 8, 512, (8000, 8192), 16, 64, (26, 26), 26, 0),   # 0 levels: continuous scores
     (3, 2, 33, (1, 33), 1, 0, (0, 40), 33, 2),
+    # single-token blocks at the size of an 8192-token context (keys parked in
+    # LDS), and past the LDS room for keys (read from global memory each pass)
+    (2, 2, 8192, (8000, 8192), 1, 64, (410, 410), 410, 50),
+    (1, 2, 20000, (19000, 20000), 1, 64, (500, 1500), 1500, 0),
 ]
 
 
@@ -150,6 +168,8 @@ def test_topk_bit_exact(case):
             scores = (g.integers(0, levels, (B, hkv, mb)) / levels).astype(np.float32)
         else:
             scores = g.random((B, hkv, mb)).astype(np.float32)
+        if trial == 2:
+            scores -= np.float32(0.5)    # negative scores order like any others
         if trial == 3:
             scores[..., ::3] = -0.0      # -0.0 must tie with +0.0
             scores[..., 1::3] = 0.0
