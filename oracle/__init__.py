@@ -12,7 +12,10 @@ from .sss_oracle import (  # noqa: F401
     gather_unit,
     kv_commit,
     kv_write,
+    layout_union,
     merge,
+    sparse_verify,
+    sparse_verify_token_set,
     topk_unit,
     verify,
     verify_unit,

@@ -22,6 +22,10 @@ What it computes (the pages it follows):
   tokens is kept for later queries, the KV of rejected ones is refreshed.
   Here: writing the new positions' K/V into the paged cache (kv_write) and
   shortening each request to the positions it keeps (kv_commit).
+  核心创新 / 重叠感知分组查询执行 (overlap-aware grouped query execution) and
+  稀疏布局的动态管理 (sparse layout management): each query position of a
+  verify step has its own sparse layout (sparse_verify); a grouped execution
+  loads the union of the layouts once (layout_union).
 
 Every step below is the plain mathematical definition written out with numpy
 (matrix products, exp/log, Python sorting).  No blocking, online softmax,
@@ -267,6 +271,74 @@ def draft(q, k_cache, v_cache, page_table, seq_lens, sel, sel_count,
         O[b, 0, h * G:(h + 1) * G] = P @ V[idx]
         LSE[b, 0, h * G:(h + 1) * G] = lse
     return O, LSE
+
+
+# ---------------------------------------------------------------------------
+# Sparse verification with a layout per query position (SpecSA 核心创新 /
+# 重叠感知分组查询执行 and 技术细节与实现挑战 / 稀疏布局的动态管理: every query
+# has its own sparse layout; queries whose layouts overlap are run as a group
+# that shares the KV blocks.  The grouping changes which loads are shared,
+# not what each query computes, so the oracle computes every query alone.)
+# ---------------------------------------------------------------------------
+def sparse_verify_token_set(seq_len: int, n_q: int, i: int, sel_row, count: int,
+                            block_size: int, window: int):
+    """Sorted tokens that query position i of a verify step attends to: the
+    tokens of its own selected blocks that lie before the window start, plus
+    the window, restricted to the causal limit t <= L - n_q + i."""
+    count = max(0, min(int(count), len(sel_row)))
+    pos = seq_len - n_q + i
+    return [t for t in draft_token_set(seq_len, sel_row, count, block_size, window) if t <= pos]
+
+
+def sparse_verify(q, k_cache, v_cache, page_table, seq_lens, row_sel, row_cnt,
+                  block_size: int, window: int, sm_scale: float, units=None):
+    """Verify attention in which query position i of request b and KV head h
+    attends only to its own layout ``row_sel[b][h][i][:row_cnt[b][h][i]]``
+    (block indices; negative entries and blocks at or past the window start
+    add nothing) plus the recent window, causally.  Every query head of the
+    KV head's group shares the position's layout.
+
+    q: [B][n_q][Hq][d]; row_sel: [B][Hkv][n_q][max_sel]; row_cnt:
+    [B][Hkv][n_q].  Returns O [B][n_q][Hq][d] and LSE [B][n_q][Hq] (fp64); an
+    empty token set gives O = 0 and LSE = -inf.
+    """
+    B, n_q, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    O = np.full((B, n_q, Hq, d), np.nan)
+    LSE = np.full((B, n_q, Hq), np.nan)
+    todo = units if units is not None else [(b, h) for b in range(B) for h in range(Hkv)]
+    for b, h in todo:
+        L = int(seq_lens[b])
+        K, V = gather_unit(k_cache, v_cache, page_table[b], L, h)
+        for i in range(n_q):
+            toks = sparse_verify_token_set(L, n_q, i, row_sel[b, h, i], int(row_cnt[b, h, i]),
+                                           block_size, window)
+            heads = slice(h * G, (h + 1) * G)
+            if not toks:
+                O[b, i, heads] = 0.0
+                LSE[b, i, heads] = NEG_INF
+                continue
+            idx = np.asarray(toks)
+            S = sm_scale * (_f64(q[b, i, heads]) @ K[idx].T)   # [G][|toks|]
+            lse, P = _softmax_rows(S)
+            O[b, i, heads] = P @ V[idx]
+            LSE[b, i, heads] = lse
+    return O, LSE
+
+
+def layout_union(row_sel, row_cnt, seq_len: int, block_size: int, window: int):
+    """Blocks that at least one query position of a unit selects (before the
+    window start), ascending: the blocks a grouped execution loads once."""
+    ws = window_start(seq_len, window)
+    blocks = set()
+    for i in range(row_sel.shape[0]):
+        c = max(0, min(int(row_cnt[i]), row_sel.shape[1]))
+        for j in row_sel[i, :c]:
+            j = int(j)
+            if j >= 0 and j * block_size < ws:
+                blocks.add(j)
+    return sorted(blocks)
 
 
 # ---------------------------------------------------------------------------

@@ -362,6 +362,138 @@ def test_draft_order_of_selection_irrelevant_and_empty_set():
 
 
 # --------------------------------------------------------------------------
+# sparse verification: a layout per query position
+# --------------------------------------------------------------------------
+def sdpa_sparse_verify(q, kc, vc, table, lens, row_sel, row_cnt, bs, window, scale):
+    """Masked SDPA: position i of (b, hq) sees its own selected blocks before
+    the window start, the window, and nothing past L - n_q + i."""
+    B, n_q, Hq, d = q.shape
+    Hkv = kc.shape[1]
+    G = Hq // Hkv
+    O = np.zeros((B, n_q, Hq, d))
+    LSE = np.zeros((B, n_q, Hq))
+    for b in range(B):
+        L = int(lens[b])
+        ws = L if window <= 0 else max(0, L - window)
+        t = torch.arange(L)
+        for hq in range(Hq):
+            h = hq // G
+            mask = torch.zeros((n_q, L), dtype=torch.bool)
+            for i in range(n_q):
+                for j in row_sel[b, h, i, :max(0, int(row_cnt[b, h, i]))]:
+                    mask[i] |= (t // bs == int(j)) & (t < ws)
+                mask[i] |= t >= ws
+                mask[i] &= t <= L - n_q + i
+            K = contiguous(kc, table[b], L, h).double()
+            V = contiguous(vc, table[b], L, h).double()
+            Q = torch.as_tensor(q[b, :, hq]).double()
+            live = mask.any(dim=1)
+            out = F.scaled_dot_product_attention(Q[None], K[None], V[None],
+                                                 attn_mask=mask[None], scale=scale)[0]
+            logits = ((Q @ K.T) * scale).masked_fill(~mask, -math.inf)
+            O[b, :, hq] = torch.where(live[:, None], out, torch.zeros_like(out)).numpy()
+            LSE[b, :, hq] = torch.logsumexp(logits, dim=-1).numpy()
+    return O, LSE
+
+
+def random_row_sel(g, lens, Hkv, n_q, bs, window, budget, max_sel, shared):
+    """Layouts with `shared` blocks common to every position of a unit and the
+    rest drawn per position; entries shuffled, some repeated, -1 padded."""
+    B = len(lens)
+    sel = np.full((B, Hkv, n_q, max_sel), -1, dtype=np.int32)
+    cnt = np.zeros((B, Hkv, n_q), dtype=np.int32)
+    for b, L in enumerate(lens):
+        ws = L if window <= 0 else max(0, L - window)
+        C = [j for j in range(-(-L // bs)) if j * bs < ws]
+        for h in range(Hkv):
+            core = g.choice(C, min(shared, len(C)), replace=False).tolist() if C else []
+            for i in range(n_q):
+                extra = g.choice(C, min(budget, len(C)), replace=False).tolist() if C else []
+                pick = (core + extra)[:max_sel]
+                if pick and len(pick) < max_sel:
+                    pick.append(pick[0])                       # a repeated entry
+                g.shuffle(pick)
+                sel[b, h, i, :len(pick)] = pick
+                cnt[b, h, i] = len(pick)
+    return sel, cnt
+
+
+@pytest.mark.parametrize("window", [0, 2, 5, 16])
+def test_sparse_verify_matches_masked_sdpa(window):
+    g = np.random.default_rng(21)
+    q, kc, vc, table, lens = paged_case(B=2, Ls=(53, 80), Hq=4, Hkv=2, n_q=4, P=4)
+    sel, cnt = random_row_sel(g, lens.tolist(), 2, 4, 8, window, 2, 5, 1)
+    O, LSE = oracle.sparse_verify(q, kc, vc, table, lens, sel, cnt, 8, window, 0.4)
+    Or, LSEr = sdpa_sparse_verify(q, kc, vc, table, lens, sel, cnt, 8, window, 0.4)
+    assert np.abs(O - Or).max() < 1e-12
+    assert np.abs(LSE - LSEr).max() < 1e-12
+
+
+def test_sparse_verify_full_layouts_equal_dense_verify():
+    q, kc, vc, table, lens = paged_case(B=2, Ls=(53, 80), Hq=4, Hkv=2, n_q=3, P=4)
+    nblk = -(-80 // 8)
+    sel = np.tile(np.arange(nblk, dtype=np.int32), (2, 2, 3, 1))
+    cnt = np.full((2, 2, 3), nblk, dtype=np.int32)
+    Od, LSEd = sdpa_verify(q, kc, vc, table, lens, 0.4)
+    for window in (0, 1, 7, 1000):
+        O, LSE = oracle.sparse_verify(q, kc, vc, table, lens, sel, cnt, 8, window, 0.4)
+        assert np.abs(O - Od).max() < 1e-12 and np.abs(LSE - LSEd).max() < 1e-12
+
+
+def test_sparse_verify_single_position_equals_draft():
+    g = np.random.default_rng(22)
+    q, kc, vc, table, lens = paged_case(B=2, Ls=(53, 80), n_q=1, P=4)
+    for window in (0, 5, 16):
+        sel, cnt = random_sel(g, lens.tolist(), kc.shape[1], 8, window, 3, 4)
+        O, LSE = oracle.sparse_verify(q, kc, vc, table, lens, sel[:, :, None], cnt[:, :, None],
+                                      8, window, 0.4)
+        Od, LSEd = oracle.draft(q, kc, vc, table, lens, sel, cnt, 8, window, 0.4)
+        assert np.abs(O - Od).max() < 1e-12 and np.array_equal(np.isneginf(LSE), np.isneginf(LSEd))
+        fin = np.isfinite(LSEd)
+        assert np.abs(LSE[fin] - LSEd[fin]).max() < 1e-12
+
+
+def test_sparse_verify_positions_independent_and_order_free():
+    g = np.random.default_rng(23)
+    q, kc, vc, table, lens = paged_case(B=1, Ls=(96,), Hq=4, Hkv=2, n_q=3, P=8)
+    sel, cnt = random_row_sel(g, [96], 2, 3, 8, 8, 3, 6, 2)
+    O1, L1 = oracle.sparse_verify(q, kc, vc, table, lens, sel, cnt, 8, 8, 0.4)
+    # another position's layout does not move this one's output
+    sel2, cnt2 = sel.copy(), cnt.copy()
+    sel2[0, :, 2] = -1
+    cnt2[0, :, 2] = 0
+    O2, L2 = oracle.sparse_verify(q, kc, vc, table, lens, sel2, cnt2, 8, 8, 0.4)
+    assert np.array_equal(O1[:, :2], O2[:, :2]) and np.array_equal(L1[:, :2], L2[:, :2])
+    assert not np.allclose(O1[:, 2], O2[:, 2])
+    # the order of a layout's entries is irrelevant
+    perm = sel.copy()
+    for i in range(3):
+        for h in range(2):
+            c = int(cnt[0, h, i])
+            perm[0, h, i, :c] = perm[0, h, i, :c][::-1]
+    O3, L3 = oracle.sparse_verify(q, kc, vc, table, lens, perm, cnt, 8, 8, 0.4)
+    assert np.array_equal(O1, O3) and np.array_equal(L1, L3)
+    # no selection and no window: empty sets apart from the causal window-free case
+    O4, L4 = oracle.sparse_verify(q, kc, vc, table, lens, sel, np.zeros_like(cnt), 8, 0, 0.4)
+    assert np.all(O4 == 0) and np.all(np.isneginf(L4))
+
+
+def test_layout_union_contains_exactly_the_selected_blocks():
+    g = np.random.default_rng(24)
+    for window in (0, 8, 40):
+        sel, cnt = random_row_sel(g, [96], 1, 4, 8, window, 3, 6, 2)
+        ws = 96 if window == 0 else 96 - window
+        u = oracle.layout_union(sel[0, 0], cnt[0, 0], 96, 8, window)
+        assert u == sorted(set(u))
+        picked = {int(j) for i in range(4) for j in sel[0, 0, i, :cnt[0, 0, i]] if j * 8 < ws}
+        assert set(u) == picked
+        # every query's token set lies inside the union's blocks plus the window
+        for i in range(4):
+            toks = oracle.sparse_verify_token_set(96, 4, i, sel[0, 0, i], cnt[0, 0, i], 8, window)
+            assert all(t >= ws or t // 8 in picked for t in toks)
+
+
+# --------------------------------------------------------------------------
 # merge
 # --------------------------------------------------------------------------
 def test_merge_partition_equals_unsplit():
@@ -550,6 +682,45 @@ def test_mutations_are_caught():
     bad = oracle.block_mass_unit(P, 40, 3, 2, 4, 0, 10)
     ref = softmax_block_scores(q, kc, vc, table, lens, 0.25, 4, 10, 0)[0, 0]
     assert np.abs(bad - ref).max() > 1e-3
+
+
+def test_sparse_verify_mutations_are_caught():
+    """Two plausible mistakes of a grouped execution fail the masked-SDPA pin:
+    every query attending to the whole union of the group's layouts, and
+    selected tokens escaping the causal limit when the window is shorter than
+    the step."""
+    g = np.random.default_rng(25)
+    q, kc, vc, table, lens = paged_case(B=1, Ls=(80,), Hq=4, Hkv=2, n_q=4, P=4)
+    sel, cnt = random_row_sel(g, [80], 2, 4, 8, 2, 2, 5, 1)
+    ref, _ = sdpa_sparse_verify(q, kc, vc, table, lens, sel, cnt, 8, 2, 0.4)
+
+    def mut_union(q_, kc_, vc_, table_, lens_, sel_, cnt_, bs, window, scale):
+        u = np.full(sel_.shape[:3] + (64,), -1, dtype=np.int32)
+        c = np.zeros_like(cnt_)
+        for h in range(sel_.shape[1]):
+            blocks = oracle.layout_union(sel_[0, h], cnt_[0, h], int(lens_[0]), bs, window)
+            u[0, h, :, :len(blocks)] = blocks
+            c[0, h, :] = len(blocks)
+        return oracle.sparse_verify(q_, kc_, vc_, table_, lens_, u, c, bs, window, scale)
+
+    def mut_causal(q_, kc_, vc_, table_, lens_, sel_, cnt_, bs, window, scale):
+        B, n_q, Hq, d = q_.shape
+        O = np.zeros((B, n_q, Hq, d))
+        G = Hq // kc_.shape[1]
+        L = int(lens_[0])
+        for hq in range(Hq):
+            K, V = oracle.gather_unit(kc_, vc_, table_[0], L, hq // G)
+            for i in range(n_q):
+                toks = oracle.draft_token_set(L, sel_[0, hq // G, i], int(cnt_[0, hq // G, i]),
+                                              bs, window)
+                S = scale * (q_[0, i, hq] @ K[toks].T)
+                S[np.asarray(toks) > L - 1] = -np.inf              # limit of the last row
+                lse, P = so._softmax_rows(S[None])
+                O[0, i, hq] = (P @ V[toks])[0]
+        return O, None
+
+    assert np.abs(mut_union(q, kc, vc, table, lens, sel, cnt, 8, 2, 0.4)[0] - ref).max() > 1e-3
+    assert np.abs(mut_causal(q, kc, vc, table, lens, sel, cnt, 8, 2, 0.4)[0] - ref).max() > 1e-3
 
 
 def test_kv_write_mutation_is_caught():
