@@ -184,6 +184,152 @@ def cpu_baseline(wl, n_req):
                        f"and draft, {elapsed:.1f} s wall on the host")}
 
 
+def sparse_bytes(wl):
+    """Sparse verification: K and V of the union of each unit's layouts (plus
+    the window) read once, queries, outputs, LSEs, layouts, page tables; and,
+    for comparison, the KV bytes if every query position loaded its own
+    blocks separately."""
+    s = wl.shape
+    vb = wl.verify
+    el = 2 if s.dtype == "bf16" else 4
+    lens = vb.seq_lens.cpu().numpy()
+    rs, rc = vb.row_sel.cpu().numpy(), vb.row_sel_count.cpu().numpy()
+    union_toks = per_pos_toks = 0
+    for b in range(vb.B):
+        L = int(lens[b])
+        ws = L if s.window <= 0 else max(0, L - s.window)
+        ncand = -(-ws // s.block_size)
+        for h in range(s.Hkv):
+            blocks = set()
+            for i in range(s.n_q):
+                c = max(0, min(int(rc[b, h, i]), rs.shape[3]))
+                mine = {int(j) for j in rs[b, h, i, :c] if 0 <= int(j) < ncand}
+                blocks |= mine
+                per_pos_toks += sum(min((j + 1) * s.block_size, ws) - j * s.block_size
+                                    for j in mine) + (L - ws)
+            union_toks += sum(min((j + 1) * s.block_size, ws) - j * s.block_size
+                              for j in blocks) + (L - ws)
+    kv = union_toks * s.d * el * 2
+    q_bytes = vb.B * s.n_q * s.Hq * s.d * el
+    total = (kv + 2 * q_bytes + vb.B * s.n_q * s.Hq * 4 + rs.size * 4 + rc.size * 4
+             + sum(-(-int(L) // s.page_size) for L in lens) * 4 + vb.B * 4)
+    return {"total": total, "kv": kv, "kv_per_position": per_pos_toks * s.d * el * 2}
+
+
+def run_sparse(args, wl, dev):
+    """One step = one sss_sparse_verify_attn call over the batch (every
+    position attends to its own layout; each unit's union is loaded once)."""
+    import numpy as np
+    import torch
+    import oracle
+    from sparse_self_speculative_sss_amd import sss
+    from sparse_self_speculative_sss_amd import workload as W
+    s = wl.shape
+    vb = wl.verify
+    B, n_q = vb.B, s.n_q
+    kv = sss.paged_kv(wl.k_cache, wl.v_cache, vb.page_table, vb.seq_lens, vb.max_seq_len)
+    o = torch.empty_like(vb.q)
+    lse = torch.empty((B, n_q, s.Hq), dtype=torch.float32, device=dev)
+    splits = max(0, args.verify_splits)
+    ws = sss.workspace(sss.sparse_verify_workspace_size(kv, B, n_q, s.Hq, s.block_size,
+                                                        vb.row_sel.shape[3], s.window, splits),
+                       dev)
+
+    def step():
+        sss.sparse_verify_attn(kv, vb.q, wl.sm_scale, s.block_size, vb.row_sel,
+                               vb.row_sel_count, s.window, o, lse, ws=ws, num_splits=splits)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nb = sparse_bytes(wl)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gbs = nb["total"] / (k_ms * 1e-3) / 1e9
+
+    # the same loads without grouping: one launch per query position, each
+    # holding only that position's layout (every KV block a position selects
+    # is loaded once per position; outputs go to scratch and are not used)
+    solo = []
+    for i in range(n_q):
+        rc_i = torch.zeros_like(vb.row_sel_count)
+        rc_i[:, :, i] = vb.row_sel_count[:, :, i]
+        solo.append(rc_i)
+    o_s, lse_s = torch.empty_like(o), torch.empty_like(lse)
+
+    def ungrouped():
+        for rc_i in solo:
+            sss.sparse_verify_attn(kv, vb.q, wl.sm_scale, s.block_size, vb.row_sel, rc_i,
+                                   s.window, o_s, lse_s, ws=ws, num_splits=splits)
+
+    for _ in range(2):
+        ungrouped()
+    eu = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    eu[0].record()
+    for _ in range(args.steps):
+        ungrouped()
+    eu[1].record()
+    torch.cuda.synchronize()
+    u_ms = eu[0].elapsed_time(eu[1]) / args.steps
+    rec = {
+        "metric": "sparse verify attn tokens/s and KV HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": round(B * n_q / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic (seeded; Qwen3-8B attention shape, per-position layouts sharing "
+                f"{int(round(100 * s.layout_shared))}% of their blocks)",
+        "config": {"workload": s.name, "batch": B, "context": int(vb.seq_lens.max()),
+                   "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.d, "k_plus_1": n_q,
+                   "block": s.block_size, "page": s.page_size, "window": s.window,
+                   "layout_blocks": int(vb.row_sel_count.max()),
+                   "layout_shared": s.layout_shared, "splits": splits},
+        "roofline": {
+            "kernel": "sss_sparse_verify_attn (attn_mfma_kernel<sparse verify>; split merge "
+                      "launch included when units are split)",
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes": nb["total"], "ms": round(k_ms, 4),
+        },
+        "grouping": {"kv_bytes_union": nb["kv"], "kv_bytes_per_position": nb["kv_per_position"],
+                     "ratio": round(nb["kv_per_position"] / max(1, nb["kv"]), 3),
+                     "grouped_ms": round(k_ms, 4),
+                     "one_launch_per_position_ms": round(u_ms, 4),
+                     "speedup": round(u_ms / k_ms, 3)},
+    }
+    if args.cpu_sample > 0:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        n = min(args.cpu_sample, B)
+        q = W.to_numpy64(vb.q[:n])
+        rs, rc = vb.row_sel.cpu().numpy(), vb.row_sel_count.cpu().numpy()
+        elapsed = 0.0
+        for b in range(n):
+            k, v, table, lens = _request_copy(wl, vb, b)
+            t0 = time.perf_counter()
+            oracle.sparse_verify(q[b:b + 1], k, v, table, lens, rs[b:b + 1], rc[b:b + 1],
+                                 s.block_size, s.window, wl.sm_scale)
+            elapsed += time.perf_counter() - t0
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        rec["cpu_baseline"] = {"value": n * n_q / elapsed, "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"{n} of {B} requests (all {s.Hkv} KV heads each): fp64 "
+                                         f"sparse verify, {elapsed:.1f} s wall on the host"}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
 def time_kv_update(wl, kv, vb, dev, steps):
     """sss_kv_write of the last n_q positions of every verify request (the
     values already there, so the cache is unchanged) and sss_kv_commit keeping
@@ -250,6 +396,9 @@ def main():
     print(f"[bench] generating {args.workload} seed={args.seed}", file=sys.stderr, flush=True)
     wl = W.make(args.workload, seed=args.seed, device=dev)
     s = wl.shape
+    if s.layout_shared is not None:
+        run_sparse(args, wl, dev)
+        return
     vb, db = wl.verify, wl.draft
     shared = s.p_verify is None      # draft reads the selection this step's verify made
     if args.path == "auto":

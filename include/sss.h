@@ -206,6 +206,59 @@ size_t sss_draft_workspace_size(const sss_paged_kv* kv, int32_t batch, int32_t n
                                 int32_t num_splits);
 
 /*
+ * Sparse verification with a layout per query position (SpecSA, 核心创新 /
+ * 重叠感知分组查询执行 and 技术细节与实现挑战 / 稀疏布局的动态管理: each query of
+ * a verify step has its own sparse layout, and queries whose layouts
+ * overlap run as one group that shares the KV blocks they have in common).
+ *
+ * Definition: for request b, KV head h and query position i in [0, n_q)
+ * (row r = i*G + g, position pos = L_b - n_q + i), the query heads of the
+ * group attend to
+ *     S_i = ({ t in block j : j in row_sel[b][h][i][0..row_sel_count[b][h][i]),
+ *              t < ws }  U  [ws, L_b))  restricted to t <= pos,
+ * with ws = max(0, L_b - window) (ws = L_b when window == 0):
+ *     lse[b][i][hq] = log sum_{t in S_i} exp(s_t),
+ *     o[b][i][hq]   = sum_{t in S_i} exp(s_t - lse) v_t.
+ * An empty S_i gives o = 0 and lse = -inf.  Layout entries that are
+ * negative or name a block at or past the window start add nothing;
+ * repeated entries and their order do not matter.
+ *
+ * Execution: each workgroup (one chunk of one request and KV head) builds the union of
+ * the n_q layouts in LDS, loads each block of the union once for all the
+ * unit's rows, and masks each row to its own position's blocks; a row wave
+ * whose positions hold none of a tile's blocks skips that tile.
+ *
+ * q, o     [batch][n_q][num_q_heads][head_dim] BF16, 16-byte aligned.
+ * lse      [batch][n_q][num_q_heads] float.
+ * row_sel  [batch][num_kv_heads][n_q][max_sel] int32 block indices.
+ * row_sel_count [batch][num_kv_heads][n_q] int32 (clamped to [0, max_sel]).
+ * num_splits  chunks the longest possible union list is cut into (0 =
+ *             chosen by the library).
+ * workspace   device scratch of at least sss_sparse_verify_workspace_size()
+ *             bytes, 256-byte aligned (0 bytes when nothing is split).
+ *
+ * Preconditions (host-checked): batch >= 0; 1 <= n_q <= 32;
+ * num_q_heads % num_kv_heads == 0; n_q * G <= 128; max_sel >= 1;
+ * window >= 0; num_splits >= 0; max_seq_len >= n_q; a BF16 cache with
+ * page_size and block_size multiples of 16 (else SSS_ERR_UNSUPPORTED);
+ * ceil(max_seq_len / block_size) * 12 bytes of LDS for the union beside the
+ * tiles.  Device-side: n_q <= seq_lens[b] <= max_seq_len (else that unit's
+ * outputs are NaN).  Caller owns every buffer; nothing is allocated.
+ */
+sss_status sss_sparse_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
+                                  int32_t n_q, int32_t num_q_heads, float sm_scale,
+                                  int32_t block_size, const int32_t* row_sel,
+                                  const int32_t* row_sel_count, int32_t max_sel, int32_t window,
+                                  int32_t num_splits, void* o, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sss_sparse_verify_attn needs (0 when nothing is split or
+ * on invalid arguments; call sss_last_error() to tell them apart). */
+size_t sss_sparse_verify_workspace_size(const sss_paged_kv* kv, int32_t batch, int32_t n_q,
+                                        int32_t num_q_heads, int32_t block_size, int32_t max_sel,
+                                        int32_t window, int32_t num_splits);
+
+/*
  * Log-sum-exp merge of attention partials over disjoint KV subsets (the
  * verification kernel keeps the log-sum-exp of the logits, SparseSpec §4.1,
  * which is what makes partial results combinable):

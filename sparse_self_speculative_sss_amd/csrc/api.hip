@@ -99,6 +99,7 @@ struct Plan {
   bool ell_in_lds = false;
   long long ell_lds_floats = 0;
   size_t ell_off, opart_off, lpart_off, bytes;
+  size_t list_off = 0;  // sparse verify: segment list length per unit
 };
 
 void layout(Plan& pl, long long units, int head_dim, long long ell_elems) {
@@ -230,6 +231,63 @@ sss_status plan_draft(const sss_paged_kv* kv, int batch, int hq, int block_size,
   pl.chunk = (int)chunk;
   pl.num_chunks = (int)((list_max + chunk - 1) / chunk);
   layout(pl, units, kv->head_dim, 0);
+  return ok();
+}
+
+// Sparse verify (a layout per query position): always the matrix-core path.
+// The list of a unit is the union of its positions' layouts (at most
+// min(max_blocks, n_q * max_sel) blocks) in 16-token segments, then the
+// window; its chunks are split like a draft list's.
+sss_status plan_sparse(const sss_paged_kv* kv, int batch, int n_q, int hq, int block_size,
+                       int max_sel, int window, int num_splits, Plan& pl) {
+  sss_status st = check_kv(kv, batch);
+  if (st != SSS_OK) return st;
+  if (batch < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "batch %d < 0", batch);
+  if (n_q < 1 || n_q > 32) return fail(SSS_ERR_INVALID_ARGUMENT, "n_q %d outside [1, 32]", n_q);
+  if (hq < 1 || hq % kv->num_kv_heads != 0)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                hq, kv->num_kv_heads);
+  const int G = hq / kv->num_kv_heads;
+  if ((long long)n_q * G > 128)
+    return fail(SSS_ERR_UNSUPPORTED, "n_q * G = %lld rows per KV head exceeds 128", (long long)n_q * G);
+  if (block_size < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "block_size %d < 1", block_size);
+  if (max_sel < 1) return fail(SSS_ERR_INVALID_ARGUMENT, "max_sel %d < 1", max_sel);
+  if (window < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "window %d < 0", window);
+  if (num_splits < 0) return fail(SSS_ERR_INVALID_ARGUMENT, "num_splits %d < 0", num_splits);
+  if (kv->max_seq_len < n_q)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "kv->max_seq_len %d < n_q %d", kv->max_seq_len, n_q);
+  if (kv->dtype != SSS_BF16 || kv->page_size % kSeg != 0 || block_size % kSeg != 0)
+    return fail(SSS_ERR_UNSUPPORTED,
+                "sparse verify needs a BF16 cache with page_size and block_size multiples of 16");
+  pl.mfma = true;
+  pl.rows = n_q * G;
+  const int nwr = ceil_div(pl.rows, 32);
+  const int nwt = mfma_token_groups(pl.rows, false);
+  const int max_blocks = ceil_div(kv->max_seq_len, block_size);
+  if (mfma_smem_bytes(kv->head_dim, nwr, nwt, 0) + sparse_union_lds_bytes(max_blocks) > kMaxLds)
+    return fail(SSS_ERR_UNSUPPORTED, "%d blocks per request leave no LDS room for the layout union",
+                max_blocks);
+  const long long units = (long long)batch * kv->num_kv_heads;
+  const long long Lmax = kv->max_seq_len;
+  const long long wtok = window > 0 ? (window < Lmax ? window : Lmax) : 0;
+  const long long umax = std::min<long long>(max_blocks, (long long)n_q * max_sel);
+  long long list_max = umax * (block_size / kSeg) + (wtok > 0 ? (wtok + kSeg - 1) / kSeg + 1 : 0);
+  if (list_max < 1) list_max = 1;
+  const long long align = 2LL * nwt;
+  long long S = num_splits;
+  if (S == 0) {
+    const long long wgs_target = kTargetWaves / ((long long)nwr * nwt);
+    S = units > 0 ? (wgs_target + units - 1) / units : 1;
+  }
+  if (S < 1) S = 1;
+  long long chunk = (list_max + S - 1) / S;
+  chunk = (chunk + align - 1) / align * align;
+  if (chunk > (1LL << 30)) return fail(SSS_ERR_UNSUPPORTED, "chunk too large");
+  pl.chunk = (int)chunk;
+  pl.num_chunks = (int)((list_max + chunk - 1) / chunk);
+  layout(pl, units, kv->head_dim, 0);
+  pl.list_off = pl.bytes;
+  if (pl.num_chunks > 1) pl.bytes += align_up((size_t)units * 4, 256);
   return ok();
 }
 
@@ -654,6 +712,89 @@ sss_status sss_draft_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
     e = launch_finalize(f, s);
     if (e != hipSuccess) return fail(SSS_ERR_HIP, "draft finalize launch: %s", hipGetErrorString(e));
   }
+  return ok();
+}
+
+size_t sss_sparse_verify_workspace_size(const sss_paged_kv* kv, int32_t batch, int32_t n_q,
+                                        int32_t num_q_heads, int32_t block_size, int32_t max_sel,
+                                        int32_t window, int32_t num_splits) {
+  Plan pl;
+  if (plan_sparse(kv, batch, n_q, num_q_heads, block_size, max_sel, window, num_splits, pl) !=
+      SSS_OK)
+    return 0;
+  return pl.bytes;
+}
+
+sss_status sss_sparse_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
+                                  int32_t n_q, int32_t num_q_heads, float sm_scale,
+                                  int32_t block_size, const int32_t* row_sel,
+                                  const int32_t* row_sel_count, int32_t max_sel, int32_t window,
+                                  int32_t num_splits, void* o, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Plan pl;
+  sss_status st =
+      plan_sparse(kv, batch, n_q, num_q_heads, block_size, max_sel, window, num_splits, pl);
+  if (st != SSS_OK) return st;
+  if (!std::isfinite(sm_scale)) return fail(SSS_ERR_INVALID_ARGUMENT, "sm_scale is not finite");
+  if (batch == 0) return ok();
+  if (!q || !o || !lse || !row_sel || !row_sel_count)
+    return fail(SSS_ERR_INVALID_ARGUMENT, "q, o, lse, row_sel and row_sel_count must be non-NULL");
+  if (!aligned(q, 16) || !aligned(o, 16))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "q and o must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(row_sel, 4) || !aligned(row_sel_count, 4))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "lse, row_sel and row_sel_count must be 4-byte aligned");
+  if (workspace_bytes < pl.bytes)
+    return fail(SSS_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace_bytes,
+                pl.bytes);
+  if (pl.bytes > 0 && (!workspace || !aligned(workspace, 256)))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  AttnParams p = base_params(kv, q, batch, n_q, num_q_heads, sm_scale, pl);
+  p.chunk_tokens = 0;
+  p.chunk_items = pl.chunk;
+  p.o_part = reinterpret_cast<float*>(ws + pl.opart_off);
+  p.lse_part = reinterpret_cast<float*>(ws + pl.lpart_off);
+  p.o = o;
+  p.lse = lse;
+  p.block_size = block_size;
+  p.max_blocks = ceil_div(kv->max_seq_len, block_size);
+  p.sel = row_sel;
+  p.sel_count = row_sel_count;
+  p.max_sel = max_sel;
+  p.window = window;
+  p.list_len = pl.num_chunks > 1 ? reinterpret_cast<int32_t*>(ws + pl.list_off) : nullptr;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_sparse_verify_mfma(p, s);
+  if (e != hipSuccess) return fail(SSS_ERR_HIP, "sparse verify launch: %s", hipGetErrorString(e));
+  if (pl.num_chunks == 1) return ok();
+  FinalizeParams f = {};
+  f.batch = batch;
+  f.num_kv_heads = kv->num_kv_heads;
+  f.n_q = n_q;
+  f.group = p.group;
+  f.rows = pl.rows;
+  f.head_dim = kv->head_dim;
+  f.num_chunks = pl.num_chunks;
+  f.chunk_items = pl.chunk;
+  f.dtype = kv->dtype;
+  f.seq_lens = kv->seq_lens;
+  f.max_seq_len = kv->max_seq_len;
+  f.max_pages = kv->max_pages_per_req;
+  f.page_size = kv->page_size;
+  f.o_part = p.o_part;
+  f.lse_part = p.lse_part;
+  f.o = o;
+  f.lse = lse;
+  f.ell = nullptr;
+  f.block_size = block_size;
+  f.max_blocks = p.max_blocks;
+  f.single_done = 1;
+  f.skip_len = -1;
+  f.list_len = p.list_len;
+  e = launch_finalize(f, s);
+  if (e != hipSuccess)
+    return fail(SSS_ERR_HIP, "sparse verify finalize launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -29,6 +29,7 @@
 #pragma once
 
 #include "sss_common.h"
+#include "topk_dev.h"
 
 namespace sss {
 
@@ -96,6 +97,7 @@ __device__ __forceinline__ void group_sync() {
 struct Seg {
   long long base;  // element offset of token t0 of this (page, head) run
   int t0, lo, hi;  // 16-aligned start; valid tokens are [lo, hi)
+  uint32_t pm;     // sparse verify: query positions whose layout holds it
 };
 
 // Descriptor of one 16-token segment, held by one lane: 64 consecutive
@@ -104,22 +106,27 @@ struct Seg {
 // batch ahead instead of once per tile.
 struct SegLane {
   int t0;
-  int lohi;  // (lo - t0) | ((hi - t0) << 8)
-  int pg;    // page id (0 for an empty segment)
+  int lohi;     // (lo - t0) | ((hi - t0) << 8)
+  int pg;       // page id (0 for an empty segment)
+  uint32_t pm;  // sparse verify: query positions whose layout holds it
 };
 
 // Segment k of a verify unit (16 tokens starting at 16k), or entry k of a
-// draft unit's list: first the segments of the selected blocks (only their
-// tokens before the window start), then the window.
+// list (LIST: a draft unit's selection, or the union of a sparse verify
+// unit's layouts held in LDS with the query positions of each block in
+// pm_s): first the segments of the listed blocks (only their tokens before
+// the window start), then the window, which every position sees.
 // The page id is loaded for every lane (the table index is clamped into the
 // request's row) and only checked when a tile reads the descriptor, so the
 // load is never waited for here.
-template <bool DRAFT>
+template <bool LIST>
 __device__ __forceinline__ SegLane seg_lane(const AttnParams& p, const int32_t* sel_s, int b,
-                                            int h, int k, int k_end, int nsel, int L, int ws) {
+                                            int h, int k, int k_end, int nsel, int L, int ws,
+                                            const uint32_t* pm_s = nullptr) {
   int t0 = 0, lo = 0, hi = 0;
+  uint32_t pm = 0xffffffffu;
   if (k < k_end) {
-    if (!DRAFT) {
+    if (!LIST) {
       t0 = k * kSeg;
       lo = t0;
       hi = min(t0 + kSeg, L);
@@ -128,6 +135,7 @@ __device__ __forceinline__ SegLane seg_lane(const AttnParams& p, const int32_t* 
       if (k < nsel * spb) {
         const int j = sel_s ? sel_s[k / spb]
                             : p.sel[((long long)b * p.num_kv_heads + h) * p.max_sel + k / spb];
+        if (pm_s) pm = pm_s[k / spb];
         if (j >= 0 && j < ceil_div(ws, p.block_size)) {
           t0 = j * p.block_size + kSeg * (k % spb);
           lo = t0;
@@ -144,15 +152,24 @@ __device__ __forceinline__ SegLane seg_lane(const AttnParams& p, const int32_t* 
   d.t0 = t0;
   d.lohi = lo < hi ? ((lo - t0) | ((hi - t0) << 8)) : 0;
   d.pg = p.page_table[(long long)b * p.max_pages + min(t0 / p.page_size, p.max_pages - 1)];
+  d.pm = pm;
   return d;
 }
 
 // Descriptor idx of the current (or next) batch as uniform values.  An
 // empty segment reads page 0; a page id outside [0, num_pages) also reads
-// page 0 and sets `bad` (the unit's outputs become NaN).
+// page 0 and sets `bad` (the unit's outputs become NaN).  PM: also read
+// the position mask.
+template <bool PM = false>
 __device__ __forceinline__ Seg seg_of(const AttnParams& p, int h, const SegLane& cur,
                                       const SegLane& nxt, bool use_nxt, int idx, int& bad) {
   Seg s;
+  s.pm = 0xffffffffu;
+  if (PM) {
+    const uint32_t pmc = __builtin_amdgcn_readlane(cur.pm, idx);
+    const uint32_t pmn = __builtin_amdgcn_readlane(nxt.pm, idx);
+    s.pm = use_nxt ? pmn : pmc;
+  }
   const int t0c = __builtin_amdgcn_readlane(cur.t0, idx);
   const int t0n = __builtin_amdgcn_readlane(nxt.t0, idx);
   const int lhc = __builtin_amdgcn_readlane(cur.lohi, idx);
@@ -292,6 +309,54 @@ __device__ __forceinline__ void store_tile(TileRegs<D, NWR>& r, char* grp, int l
   }
 }
 
+// ---- sparse verify: the union of a unit's per-position layouts ----
+
+// Builds, in LDS at `area`, the union of the layouts of unit (b, h): the
+// blocks before the window start that at least one query position selects,
+// ascending, each with the mask of the positions selecting it.  Layout:
+// pm[ncand] (a mask per candidate block), then blk[ncand], msk[ncand] (the
+// union, compacted).  `scratch` holds NT / 64 ints.  Returns the union's
+// size; all NT threads call it, and it ends with a barrier.
+template <int NT>
+__device__ int layout_union(const AttnParams& p, int b, int h, int ws, char* area, int* scratch) {
+  const int ncand = min(ceil_div(ws, p.block_size), p.max_blocks);
+  uint32_t* pm = reinterpret_cast<uint32_t*>(area);
+  int32_t* blk = reinterpret_cast<int32_t*>(pm + ncand);
+  uint32_t* msk = reinterpret_cast<uint32_t*>(blk + ncand);
+  const int tid = threadIdx.x;
+  for (int j = tid; j < ncand; j += NT) pm[j] = 0u;
+  __syncthreads();
+  const long long unit = (long long)b * p.num_kv_heads + h;
+  const int32_t* rs = p.sel + unit * p.n_q * p.max_sel;  // [n_q][max_sel]
+  const int32_t* rc = p.sel_count + unit * p.n_q;        // [n_q]
+  for (int e = tid; e < p.n_q * p.max_sel; e += NT) {
+    const int i = e / p.max_sel, k = e - i * p.max_sel;
+    const int cnt = rc[i];
+    if (k < cnt) {
+      const int j = rs[e];
+      if (j >= 0 && j < ncand) atomicOr(&pm[j], 1u << i);
+    }
+  }
+  __syncthreads();
+  // compaction in block order: thread t owns a contiguous range of blocks
+  const int per = (ncand + NT - 1) / NT;
+  const int j0 = min(tid * per, ncand), j1 = min(j0 + per, ncand);
+  int mine = 0;
+  for (int j = j0; j < j1; ++j) mine += pm[j] != 0u;
+  int total;
+  int pos = wg_exclusive_sum<NT>(mine, scratch, total);
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t m = pm[j];
+    if (m != 0u) {
+      blk[pos] = j;
+      msk[pos] = m;
+      ++pos;
+    }
+  }
+  __syncthreads();
+  return total;
+}
+
 // ---- single-token draft lists (block size 1): a tile is 32 arbitrary
 // tokens, each a row (page, head, slot) of the cache, read from a list
 // staged in LDS for the whole chunk ----
@@ -400,9 +465,13 @@ constexpr float kRescaleSlack = 8.f;
 // TOKENS: blocks of one token.  A draft then gathers its tiles token by
 // token from a list (one row tile only); a verify stores each token's logit
 // as its log mass.
-template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS = false>
+template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS = false,
+          bool SPARSE = false>
 __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
+  static_assert(!SPARSE || (!DRAFT && !ELL_LDS && !TOKENS), "sparse verify is its own mode");
   constexpr bool GATHER = DRAFT && TOKENS;
+  constexpr bool LIST = DRAFT || SPARSE;     // segments come from a block list
+  constexpr bool SCORES = !DRAFT && !SPARSE;  // block importance is computed
   static_assert(!GATHER || NWR == 1, "token lists serve one-row-tile drafts");
   constexpr int PD = NWR >= 2 ? 2 : 1;
   constexpr int NT = 64 * NWR * NWT;
@@ -436,7 +505,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       for (int d = hl; d < D; d += 2) o[orow * D + d] = from_f32<bf16>(qnan());
       if (hl == 0) p.lse[orow] = qnan();
     }
-    if (!DRAFT)
+    if (SCORES)
       for (int j = threadIdx.x; j < p.max_blocks; j += NT)
         p.block_scores[(long long)u * p.max_blocks + j] = qnan();
     return kItemFinal;
@@ -444,7 +513,11 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
 
   // ---- this item's segment range, split among token groups ----
   int seg_lo, seg_hi, nsel = 0, ws = L, nseg = 0;
-  if (!DRAFT) {
+  // sparse verify: the union of the unit's layouts in LDS at it.list_off,
+  // ascending block ids with the query positions holding each
+  const int32_t* ublk = nullptr;
+  const uint32_t* umsk = nullptr;
+  if (!LIST) {
     const int t_lo = c * it.chunk;
     if (t_lo >= L) return kItemNone;  // chunk past this request's length
     const int t_hi = min(t_lo + it.chunk, L);
@@ -452,26 +525,37 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
     seg_hi = ceil_div(t_hi, kSeg);
   } else {
     ws = window_start(L, p.window);
-    nsel = it.sel_off >= 0 ? it.nsel_s : p.sel_count[(long long)b * p.num_kv_heads + h];
-    nsel = nsel < 0 ? 0 : (nsel > p.max_sel ? p.max_sel : nsel);
+    if constexpr (SPARSE) {
+      nsel = layout_union<NT>(p, b, h, ws, smem + it.list_off, reinterpret_cast<int*>(smem));
+      const int ncand = min(ceil_div(ws, p.block_size), p.max_blocks);
+      ublk = reinterpret_cast<const int32_t*>(smem + it.list_off) + ncand;
+      umsk = reinterpret_cast<const uint32_t*>(ublk + ncand);
+    } else {
+      nsel = it.sel_off >= 0 ? it.nsel_s : p.sel_count[(long long)b * p.num_kv_heads + h];
+      nsel = nsel < 0 ? 0 : (nsel > p.max_sel ? p.max_sel : nsel);
+    }
     nseg = GATHER ? draft_list_len_simple(nsel, 1, L, ws)
                   : draft_list_len_mfma(nsel, p.block_size, L, ws);
     seg_lo = c * it.chunk;
+    // the merge learns a sparse unit's list length from its chunk 0
+    if (SPARSE && c == 0 && threadIdx.x == 0 && p.list_len) p.list_len[u] = nseg;
     if (seg_lo >= nseg && c > 0) return kItemNone;
     seg_hi = min(seg_lo + it.chunk, nseg);
   }
   // a unit that fits in its first chunk is finished here (outputs, scores)
   const bool final_out =
-      it.single || (DRAFT ? (c == 0 && nseg <= it.chunk) : (c == 0 && L <= it.chunk));
-  constexpr bool ell_lds = !DRAFT && ELL_LDS;
+      it.single || (LIST ? (c == 0 && nseg <= it.chunk) : (c == 0 && L <= it.chunk));
+  constexpr bool ell_lds = SCORES && ELL_LDS;
   // first block of the chunk (chunks hold whole blocks); the LDS copy of the
   // block log masses holds the chunk's blocks only and is addressed by
   // absolute block index through an offset base
-  const int blk0 = DRAFT ? 0 : c * (it.chunk / p.block_size);
+  const int blk0 = LIST ? 0 : c * (it.chunk / p.block_size);
   float* const ell_s = reinterpret_cast<float*>(smem + it.ell_off) - (ptrdiff_t)blk0 * p.rows;
   const int32_t* const sel_s =
-      (DRAFT && it.sel_off >= 0) ? reinterpret_cast<const int32_t*>(smem + it.sel_off) : nullptr;
-  const int per_group = (DRAFT ? it.chunk : it.chunk / kSeg) / NWT;
+      SPARSE ? ublk
+             : ((DRAFT && it.sel_off >= 0) ? reinterpret_cast<const int32_t*>(smem + it.sel_off)
+                                           : nullptr);
+  const int per_group = (LIST ? it.chunk : it.chunk / kSeg) / NWT;
   const int g_lo = min(seg_lo + tg * per_group, seg_hi);
   const int g_hi = min(g_lo + per_group, seg_hi);
   // list entries per tile: two 16-token segments, or 32 single tokens
@@ -488,8 +572,8 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   // segment descriptors of the first two batches of 64
   SegLane cur = {}, nxt = {};
   if constexpr (!GATHER) {
-    cur = seg_lane<DRAFT>(p, sel_s, b, h, g_lo + lane, g_hi, nsel, L, ws);
-    nxt = seg_lane<DRAFT>(p, sel_s, b, h, g_lo + 64 + lane, g_hi, nsel, L, ws);
+    cur = seg_lane<LIST>(p, sel_s, b, h, g_lo + lane, g_hi, nsel, L, ws, umsk);
+    nxt = seg_lane<LIST>(p, sel_s, b, h, g_lo + 64 + lane, g_hi, nsel, L, ws, umsk);
   }
   int cur_batch = 0;
   // gathered tiles: list entry of the token group's first token, relative
@@ -544,6 +628,11 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   __syncthreads();
   const int pos_r = DRAFT ? (L - 1) : (L - p.n_q + iq);
   const int pos_min = DRAFT ? (L - 1) : (L - p.n_q);  // smallest causal limit of the unit's rows
+  // sparse verify: every query position of the unit, and those of this row
+  // wave's rows
+  const uint32_t all_pos = (uint32_t)((2ull << (p.n_q - 1)) - 1ull);
+  const uint32_t wave_pos =
+      (uint32_t)((2ull << ((min(rt * 32 + 32, R) - 1) / p.group)) - (1ull << ((rt * 32) / p.group)));
 
   f32x16 oacc[G::MT];
 #pragma unroll
@@ -572,8 +661,8 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       vm[q] = gather_mask(rows_s, g_rel + 32 * q, g_len - 32 * q);
       load_tile_gather<D, NWR>(regs[q], kc, vc, rows_s, g_rel + 32 * q, vm[q], lig);
     } else {
-      sa[q] = seg_of(p, h, cur, nxt, false, 2 * q, bad);
-      sb[q] = seg_of(p, h, cur, nxt, false, 2 * q + 1, bad);
+      sa[q] = seg_of<SPARSE>(p, h, cur, nxt, false, 2 * q, bad);
+      sb[q] = seg_of<SPARSE>(p, h, cur, nxt, false, 2 * q + 1, bad);
       load_tile<D, NWR>(regs[q], kc, vc, sa[q], sb[q], lig);
     }
   }
@@ -599,10 +688,11 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       // move to the next batch of descriptors; fetch the one after it
       cur = nxt;
       ++cur_batch;
-      nxt = seg_lane<DRAFT>(p, sel_s, b, h, g_lo + 64 * (cur_batch + 1) + lane, g_hi, nsel, L, ws);
+      nxt = seg_lane<LIST>(p, sel_s, b, h, g_lo + 64 * (cur_batch + 1) + lane, g_hi, nsel, L, ws,
+                           umsk);
     }
     group_sync<NWR>();
-    if (!DRAFT && !ell_lds) {
+    if (SCORES && !ell_lds) {
       if (ell_at >= 0) ell_u[ell_at] = ell_val;
       ell_at = -1;
       __builtin_amdgcn_sched_barrier(0);
@@ -614,12 +704,15 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
         load_tile_gather<D, NWR>(regs[q], kc, vc, rows_s, g_rel + rn, vm[q], lig);
       } else {
         const int ra = rel0 + 2 * PD, rb = ra + 1;
-        sa[q] = seg_of(p, h, cur, nxt, (ra >> 6) != cur_batch, ra & 63, bad);
-        sb[q] = seg_of(p, h, cur, nxt, (rb >> 6) != cur_batch, rb & 63, bad);
+        sa[q] = seg_of<SPARSE>(p, h, cur, nxt, (ra >> 6) != cur_batch, ra & 63, bad);
+        sb[q] = seg_of<SPARSE>(p, h, cur, nxt, (rb >> 6) != cur_batch, rb & 63, bad);
         load_tile<D, NWR>(regs[q], kc, vc, sa[q], sb[q], lig);
       }
     }
-    if (tile_live) {
+    // sparse verify: a row wave skips a tile that none of its query
+    // positions selected (the window segments count for every position)
+    const bool wave_live = tile_live && (!SPARSE || ((ca.pm | cb.pm) & wave_pos) != 0u);
+    if (wave_live) {
       // S^T = K Q^T
       f32x16 sacc;
 #pragma unroll
@@ -635,7 +728,8 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       // online softmax (log2 domain); interior tiles need no mask
       float s[16];
       float mx = neg_inf();
-      const bool interior = full && (GATHER || cb.t0 + kSeg - 1 <= pos_min);
+      const bool interior = full && (GATHER || cb.t0 + kSeg - 1 <= pos_min) &&
+                            (!SPARSE || (ca.pm & cb.pm & all_pos) == all_pos);
       if (interior) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -656,7 +750,8 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
           const int m = (i >> 2) * 8 + 4 * hl + (i & 3);
           const Seg& sg = (m < kSeg) ? ca : cb;
           const int tok = sg.t0 + (m % kSeg);
-          const bool ok = tok >= sg.lo && tok < sg.hi && tok <= pos_r;
+          bool ok = tok >= sg.lo && tok < sg.hi && tok <= pos_r;
+          if (SPARSE) ok = ok && ((sg.pm >> iq) & 1u);
           s[i] = ok ? sacc[i] * p.scale_log2 : neg_inf();
           mx = fmaxf(mx, s[i]);
         }
@@ -712,7 +807,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
           oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[mt], 0, 0, 0);
         }
       }
-      if (!DRAFT) {
+      if (SCORES) {
         // per-block log mass of this row, frame m_use
         const int bs = p.block_size;
         if (TOKENS) {
@@ -780,12 +875,12 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
     group_sync<NWR>();
   }
 
-  if (!DRAFT && ell_at >= 0) ell_u[ell_at] = ell_val;
+  if (SCORES && ell_at >= 0) ell_u[ell_at] = ell_val;
 
   // ---- combine the lane pair, then the token groups ----
   l_run += __shfl_xor(l_run, 32);
   bad = __syncthreads_or(bad);
-  if (!DRAFT && ell_lds && !final_out) {
+  if (SCORES && ell_lds && !final_out) {
     // the chunk's block log masses -> workspace, for the split merge
     const int blk_end = ceil_div(min((c + 1) * it.chunk, L), p.block_size);
     for (int i = blk0 * R + threadIdx.x; i < blk_end * R; i += NT) ell_u[i] = ell_s[i];
@@ -860,7 +955,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
         }
       if (hl == 0) {
         p.lse[orow] = lse2 * kLn2;
-        if (!DRAFT) lse2s[r] = lse2;
+        if (SCORES) lse2s[r] = lse2;
       }
     } else {
       const long long prow = it.part_row0 + (long long)c * R + r;
@@ -878,7 +973,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
     }
   }
 
-  if (!DRAFT && final_out) {
+  if (SCORES && final_out) {
     // the whole unit ran in this item: block scores from its block log
     // masses (LDS, or read back from L2) and the final row LSEs
     __threadfence_block();

@@ -6,7 +6,7 @@
 namespace sss {
 namespace {
 
-template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS>
+template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS, bool SPARSE = false>
 __global__ void __launch_bounds__(64 * NWR * NWT, 2) attn_mfma_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   if (p.skip_len >= 0 && p.seq_lens[(blockIdx.x / p.num_chunks) / p.num_kv_heads] <= p.skip_len)
@@ -14,17 +14,18 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2) attn_mfma_kernel(AttnParams
   Item it;
   it.u = blockIdx.x / p.num_chunks;
   it.c = blockIdx.x % p.num_chunks;
-  it.chunk = DRAFT ? p.chunk_items : p.chunk_tokens;
+  it.chunk = (DRAFT || SPARSE) ? p.chunk_items : p.chunk_tokens;
   it.single = p.num_chunks == 1;
   it.part_row0 = (long long)it.u * p.num_chunks * p.rows;
   // block log masses of the chunk in LDS, after the routine's own area
   it.ell_off = (int)item_lds_bytes(D, NWR, NWT);
   it.sel_off = -1;
   it.nsel_s = 0;
-  // after the tiles: a single-token draft's token list, or the logit
-  // staging slots of a single-token verify with several row tiles
+  // after the tiles: a single-token draft's token list, the logit staging
+  // slots of a single-token verify with several row tiles, or the union of
+  // a sparse verify unit's layouts
   it.list_off = (int)item_lds_bytes(D, NWR, NWT);
-  attn_item<D, NWR, NWT, DRAFT, ELL_LDS, TOKENS>(p, it, smem);
+  attn_item<D, NWR, NWT, DRAFT, ELL_LDS, TOKENS, SPARSE>(p, it, smem);
 }
 
 }  // namespace
@@ -37,9 +38,9 @@ size_t mfma_smem_bytes(int D, int nwr, int nwt, long long ell_floats) {
 
 namespace {
 
-template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS>
+template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS, bool SPARSE = false>
 hipError_t launch_one(const AttnParams& p, size_t smem, unsigned grid, hipStream_t s) {
-  auto kern = attn_mfma_kernel<D, NWR, NWT, DRAFT, ELL_LDS, TOKENS>;
+  auto kern = attn_mfma_kernel<D, NWR, NWT, DRAFT, ELL_LDS, TOKENS, SPARSE>;
   // dynamic LDS above 64 KiB must be opted into; allow the whole LDS once
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -121,6 +122,41 @@ int mfma_token_groups(int rows, bool draft) {
 }
 
 hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s) { return dispatch<false>(p, s); }
+
+// Sparse verify: the union of a unit's layouts (a mask per candidate block,
+// then the compacted block ids and masks) follows the tiles in LDS.
+size_t sparse_union_lds_bytes(int max_blocks) { return (size_t)max_blocks * 12; }
+
+namespace {
+template <int D, int NWR, int NWT>
+hipError_t launch_sparse_cfg(const AttnParams& p, hipStream_t s) {
+  const unsigned grid = (unsigned)((long long)p.batch * p.num_kv_heads * p.num_chunks);
+  if (grid == 0) return hipSuccess;
+  const size_t smem = mfma_smem_bytes(D, NWR, NWT, 0) + sparse_union_lds_bytes(p.max_blocks);
+  if (smem > kMaxLds) return hipErrorInvalidValue;
+  return launch_one<D, NWR, NWT, false, false, false, true>(p, smem, grid, s);
+}
+}  // namespace
+
+hipError_t launch_sparse_verify_mfma(const AttnParams& p, hipStream_t s) {
+  const int nwr = ceil_div(p.rows, 32);
+  if (p.head_dim == 128) {
+    switch (nwr) {
+      case 1: return launch_sparse_cfg<128, 1, 4>(p, s);
+      case 2: return launch_sparse_cfg<128, 2, 2>(p, s);
+      case 3: return launch_sparse_cfg<128, 3, 1>(p, s);
+      case 4: return launch_sparse_cfg<128, 4, 1>(p, s);
+    }
+  } else if (p.head_dim == 64) {
+    switch (nwr) {
+      case 1: return launch_sparse_cfg<64, 1, 4>(p, s);
+      case 2: return launch_sparse_cfg<64, 2, 2>(p, s);
+      case 3: return launch_sparse_cfg<64, 3, 1>(p, s);
+      case 4: return launch_sparse_cfg<64, 4, 1>(p, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
 hipError_t launch_draft_mfma(const AttnParams& p, hipStream_t s) { return dispatch<true>(p, s); }
 
 }  // namespace sss

@@ -66,7 +66,10 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinalizeParams p)
 
   if (p.num_chunks > 1) {
     int S;
-    if (!p.draft) {
+    if (p.list_len) {
+      const int n = p.list_len[u];
+      S = n > 0 ? ceil_div(n, p.chunk_items) : 1;
+    } else if (!p.draft) {
       S = ceil_div(L, p.chunk_tokens);
     } else {
       const int ws = window_start(L, p.window);

@@ -83,6 +83,10 @@ struct AttnParams {
   // >= 0: units whose request length is <= skip_len were finished by the
   // fused step kernel and are skipped; -1: none
   int32_t skip_len;
+  // sparse verify: sel / sel_count hold a layout per query position,
+  // [U][n_q][max_sel] / [U][n_q]; chunk 0 of each unit writes the length of
+  // its segment list here (for the split merge)
+  int32_t* list_len;
 };
 
 // Finalize a verify or draft launch: merge split partials (if any) and, for
@@ -107,6 +111,7 @@ struct FinalizeParams {
   int32_t simple_list;  // draft list enumerated token by token (vector-ALU path)
   int32_t single_done;  // units that fit in one chunk were finished by the attention kernel
   int32_t skip_len;     // as in AttnParams
+  const int32_t* list_len;  // sparse verify: segment list length per unit
 };
 
 // Fused step (fused.hip): work-list shape and in-kernel selection state.  The
@@ -171,6 +176,10 @@ hipError_t launch_fused(const FusedParams& f, const AttnParams& pv, const AttnPa
 // One workgroup per split verify unit: merge, scores and selection.
 hipError_t launch_fused_finish(const FusedParams& f, const AttnParams& pv, hipStream_t s);
 hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s);
+// Sparse verify (a layout per query position): LDS bytes beyond the tiles,
+// and the launch.
+size_t sparse_union_lds_bytes(int max_blocks);
+hipError_t launch_sparse_verify_mfma(const AttnParams& p, hipStream_t s);
 hipError_t launch_draft_mfma(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_simple(const AttnParams& p, int dtype, bool draft, hipStream_t s);
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t s);

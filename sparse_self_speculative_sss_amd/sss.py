@@ -52,6 +52,13 @@ _lib.sss_draft_attn.argtypes = [ctypes.POINTER(PagedKV), _vp, _c_int, _c_int, ct
 _lib.sss_draft_workspace_size.restype = ctypes.c_size_t
 _lib.sss_draft_workspace_size.argtypes = [ctypes.POINTER(PagedKV), _c_int, _c_int, _c_int, _c_int,
                                           _c_int, _c_int]
+_lib.sss_sparse_verify_attn.restype = _c_int
+_lib.sss_sparse_verify_attn.argtypes = [ctypes.POINTER(PagedKV), _vp, _c_int, _c_int, _c_int,
+                                        ctypes.c_float, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
+                                        _vp, _fp, _vp, ctypes.c_size_t, _vp]
+_lib.sss_sparse_verify_workspace_size.restype = ctypes.c_size_t
+_lib.sss_sparse_verify_workspace_size.argtypes = [ctypes.POINTER(PagedKV), _c_int, _c_int, _c_int,
+                                                  _c_int, _c_int, _c_int, _c_int]
 _lib.sss_merge.restype = _c_int
 _lib.sss_merge.argtypes = [_fp, _fp, _c_int, _c_int, _c_int, _vp, _c_int, _fp, _vp]
 
@@ -94,7 +101,9 @@ _lib.sss_version.argtypes = []
 
 EXPORTED = ["sss_verify_attn", "sss_verify_workspace_size", "sss_block_topk", "sss_draft_attn",
             "sss_draft_workspace_size", "sss_merge", "sss_fused_step", "sss_fused_workspace_size",
-            "sss_kv_write", "sss_kv_commit", "sss_status_string", "sss_last_error", "sss_version"]
+            "sss_kv_write", "sss_kv_commit", "sss_sparse_verify_attn",
+            "sss_sparse_verify_workspace_size", "sss_status_string", "sss_last_error",
+            "sss_version"]
 
 
 class SSSError(RuntimeError):
@@ -152,6 +161,15 @@ def draft_workspace_size(kv: PagedKV, batch, num_q_heads, block_size, max_sel, w
     return n
 
 
+def sparse_verify_workspace_size(kv: PagedKV, batch, n_q, num_q_heads, block_size, max_sel,
+                                 window, num_splits=0) -> int:
+    n = _lib.sss_sparse_verify_workspace_size(ctypes.byref(kv), batch, n_q, num_q_heads,
+                                              block_size, max_sel, window, num_splits)
+    if n == 0 and _lib.sss_last_error():
+        raise SSSError(SSS_ERR_INVALID_ARGUMENT, "sss_sparse_verify_workspace_size")
+    return n
+
+
 def workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
@@ -169,6 +187,23 @@ def verify_attn(kv: PagedKV, q, sm_scale, block_size, max_blocks, o, lse, block_
                                 _ptr(block_scores), max_blocks, _ptr(ws), ws.numel(), _stream()),
            "sss_verify_attn")
     return o, lse, block_scores
+
+
+def sparse_verify_attn(kv: PagedKV, q, sm_scale, block_size, row_sel, row_sel_count, window, o,
+                       lse, ws=None, num_splits=0):
+    """sss_sparse_verify_attn: q/o [B][n_q][Hq][d], lse [B][n_q][Hq],
+    row_sel [B][Hkv][n_q][max_sel], row_sel_count [B][Hkv][n_q]."""
+    B, n_q, hq, _ = q.shape
+    max_sel = row_sel.shape[3]
+    if ws is None:
+        ws = workspace(sparse_verify_workspace_size(kv, B, n_q, hq, block_size, max_sel, window,
+                                                    num_splits), q.device)
+    _check(_lib.sss_sparse_verify_attn(ctypes.byref(kv), _ptr(q), B, n_q, hq, float(sm_scale),
+                                       block_size, _ptr(row_sel), _ptr(row_sel_count), max_sel,
+                                       window, num_splits, _ptr(o), _ptr(lse), _ptr(ws),
+                                       ws.numel(), _stream()),
+           "sss_sparse_verify_attn")
+    return o, lse
 
 
 def block_topk(block_scores, seq_lens, block_size, budget, window, sel, sel_count):

@@ -25,7 +25,13 @@ order below is fixed):
    again); positions are distinct draws below the window start, or whole
    blocks in contiguous clusters;
 5. for mixed-batch draft requests, a random sorted set of distinct candidate
-   blocks of the requested budget.
+   blocks of the requested budget;
+6. for sparse verification (``layout_shared`` set), a layout per (verify
+   request, KV head, query position): N = the block budget, of which
+   round(layout_shared * N) blocks are common to every position of the unit
+   (blocks holding planted keys first, in random order, then other random
+   candidates) and the rest are drawn per position; entries shuffled, -1
+   padded.
 """
 from __future__ import annotations
 
@@ -56,6 +62,7 @@ class Shape:
     table: str = "permuted"               # "identity" or "permuted"
     num_splits: int = 0                   # 0 = library heuristic
     p_verify: Optional[float] = None      # mixed batch: P(request verifies)
+    layout_shared: Optional[float] = None  # sparse verify: shared part of the layouts
 
 
 SHAPES = {
@@ -78,6 +85,12 @@ SHAPES = {
         # shape with blocks of one token, 5% of the tokens selected
         Shape("tokensel_b128_l8192", B=128, L=8192, Hq=32, Hkv=8, d=128, dtype="bf16", n_q=5,
               block_size=1, page_size=16, window=64, budget_frac=0.05),
+        # sparse verification: each of the k+1 verify positions attends to its
+        # own 5% of the blocks (70% of them shared by the unit's positions)
+        # plus the window
+        Shape("sparsever_b128_l8192", B=128, L=8192, Hq=32, Hkv=8, d=128, dtype="bf16",
+              n_q=5, block_size=16, page_size=16, window=64, budget_frac=0.05,
+              layout_shared=0.7),
     ]
 }
 SHAPE_ORDER = list(SHAPES)
@@ -93,6 +106,8 @@ class Batch:
     req_ids: list                # indices into the full batch
     sel: Optional[torch.Tensor] = None        # [B][Hkv][max_sel] int32 (given lists)
     sel_count: Optional[torch.Tensor] = None  # [B][Hkv] int32
+    row_sel: Optional[torch.Tensor] = None    # [B][Hkv][n][max_sel] int32 (sparse verify)
+    row_sel_count: Optional[torch.Tensor] = None  # [B][Hkv][n] int32
 
     @property
     def B(self) -> int:
@@ -134,7 +149,7 @@ def make(shape, seed: int = 0, device="cpu", sigma: Optional[str] = None,
          Hq: Optional[int] = None, Hkv: Optional[int] = None, d: Optional[int] = None,
          dtype: Optional[str] = None, block_size: Optional[int] = None,
          page_size: Optional[int] = None, planted=None, table: Optional[str] = None,
-         p_verify="keep") -> Workload:
+         p_verify="keep", layout_shared="keep") -> Workload:
     """Build a workload.  ``shape`` is a Shape or a name in SHAPES; keyword
     arguments override single fields (used for reduced-size and edge cases)."""
     if isinstance(shape, str):
@@ -148,6 +163,8 @@ def make(shape, seed: int = 0, device="cpu", sigma: Optional[str] = None,
         over["budget_frac"] = None
     if p_verify != "keep":
         over["p_verify"] = p_verify
+    if layout_shared != "keep":
+        over["layout_shared"] = layout_shared
     shape = replace(shape, **over)
     device = torch.device(device)
     gen = torch.Generator(device=device)
@@ -292,6 +309,34 @@ def make(shape, seed: int = 0, device="cpu", sigma: Optional[str] = None,
                 cnt[i, h] = n_eff
         draft.sel = sel.to(device)
         draft.sel_count = cnt.to(device)
+
+    # 6. sparse verify layouts
+    if verify is not None and shape.layout_shared is not None:
+        rs = torch.full((verify.B, Hkv_, shape.n_q, max_sel), -1, dtype=torch.int32)
+        rc = torch.zeros((verify.B, Hkv_, shape.n_q), dtype=torch.int32)
+        for i, b in enumerate(vids):
+            Lb = lens[b]
+            ws = Lb if shape.window <= 0 else max(0, Lb - shape.window)
+            ncand = min(nblk_of[b], _ceil_div(ws, shape.block_size))
+            n_eff = min(budgets[b], ncand, max_sel)
+            n_shared = int(round(shape.layout_shared * n_eff))
+            for h in range(Hkv_):
+                heavy = {t // shape.block_size for t in planted_pos.get((b, h), [])
+                         if t // shape.block_size < ncand}
+                order = torch.randperm(ncand, generator=cpu_gen).tolist()
+                core = ([j for j in order if j in heavy] +
+                        [j for j in order if j not in heavy])[:n_shared]
+                core_set = set(core)
+                rest = [j for j in order if j not in core_set]
+                for qi in range(shape.n_q):
+                    own = torch.randperm(len(rest), generator=cpu_gen)[:n_eff - n_shared]
+                    pick = core + [rest[int(k)] for k in own]
+                    shuf = torch.randperm(len(pick), generator=cpu_gen).tolist()
+                    rs[i, h, qi, :len(pick)] = torch.tensor([pick[k] for k in shuf],
+                                                            dtype=torch.int32)
+                    rc[i, h, qi] = len(pick)
+        verify.row_sel = rs.to(device)
+        verify.row_sel_count = rc.to(device)
 
     return Workload(shape=shape, seed=seed, k_cache=k_cache, v_cache=v_cache,
                     seq_lens_all=lens, verify=verify, draft=draft,

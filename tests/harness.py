@@ -78,6 +78,20 @@ def gpu_draft(wl, batch, sel, cnt, num_splits=0, window=None, poison=True):
     return o, lse
 
 
+def gpu_sparse_verify(wl, batch, row_sel, row_cnt, num_splits=0, window=None, poison=True):
+    dev = batch.q.device
+    B, n_q, hq, d = batch.q.shape
+    o = torch.empty_like(batch.q)
+    lse = torch.empty((B, n_q, hq), dtype=torch.float32, device=dev)
+    if poison:
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+    win = wl.shape.window if window is None else window
+    sss().sparse_verify_attn(kv_of(wl, batch), batch.q, wl.sm_scale, wl.shape.block_size,
+                             row_sel, row_cnt, win, o, lse, num_splits=num_splits)
+    return o, lse
+
+
 # --------------------------------------------------------------------------
 # oracle on a subset of requests: copy only those requests' pages
 # --------------------------------------------------------------------------
@@ -122,6 +136,23 @@ def oracle_draft_units(wl, batch, sel, cnt, units, window=None):
         k, v, table, L = request_view(wl, batch, b)
         O, LSE = oracle.draft(q[b:b + 1], k, v, table, np.array([L]), sel[b:b + 1], cnt[b:b + 1],
                               wl.shape.block_size, win, wl.sm_scale, units=[(0, h) for h in hs])
+        for h in hs:
+            out[(b, h)] = (O[0], LSE[0])
+    return out
+
+
+def oracle_sparse_units(wl, batch, row_sel, row_cnt, units, window=None):
+    q = W.to_numpy64(batch.q)
+    win = wl.shape.window if window is None else window
+    out = {}
+    by_req = {}
+    for b, h in units:
+        by_req.setdefault(b, []).append(h)
+    for b, hs in by_req.items():
+        k, v, table, L = request_view(wl, batch, b)
+        O, LSE = oracle.sparse_verify(q[b:b + 1], k, v, table, np.array([L]), row_sel[b:b + 1],
+                                      row_cnt[b:b + 1], wl.shape.block_size, win, wl.sm_scale,
+                                      units=[(0, h) for h in hs])
         for h in hs:
             out[(b, h)] = (O[0], LSE[0])
     return out
@@ -208,6 +239,21 @@ def compare_draft(wl, batch, gpu_out, sel_np, cnt_np, units, window=None, stats=
             continue
         st.add_o(o[b, :, gs].astype(np.float64), Or[:, gs])
         st.add_lse(lse[b, :, gs].astype(np.float64), LSEr[:, gs])
+    return st
+
+
+def compare_sparse(wl, batch, gpu_out, row_sel_np, row_cnt_np, units, window=None, stats=None):
+    """Rows with an empty token set must be exactly O = 0, LSE = -inf (the
+    LSE comparison checks the infinities, the O comparison the zeros)."""
+    o, lse = (t.float().cpu().numpy() for t in gpu_out)
+    st = stats or Stats()
+    ref = oracle_sparse_units(wl, batch, row_sel_np, row_cnt_np, units, window)
+    for (b, h), (Or, LSEr) in ref.items():
+        gs = group_slice(wl, h)
+        st.add_o(o[b, :, gs].astype(np.float64), Or[:, gs])
+        st.add_lse(lse[b, :, gs].astype(np.float64), LSEr[:, gs])
+        empty = np.isneginf(LSEr[:, gs])
+        assert np.all(o[b, :, gs][empty] == 0)
     return st
 
 

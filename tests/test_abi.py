@@ -242,3 +242,51 @@ def test_kv_update_rejects_bad_arguments():
     assert c(256, 512, -1, 5, 256, None) == 1
     assert c(None, 512, 2, 5, 256, None) == 1
     assert c(256, 512, 0, 5, 256, None) == 0
+
+
+def call_sparse(sss, kv, **kw):
+    a = dict(q=4096, batch=2, n_q=5, hq=8, scale=0.1, bs=16, rsel=256, rcnt=512, max_sel=4,
+             window=16, splits=0, o=8192, lse=16384, ws=65536, wsb=1 << 30)
+    a.update(kw)
+    return sss.raw().sss_sparse_verify_attn(ctypes.byref(kv), a["q"], a["batch"], a["n_q"],
+                                            a["hq"], a["scale"], a["bs"], a["rsel"], a["rcnt"],
+                                            a["max_sel"], a["window"], a["splits"], a["o"],
+                                            a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kvkw,callkw,status", [
+    (dict(dtype=0), {}, 2),                      # fp32 cache: matrix-core path only
+    (dict(page_size=8, max_pages_per_req=16), {}, 2),
+    ({}, dict(bs=8), 2),
+    ({}, dict(n_q=0), 1),
+    ({}, dict(n_q=33), 1),
+    ({}, dict(hq=7), 1),
+    ({}, dict(hq=128, n_q=5), 2),                # 5 * 64 rows > 128
+    ({}, dict(max_sel=0), 1),
+    ({}, dict(window=-1), 1),
+    ({}, dict(splits=-1), 1),
+    ({}, dict(scale=float("inf")), 1),
+    ({}, dict(q=4100), 1),
+    ({}, dict(o=0), 1),
+    ({}, dict(rsel=0), 1),
+    ({}, dict(rcnt=514), 1),                     # misaligned counts
+    (dict(max_seq_len=1024, max_pages_per_req=64), dict(wsb=16, splits=4), 3),
+    (dict(max_seq_len=1024, max_pages_per_req=64), dict(ws=65537, splits=4), 1),
+])
+def test_sparse_verify_rejects_bad_arguments(kvkw, callkw, status):
+    sss = _binding()
+    kv = good_kv(sss, **kvkw)
+    assert call_sparse(sss, kv, **callkw) == status
+    assert sss.raw().sss_last_error()
+
+
+def test_sparse_verify_workspace_and_empty_batch():
+    sss = _binding()
+    kv = good_kv(sss)
+    assert call_sparse(sss, kv, batch=0) == 0
+    assert sss.sparse_verify_workspace_size(kv, 2, 5, 8, 16, 4, 16, 1) == 0   # one chunk
+    long_kv = good_kv(sss, max_seq_len=1024, max_pages_per_req=64)
+    n = sss.sparse_verify_workspace_size(long_kv, 2, 5, 8, 16, 40, 16, 4)
+    assert n > 0 and n % 256 == 0
+    with pytest.raises(sss.SSSError):
+        sss.sparse_verify_workspace_size(good_kv(sss, dtype=0), 2, 5, 8, 16, 4, 16, 0)
