@@ -80,7 +80,9 @@ typedef enum { SSS_F32 = 0, SSS_BF16 = 1 } sss_dtype;
  * max_seq_len host-side upper bound of seq_lens, used to size grids.
  *
  * Supported: dtype F32 or BF16; head_dim 64 or 128; page_size >= 1;
- * num_pages >= 1; max_pages_per_req >= ceil(max_seq_len / page_size).
+ * num_pages >= 1; max_pages_per_req >= ceil(max_seq_len / page_size);
+ * num_pages * num_kv_heads * page_size < 2^31 token rows per tensor (else
+ * SSS_ERR_UNSUPPORTED).
  */
 typedef struct {
   const void* k;
@@ -127,11 +129,11 @@ typedef struct {
  * 0 <= score_row_start < n_q; max_blocks >= ceil(max_seq_len / block_size);
  * max_seq_len >= n_q; num_splits >= 0.  Device-side:
  * n_q <= seq_lens[b] <= max_seq_len.
- * Path: BF16 caches with page_size a multiple of 16 and block_size a
- * multiple of 16, or block_size == 1 (single tokens, the page-size-1
- * selection of SparseSpec §4.1), run the matrix-core (MFMA) kernel; every
- * other supported case runs the vector-ALU kernel.  Both compute in fp32
- * and round o once to kv->dtype.
+ * Path: BF16 caches with page_size a multiple of 16 and block_size 16, a
+ * multiple of 32, or 1 (single tokens, the page-size-1 selection of
+ * SparseSpec §4.1) run the matrix-core (MFMA) kernel; every other supported
+ * case runs the vector-ALU kernel.  Both compute in fp32 and round o once
+ * to kv->dtype.
  */
 sss_status sss_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch, int32_t n_q,
                            int32_t num_q_heads, float sm_scale, int32_t block_size,
@@ -306,8 +308,9 @@ sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_p
  * scoring, selection, draft), which touch only those units.
  *
  * Requirements beyond those of the separate entry points: both halves use
- * the matrix-core path (BF16 cache, page_size and block_size multiples of
- * 16) and the same head_dim; the draft group size G <= 32; otherwise
+ * the matrix-core path (BF16 cache, page_size a multiple of 16, block_size
+ * a multiple of 16 and, for a verify half, 16 or a multiple of 32) and the
+ * same head_dim; the draft group size G <= 32; otherwise
  * SSS_ERR_UNSUPPORTED.  workspace: at least sss_fused_workspace_size()
  * bytes (0 when no unit can be split: NULL is then allowed), 256-byte
  * aligned, contents irrelevant on entry.  Results equal the separate entry

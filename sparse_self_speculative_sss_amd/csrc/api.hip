@@ -62,6 +62,10 @@ sss_status check_kv(const sss_paged_kv* kv, int batch) {
     return fail(SSS_ERR_INVALID_ARGUMENT, "kv->max_pages_per_req %d < 1", kv->max_pages_per_req);
   if (kv->max_seq_len < 1)
     return fail(SSS_ERR_INVALID_ARGUMENT, "kv->max_seq_len %d < 1", kv->max_seq_len);
+  // kernels address the pool by 32-bit token rows (page, head, slot)
+  if ((long long)kv->num_pages * kv->num_kv_heads * kv->page_size >= (1LL << 31))
+    return fail(SSS_ERR_UNSUPPORTED, "the pool holds %lld token rows per tensor (limit 2^31 - 1)",
+                (long long)kv->num_pages * kv->num_kv_heads * kv->page_size);
   if ((long long)kv->max_pages_per_req * kv->page_size < kv->max_seq_len)
     return fail(SSS_ERR_INVALID_ARGUMENT,
                 "kv->max_pages_per_req * page_size = %lld < max_seq_len %d",
@@ -79,13 +83,14 @@ sss_status check_kv(const sss_paged_kv* kv, int batch) {
 }
 
 // Matrix-core path: BF16 caches.  Verify reads 16-token page runs (pages of
-// a multiple of 16 tokens) and scores blocks of a multiple of 16 tokens, or
-// single tokens.  Draft reads blocks of a multiple of 16 tokens as page runs
-// (same page rule), or single selected tokens gathered one row at a time
-// (one row tile: G <= 32).
+// a multiple of 16 tokens) and scores blocks of 16 tokens, of a multiple of
+// 32 (a block then ends where a 32-token tile ends), or single tokens.
+// Draft reads blocks of a multiple of 16 tokens as page runs (same page
+// rule), or single selected tokens gathered one row at a time (one row
+// tile: G <= 32).
 bool use_mfma_verify(const sss_paged_kv* kv, int block_size) {
   return kv->dtype == SSS_BF16 && kv->page_size % kSeg == 0 &&
-         (block_size % kSeg == 0 || block_size == 1);
+         (block_size == kSeg || block_size % (2 * kSeg) == 0 || block_size == 1);
 }
 bool use_mfma_draft(const sss_paged_kv* kv, int block_size, int group) {
   if (kv->dtype != SSS_BF16) return false;
@@ -355,7 +360,8 @@ sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int ch
     if (fs.has_v) {
       if (!pv.mfma)
         return fail(SSS_ERR_UNSUPPORTED,
-                    "fused step needs a BF16 cache with page_size and block_size multiples of 16");
+                    "fused step needs a BF16 cache with page_size a multiple of 16 and "
+                    "block_size 16 or a multiple of 32");
       if (!v->q || !v->o || !v->lse || !v->block_scores)
         return fail(SSS_ERR_INVALID_ARGUMENT, "verify q, o, lse and block_scores must be non-NULL");
       if (!aligned(v->q, 16) || !aligned(v->o, 16))

@@ -94,6 +94,26 @@ __device__ __forceinline__ void group_sync() {
   }
 }
 
+// Division by a runtime divisor 1 <= d <= 2^31 of a dividend 0 <= x < 2^31
+// as a multiply-high, add and shift (Granlund and Montgomery's round-up
+// method with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1; the
+// sum cannot overflow for x < 2^31).  The tile loop divides token positions
+// by the page and block sizes; a plain integer division costs ~25 scalar
+// instructions each time.
+struct FastDiv {
+  uint32_t d, m;
+  int l;
+  __device__ explicit FastDiv(int divisor) {
+    d = (uint32_t)divisor;
+    l = d > 1u ? 32 - __builtin_clz(d - 1u) : 0;
+    m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1ull);
+  }
+  __device__ __forceinline__ int div(int x) const {
+    return (int)((__umulhi((uint32_t)x, m) + (uint32_t)x) >> l);
+  }
+  __device__ __forceinline__ int mod(int x) const { return x - div(x) * (int)d; }
+};
+
 struct Seg {
   long long base;  // element offset of token t0 of this (page, head) run
   int t0, lo, hi;  // 16-aligned start; valid tokens are [lo, hi)
@@ -161,8 +181,9 @@ __device__ __forceinline__ SegLane seg_lane(const AttnParams& p, const int32_t* 
 // page 0 and sets `bad` (the unit's outputs become NaN).  PM: also read
 // the position mask.
 template <bool PM = false>
-__device__ __forceinline__ Seg seg_of(const AttnParams& p, int h, const SegLane& cur,
-                                      const SegLane& nxt, bool use_nxt, int idx, int& bad) {
+__device__ __forceinline__ Seg seg_of(const AttnParams& p, const FastDiv& pdiv, int h,
+                                      const SegLane& cur, const SegLane& nxt, bool use_nxt,
+                                      int idx, int& bad) {
   Seg s;
   s.pm = 0xffffffffu;
   if (PM) {
@@ -187,8 +208,9 @@ __device__ __forceinline__ Seg seg_of(const AttnParams& p, int h, const SegLane&
   }
   s.lo = s.t0 + (lh & 255);
   s.hi = s.t0 + (lh >> 8);
-  s.base = (((long long)pg * p.num_kv_heads + h) * p.page_size + (s.t0 % p.page_size)) *
-           (long long)p.head_dim;
+  // cache row of token t0 (rows of the pool number < 2^31; checked on the host)
+  const int row = (pg * p.num_kv_heads + h) * p.page_size + pdiv.mod(s.t0);
+  s.base = (long long)row * p.head_dim;
   return s;
 }
 
@@ -567,6 +589,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   const bf16* __restrict__ kc = reinterpret_cast<const bf16*>(p.k);
   const bf16* __restrict__ vc = reinterpret_cast<const bf16*>(p.v);
   char* grp = smem + tg * G::GROUP_BYTES;
+  const FastDiv pdiv(p.page_size), bdiv(p.block_size);
 
   int bad = 0;
   // segment descriptors of the first two batches of 64
@@ -661,8 +684,8 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       vm[q] = gather_mask(rows_s, g_rel + 32 * q, g_len - 32 * q);
       load_tile_gather<D, NWR>(regs[q], kc, vc, rows_s, g_rel + 32 * q, vm[q], lig);
     } else {
-      sa[q] = seg_of<SPARSE>(p, h, cur, nxt, false, 2 * q, bad);
-      sb[q] = seg_of<SPARSE>(p, h, cur, nxt, false, 2 * q + 1, bad);
+      sa[q] = seg_of<SPARSE>(p, pdiv, h, cur, nxt, false, 2 * q, bad);
+      sb[q] = seg_of<SPARSE>(p, pdiv, h, cur, nxt, false, 2 * q + 1, bad);
       load_tile<D, NWR>(regs[q], kc, vc, sa[q], sb[q], lig);
     }
   }
@@ -704,8 +727,8 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
         load_tile_gather<D, NWR>(regs[q], kc, vc, rows_s, g_rel + rn, vm[q], lig);
       } else {
         const int ra = rel0 + 2 * PD, rb = ra + 1;
-        sa[q] = seg_of<SPARSE>(p, h, cur, nxt, (ra >> 6) != cur_batch, ra & 63, bad);
-        sb[q] = seg_of<SPARSE>(p, h, cur, nxt, (rb >> 6) != cur_batch, rb & 63, bad);
+        sa[q] = seg_of<SPARSE>(p, pdiv, h, cur, nxt, (ra >> 6) != cur_batch, ra & 63, bad);
+        sb[q] = seg_of<SPARSE>(p, pdiv, h, cur, nxt, (rb >> 6) != cur_batch, rb & 63, bad);
         load_tile<D, NWR>(regs[q], kc, vc, sa[q], sb[q], lig);
       }
     }
@@ -855,15 +878,15 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
         } else {
           blk_run += psum;
           const int tile_end = ca.t0 + 2 * kSeg;
-          const bool last = (tile_end % bs == 0) || (g_lo + rel0 + 2 >= g_hi);
+          const bool last = (bdiv.mod(tile_end) == 0) || (g_lo + rel0 + 2 >= g_hi);
           if (last) {
             const float tot = blk_run + __shfl_xor(blk_run, 32);
             if (row_ok && hl == 0) {
               const float v = m_use + fast_log2(tot);
               if (ell_lds) {
-                ell_s[(ca.t0 / bs) * R + r] = v;
+                ell_s[bdiv.div(ca.t0) * R + r] = v;
               } else {
-                ell_at = (long long)(ca.t0 / bs) * R + r;
+                ell_at = (long long)bdiv.div(ca.t0) * R + r;
                 ell_val = v;
               }
             }

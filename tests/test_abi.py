@@ -290,3 +290,10 @@ def test_sparse_verify_workspace_and_empty_batch():
     assert n > 0 and n % 256 == 0
     with pytest.raises(sss.SSSError):
         sss.sparse_verify_workspace_size(good_kv(sss, dtype=0), 2, 5, 8, 16, 4, 16, 0)
+
+
+def test_pool_of_2_31_rows_is_unsupported():
+    sss = _binding()
+    kv = good_kv(sss, num_pages=1 << 26, page_size=16, num_kv_heads=2)   # 2^31 rows
+    assert call_verify(sss, kv) == 2
+    assert b"2^31" in sss.raw().sss_last_error()

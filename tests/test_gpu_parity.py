@@ -35,6 +35,11 @@ SMALL = [
     ("page64_blk64", "longctx_b4_l128k", dict(B=1, L=2000, sigma="one"), [0, 3]),
     ("page32_blk16", "qwen3_8b_layer_b16_l4096", dict(B=2, L=700, page_size=32, sigma="one"), [0]),
     ("page16_blk64", "qwen3_8b_layer_b16_l4096", dict(B=2, L=700, block_size=64, sigma="one"), [0, 2]),
+    # page and block sizes that are not powers of two (division by multiply-high)
+    ("page48_blk48", "qwen3_8b_layer_b16_l4096", dict(B=2, L=700, page_size=48, block_size=48,
+                                                      sigma="one"), [0, 2]),
+    ("page80_blk32", "longctx_b4_l128k", dict(B=1, L=1500, page_size=80, block_size=32,
+                                              budget=6, sigma="one"), [0, 3]),
     ("bf16_page8_simple", "qwen3_8b_layer_b16_l4096",
      dict(B=2, L=150, page_size=8, block_size=8, Hq=8, Hkv=2, sigma="one"), [0, 2]),
     ("f32_d128", "qwen3_8b_layer_b16_l4096", dict(B=1, L=100, dtype="f32", Hq=8, Hkv=2), [0]),
