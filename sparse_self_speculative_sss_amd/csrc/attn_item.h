@@ -638,19 +638,30 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       const int ci = lane + 64 * j;
       const int row = ci / G::CPT, cc = ci % G::CPT;
       const int rr = rt * 32 + row;
-      bf16x8 v = {};
+      uint4 v = {0u, 0u, 0u, 0u};
       if (rr < R) {
         const int qi = rr / p.group, qh = h * p.group + rr % p.group;
-        v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(p.q) +
-                                             (((long long)b * p.n_q + qi) * p.num_q_heads + qh) * D +
-                                             8 * cc);
+        v = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16*>(p.q) +
+                                            (((long long)b * p.n_q + qi) * p.num_q_heads + qh) * D +
+                                            8 * cc);
+        // a negative scale is folded into Q (an exact sign flip), so the
+        // tile loop scales by |scale| and max-reduces unscaled logits
+        if (p.scale_log2 < 0.f) {
+          v.x ^= 0x80008000u;
+          v.y ^= 0x80008000u;
+          v.z ^= 0x80008000u;
+          v.w ^= 0x80008000u;
+        }
       }
-      *reinterpret_cast<bf16x8*>(qtile + row * G::K_STRIDE + 16 * cc) = v;
+      *reinterpret_cast<uint4*>(qtile + row * G::K_STRIDE + 16 * cc) = v;
     }
   }
   __syncthreads();
   const int pos_r = DRAFT ? (L - 1) : (L - p.n_q + iq);
   const int pos_min = DRAFT ? (L - 1) : (L - p.n_q);  // smallest causal limit of the unit's rows
+  // |scale| (log2 domain), kept positive so that a masked -inf logit times
+  // it stays -inf (a zero scale becomes a negligible positive one)
+  const float scl = fmaxf(fabsf(p.scale_log2), 1e-30f);
   // sparse verify: every query position of the unit, and those of this row
   // wave's rows
   const uint32_t all_pos = (uint32_t)((2ull << (p.n_q - 1)) - 1ull);
@@ -748,7 +759,9 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
             *reinterpret_cast<const bf16x8*>(qtile + rl * G::K_STRIDE + 32 * ks + 16 * hl);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb, sacc, 0, 0, 0);
       }
-      // online softmax (log2 domain); interior tiles need no mask
+      // online softmax (log2 domain; s holds unscaled logits, masked ones
+      // -inf, and the scale enters with the exponent); interior tiles need
+      // no mask
       float s[16];
       float mx = neg_inf();
       const bool interior = full && (GATHER || cb.t0 + kSeg - 1 <= pos_min) &&
@@ -756,7 +769,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       if (interior) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          s[i] = sacc[i] * p.scale_log2;
+          s[i] = sacc[i];
           mx = fmaxf(mx, s[i]);
         }
       } else if constexpr (GATHER) {
@@ -764,7 +777,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int m = (i >> 2) * 8 + 4 * hl + (i & 3);
-          s[i] = ((vmq >> m) & 1u) ? sacc[i] * p.scale_log2 : neg_inf();
+          s[i] = ((vmq >> m) & 1u) ? sacc[i] : neg_inf();
           mx = fmaxf(mx, s[i]);
         }
       } else {
@@ -775,7 +788,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
           const int tok = sg.t0 + (m % kSeg);
           bool ok = tok >= sg.lo && tok < sg.hi && tok <= pos_r;
           if (SPARSE) ok = ok && ((sg.pm >> iq) & 1u);
-          s[i] = ok ? sacc[i] * p.scale_log2 : neg_inf();
+          s[i] = ok ? sacc[i] : neg_inf();
           mx = fmaxf(mx, s[i]);
         }
       }
@@ -786,9 +799,10 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
         // tile's K rows, which S has consumed; else a slot at it.list_off)
         // and stores them once the tile is done
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tok_stage[((i >> 2) * 8 + 4 * hl + (i & 3)) * 32 + rl] = s[i];
+        for (int i = 0; i < 16; ++i)
+          tok_stage[((i >> 2) * 8 + 4 * hl + (i & 3)) * 32 + rl] = s[i] * scl;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scl;
       // lazy rescaling: the reference max m_run moves only when a row's max
       // exceeds it by more than kRescaleSlack (log2 units), so softmax terms
       // stay <= 2^kRescaleSlack and most tiles skip the O rescale entirely
@@ -810,7 +824,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        pr[i] = fast_exp2(s[i] - m_use);
+        pr[i] = fast_exp2(fmaf(s[i], scl, -m_use));
         psum += pr[i];
       }
       l_run += psum;

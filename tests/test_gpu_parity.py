@@ -278,3 +278,24 @@ def test_invalid_seq_len_poisons_outputs():
     torch.cuda.synchronize()
     assert torch.isnan(o[1].float()).all() and torch.isnan(lse[1]).all() and torch.isnan(sc[1]).all()
     assert torch.isfinite(o[0].float()).all() and torch.isfinite(lse[0]).all()
+
+
+@pytest.mark.parametrize("scale", [-0.06, 0.0])
+def test_negative_and_zero_scale(scale):
+    """The tile loop scales by |scale| with a negative scale folded into Q: a
+    negative and a zero softmax scale still match the oracle (verify with
+    scores, split and unsplit, and the draft)."""
+    wl = mk("qwen3_8b_layer_b16_l4096", seed=21, B=2, L=300, sigma="one")
+    wl.sm_scale = scale
+    vb, db = wl.verify, wl.draft
+    units = H.all_units(vb, wl.shape.Hkv)
+    for ns in (0, 2):
+        print(f"[scale] {scale} verify num_splits={ns}", flush=True)
+        out = H.gpu_verify(wl, vb, num_splits=ns)
+        torch.cuda.synchronize()
+        H.compare_verify(wl, vb, out, units).check(f"scale={scale} splits={ns}")
+    _, sel, cnt = H.oracle_selection(wl, vb, units)
+    print(f"[scale] {scale} draft", flush=True)
+    out = H.gpu_draft(wl, db, torch.from_numpy(sel).to(DEV), torch.from_numpy(cnt).to(DEV))
+    torch.cuda.synchronize()
+    H.compare_draft(wl, db, out, sel, cnt, units).check(f"draft scale={scale}")
