@@ -51,11 +51,18 @@ struct Geo {
 // Token groups per workgroup for a given number of 32-row tiles.
 __host__ __device__ constexpr int token_groups_for(int nwr) { return nwr == 1 ? 4 : (nwr == 2 ? 2 : 1); }
 
+// K/V tile buffers in LDS: one per token group, or two (alternating tiles)
+// for a single token group of three or four row waves, so that those waves
+// meet at one barrier per tile instead of two.
+__host__ __device__ constexpr int tile_buffers(int nwr, int nwt) {
+  return (nwt == 1 && nwr >= 3) ? 2 : nwt;
+}
+
 // LDS bytes attn_item<D, NWR, NWT, *> uses from the start of its LDS area:
 // K/V tiles (or the token-group merge scratch, which reuses them), Q tiles,
 // row LSEs.
 __host__ __device__ constexpr size_t item_lds_bytes(int D, int nwr, int nwt) {
-  return (size_t)nwt * ((size_t)32 * (D * 2 + 16) + (size_t)D * 64) +
+  return (size_t)tile_buffers(nwr, nwt) * ((size_t)32 * (D * 2 + 16) + (size_t)D * 64) +
          (size_t)nwr * 32 * (D * 2 + 16) + 128 * 4;
 }
 
@@ -512,7 +519,11 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   const bool row_ok = r < R;
   const int iq = row_ok ? r / p.group : 0;
   const int hq = h * p.group + (row_ok ? r % p.group : 0);
-  float* lse2s = reinterpret_cast<float*>(smem + NWT * G::GROUP_BYTES + NWR * G::Q_BYTES);
+  // double-buffered K/V tiles (tile t in buffer t & 1); otherwise one
+  // buffer per token group, reused by every tile
+  constexpr bool DB = tile_buffers(NWR, NWT) == 2 && NWT == 1;
+  constexpr int NBUF = tile_buffers(NWR, NWT);
+  float* lse2s = reinterpret_cast<float*>(smem + NBUF * G::GROUP_BYTES + NWR * G::Q_BYTES);
 
   const int L = p.seq_lens[b];
   const int minL = DRAFT ? 1 : p.n_q;
@@ -631,7 +642,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   }
 
   // ---- Q rows of each row tile -> LDS (the Q^T operand is read from there) ----
-  char* qtile = smem + NWT * G::GROUP_BYTES + rt * G::Q_BYTES;
+  char* qtile = smem + NBUF * G::GROUP_BYTES + rt * G::Q_BYTES;
   if (tg == 0) {
 #pragma unroll
     for (int j = 0; j < (32 * G::CPT) / 64; ++j) {
@@ -709,14 +720,15 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
     const int rel0 = kTileEntries * t;
     const bool tile_live = g_lo + rel0 < g_hi;
     const Seg ca = sa[q], cb = sb[q];
+    char* const gt = DB ? smem + (t & 1) * G::GROUP_BYTES : grp;
     const uint32_t vmq = GATHER ? vm[q] : 0u;
     bool full;
     if constexpr (GATHER) {
       full = vmq == 0xffffffffu;
-      store_tile_gather<D, NWR>(regs[q], grp, lig, vmq);
+      store_tile_gather<D, NWR>(regs[q], gt, lig, vmq);
     } else {
       full = seg_full(ca) && seg_full(cb);
-      store_tile<D, NWR>(regs[q], grp, lig, ca, cb, full);
+      store_tile<D, NWR>(regs[q], gt, lig, ca, cb, full);
     }
     if (!GATHER && rel0 > 0 && (rel0 & 63) == 0) {
       // move to the next batch of descriptors; fetch the one after it
@@ -754,7 +766,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
 #pragma unroll
       for (int ks = 0; ks < G::KS; ++ks) {
         const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(grp + rl * G::K_STRIDE + 32 * ks + 16 * hl);
+            *reinterpret_cast<const bf16x8*>(gt + rl * G::K_STRIDE + 32 * ks + 16 * hl);
         const bf16x8 qb =
             *reinterpret_cast<const bf16x8*>(qtile + rl * G::K_STRIDE + 32 * ks + 16 * hl);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb, sacc, 0, 0, 0);
@@ -829,7 +841,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       }
       l_run += psum;
       // O^T += V^T P^T
-      char* vt = grp + G::K_BYTES;
+      char* vt = gt + G::K_BYTES;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 pb;
@@ -909,7 +921,10 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
         }
       }
     }
-    group_sync<NWR>();
+    // a double-buffered tile needs no second barrier: the next tile goes to
+    // the other buffer, and the waves meet at the next tile's barrier before
+    // the buffer after it is written
+    if (!DB) group_sync<NWR>();
   }
 
   if (SCORES && ell_at >= 0) ell_u[ell_at] = ell_val;
