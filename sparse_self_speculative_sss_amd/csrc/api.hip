@@ -337,6 +337,10 @@ struct FusedSetup {
   Plan chain_draft = {};  // chained draft of split units (one-launch-per-stage kernels)
   size_t ell_off = 0, opv_off = 0, lpv_off = 0, opd_off = 0,
          lpd_off = 0, chain_off = 0, bytes = 0;
+  // chained step of whole units run as two launches: the unsplit verify
+  // kernel (block masses in LDS), then selection + draft per unit
+  bool two_launch = false;
+  Plan vplan = {};
 };
 
 sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int chained,
@@ -453,6 +457,23 @@ sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int ch
     return fail(SSS_ERR_UNSUPPORTED, "fused step: too many work items");
   fs.split_v = fs.has_v && fs.pl.maxch_v > 1;
   fs.split_d = fs.nd > 0 && fs.pl.maxch_d > 1;
+  if (chained && !fs.split_v && fs.nd == 0) {
+    // Whole units of a chained step: the unsplit verify kernel keeps two
+    // workgroups' worth of streaming per CU busy while no unit's selection
+    // and draft hold a CU, and the selection + draft kernel then runs every
+    // unit at once.  Used when that verify plan keeps its block masses in
+    // LDS and needs no workspace.
+    Plan vp;
+    if (plan_verify(&v->kv, v->batch, v->n_q, v->num_q_heads, v->block_size, v->max_blocks, 1,
+                    vp) == SSS_OK &&
+        vp.mfma && vp.num_chunks == 1 && vp.ell_in_lds && vp.bytes == 0) {
+      int32_t a, b;
+      if (select_draft_lds(fs.head_dim, v->max_sel, v->max_blocks, a, b) <= kMaxLds) {
+        fs.two_launch = true;
+        fs.vplan = vp;
+      }
+    }
+  }
   if (chained && fs.split_v) {
     // split units draft after their selection, with the one-launch kernels
     sss_status st = plan_draft(&d->kv, d->batch, d->num_q_heads, d->block_size, d->max_sel,
@@ -947,6 +968,27 @@ sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* d
   f.chained = chained ? 1 : 0;
   f.off_ell = fs.pl.off_ell;
   f.off_sel = fs.pl.off_sel;
+  if (fs.two_launch) {
+    const sss_verify_step* v = verify;
+    const Plan& vp = fs.vplan;
+    AttnParams p = base_params(&v->kv, v->q, v->batch, v->n_q, v->num_q_heads, v->sm_scale, vp);
+    p.chunk_tokens = vp.chunk;
+    p.o = v->o;
+    p.lse = v->lse;
+    p.block_size = v->block_size;
+    p.max_blocks = v->max_blocks;
+    p.score_row_start = v->score_row_start;
+    p.block_scores = v->block_scores;
+    p.ell_in_lds = 1;
+    p.ell_lds_floats = (int32_t)vp.ell_lds_floats;
+    hipError_t e = launch_verify_mfma(p, s);
+    if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step verify launch: %s", hipGetErrorString(e));
+    select_draft_lds(fs.head_dim, f.max_sel, v->max_blocks, f.off_sel, f.off_ell);
+    e = launch_select_draft(f, pv, pd, fs.head_dim, s);
+    if (e != hipSuccess)
+      return fail(SSS_ERR_HIP, "fused step select + draft launch: %s", hipGetErrorString(e));
+    return ok();
+  }
   hipError_t e = launch_fused(f, pv, pd, fs.pl, fs.head_dim, s);
   if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step launch: %s", hipGetErrorString(e));
 

@@ -48,6 +48,46 @@ __device__ __forceinline__ int draft_segments(const AttnParams& pd, int u, int& 
   return draft_list_len_mfma(nsel, pd.block_size, L, window_start(L, pd.window));
 }
 
+// Top-N selection of verify unit u from its block scores (written by this
+// workgroup before a workgroup barrier, or by an earlier launch) and, for a
+// chained step, the draft of the same unit over that selection, read from
+// an LDS copy at f.off_sel.  `keys` (LDS room for keys_cap words, or null)
+// parks the selection's keys.  All NT = 64 * NWTD threads call it.
+template <int D, int NWTD>
+__device__ void select_then_draft(const FusedParams& f, const AttnParams& pv,
+                                  const AttnParams& pd, int u, char* smem, uint32_t* keys,
+                                  int keys_cap) {
+  constexpr int NT = 64 * NWTD;
+  const int b = u / pv.num_kv_heads;
+  const int L = pv.seq_lens[b];
+  int ncand, n;
+  topk_bounds(L, pv.block_size, f.topk_window, pv.max_blocks, f.budget[b], f.max_sel, ncand, n);
+  if (threadIdx.x == 0) f.sel_count[u] = n;
+  int32_t* sel_s = reinterpret_cast<int32_t*>(smem + f.off_sel);
+  static_assert(kTopkLdsWords * 4 <= Geo<D>::GROUP_BYTES,
+                "selection scratch must fit in the tile area");
+  topk_select<NT>(pv.block_scores + (long long)u * pv.max_blocks, ncand, n,
+                  f.sel + (long long)u * f.max_sel, f.max_sel, f.chained ? sel_s : nullptr,
+                  reinterpret_cast<int*>(smem), keys, keys_cap);
+  if (!f.chained) return;
+  // draft of the same unit over the selection just made
+  const int Ld = pd.seq_lens[b];
+  const int nseg = unit_valid(pd, Ld, 1)
+                       ? draft_list_len_mfma(n, pd.block_size, Ld, window_start(Ld, pd.window))
+                       : 0;
+  Item dt;
+  dt.u = u;
+  dt.c = 0;
+  dt.chunk = max(2 * NWTD, (nseg + 2 * NWTD - 1) / (2 * NWTD) * (2 * NWTD));
+  dt.single = 1;
+  dt.part_row0 = 0;
+  dt.ell_off = 0;
+  dt.sel_off = f.off_sel;
+  dt.nsel_s = n;
+  dt.list_off = 0;
+  attn_item<D, 1, NWTD, true, false>(pd, dt, smem);
+}
+
 // One workgroup per work-list slot.  NWR row waves x NWT token groups for
 // verify items; draft items (one row tile) use all NWR * NWT waves as token
 // groups.
@@ -93,35 +133,10 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
     // a split unit's chunk leaves its partial; the follow-up launches finish it
     if (attn_item<D, NWR, NWT, false, true>(pv, it, smem) != kItemFinal || !f.topk) return;
     // this workgroup wrote the unit's block scores: order them before its
-    // own reads, then select
+    // own reads, then select (and draft)
     __threadfence_block();
     __syncthreads();
-    const int L = pv.seq_lens[b];
-    int ncand, n;
-    topk_bounds(L, pv.block_size, f.topk_window, pv.max_blocks, f.budget[b], f.max_sel, ncand, n);
-    if (tid == 0) f.sel_count[u] = n;
-    int32_t* sel_s = reinterpret_cast<int32_t*>(smem + f.off_sel);
-    static_assert(kTopkLdsWords * 4 <= NWT * Geo<D>::GROUP_BYTES,
-                  "selection scratch must fit in the tile area");
-    topk_select<NT>(pv.block_scores + (long long)u * pv.max_blocks, ncand, n,
-                    f.sel + (long long)u * f.max_sel, f.max_sel, f.chained ? sel_s : nullptr,
-                    reinterpret_cast<int*>(smem));
-    if (!f.chained) return;
-    // draft of the same unit over the selection just made
-    const int Ld = pd.seq_lens[b];
-    const int nseg = unit_valid(pd, Ld, 1)
-                         ? draft_list_len_mfma(n, pd.block_size, Ld, window_start(Ld, pd.window))
-                         : 0;
-    Item dt;
-    dt.u = u;
-    dt.c = 0;
-    dt.chunk = max(2 * NWTD, (nseg + 2 * NWTD - 1) / (2 * NWTD) * (2 * NWTD));
-    dt.single = 1;
-    dt.part_row0 = 0;
-    dt.ell_off = 0;
-    dt.sel_off = f.off_sel;
-    dt.nsel_s = n;
-    attn_item<D, 1, NWTD, true, false>(pd, dt, smem);
+    select_then_draft<D, NWTD>(f, pv, pd, u, smem, nullptr, 0);
   } else {
     Item it;
     it.u = u;
@@ -134,6 +149,24 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
     it.nsel_s = 0;
     attn_item<D, 1, NWTD, true, false>(pd, it, smem);
   }
+}
+
+// Selection and chained draft of whole verify units whose scores an
+// unsplit verify launch wrote: one workgroup (one row tile of draft rows,
+// kDraftWaves token groups) per unit.  LDS: the draft item's area, the
+// selection at f.off_sel, then the unit's Top-N keys (f.off_ell) when
+// max_blocks <= kSelectMaxKeys.
+constexpr int kDraftWaves = 4;
+constexpr int kSelectMaxKeys = 4096;
+
+template <int D>
+__global__ void __launch_bounds__(64 * kDraftWaves, 2)
+    select_draft_kernel(FusedParams f, AttnParams pv, AttnParams pd) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const bool park = pv.max_blocks <= kSelectMaxKeys;
+  select_then_draft<D, kDraftWaves>(f, pv, pd, blockIdx.x, smem,
+                                    park ? reinterpret_cast<uint32_t*>(smem + f.off_ell) : nullptr,
+                                    park ? pv.max_blocks : 0);
 }
 
 // Finishes the split verify units of a fused step, one workgroup per unit:
@@ -321,6 +354,33 @@ void fused_plan(const FusedPlanIn& in, FusedPlan& pl) {
     plan_with(in, nwr, nwt / 2, kMaxLds / 2 - 512, half);
     if (in.nv == 0 || half.chunk_v > 0) pl = half;
   }
+}
+
+size_t select_draft_lds(int head_dim, int max_sel, int max_blocks, int32_t& off_sel,
+                        int32_t& off_keys) {
+  off_sel = (int32_t)align_up(item_lds_bytes(head_dim, 1, kDraftWaves), 16);
+  off_keys = off_sel + (int32_t)align_up((size_t)max_sel * 4, 16);
+  return (size_t)off_keys + (max_blocks <= kSelectMaxKeys ? (size_t)max_blocks * 4 : 0);
+}
+
+hipError_t launch_select_draft(const FusedParams& f, const AttnParams& pv, const AttnParams& pd,
+                               int head_dim, hipStream_t s) {
+  if (f.nv_units == 0) return hipSuccess;
+  int32_t off_sel, off_keys;
+  const size_t smem = select_draft_lds(head_dim, f.max_sel, pv.max_blocks, off_sel, off_keys);
+  if (smem > kMaxLds || off_sel != f.off_sel || off_keys != f.off_ell) return hipErrorInvalidValue;
+  auto go = [&](auto kern) -> hipError_t {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)kMaxLds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3((unsigned)f.nv_units), dim3(64 * kDraftWaves), smem, s, f, pv,
+                       pd);
+    return hipGetLastError();
+  };
+  if (head_dim == 128) return go(select_draft_kernel<128>);
+  if (head_dim == 64) return go(select_draft_kernel<64>);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fused_finish(const FusedParams& f, const AttnParams& pv, hipStream_t s) {

@@ -173,6 +173,14 @@ hipError_t launch_kv_commit(const int32_t* seq_lens, const int32_t* keep, int ba
 // Host-side launchers (each returns hipGetLastError() of its launches).
 hipError_t launch_fused(const FusedParams& f, const AttnParams& pv, const AttnParams& pd,
                         const FusedPlan& pl, int head_dim, hipStream_t s);
+// Selection and chained draft of whole verify units after an unsplit verify
+// launch, one workgroup per unit.  select_draft_lds gives the LDS bytes and
+// the offsets of the selection and of the parked keys (FusedParams::off_sel,
+// ::off_ell).
+size_t select_draft_lds(int head_dim, int max_sel, int max_blocks, int32_t& off_sel,
+                        int32_t& off_keys);
+hipError_t launch_select_draft(const FusedParams& f, const AttnParams& pv, const AttnParams& pd,
+                               int head_dim, hipStream_t s);
 // One workgroup per split verify unit: merge, scores and selection.
 hipError_t launch_fused_finish(const FusedParams& f, const AttnParams& pv, hipStream_t s);
 hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s);
