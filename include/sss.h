@@ -243,8 +243,10 @@ size_t sss_draft_workspace_size(const sss_paged_kv* kv, int32_t batch, int32_t n
  * num_q_heads % num_kv_heads == 0; n_q * G <= 128; max_sel >= 1;
  * window >= 0; num_splits >= 0; max_seq_len >= n_q; a BF16 cache with
  * page_size and block_size multiples of 16 (else SSS_ERR_UNSUPPORTED);
- * ceil(max_seq_len / block_size) * 12 bytes of LDS for the union beside the
- * tiles.  Device-side: n_q <= seq_lens[b] <= max_seq_len (else that unit's
+ * a 4-byte mask per block of the longest request, ceil(max_seq_len /
+ * block_size), fits in the workgroup's K/V tile area while the union is
+ * built (16880 blocks for up to 32 rows at head_dim 128, fewer for more rows
+ * or head_dim 64), else SSS_ERR_UNSUPPORTED.  Device-side: n_q <= seq_lens[b] <= max_seq_len (else that unit's
  * outputs are NaN).  Caller owns every buffer; nothing is allocated.
  */
 sss_status sss_sparse_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch,

@@ -269,7 +269,9 @@ sss_status plan_sparse(const sss_paged_kv* kv, int batch, int n_q, int hq, int b
   const int nwr = ceil_div(pl.rows, 32);
   const int nwt = mfma_token_groups(pl.rows, false);
   const int max_blocks = ceil_div(kv->max_seq_len, block_size);
-  if (mfma_smem_bytes(kv->head_dim, nwr, nwt, 0) + sparse_union_lds_bytes(max_blocks) > kMaxLds)
+  if (mfma_smem_bytes(kv->head_dim, nwr, nwt, 0) + sparse_union_lds_bytes(max_blocks, n_q, max_sel) >
+          kMaxLds ||
+      !sparse_union_fits(kv->head_dim, nwr, max_blocks))
     return fail(SSS_ERR_UNSUPPORTED, "%d blocks per request leave no LDS room for the layout union",
                 max_blocks);
   const long long units = (long long)batch * kv->num_kv_heads;

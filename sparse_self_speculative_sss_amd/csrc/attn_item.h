@@ -340,18 +340,27 @@ __device__ __forceinline__ void store_tile(TileRegs<D, NWR>& r, char* grp, int l
 
 // ---- sparse verify: the union of a unit's per-position layouts ----
 
-// Builds, in LDS at `area`, the union of the layouts of unit (b, h): the
-// blocks before the window start that at least one query position selects,
-// ascending, each with the mask of the positions selecting it.  Layout:
-// pm[ncand] (a mask per candidate block), then blk[ncand], msk[ncand] (the
-// union, compacted).  `scratch` holds NT / 64 ints.  Returns the union's
+// Most blocks a unit's union can hold: every entry of every layout, and no
+// more than the request has blocks.
+__host__ __device__ __forceinline__ int union_max(int max_blocks, int n_q, int max_sel) {
+  const long long e = (long long)n_q * max_sel;
+  return e < max_blocks ? (int)e : max_blocks;
+}
+
+// Builds the union of the layouts of unit (b, h): the blocks before the
+// window start that at least one query position selects, ascending, each
+// with the mask of the positions selecting it, compacted into blk[] and
+// msk[] (union_max entries each, at `list`).  `work` holds a mask per
+// candidate block and then NT / 64 ints of scan scratch; it is only used
+// here (the tile area, before any tile is stored).  Returns the union's
 // size; all NT threads call it, and it ends with a barrier.
 template <int NT>
-__device__ int layout_union(const AttnParams& p, int b, int h, int ws, char* area, int* scratch) {
+__device__ int layout_union(const AttnParams& p, int b, int h, int ws, char* work, char* list) {
   const int ncand = min(ceil_div(ws, p.block_size), p.max_blocks);
-  uint32_t* pm = reinterpret_cast<uint32_t*>(area);
-  int32_t* blk = reinterpret_cast<int32_t*>(pm + ncand);
-  uint32_t* msk = reinterpret_cast<uint32_t*>(blk + ncand);
+  uint32_t* pm = reinterpret_cast<uint32_t*>(work);
+  int* scratch = reinterpret_cast<int*>(pm + p.max_blocks);
+  int32_t* blk = reinterpret_cast<int32_t*>(list);
+  uint32_t* msk = reinterpret_cast<uint32_t*>(blk + union_max(p.max_blocks, p.n_q, p.max_sel));
   const int tid = threadIdx.x;
   for (int j = tid; j < ncand; j += NT) pm[j] = 0u;
   __syncthreads();
@@ -559,10 +568,9 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   } else {
     ws = window_start(L, p.window);
     if constexpr (SPARSE) {
-      nsel = layout_union<NT>(p, b, h, ws, smem + it.list_off, reinterpret_cast<int*>(smem));
-      const int ncand = min(ceil_div(ws, p.block_size), p.max_blocks);
-      ublk = reinterpret_cast<const int32_t*>(smem + it.list_off) + ncand;
-      umsk = reinterpret_cast<const uint32_t*>(ublk + ncand);
+      nsel = layout_union<NT>(p, b, h, ws, smem, smem + it.list_off);
+      ublk = reinterpret_cast<const int32_t*>(smem + it.list_off);
+      umsk = reinterpret_cast<const uint32_t*>(ublk + union_max(p.max_blocks, p.n_q, p.max_sel));
     } else {
       nsel = it.sel_off >= 0 ? it.nsel_s : p.sel_count[(long long)b * p.num_kv_heads + h];
       nsel = nsel < 0 ? 0 : (nsel > p.max_sel ? p.max_sel : nsel);
@@ -588,7 +596,11 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       SPARSE ? ublk
              : ((DRAFT && it.sel_off >= 0) ? reinterpret_cast<const int32_t*>(smem + it.sel_off)
                                            : nullptr);
-  const int per_group = (LIST ? it.chunk : it.chunk / kSeg) / NWT;
+  // the item's entries split evenly over the token groups, in whole tiles
+  // (and, for block masses, whole blocks): a list or a request shorter
+  // than the chunk still keeps every group busy
+  const int galign = GATHER ? 32 : ((LIST || p.block_size < 2 * kSeg) ? 2 : p.block_size / kSeg);
+  const int per_group = ceil_div(ceil_div(seg_hi - seg_lo, NWT), galign) * galign;
   const int g_lo = min(seg_lo + tg * per_group, seg_hi);
   const int g_hi = min(g_lo + per_group, seg_hi);
   // list entries per tile: two 16-token segments, or 32 single tokens

@@ -123,17 +123,27 @@ int mfma_token_groups(int rows, bool draft) {
 
 hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s) { return dispatch<false>(p, s); }
 
-// Sparse verify: the union of a unit's layouts (a mask per candidate block,
-// then the compacted block ids and masks) follows the tiles in LDS.
-size_t sparse_union_lds_bytes(int max_blocks) { return (size_t)max_blocks * 12; }
+// Sparse verify: the compacted union of a unit's layouts (block ids and
+// position masks) follows the routine's area in LDS; the per-block masks
+// it is built from, and a scan scratch, borrow the tile area first.
+size_t sparse_union_lds_bytes(int max_blocks, int n_q, int max_sel) {
+  return (size_t)union_max(max_blocks, n_q, max_sel) * 8;
+}
+bool sparse_union_fits(int head_dim, int nwr, int max_blocks) {
+  const int nwt = token_groups_for(nwr);
+  const size_t tiles = (size_t)tile_buffers(nwr, nwt) *
+                       ((size_t)32 * (head_dim * 2 + 16) + (size_t)head_dim * 64);
+  return (size_t)max_blocks * 4 + 16 * 4 <= tiles;
+}
 
 namespace {
 template <int D, int NWR, int NWT>
 hipError_t launch_sparse_cfg(const AttnParams& p, hipStream_t s) {
   const unsigned grid = (unsigned)((long long)p.batch * p.num_kv_heads * p.num_chunks);
   if (grid == 0) return hipSuccess;
-  const size_t smem = mfma_smem_bytes(D, NWR, NWT, 0) + sparse_union_lds_bytes(p.max_blocks);
-  if (smem > kMaxLds) return hipErrorInvalidValue;
+  const size_t smem =
+      mfma_smem_bytes(D, NWR, NWT, 0) + sparse_union_lds_bytes(p.max_blocks, p.n_q, p.max_sel);
+  if (smem > kMaxLds || !sparse_union_fits(D, NWR, p.max_blocks)) return hipErrorInvalidValue;
   return launch_one<D, NWR, NWT, false, false, false, true>(p, smem, grid, s);
 }
 }  // namespace

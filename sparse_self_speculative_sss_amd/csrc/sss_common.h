@@ -186,7 +186,10 @@ hipError_t launch_fused_finish(const FusedParams& f, const AttnParams& pv, hipSt
 hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s);
 // Sparse verify (a layout per query position): LDS bytes beyond the tiles,
 // and the launch.
-size_t sparse_union_lds_bytes(int max_blocks);
+size_t sparse_union_lds_bytes(int max_blocks, int n_q, int max_sel);
+// whether the per-block masks of a request of max_blocks blocks fit in the
+// tile area of the configuration for nwr row tiles
+bool sparse_union_fits(int head_dim, int nwr, int max_blocks);
 hipError_t launch_sparse_verify_mfma(const AttnParams& p, hipStream_t s);
 hipError_t launch_draft_mfma(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_simple(const AttnParams& p, int dtype, bool draft, hipStream_t s);
