@@ -214,7 +214,14 @@ sss_status plan_draft(const sss_paged_kv* kv, int batch, int hq, int block_size,
   if (list_max < 1) list_max = 1;
   long long S = num_splits;
   if (S == 0) {
-    if (pl.mfma) {
+    // split only lists long enough to keep every token group of each chunk
+    // busy: a short list in several chunks costs more in per-workgroup
+    // latency and the merge launch than the extra workgroups bring (16
+    // requests x 8 heads with 18-segment lists: 16 us unsplit, 23 us in 4
+    // chunks; 8 units with 73-segment lists: 20 us in 10 chunks, 25 us
+    // unsplit)
+    const long long long_list = (pl.mfma && block_size % kSeg == 0) ? 64 : 64LL * kSeg;
+    if (pl.mfma && list_max >= long_list) {
       const long long wgs_target = kTargetWaves / ((long long)nwr * nwt);
       S = units > 0 ? (wgs_target + units - 1) / units : 1;
     } else {
