@@ -5,11 +5,11 @@
 namespace sss {
 namespace {
 
-constexpr int kTopkThreads = 256;
 // keys parked in LDS up to this many candidates (64 KiB)
 constexpr int kTopkMaxKeys = 16384;
 
-__global__ void __launch_bounds__(kTopkThreads)
+template <int NT>
+__global__ void __launch_bounds__(NT)
     topk_kernel(const float* __restrict__ scores, int hkv, int max_blocks,
                 const int32_t* __restrict__ seq_lens, int bs, const int32_t* __restrict__ budget,
                 int window, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
@@ -24,9 +24,8 @@ __global__ void __launch_bounds__(kTopkThreads)
   int ncand, n;
   topk_bounds(seq_lens[b], bs, window, max_blocks, budget[b], max_sel, ncand, n);
   if (threadIdx.x == 0) sel_count[u] = n;
-  topk_select<kTopkThreads>(scores + (long long)u * max_blocks, ncand, n,
-                            sel + (long long)u * max_sel, max_sel, nullptr, lds, keys,
-                            max_blocks <= kTopkMaxKeys ? max_blocks : 0);
+  topk_select<NT>(scores + (long long)u * max_blocks, ncand, n, sel + (long long)u * max_sel,
+                  max_sel, nullptr, lds, keys, max_blocks <= kTopkMaxKeys ? max_blocks : 0);
 }
 
 }  // namespace
@@ -38,14 +37,22 @@ hipError_t launch_topk(const float* scores, int batch, int hkv, int max_blocks,
   const unsigned grid = (unsigned)((long long)batch * hkv);
   if (grid == 0) return hipSuccess;
   const size_t smem = max_blocks <= kTopkMaxKeys ? (size_t)max_blocks * 4 : 0;
-  // dynamic LDS above 64 KiB (with the static part) must be opted into
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(topk_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      kTopkMaxKeys * 4);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(topk_kernel, dim3(grid), dim3(kTopkThreads), smem, s, scores, hkv, max_blocks,
-                     seq_lens, block_size, budget, window, sel, sel_count, max_sel, skip_len);
-  return hipGetLastError();
+  // few units with many candidates: a wider workgroup per unit (the units
+  // then run one wave of workgroups at once; 8 units of 2046 blocks take
+  // 15 us with 256 threads); many units: 256 threads, so that more
+  // workgroups share a CU
+  auto go = [&](auto kern, int nt) -> hipError_t {
+    // dynamic LDS above 64 KiB (with the static part) must be opted into
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+        kTopkMaxKeys * 4);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(nt), smem, s, scores, hkv, max_blocks, seq_lens,
+                       block_size, budget, window, sel, sel_count, max_sel, skip_len);
+    return hipGetLastError();
+  };
+  if (grid <= 256 && max_blocks >= 1024) return go(topk_kernel<1024>, 1024);
+  return go(topk_kernel<256>, 256);
 }
 
 }  // namespace sss
