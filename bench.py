@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=128,
                     help="requests the CPU oracle processes for the baseline (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="the CPU baseline stops taking requests after this much oracle time")
     ap.add_argument("--verify-splits", type=int, default=-1,
                     help="override num_splits of the verify call (-1: workload default)")
     ap.add_argument("--draft-splits", type=int, default=0)
@@ -134,11 +136,12 @@ def _request_copy(wl, batch, b):
     return k, v, np.arange(n, dtype=np.int32)[None], np.array([L], dtype=np.int32)
 
 
-def cpu_baseline(wl, n_req):
+def cpu_baseline(wl, n_req, budget_s=20.0):
     """Time the fp64 oracle (as it stands) on up to n_req verify requests
     (verify + block scores + Top-N) and up to n_req draft requests (draft over
     the selection: the oracle's own for verify->draft workloads, the given
-    lists for the mixed batch).  Returns query tokens/s."""
+    lists for the mixed batch), taking no further request once budget_s
+    seconds of oracle time are spent.  Returns query tokens/s."""
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_info
@@ -151,7 +154,11 @@ def cpu_baseline(wl, n_req):
         nv = min(n_req, vb.B)
         q = W.to_numpy64(vb.q[:nv])
         qd = W.to_numpy64(db.q[:nv]) if shared else None
+        done = 0
         for b in range(nv):
+            if elapsed >= budget_s:
+                break
+            done += 1
             k, v, table, lens = _request_copy(wl, vb, b)
             t0 = time.perf_counter()
             _, _, sc = oracle.verify_with_scores(q[b:b + 1], k, v, table, lens, wl.sm_scale,
@@ -164,11 +171,16 @@ def cpu_baseline(wl, n_req):
             elapsed += time.perf_counter() - t0
             tokens += s.n_q + (1 if shared else 0)
             del k, v
+        nv = done
     if not shared and db is not None:
         nd = min(n_req, db.B)
         qd = W.to_numpy64(db.q[:nd])
         sel_all, cnt_all = db.sel.cpu().numpy(), db.sel_count.cpu().numpy()
+        done = 0
         for b in range(nd):
+            if elapsed >= 2 * budget_s:
+                break
+            done += 1
             k, v, table, lens = _request_copy(wl, db, b)
             t0 = time.perf_counter()
             oracle.draft(qd[b:b + 1], k, v, table, lens, sel_all[b:b + 1], cnt_all[b:b + 1],
@@ -176,6 +188,7 @@ def cpu_baseline(wl, n_req):
             elapsed += time.perf_counter() - t0
             tokens += 1
             del k, v
+        nd = done
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     what = (f"{nv} of {vb.B if vb else 0} verify requests" +
             ("" if shared else f" and {nd} of {db.B if db else 0} draft requests"))
@@ -313,7 +326,11 @@ def run_sparse(args, wl, dev):
         q = W.to_numpy64(vb.q[:n])
         rs, rc = vb.row_sel.cpu().numpy(), vb.row_sel_count.cpu().numpy()
         elapsed = 0.0
+        done = 0
         for b in range(n):
+            if elapsed >= args.cpu_seconds:
+                break
+            done += 1
             k, v, table, lens = _request_copy(wl, vb, b)
             t0 = time.perf_counter()
             oracle.sparse_verify(q[b:b + 1], k, v, table, lens, rs[b:b + 1], rc[b:b + 1],
@@ -321,9 +338,9 @@ def run_sparse(args, wl, dev):
             elapsed += time.perf_counter() - t0
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        rec["cpu_baseline"] = {"value": n * n_q / elapsed, "unit": "tokens/s", "cores": threads,
-                               "kind": "oracle",
-                               "sample": f"{n} of {B} requests (all {s.Hkv} KV heads each): fp64 "
+        rec["cpu_baseline"] = {"value": done * n_q / elapsed, "unit": "tokens/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"{done} of {B} requests (all {s.Hkv} KV heads each): fp64 "
                                          f"sparse verify, {elapsed:.1f} s wall on the host"}
     else:
         rec["cpu_baseline"] = None
@@ -570,7 +587,7 @@ def main():
         rec["kv_update"] = time_kv_update(wl, kv_v, vb, dev, args.steps)
     if args.cpu_sample > 0:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample, args.cpu_seconds)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
