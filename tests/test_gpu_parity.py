@@ -158,6 +158,8 @@ TOPK_CASES = [
     # LDS), and past the LDS room for keys (read from global memory each pass)
     (2, 2, 8192, (8000, 8192), 1, 64, (410, 410), 410, 50),
     (1, 2, 20000, (19000, 20000), 1, 64, (500, 1500), 1500, 0),
+    # more than 256 units of thousands of candidates (512-thread workgroups)
+    (40, 8, 4096, (3900, 4096), 1, 64, (150, 220), 220, 30),
 ]
 
 
