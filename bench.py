@@ -522,8 +522,9 @@ def main():
     if args.path == "fused":
         # one call does the whole step: its bytes are the step's bytes
         roofline = {
-            "kernel": "sss_fused_step (fused_kernel work-list launch; plan and split-merge "
-                      "launches included in the time)",
+            "kernel": "sss_fused_step (the fused_kernel work-list launch, or for chained whole "
+                      "units the verify and select-and-draft launches; split-merge launches "
+                      "included in the time)",
             "bound": "hbm",
             "achieved": round(nbytes["total"] / (v_ms * 1e-3) / 1e9, 1),
             "peak": HBM_PEAK_GBS,
@@ -537,7 +538,8 @@ def main():
         roofline = {
             "kernel": ("attn_mfma_kernel<verify> (the one launch of sss_verify_attn when units "
                        "run unsplit)" if verify_launches == 1 else
-                       "sss_verify_attn (attention + split merge/score finalize launches)"),
+                       "sss_verify_attn (attention, plus the merge / scoring launch when units "
+                       "are split)"),
             "bound": "hbm",
             "achieved": round(v_gbs, 1),
             "peak": HBM_PEAK_GBS,
