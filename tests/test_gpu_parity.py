@@ -35,6 +35,11 @@ SMALL = [
     ("page64_blk64", "longctx_b4_l128k", dict(B=1, L=2000, sigma="one"), [0, 3]),
     ("page32_blk16", "qwen3_8b_layer_b16_l4096", dict(B=2, L=700, page_size=32, sigma="one"), [0]),
     ("page16_blk64", "qwen3_8b_layer_b16_l4096", dict(B=2, L=700, block_size=64, sigma="one"), [0, 2]),
+    ("page16_blk128", "qwen3_8b_layer_b16_l4096", dict(B=2, L=900, block_size=128, budget=3,
+                                                       sigma="one"), [0, 2]),
+    # the most query positions a verify step takes (32 x G=4 = 128 rows)
+    ("nq32", "qwen3_8b_layer_b16_l4096", dict(B=2, L=200, n_q=32, Hq=4, Hkv=1, window=16,
+                                              sigma="one"), [0, 2]),
     # page and block sizes that are not powers of two (division by multiply-high)
     ("page48_blk48", "qwen3_8b_layer_b16_l4096", dict(B=2, L=700, page_size=48, block_size=48,
                                                       sigma="one"), [0, 2]),
