@@ -20,7 +20,10 @@
  *                    recent window;
  *   sss_merge        log-sum-exp merge of split-KV partials;
  *   sss_fused_step   all of the above for a (mixed or chained) batch in one
- *                    work-list launch;
+ *                    work-list launch (or, for a chained step of whole
+ *                    units, a verify launch and a select-and-draft launch);
+ *   sss_sparse_verify_attn  verify rows over a block layout per query
+ *                    position, the union of a request's layouts loaded once;
  *   sss_kv_write     K/V of new token positions into the paged cache;
  *   sss_kv_commit    lengths after acceptance (drops rejected positions).
  *
@@ -43,6 +46,8 @@
  *   kv->max_seq_len, kv->max_pages_per_req * page_size, or falls below the
  *   entry point's minimum gets NaN in its floating outputs.
  * - Results are bitwise reproducible for equal arguments on one GPU.
+ * - Entry points only enqueue kernels (no allocation, memset or
+ *   synchronisation), so they can be captured in a HIP graph.
  * - Query head hq reads KV head hq / G with G = num_q_heads / num_kv_heads.
  * - LSE values are natural-log log-sum-exp of the scaled logits.
  */
@@ -307,7 +312,11 @@ sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_p
  * exit at once.  A unit that fits in one chunk is finished inside the
  * launch (outputs, scores, selection and, when chained, its draft).  Split
  * units are finished by follow-up launches on the same stream (merge and
- * scoring, selection, draft), which touch only those units.
+ * scoring, selection, draft), which touch only those units.  A chained step
+ * whose verify units all fit in one chunk, with no separate draft half,
+ * runs as two launches instead: the one-launch verify kernel, then one
+ * workgroup per unit that selects and drafts over the selection held in
+ * LDS.
  *
  * Requirements beyond those of the separate entry points: both halves use
  * the matrix-core path (BF16 cache, page_size a multiple of 16, block_size
