@@ -119,7 +119,27 @@ def _check(status: int, where: str):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a tensor.  The library reads plain pointers, so a
+    host or strided tensor is refused here rather than handed to a kernel."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"expected a device tensor, got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"expected a contiguous tensor (shape {tuple(t.shape)}, "
+                         f"strides {t.stride()})")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _addr(t):
+    """_ptr as a plain integer (for the step structs)."""
+    return None if t is None else _ptr(t).value
+
+
+def _i32(t, what):
+    if t is not None and t.dtype != torch.int32:
+        raise TypeError(f"{what} must be int32, got {t.dtype}")
+    return t
 
 
 def _stream():
@@ -136,6 +156,12 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 def paged_kv(k_cache, v_cache, page_table, seq_lens, max_seq_len: int) -> PagedKV:
     """Describe a paged cache [num_pages][Hkv][page_size][d] to the library."""
+    if k_cache.dtype != v_cache.dtype or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same dtype and shape")
+    _i32(page_table, "page_table")
+    _i32(seq_lens, "seq_lens")
+    for t in (k_cache, v_cache, page_table, seq_lens):
+        _ptr(t)
     return PagedKV(k=k_cache.data_ptr(), v=v_cache.data_ptr(), dtype=_dtype_code(k_cache),
                    num_pages=k_cache.shape[0], page_size=k_cache.shape[2],
                    num_kv_heads=k_cache.shape[1], head_dim=k_cache.shape[3],
@@ -245,22 +271,22 @@ def verify_step(kv: PagedKV, q, sm_scale, block_size, max_blocks, o, lse, block_
     """Verify half of a fused step (tensors as for verify_attn; with sel /
     sel_count / budget, the step also selects, as block_topk does)."""
     B, n_q, hq, _ = q.shape
-    return VerifyStep(kv=kv, q=q.data_ptr(), batch=B, n_q=n_q, num_q_heads=hq,
+    return VerifyStep(kv=kv, q=_addr(q), batch=B, n_q=n_q, num_q_heads=hq,
                       sm_scale=float(sm_scale), block_size=block_size,
-                      score_row_start=score_row_start, max_blocks=max_blocks, o=o.data_ptr(),
-                      lse=lse.data_ptr(), block_scores=block_scores.data_ptr(),
-                      budget=None if budget is None else budget.data_ptr(), window=int(window),
-                      sel=None if sel is None else sel.data_ptr(),
-                      sel_count=None if sel_count is None else sel_count.data_ptr(),
+                      score_row_start=score_row_start, max_blocks=max_blocks, o=_addr(o),
+                      lse=_addr(lse), block_scores=_addr(block_scores),
+                      budget=_addr(budget), window=int(window),
+                      sel=_addr(sel),
+                      sel_count=_addr(sel_count),
                       max_sel=0 if sel is None else sel.shape[2])
 
 
 def draft_step(kv: PagedKV, q, sm_scale, block_size, sel, sel_count, window, o, lse) -> DraftStep:
     """Draft half of a fused step (tensors as for draft_attn)."""
     B, _, hq, _ = q.shape
-    return DraftStep(kv=kv, q=q.data_ptr(), batch=B, num_q_heads=hq, sm_scale=float(sm_scale),
-                     block_size=block_size, sel=sel.data_ptr(), sel_count=sel_count.data_ptr(),
-                     max_sel=sel.shape[2], window=int(window), o=o.data_ptr(), lse=lse.data_ptr())
+    return DraftStep(kv=kv, q=_addr(q), batch=B, num_q_heads=hq, sm_scale=float(sm_scale),
+                     block_size=block_size, sel=_addr(sel), sel_count=_addr(sel_count),
+                     max_sel=sel.shape[2], window=int(window), o=_addr(o), lse=_addr(lse))
 
 
 def _byref_or_null(x, ctype):

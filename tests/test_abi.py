@@ -297,3 +297,19 @@ def test_pool_of_2_31_rows_is_unsupported():
     kv = good_kv(sss, num_pages=1 << 26, page_size=16, num_kv_heads=2)   # 2^31 rows
     assert call_verify(sss, kv) == 2
     assert b"2^31" in sss.raw().sss_last_error()
+
+
+def test_binding_refuses_host_and_strided_tensors():
+    """The library reads plain device pointers: the binding refuses host
+    tensors, strided views and wrong index dtypes before any call."""
+    import torch
+    sss = _binding()
+    k = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16)
+    table = torch.zeros((1, 4), dtype=torch.int32)
+    lens = torch.ones((1,), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sss.paged_kv(k, k, table, lens, 64)                      # host memory
+    with pytest.raises(TypeError):
+        sss.paged_kv(k, k, table.long(), lens, 64)                # int64 page table
+    with pytest.raises(ValueError):
+        sss._ptr(torch.zeros((4, 4))[:, ::2])
