@@ -136,6 +136,27 @@ def _addr(t):
     return None if t is None else _ptr(t).value
 
 
+_TORCH_DTYPE = {SSS_F32: torch.float32, SSS_BF16: torch.bfloat16}
+
+
+def _expect(t, shape, what, dtype=None):
+    """Buffer sizes cannot be checked by the library (plain pointers): a
+    tensor of another shape would be read or written out of bounds."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what}: dtype {t.dtype}, expected {dtype}")
+
+
+def _requests(kv, B, what):
+    """The batch of a call may not exceed the requests kv describes."""
+    n = getattr(kv, "_batch", None)
+    if n is not None and B > n:
+        raise ValueError(f"{what}: batch {B} exceeds the {n} requests of the paged cache")
+
+
 def _i32(t, what):
     if t is not None and t.dtype != torch.int32:
         raise TypeError(f"{what} must be int32, got {t.dtype}")
@@ -162,11 +183,15 @@ def paged_kv(k_cache, v_cache, page_table, seq_lens, max_seq_len: int) -> PagedK
     _i32(seq_lens, "seq_lens")
     for t in (k_cache, v_cache, page_table, seq_lens):
         _ptr(t)
-    return PagedKV(k=k_cache.data_ptr(), v=v_cache.data_ptr(), dtype=_dtype_code(k_cache),
-                   num_pages=k_cache.shape[0], page_size=k_cache.shape[2],
-                   num_kv_heads=k_cache.shape[1], head_dim=k_cache.shape[3],
-                   max_pages_per_req=page_table.shape[1], page_table=page_table.data_ptr(),
-                   seq_lens=seq_lens.data_ptr(), max_seq_len=int(max_seq_len))
+    if page_table.dim() != 2 or tuple(seq_lens.shape) != (page_table.shape[0],):
+        raise ValueError("page_table must be [batch][max_pages] and seq_lens [batch]")
+    kv = PagedKV(k=k_cache.data_ptr(), v=v_cache.data_ptr(), dtype=_dtype_code(k_cache),
+                 num_pages=k_cache.shape[0], page_size=k_cache.shape[2],
+                 num_kv_heads=k_cache.shape[1], head_dim=k_cache.shape[3],
+                 max_pages_per_req=page_table.shape[1], page_table=page_table.data_ptr(),
+                 seq_lens=seq_lens.data_ptr(), max_seq_len=int(max_seq_len))
+    kv._batch = int(page_table.shape[0])
+    return kv
 
 
 def verify_workspace_size(kv: PagedKV, batch, n_q, num_q_heads, block_size, max_blocks,
@@ -205,6 +230,11 @@ def verify_attn(kv: PagedKV, q, sm_scale, block_size, max_blocks, o, lse, block_
     """sss_verify_attn on tensors: q/o [B][n_q][Hq][d], lse [B][n_q][Hq],
     block_scores [B][Hkv][max_blocks]."""
     B, n_q, hq, _ = q.shape
+    _requests(kv, B, "verify_attn")
+    _expect(q, (B, n_q, hq, kv.head_dim), "q", _TORCH_DTYPE.get(kv.dtype))
+    _expect(o, q.shape, "o", q.dtype)
+    _expect(lse, (B, n_q, hq), "lse", torch.float32)
+    _expect(block_scores, (B, kv.num_kv_heads, max_blocks), "block_scores", torch.float32)
     if ws is None:
         ws = workspace(verify_workspace_size(kv, B, n_q, hq, block_size, max_blocks, num_splits),
                        q.device)
@@ -221,6 +251,12 @@ def sparse_verify_attn(kv: PagedKV, q, sm_scale, block_size, row_sel, row_sel_co
     row_sel [B][Hkv][n_q][max_sel], row_sel_count [B][Hkv][n_q]."""
     B, n_q, hq, _ = q.shape
     max_sel = row_sel.shape[3]
+    _requests(kv, B, "sparse_verify_attn")
+    _expect(q, (B, n_q, hq, kv.head_dim), "q", _TORCH_DTYPE.get(kv.dtype))
+    _expect(o, q.shape, "o", q.dtype)
+    _expect(lse, (B, n_q, hq), "lse", torch.float32)
+    _expect(row_sel, (B, kv.num_kv_heads, n_q, max_sel), "row_sel", torch.int32)
+    _expect(row_sel_count, (B, kv.num_kv_heads, n_q), "row_sel_count", torch.int32)
     if ws is None:
         ws = workspace(sparse_verify_workspace_size(kv, B, n_q, hq, block_size, max_sel, window,
                                                     num_splits), q.device)
@@ -235,6 +271,11 @@ def sparse_verify_attn(kv: PagedKV, q, sm_scale, block_size, row_sel, row_sel_co
 def block_topk(block_scores, seq_lens, block_size, budget, window, sel, sel_count):
     """sss_block_topk: sel [B][Hkv][max_sel], sel_count [B][Hkv]."""
     B, hkv, max_blocks = block_scores.shape
+    _expect(block_scores, (B, hkv, max_blocks), "block_scores", torch.float32)
+    _expect(seq_lens, (B,), "seq_lens", torch.int32)
+    _expect(budget, (B,), "budget", torch.int32)
+    _expect(sel, (B, hkv, sel.shape[2]), "sel", torch.int32)
+    _expect(sel_count, (B, hkv), "sel_count", torch.int32)
     _check(_lib.sss_block_topk(_ptr(block_scores), B, hkv, max_blocks, _ptr(seq_lens), block_size,
                                _ptr(budget), window, _ptr(sel), _ptr(sel_count), sel.shape[2],
                                _stream()),
@@ -247,6 +288,12 @@ def draft_attn(kv: PagedKV, q, sm_scale, block_size, sel, sel_count, window, o, 
     """sss_draft_attn: q/o [B][1][Hq][d], lse [B][1][Hq]."""
     B, _, hq, _ = q.shape
     max_sel = sel.shape[2]
+    _requests(kv, B, "draft_attn")
+    _expect(q, (B, 1, hq, kv.head_dim), "q", _TORCH_DTYPE.get(kv.dtype))
+    _expect(o, q.shape, "o", q.dtype)
+    _expect(lse, (B, 1, hq), "lse", torch.float32)
+    _expect(sel, (B, kv.num_kv_heads, max_sel), "sel", torch.int32)
+    _expect(sel_count, (B, kv.num_kv_heads), "sel_count", torch.int32)
     if ws is None:
         ws = workspace(draft_workspace_size(kv, B, hq, block_size, max_sel, window, num_splits),
                        q.device)
@@ -260,6 +307,10 @@ def draft_attn(kv: PagedKV, q, sm_scale, block_size, sel, sel_count, window, o, 
 def merge(o_parts, lse_parts, o, lse=None):
     """sss_merge: o_parts [S][rows][d] fp32, lse_parts [S][rows] -> o [rows][d]."""
     S, rows, d = o_parts.shape
+    _expect(o_parts, (S, rows, d), "o_parts", torch.float32)
+    _expect(lse_parts, (S, rows), "lse_parts", torch.float32)
+    _expect(o, (rows, d), "o")
+    _expect(lse, (rows,), "lse", torch.float32)
     _check(_lib.sss_merge(_ptr(o_parts), _ptr(lse_parts), S, rows, d, _ptr(o), _dtype_code(o),
                           _ptr(lse), _stream()),
            "sss_merge")
@@ -271,6 +322,15 @@ def verify_step(kv: PagedKV, q, sm_scale, block_size, max_blocks, o, lse, block_
     """Verify half of a fused step (tensors as for verify_attn; with sel /
     sel_count / budget, the step also selects, as block_topk does)."""
     B, n_q, hq, _ = q.shape
+    _requests(kv, B, "verify_step")
+    _expect(q, (B, n_q, hq, kv.head_dim), "q", _TORCH_DTYPE.get(kv.dtype))
+    _expect(o, q.shape, "o", q.dtype)
+    _expect(lse, (B, n_q, hq), "lse", torch.float32)
+    _expect(block_scores, (B, kv.num_kv_heads, max_blocks), "block_scores", torch.float32)
+    _expect(budget, (B,), "budget", torch.int32)
+    if sel is not None:
+        _expect(sel, (B, kv.num_kv_heads, sel.shape[2]), "sel", torch.int32)
+    _expect(sel_count, (B, kv.num_kv_heads), "sel_count", torch.int32)
     return VerifyStep(kv=kv, q=_addr(q), batch=B, n_q=n_q, num_q_heads=hq,
                       sm_scale=float(sm_scale), block_size=block_size,
                       score_row_start=score_row_start, max_blocks=max_blocks, o=_addr(o),
@@ -284,6 +344,12 @@ def verify_step(kv: PagedKV, q, sm_scale, block_size, max_blocks, o, lse, block_
 def draft_step(kv: PagedKV, q, sm_scale, block_size, sel, sel_count, window, o, lse) -> DraftStep:
     """Draft half of a fused step (tensors as for draft_attn)."""
     B, _, hq, _ = q.shape
+    _requests(kv, B, "draft_step")
+    _expect(q, (B, 1, hq, kv.head_dim), "q", _TORCH_DTYPE.get(kv.dtype))
+    _expect(o, q.shape, "o", q.dtype)
+    _expect(lse, (B, 1, hq), "lse", torch.float32)
+    _expect(sel, (B, kv.num_kv_heads, sel.shape[2]), "sel", torch.int32)
+    _expect(sel_count, (B, kv.num_kv_heads), "sel_count", torch.int32)
     return DraftStep(kv=kv, q=_addr(q), batch=B, num_q_heads=hq, sm_scale=float(sm_scale),
                      block_size=block_size, sel=_addr(sel), sel_count=_addr(sel_count),
                      max_sel=sel.shape[2], window=int(window), o=_addr(o), lse=_addr(lse))
@@ -316,6 +382,10 @@ def kv_write(kv: PagedKV, k_new, v_new, pos0):
     """sss_kv_write: rows k_new / v_new [B][n_new][Hkv][d] to positions
     pos0[b] + i of the paged cache kv describes (the cache is written)."""
     B, n_new = k_new.shape[0], k_new.shape[1]
+    _requests(kv, B, "kv_write")
+    _expect(k_new, (B, n_new, kv.num_kv_heads, kv.head_dim), "k_new", _TORCH_DTYPE.get(kv.dtype))
+    _expect(v_new, k_new.shape, "v_new", k_new.dtype)
+    _expect(pos0, (B,), "pos0", torch.int32)
     _check(_lib.sss_kv_write(ctypes.byref(kv), _ptr(k_new), _ptr(v_new), B, n_new, _ptr(pos0),
                              _stream()),
            "sss_kv_write")
@@ -325,6 +395,9 @@ def kv_commit(seq_lens, keep, n_q, out=None):
     """sss_kv_commit: lengths after keeping keep[b] of the last n_q positions
     (in place when out is None)."""
     out = seq_lens if out is None else out
+    _expect(seq_lens, (seq_lens.shape[0],), "seq_lens", torch.int32)
+    _expect(keep, seq_lens.shape, "keep", torch.int32)
+    _expect(out, seq_lens.shape, "out", torch.int32)
     _check(_lib.sss_kv_commit(_ptr(seq_lens), _ptr(keep), seq_lens.shape[0], int(n_q), _ptr(out),
                               _stream()),
            "sss_kv_commit")

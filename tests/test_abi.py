@@ -313,3 +313,32 @@ def test_binding_refuses_host_and_strided_tensors():
         sss.paged_kv(k, k, table.long(), lens, 64)                # int64 page table
     with pytest.raises(ValueError):
         sss._ptr(torch.zeros((4, 4))[:, ::2])
+
+
+def test_binding_checks_shapes_against_the_cache():
+    """Sizes cannot be checked below the C ABI (plain pointers): the binding
+    compares every buffer with the cache description before any call."""
+    import torch
+    sss = _binding()
+    kv = good_kv(sss)                                   # bf16, Hkv 2, d 128
+    kv._batch = 2
+    q = torch.zeros((2, 5, 8, 128), dtype=torch.bfloat16)
+    lse = torch.zeros((2, 5, 8))
+    sc = torch.zeros((2, 2, 8))
+    with pytest.raises(ValueError):                     # head_dim 64 against 128
+        sss.verify_attn(kv, q[..., :64].contiguous(), 0.1, 16, 8, q[..., :64].contiguous(), lse, sc)
+    with pytest.raises(TypeError):                      # fp32 queries on a bf16 cache
+        sss.verify_attn(kv, q.float(), 0.1, 16, 8, q.float(), lse, sc)
+    with pytest.raises(ValueError):                     # more requests than the table holds
+        q3 = torch.zeros((3, 5, 8, 128), dtype=torch.bfloat16)
+        sss.verify_attn(kv, q3, 0.1, 16, 8, q3, torch.zeros((3, 5, 8)), torch.zeros((3, 2, 8)))
+    with pytest.raises(ValueError):                     # block scores too short
+        sss.verify_attn(kv, q, 0.1, 16, 8, q, lse, sc[..., :4].contiguous())
+    sel = torch.zeros((2, 2, 4), dtype=torch.int32)
+    with pytest.raises(ValueError):                     # sel_count of another shape
+        sss.block_topk(sc, torch.ones(2, dtype=torch.int32), 16,
+                       torch.ones(2, dtype=torch.int32), 0, sel, torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError):                     # new rows of another head count
+        sss.kv_write(kv, torch.zeros((2, 5, 4, 128), dtype=torch.bfloat16),
+                     torch.zeros((2, 5, 4, 128), dtype=torch.bfloat16),
+                     torch.zeros(2, dtype=torch.int32))
