@@ -59,11 +59,11 @@ __host__ __device__ constexpr int tile_buffers(int nwr, int nwt) {
 }
 
 // LDS bytes attn_item<D, NWR, NWT, *> uses from the start of its LDS area:
-// K/V tiles (or the token-group merge scratch, which reuses them), Q tiles,
-// row LSEs.
-__host__ __device__ constexpr size_t item_lds_bytes(int D, int nwr, int nwt) {
+// K/V tiles (or the token-group merge scratch, which reuses them), Q tiles
+// (none when the Q operand is held in registers: QREG), row LSEs.
+__host__ __device__ constexpr size_t item_lds_bytes(int D, int nwr, int nwt, bool qreg = false) {
   return (size_t)tile_buffers(nwr, nwt) * ((size_t)32 * (D * 2 + 16) + (size_t)D * 64) +
-         (size_t)nwr * 32 * (D * 2 + 16) + 128 * 4;
+         (qreg ? (size_t)0 : (size_t)nwr * 32 * (D * 2 + 16)) + 128 * 4;
 }
 
 // What attn_item left behind.
@@ -503,8 +503,11 @@ constexpr float kRescaleSlack = 8.f;
 // TOKENS: blocks of one token.  A draft then gathers its tiles token by
 // token from a list (one row tile only); a verify stores each token's logit
 // as its log mass.
+// QREG: the Q operand is held in registers (staged once through the first
+// tile buffer, before any tile is stored) instead of LDS, for block-level
+// verify of one row tile; it frees the Q tile's LDS.
 template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS = false,
-          bool SPARSE = false>
+          bool SPARSE = false, bool QREG = false>
 __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   static_assert(!SPARSE || (!DRAFT && !ELL_LDS && !TOKENS), "sparse verify is its own mode");
   constexpr bool GATHER = DRAFT && TOKENS;
@@ -532,7 +535,10 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   // buffer per token group, reused by every tile
   constexpr bool DB = tile_buffers(NWR, NWT) == 2 && NWT == 1;
   constexpr int NBUF = tile_buffers(NWR, NWT);
-  float* lse2s = reinterpret_cast<float*>(smem + NBUF * G::GROUP_BYTES + NWR * G::Q_BYTES);
+  static_assert(!QREG || (NWR == 1 && !DRAFT && !TOKENS && !SPARSE),
+                "Q in registers: block-level verify of one row tile only");
+  float* lse2s =
+      reinterpret_cast<float*>(smem + NBUF * G::GROUP_BYTES + (QREG ? 0 : NWR * G::Q_BYTES));
 
   const int L = p.seq_lens[b];
   const int minL = DRAFT ? 1 : p.n_q;
@@ -653,8 +659,9 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
     }
   }
 
-  // ---- Q rows of each row tile -> LDS (the Q^T operand is read from there) ----
-  char* qtile = smem + NBUF * G::GROUP_BYTES + rt * G::Q_BYTES;
+  // ---- Q rows of each row tile -> LDS (the Q^T operand is read from there,
+  // or, with QREG, staged in the first tile buffer and read into registers) ----
+  char* qtile = QREG ? smem : smem + NBUF * G::GROUP_BYTES + rt * G::Q_BYTES;
   if (tg == 0) {
 #pragma unroll
     for (int j = 0; j < (32 * G::CPT) / 64; ++j) {
@@ -680,6 +687,14 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
     }
   }
   __syncthreads();
+  bf16x8 qreg[QREG ? G::KS : 1];
+  if constexpr (QREG) {
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks)
+      qreg[ks] = *reinterpret_cast<const bf16x8*>(qtile + rl * G::K_STRIDE + 32 * ks + 16 * hl);
+    // every wave holds its Q before token group 0 stores its first tile there
+    __syncthreads();
+  }
   const int pos_r = DRAFT ? (L - 1) : (L - p.n_q + iq);
   const int pos_min = DRAFT ? (L - 1) : (L - p.n_q);  // smallest causal limit of the unit's rows
   // |scale| (log2 domain), kept positive so that a masked -inf logit times
@@ -780,7 +795,8 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
         const bf16x8 ka =
             *reinterpret_cast<const bf16x8*>(gt + rl * G::K_STRIDE + 32 * ks + 16 * hl);
         const bf16x8 qb =
-            *reinterpret_cast<const bf16x8*>(qtile + rl * G::K_STRIDE + 32 * ks + 16 * hl);
+            QREG ? qreg[QREG ? ks : 0]
+                 : *reinterpret_cast<const bf16x8*>(qtile + rl * G::K_STRIDE + 32 * ks + 16 * hl);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb, sacc, 0, 0, 0);
       }
       // online softmax (log2 domain; s holds unscaled logits, masked ones

@@ -6,8 +6,11 @@
 namespace sss {
 namespace {
 
-template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS, bool SPARSE = false>
-__global__ void __launch_bounds__(64 * NWR * NWT, 2) attn_mfma_kernel(AttnParams p) {
+// QREG workgroups run at one wave per SIMD (two of them per compute unit,
+// two waves each), so their waves may use the whole register file.
+template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS, bool SPARSE = false,
+          bool QREG = false>
+__global__ void __launch_bounds__(64 * NWR * NWT, QREG ? 1 : 2) attn_mfma_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   if (p.skip_len >= 0 && p.seq_lens[(blockIdx.x / p.num_chunks) / p.num_kv_heads] <= p.skip_len)
     return;
@@ -18,29 +21,30 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2) attn_mfma_kernel(AttnParams
   it.single = p.num_chunks == 1;
   it.part_row0 = (long long)it.u * p.num_chunks * p.rows;
   // block log masses of the chunk in LDS, after the routine's own area
-  it.ell_off = (int)item_lds_bytes(D, NWR, NWT);
+  it.ell_off = (int)item_lds_bytes(D, NWR, NWT, QREG);
   it.sel_off = -1;
   it.nsel_s = 0;
   // after the tiles: a single-token draft's token list, the logit staging
   // slots of a single-token verify with several row tiles, or the union of
   // a sparse verify unit's layouts
-  it.list_off = (int)item_lds_bytes(D, NWR, NWT);
-  attn_item<D, NWR, NWT, DRAFT, ELL_LDS, TOKENS, SPARSE>(p, it, smem);
+  it.list_off = (int)item_lds_bytes(D, NWR, NWT, QREG);
+  attn_item<D, NWR, NWT, DRAFT, ELL_LDS, TOKENS, SPARSE, QREG>(p, it, smem);
 }
 
 }  // namespace
 
 // LDS bytes of one workgroup: the routine's own area (K/V tiles or the
 // token-group merge scratch, Q tiles, row LSEs) and optional block log masses.
-size_t mfma_smem_bytes(int D, int nwr, int nwt, long long ell_floats) {
-  return item_lds_bytes(D, nwr, nwt) + (size_t)ell_floats * 4;
+size_t mfma_smem_bytes(int D, int nwr, int nwt, long long ell_floats, bool qreg) {
+  return item_lds_bytes(D, nwr, nwt, qreg) + (size_t)ell_floats * 4;
 }
 
 namespace {
 
-template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS, bool SPARSE = false>
+template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS, bool SPARSE = false,
+          bool QREG = false>
 hipError_t launch_one(const AttnParams& p, size_t smem, unsigned grid, hipStream_t s) {
-  auto kern = attn_mfma_kernel<D, NWR, NWT, DRAFT, ELL_LDS, TOKENS, SPARSE>;
+  auto kern = attn_mfma_kernel<D, NWR, NWT, DRAFT, ELL_LDS, TOKENS, SPARSE, QREG>;
   // dynamic LDS above 64 KiB must be opted into; allow the whole LDS once
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -92,9 +96,33 @@ hipError_t launch_cfg(const AttnParams& p, hipStream_t s) {
 // Token groups of a one-row-tile draft workgroup.
 constexpr int kDraftNwt = 4;
 
+// An unsplit verify of one row tile whose four-token-group workgroup, with
+// the unit's block log masses in LDS, fits only once in a compute unit runs
+// as two-token-group workgroups (Q in registers) that fit twice: while one
+// workgroup is in its prologue (page-table, then first-tile round trips) or
+// epilogue (token-group merge, block scores), the other keeps loading.
+template <int D>
+bool verify_two_per_cu(const AttnParams& p) {
+  if (!p.ell_in_lds || p.block_size == 1 || ceil_div(p.rows, 32) != 1) return false;
+  return mfma_smem_bytes(D, 1, 4, p.ell_lds_floats) > kMaxLds / 2 &&
+         mfma_smem_bytes(D, 1, 2, p.ell_lds_floats, true) <= kMaxLds / 2;
+}
+
+template <int D>
+hipError_t launch_verify_two_per_cu(const AttnParams& p, hipStream_t s) {
+  const unsigned grid = (unsigned)((long long)p.batch * p.num_kv_heads * p.num_chunks);
+  if (grid == 0) return hipSuccess;
+  return launch_one<D, 1, 2, false, true, false, false, true>(
+      p, mfma_smem_bytes(D, 1, 2, p.ell_lds_floats, true), grid, s);
+}
+
 template <bool DRAFT>
 hipError_t dispatch(const AttnParams& p, hipStream_t s) {
   const int nwr = ceil_div(p.rows, 32);
+  if (!DRAFT) {
+    if (p.head_dim == 128 && verify_two_per_cu<128>(p)) return launch_verify_two_per_cu<128>(p, s);
+    if (p.head_dim == 64 && verify_two_per_cu<64>(p)) return launch_verify_two_per_cu<64>(p, s);
+  }
   if (p.head_dim == 128) {
     switch (nwr) {
       case 1: return launch_cfg<128, 1, DRAFT ? kDraftNwt : 4, DRAFT>(p, s);

@@ -23,7 +23,7 @@ constexpr int kSeg = 16;  // tokens per segment of the matrix-core path
 constexpr size_t kMaxLds = 159 * 1024;
 
 // LDS bytes of one matrix-core workgroup (attn_mfma.hip).
-size_t mfma_smem_bytes(int head_dim, int nwr, int nwt, long long ell_floats);
+size_t mfma_smem_bytes(int head_dim, int nwr, int nwt, long long ell_floats, bool qreg = false);
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
