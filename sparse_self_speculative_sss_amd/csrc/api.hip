@@ -8,7 +8,7 @@
 #include "sss_common.h"
 
 namespace sss {
-int mfma_token_groups(int rows, bool draft);  // attn_mfma.hip
+int mfma_token_groups(int rows, bool draft, long long units);  // attn_mfma.hip
 }
 
 namespace {
@@ -144,7 +144,7 @@ sss_status plan_verify(const sss_paged_kv* kv, int batch, int n_q, int hq, int b
   pl.mfma = use_mfma_verify(kv, block_size);
   pl.rows = n_q * G;
   const long long units = (long long)batch * kv->num_kv_heads;
-  const int nwt = pl.mfma ? mfma_token_groups(pl.rows, false) : 1;
+  const int nwt = pl.mfma ? mfma_token_groups(pl.rows, false, units) : 1;
   const int nwr = ceil_div(pl.rows, 32);
   const long long align =
       pl.mfma ? lcm_ll((long long)nwt * 32, (long long)nwt * block_size) : (long long)block_size;
@@ -195,7 +195,7 @@ sss_status plan_draft(const sss_paged_kv* kv, int batch, int hq, int block_size,
   pl.mfma = use_mfma_draft(kv, block_size, G);
   pl.rows = G;
   const long long units = (long long)batch * kv->num_kv_heads;
-  const int nwt = pl.mfma ? mfma_token_groups(G, true) : 1;
+  const int nwt = pl.mfma ? mfma_token_groups(G, true, units) : 1;
   const int nwr = ceil_div(G, 32);
   const long long Lmax = kv->max_seq_len;
   const long long wtok = window > 0 ? (window < Lmax ? window : Lmax) : 0;
@@ -274,7 +274,7 @@ sss_status plan_sparse(const sss_paged_kv* kv, int batch, int n_q, int hq, int b
   pl.mfma = true;
   pl.rows = n_q * G;
   const int nwr = ceil_div(pl.rows, 32);
-  const int nwt = mfma_token_groups(pl.rows, false);
+  const int nwt = mfma_token_groups(pl.rows, false, 0);
   const int max_blocks = ceil_div(kv->max_seq_len, block_size);
   if (mfma_smem_bytes(kv->head_dim, nwr, nwt, 0) + sparse_union_lds_bytes(max_blocks, n_q, max_sel) >
           kMaxLds ||

@@ -93,8 +93,15 @@ hipError_t launch_cfg(const AttnParams& p, hipStream_t s) {
   }
 }
 
-// Token groups of a one-row-tile draft workgroup.
+// Token groups of a one-row-tile draft workgroup: four, or one when the
+// units alone fill the GPU with four waves per compute unit -- every
+// one-wave workgroup is then resident from the start, with no workgroup
+// round and no token-group merge (batch 128 x 8 heads, 30-segment lists on
+// MI355X: 61 us with four token groups, 52 us with one; deeper register
+// prefetch in the one-wave form does not help).
 constexpr int kDraftNwt = 4;
+constexpr long long kDraftOneWaveUnits = 1024;
+int draft_token_groups(long long units) { return units >= kDraftOneWaveUnits ? 1 : kDraftNwt; }
 
 // An unsplit verify of one row tile whose four-token-group workgroup, with
 // the unit's block log masses in LDS, fits only once in a compute unit runs
@@ -122,6 +129,9 @@ hipError_t dispatch(const AttnParams& p, hipStream_t s) {
   if (!DRAFT) {
     if (p.head_dim == 128 && verify_two_per_cu<128>(p)) return launch_verify_two_per_cu<128>(p, s);
     if (p.head_dim == 64 && verify_two_per_cu<64>(p)) return launch_verify_two_per_cu<64>(p, s);
+  } else if (nwr == 1 && draft_token_groups((long long)p.batch * p.num_kv_heads) == 1) {
+    if (p.head_dim == 128) return launch_cfg<128, 1, 1, true>(p, s);
+    if (p.head_dim == 64) return launch_cfg<64, 1, 1, true>(p, s);
   }
   if (p.head_dim == 128) {
     switch (nwr) {
@@ -143,10 +153,11 @@ hipError_t dispatch(const AttnParams& p, hipStream_t s) {
 
 }  // namespace
 
-// Token groups per workgroup for a given row count (must match dispatch).
-int mfma_token_groups(int rows, bool draft) {
+// Token groups per workgroup for a given row count and unit count (must
+// match dispatch).
+int mfma_token_groups(int rows, bool draft, long long units) {
   const int nwr = ceil_div(rows, 32);
-  return (draft && nwr == 1) ? kDraftNwt : token_groups_for(nwr);
+  return (draft && nwr == 1) ? draft_token_groups(units) : token_groups_for(nwr);
 }
 
 hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s) { return dispatch<false>(p, s); }

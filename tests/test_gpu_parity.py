@@ -65,6 +65,14 @@ SMALL = [
                                                         block_size=1, sigma="one"), [0, 2]),
     ("tok_blk1_rows128", "qwen3_8b_layer_b16_l4096", dict(B=1, L=400, Hq=32, Hkv=1, n_q=4,
                                                           block_size=1), [0, 2]),
+    # unsplit one-row-tile verify whose block masses make a four-token-group
+    # workgroup too large to fit twice per compute unit: two-token-group
+    # workgroups with Q in registers (num_splits=1 keeps the units whole)
+    ("two_per_cu", "decode_b128_l8192", dict(B=3, L=1500), [1, 0]),
+    ("two_per_cu_ragged", "qwen3_8b_layer_b16_l4096", dict(B=3, L=1333, sigma="one"), [1]),
+    # 1024 (request, KV head) units: one-wave draft workgroups
+    ("units1024", "decode_b128_l8192", dict(B=128, L=96, sigma="one"), [0]),
+    ("units1024_blk1", "tokensel_b128_l8192", dict(B=128, L=80, sigma="one"), [0]),
 ]
 
 
