@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--kv-update", action="store_true",
                     help="also time sss_kv_write (the k+1 speculative positions of every "
                          "request) and sss_kv_commit, outside the timed step")
+    ap.add_argument("--cold-mib", type=int, default=1024,
+                    help="after the timed steps, time each step again after filling a scratch "
+                         "buffer of this many MiB (evicts the KV lines from L2 and the 256 MB "
+                         "Infinity Cache; reported as 'cold', 0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run device copies of this size (calibrates HBM byte counters "
                          "against a transfer of known size) and exit")
@@ -514,6 +518,27 @@ def main():
     torch.cuda.synchronize()
     t_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in sev]))
     d_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in sev]))
+    # cold pass (untimed for the headline): each step after a scratch fill
+    cold = None
+    if args.cold_mib > 0:
+        scratch = torch.empty(args.cold_mib << 20, dtype=torch.uint8, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            scratch.fill_(i & 255)
+            cev[i][0].record()
+            step()
+            cev[i][1].record()
+        torch.cuda.synchronize()
+        ct = np.array([e[0].elapsed_time(e[1]) for e in cev])
+        c_med = float(np.median(ct))
+        cold = {"flush_mib": args.cold_mib,
+                "ms_per_step_median": round(c_med, 4),
+                "ms_per_step_p10": round(float(np.percentile(ct, 10)), 4),
+                "ms_per_step_p90": round(float(np.percentile(ct, 90)), 4),
+                "GB/s": round(nbytes["total"] / (c_med * 1e-3) / 1e9, 1),
+                "frac": round(nbytes["total"] / (c_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "timing": "events around each step; the fill runs before the first event"}
+        del scratch
     tokens = Bv * n_q + Bd
     value = tokens / (ms_step / 1e3)
 
@@ -585,6 +610,7 @@ def main():
                            if Bd and args.path == "separate" else None),
         },
     }
+    rec["cold"] = cold
     if args.kv_update and Bv:
         rec["kv_update"] = time_kv_update(wl, kv_v, vb, dev, args.steps)
     if args.cpu_sample > 0:
