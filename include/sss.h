@@ -325,8 +325,15 @@ sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_p
  * SSS_ERR_UNSUPPORTED.  workspace: at least sss_fused_workspace_size()
  * bytes (0 when no unit can be split: NULL is then allowed), 256-byte
  * aligned, contents irrelevant on entry.  Results equal the separate entry
- * points' up to the rounding of split merges (bitwise for requests that
- * run unsplit in both).
+ * points' up to fp32 summation order: both run the same attention routine,
+ * but a unit may be split into a different number of token groups or
+ * chunks (the separate verify runs whole one-row-tile units as two token
+ * groups when that lets two workgroups share a compute unit, the separate
+ * draft runs one wave per unit when there are 1024 or more units), which
+ * changes the rounding.  A chained step whose verify units all fit in one
+ * chunk uses the separate verify kernel itself, so its verify outputs,
+ * scores and selection are bitwise those of sss_verify_attn followed by
+ * sss_block_topk.
  */
 typedef struct {
   sss_paged_kv kv;
