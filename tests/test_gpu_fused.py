@@ -95,12 +95,14 @@ def test_fused_chained(case):
         f"fused {cid} draft")
 
 
-def test_fused_chained_matches_separate_calls():
-    """Unsplit units run the same routine as the one-launch-per-stage path:
-    verify outputs, scores and selection are bitwise equal.  (A batch of
-    1024 units keeps every unit in one chunk; smaller batches are split to
-    fill the GPU.)"""
-    wl = mk("decode_b128_l8192", seed=32, B=128, L=512)
+@pytest.mark.parametrize("L", [512, 1500])
+def test_fused_chained_matches_separate_calls(L):
+    """A chained step of whole units runs the one-launch-per-stage verify
+    kernel itself: verify outputs, scores and selection are bitwise equal.
+    (A batch of 1024 units keeps every unit in one chunk; smaller batches are
+    split to fill the GPU.  At 1500 tokens the block masses make the verify
+    run as two-token-group workgroups, two per compute unit.)"""
+    wl = mk("decode_b128_l8192", seed=32, B=128, L=L)
     vb = wl.verify
     v_out, (sel, cnt), _ = run_chained(wl)
     o, lse, sc = H.gpu_verify(wl, vb, num_splits=1)
