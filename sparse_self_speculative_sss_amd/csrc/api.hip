@@ -166,12 +166,20 @@ sss_status plan_verify(const sss_paged_kv* kv, int batch, int n_q, int hq, int b
   if (chunk > (1LL << 30)) return fail(SSS_ERR_UNSUPPORTED, "chunk too large");
   pl.chunk = (int)chunk;
   pl.num_chunks = (int)((Lmax + chunk - 1) / chunk);
-  // unsplit units keep their block log masses in LDS when they fit; split
-  // units store them to the workspace (LDS room for them would cost
-  // resident workgroups)
+  // block log masses in LDS: an unsplit unit's when they fit; a split
+  // chunk's (one row tile) when two-token-group workgroups holding Q in
+  // registers still fit twice per compute unit -- the chunk then copies them
+  // to the workspace in one burst at its end instead of storing each block's
+  // as it completes between the KV loads (16 requests x 4K tokens in 4
+  // chunks: verify + merge 0.078 -> 0.074 ms).  Otherwise they go to the
+  // workspace block by block.
   pl.ell_lds_floats = (long long)ceil_div(pl.chunk, block_size) * pl.rows;
-  pl.ell_in_lds = pl.mfma && pl.num_chunks == 1 && block_size != 1 &&
-                  mfma_smem_bytes(kv->head_dim, nwr, nwt, pl.ell_lds_floats) <= kMaxLds;
+  pl.ell_in_lds =
+      pl.mfma && block_size != 1 &&
+      (pl.num_chunks == 1
+           ? mfma_smem_bytes(kv->head_dim, nwr, nwt, pl.ell_lds_floats) <= kMaxLds
+           : (nwr == 1 &&
+              mfma_smem_bytes(kv->head_dim, 1, 2, pl.ell_lds_floats, true) <= kMaxLds / 2));
   const bool ell_global = !pl.ell_in_lds || pl.num_chunks > 1;
   layout(pl, units, kv->head_dim, ell_global ? units * (long long)max_blocks * pl.rows : 0);
   return ok();

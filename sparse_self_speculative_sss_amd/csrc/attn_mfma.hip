@@ -103,11 +103,12 @@ constexpr int kDraftNwt = 4;
 constexpr long long kDraftOneWaveUnits = 1024;
 int draft_token_groups(long long units) { return units >= kDraftOneWaveUnits ? 1 : kDraftNwt; }
 
-// An unsplit verify of one row tile whose four-token-group workgroup, with
-// the unit's block log masses in LDS, fits only once in a compute unit runs
-// as two-token-group workgroups (Q in registers) that fit twice: while one
-// workgroup is in its prologue (page-table, then first-tile round trips) or
-// epilogue (token-group merge, block scores), the other keeps loading.
+// A verify of one row tile whose four-token-group workgroup, with the
+// block log masses of its unit (or chunk) in LDS, does not fit twice in a
+// compute unit runs as two-token-group workgroups (Q in registers) that do:
+// while one workgroup is in its prologue (page-table, then first-tile round
+// trips) or epilogue (token-group merge, block scores), the other keeps
+// loading.
 template <int D>
 bool verify_two_per_cu(const AttnParams& p) {
   if (!p.ell_in_lds || p.block_size == 1 || ceil_div(p.rows, 32) != 1) return false;

@@ -70,6 +70,10 @@ SMALL = [
     # workgroups with Q in registers (num_splits=1 keeps the units whole)
     ("two_per_cu", "decode_b128_l8192", dict(B=3, L=1500), [1, 0]),
     ("two_per_cu_ragged", "qwen3_8b_layer_b16_l4096", dict(B=3, L=1333, sigma="one"), [1]),
+    # split chunks keeping their block masses in LDS (copied out in one burst
+    # for the merge): two-token-group workgroups for chunks of 1536 and 1024
+    # tokens (ragged last chunk), four token groups for smaller chunks
+    ("split_lds_masses", "decode_b128_l8192", dict(B=2, L=3000), [2, 3, 8]),
     # 1024 (request, KV head) units: one-wave draft workgroups
     ("units1024", "decode_b128_l8192", dict(B=128, L=96, sigma="one"), [0]),
     ("units1024_blk1", "tokensel_b128_l8192", dict(B=128, L=80, sigma="one"), [0]),
