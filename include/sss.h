@@ -316,7 +316,8 @@ sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_p
  * whose verify units all fit in one chunk, with no separate draft half,
  * runs as two launches instead: the one-launch verify kernel, then one
  * workgroup per unit that selects and drafts over the selection held in
- * LDS.
+ * LDS -- or, with 1024 or more units, as the verify, Top-N and draft
+ * kernels of the separate entry points (one-wave draft workgroups).
  *
  * Requirements beyond those of the separate entry points: both halves use
  * the matrix-core path (BF16 cache, page_size a multiple of 16, block_size
@@ -333,7 +334,8 @@ sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_p
  * changes the rounding.  A chained step whose verify units all fit in one
  * chunk uses the separate verify kernel itself, so its verify outputs,
  * scores and selection are bitwise those of sss_verify_attn followed by
- * sss_block_topk.
+ * sss_block_topk (and, with 1024 or more units, its draft bitwise that of
+ * sss_draft_attn over that selection).
  */
 typedef struct {
   sss_paged_kv kv;

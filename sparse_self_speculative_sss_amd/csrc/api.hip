@@ -357,6 +357,10 @@ struct FusedSetup {
   // chained step of whole units run as two launches: the unsplit verify
   // kernel (block masses in LDS), then selection + draft per unit
   bool two_launch = false;
+  // with many units the two-launch form's second launch is split in two:
+  // the Top-N kernel, then the draft kernel (one wave per unit) over
+  // chain_draft
+  bool select_then_draft_launches = false;
   Plan vplan = {};
 };
 
@@ -488,6 +492,15 @@ sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int ch
       if (select_draft_lds(fs.head_dim, v->max_sel, v->max_blocks, a, b) <= kMaxLds) {
         fs.two_launch = true;
         fs.vplan = vp;
+        // units enough for one-wave drafts: the Top-N kernel and the draft
+        // kernel beat one select-and-draft workgroup per unit (batch 128 x 8
+        // heads, 8K tokens on MI355X: 12.5 + 46.5 us against 75 us)
+        if (mfma_token_groups(fs.group_d, true, fs.nv) == 1) {
+          sss_status st = plan_draft(&d->kv, d->batch, d->num_q_heads, d->block_size, d->max_sel,
+                                     d->window, 0, fs.chain_draft);
+          if (st != SSS_OK) return st;
+          fs.select_then_draft_launches = true;
+        }
       }
     }
   }
@@ -1000,6 +1013,24 @@ sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* d
     p.ell_lds_floats = (int32_t)vp.ell_lds_floats;
     hipError_t e = launch_verify_mfma(p, s);
     if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step verify launch: %s", hipGetErrorString(e));
+    if (fs.select_then_draft_launches) {
+      e = launch_topk(v->block_scores, v->batch, v->kv.num_kv_heads, v->max_blocks, v->kv.seq_lens,
+                      v->block_size, v->budget, v->window, v->sel, v->sel_count, v->max_sel, -1, s);
+      if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step topk launch: %s", hipGetErrorString(e));
+      const Plan& cp = fs.chain_draft;
+      AttnParams q = pd;
+      q.num_chunks = cp.num_chunks;
+      q.chunk_tokens = 0;
+      q.chunk_items = cp.chunk;
+      q.o_part = reinterpret_cast<float*>(ws + fs.chain_off + cp.opart_off);
+      q.lse_part = reinterpret_cast<float*>(ws + fs.chain_off + cp.lpart_off);
+      q.skip_len = -1;
+      e = launch_draft_mfma(q, s);
+      if (e == hipSuccess && cp.num_chunks > 1)
+        e = launch_finalize(finalize_of(q, SSS_BF16, true, cp.num_chunks, cp.chunk, -1), s);
+      if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step draft launch: %s", hipGetErrorString(e));
+      return ok();
+    }
     select_draft_lds(fs.head_dim, f.max_sel, v->max_blocks, f.off_sel, f.off_ell);
     e = launch_select_draft(f, pv, pd, fs.head_dim, s);
     if (e != hipSuccess)

@@ -73,6 +73,8 @@ CHAINED = [
     ("page64_blk64_rows80", "longctx_b4_l128k", dict(B=1, L=2000, sigma="one")),
     ("rows40", "qwen3_8b_layer_b16_l4096", dict(B=2, L=333, Hq=16, Hkv=2, sigma="one")),
     ("rows128", "qwen3_8b_layer_b16_l4096", dict(B=1, L=400, Hq=32, Hkv=1, n_q=4)),
+    # 1024 units of whole verify units: verify, Top-N and one-wave draft launches
+    ("units1024", "decode_b128_l8192", dict(B=128, L=200, sigma="one")),
 ]
 
 
@@ -104,7 +106,7 @@ def test_fused_chained_matches_separate_calls(L):
     run as two-token-group workgroups, two per compute unit.)"""
     wl = mk("decode_b128_l8192", seed=32, B=128, L=L)
     vb = wl.verify
-    v_out, (sel, cnt), _ = run_chained(wl)
+    v_out, (sel, cnt), d_out = run_chained(wl)
     o, lse, sc = H.gpu_verify(wl, vb, num_splits=1)
     sel2, cnt2 = H.gpu_topk(wl, vb, sc)
     torch.cuda.synchronize()
@@ -112,6 +114,11 @@ def test_fused_chained_matches_separate_calls(L):
     assert torch.equal(v_out[1], lse)
     assert torch.equal(v_out[2], sc)
     assert torch.equal(sel, sel2) and torch.equal(cnt, cnt2)
+    # 1024 units: the step drafts with the separate draft kernel itself
+    od, lsed = H.gpu_draft(wl, wl.draft, sel2, cnt2)
+    torch.cuda.synchronize()
+    assert torch.equal(d_out[0].view(torch.uint8), od.view(torch.uint8))
+    assert torch.equal(d_out[1], lsed)
 
 
 def test_fused_score_row_start_one():
