@@ -42,6 +42,8 @@ __global__ void __launch_bounds__(kThreads) attn_simple_kernel(AttnParams p) {
   __shared__ float qs[128];
   __shared__ float ps[kThreads];
   __shared__ int ts[kThreads];
+  __shared__ long long rows_s[kThreads];   // K/V row offset of each entry's token
+  __shared__ float ored[kThreads];         // per-group partial O, reduced at the end
   __shared__ float red[kThreads / 64];
   __shared__ float carry;
   __shared__ int bad_flag;
@@ -133,8 +135,13 @@ __global__ void __launch_bounds__(kThreads) attn_simple_kernel(AttnParams p) {
   const float lse2 = l > 0.f ? m + flog2(l) : neg_inf();
   const float frame = l > 0.f ? lse2 : 0.f;
 
-  // pass 2: O and block masses in the fixed frame
-  float oacc = 0.f;  // thread d < D owns O[d]
+  // pass 2: O and block masses in the fixed frame.  Each thread resolves its
+  // own entry's token (weight and cache row) once; then the workgroup splits
+  // into kThreads / D groups, group g accumulating O over entries g, g + NG,
+  // ... with thread d owning O[d] (several loads in flight per thread)
+  const int NG = kThreads / D;  // D is 64 or 128
+  const int og = threadIdx.x / D, od = threadIdx.x % D;
+  float oacc = 0.f;
   if (threadIdx.x == 0) carry = 0.f;
   for (int base = k_lo; base < k_hi; base += kThreads) {
     const int k = base + threadIdx.x;
@@ -142,13 +149,21 @@ __global__ void __launch_bounds__(kThreads) attn_simple_kernel(AttnParams p) {
     __syncthreads();
     ps[threadIdx.x] = t >= 0 ? fexp2(logit(t) - frame) : 0.f;
     ts[threadIdx.x] = t;
+    rows_s[threadIdx.x] = t >= 0 ? row_of(t) : 0;
     __syncthreads();
     const int n_here = min(kThreads, k_hi - base);
-    if (threadIdx.x < D) {
-      for (int i = 0; i < n_here; ++i) {
-        const int ti = ts[i];
-        if (ti >= 0) oacc += ps[i] * to_f32(vc[row_of(ti) + threadIdx.x]);
+    {
+      int i = og;
+      for (; i + 3 * NG < n_here; i += 4 * NG) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = to_f32(vc[rows_s[i + e * NG] + od]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (ts[i + e * NG] >= 0) oacc += ps[i + e * NG] * x[e];
       }
+      for (; i < n_here; i += NG)
+        if (ts[i] >= 0) oacc += ps[i] * to_f32(vc[rows_s[i] + od]);
     }
     if (!DRAFT) {
       // verify: the entries base..base+n_here-1 are consecutive tokens and
@@ -179,7 +194,12 @@ __global__ void __launch_bounds__(kThreads) attn_simple_kernel(AttnParams p) {
       }
     }
   }
+  // combine the groups' partial O (group 0's threads own the result)
   __syncthreads();
+  ored[threadIdx.x] = oacc;
+  __syncthreads();
+  if (og == 0)
+    for (int g = 1; g < NG; ++g) oacc += ored[g * D + od];
   const bool bad = bad_flag != 0;
   // oacc was accumulated with the normalised weights exp2(s - lse2)
   const float poison = bad ? qnan() : 1.f;
