@@ -48,8 +48,9 @@ def parse():
     ap.add_argument("--path", choices=("auto", "separate", "fused"), default="auto",
                     help="separate: one call per stage (verify, top-N, draft); fused: "
                          "sss_fused_step (one work-list launch, plus merge launches for "
-                         "split units); auto: fused for mixed batches, separate otherwise "
-                         "(the faster of the two on each benchmark workload)")
+                         "split units); auto: fused for mixed batches and for few "
+                         "one-row-tile units, separate otherwise (the faster of the two on "
+                         "each benchmark workload)")
     ap.add_argument("--kv-update", action="store_true",
                     help="also time sss_kv_write (the k+1 speculative positions of every "
                          "request) and sss_kv_commit, outside the timed step")
@@ -423,7 +424,18 @@ def main():
     vb, db = wl.verify, wl.draft
     shared = s.p_verify is None      # draft reads the selection this step's verify made
     if args.path == "auto":
-        args.path = "separate" if shared else "fused"
+        # the faster path on MI355X: the fused step for mixed batches and for
+        # steps of few one-row-tile units on the matrix-core path (16
+        # requests x 4K: 0.088 against 0.096 ms); the per-stage calls with
+        # 1024 or more units (one-wave drafts; level or faster: 0.749 against
+        # 0.764 ms at batch 128 x 8K), several row tiles per unit (80-row
+        # long context: 0.199 against 0.201 ms), or the vector-ALU and
+        # single-token paths, which the fused step does not take
+        units = s.B * s.Hkv
+        one_tile = s.n_q * (s.Hq // s.Hkv) <= 32
+        mfma = s.dtype == "bf16" and s.block_size % 16 == 0 and s.page_size % 16 == 0
+        few = units < 1024 and one_tile and mfma
+        args.path = "fused" if (not shared or few) else "separate"
     n_q = s.n_q
     Bv = vb.B if vb is not None else 0
     Bd = db.B if db is not None else 0
