@@ -257,8 +257,10 @@ __global__ void __launch_bounds__(kFinishThreads) finish_kernel(FusedParams f, A
   int ncand, n;
   topk_bounds(L, p.block_size, f.topk_window, p.max_blocks, f.budget[b], f.max_sel, ncand, n);
   if (tid == 0) f.sel_count[u] = n;
+  // the merge weights are dead: their LDS parks the selection's keys
   topk_select<kFinishThreads>(sc_out, ncand, n, f.sel + (long long)u * f.max_sel, f.max_sel,
-                              nullptr, topk_lds);
+                              nullptr, topk_lds, reinterpret_cast<uint32_t*>(wts),
+                              kFinishWeights);
 }
 
 template <int D, int NWR, int NWT>
