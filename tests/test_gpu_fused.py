@@ -245,16 +245,17 @@ def test_fused_invalid_seq_len_poisons_outputs():
 
 
 def test_fused_full_size_sampled():
-    """Both benchmark workloads in the benchmark's launch configuration, on a
-    seeded sample of units."""
-    for name in ("decode_b128_l8192", "mixed_b96_l1k_32k"):
+    """The benchmark workloads the fused step serves, in the benchmark's
+    launch configuration, on a seeded sample of units (selection bit-exact
+    against the oracle's Top-N of the step's own scores for chained steps)."""
+    for name in ("decode_b128_l8192", "mixed_b96_l1k_32k", "qwen3_8b_layer_b16_l4096"):
         wl = mk(name, seed=0)
         hkv = wl.shape.Hkv
         vb, db = wl.verify, wl.draft
         print(f"[fused full] {name}", flush=True)
         if wl.shape.p_verify is None:
             v_out, (sel, cnt), d_out = run_chained(wl)
-            sel_np, cnt_np = sel.cpu().numpy(), cnt.cpu().numpy()
+            sel_np, cnt_np = check_selection(wl, vb, v_out[2], sel, cnt)
             vo = v_out
         else:
             v_out, d_out = run_mixed(wl)
