@@ -615,6 +615,11 @@ def main():
             "algorithmic_bytes": nbytes["total"],
             "GB/s": round(unit_gbs, 1),
             "frac": round(unit_gbs / HBM_PEAK_GBS, 4),
+            # K and V alone (every verified token once, every drafted token once)
+            "kv_bytes": nbytes["verify_kv"] + nbytes["draft_kv"],
+            "kv_GB/s": round((nbytes["verify_kv"] + nbytes["draft_kv"]) / (ms_step * 1e-3) / 1e9, 1),
+            "kv_frac": round((nbytes["verify_kv"] + nbytes["draft_kv"]) / (ms_step * 1e-3) / 1e9
+                             / HBM_PEAK_GBS, 4),
             "verify_ms": round(v_ms, 4), "topk_ms": round(t_ms, 4), "draft_ms": round(d_ms, 4),
             "stage_times": "verify_ms from the timed steps; topk_ms and draft_ms from a "
                            "separate untimed pass with events between the stages",
