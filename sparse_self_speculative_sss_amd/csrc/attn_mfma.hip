@@ -1,10 +1,20 @@
 // One-item-per-workgroup launches of the matrix-core attention routine
-// (attn_item.h): workgroup blockIdx.x runs chunk blockIdx.x % num_chunks of
-// unit blockIdx.x / num_chunks.
+// (attn_item.h): workgroup blockIdx.x runs item i = xcd_item(blockIdx.x),
+// chunk i % num_chunks of unit i / num_chunks.
 #include "attn_item.h"
 
 namespace sss {
 namespace {
+
+// The dispatcher deals workgroups round-robin over the eight XCDs
+// (workgroup b runs on XCD b % 8).  When the grid is a multiple of 8, item
+// order is made XCD-contiguous: XCD x runs items [x n/8, (x+1) n/8), so its
+// units are all KV heads of a block of requests rather than one KV head of
+// every request.  Batch 128 x 8K on MI355X: verify 0.678 -> 0.671 ms, draft
+// 47.4 -> 46.5 us, bitwise-identical outputs.
+__device__ __forceinline__ unsigned xcd_item(unsigned b, unsigned n) {
+  return (n & 7u) == 0u ? (b & 7u) * (n >> 3) + (b >> 3) : b;
+}
 
 // QREG workgroups run at one wave per SIMD (two of them per compute unit,
 // two waves each), so their waves may use the whole register file.
@@ -12,11 +22,12 @@ template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS, bool S
           bool QREG = false>
 __global__ void __launch_bounds__(64 * NWR * NWT, QREG ? 1 : 2) attn_mfma_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  if (p.skip_len >= 0 && p.seq_lens[(blockIdx.x / p.num_chunks) / p.num_kv_heads] <= p.skip_len)
+  const unsigned item = xcd_item(blockIdx.x, gridDim.x);
+  if (p.skip_len >= 0 && p.seq_lens[(item / p.num_chunks) / p.num_kv_heads] <= p.skip_len)
     return;
   Item it;
-  it.u = blockIdx.x / p.num_chunks;
-  it.c = blockIdx.x % p.num_chunks;
+  it.u = item / p.num_chunks;
+  it.c = item % p.num_chunks;
   it.chunk = (DRAFT || SPARSE) ? p.chunk_items : p.chunk_tokens;
   it.single = p.num_chunks == 1;
   it.part_row0 = (long long)it.u * p.num_chunks * p.rows;
