@@ -1,5 +1,5 @@
 // One-item-per-workgroup launches of the matrix-core attention routine
-// (attn_item.h): workgroup blockIdx.x runs item i = xcd_item(blockIdx.x),
+// (attn_item.h): workgroup blockIdx.x runs item i = xcd_item(blockIdx.x, p),
 // chunk i % num_chunks of unit i / num_chunks.
 #include "attn_item.h"
 
@@ -7,22 +7,28 @@ namespace sss {
 namespace {
 
 // The dispatcher deals workgroups round-robin over the eight XCDs
-// (workgroup b runs on XCD b % 8).  When the grid is a multiple of 8, item
-// order is made XCD-contiguous: XCD x runs items [x n/8, (x+1) n/8), so its
-// units are all KV heads of a block of requests rather than one KV head of
-// every request.  Batch 128 x 8K on MI355X: verify 0.678 -> 0.671 ms, draft
-// 47.4 -> 46.5 us, bitwise-identical outputs.
-__device__ __forceinline__ unsigned xcd_item(unsigned b, unsigned n) {
-  return (n & 7u) == 0u ? (b & 7u) * (n >> 3) + (b >> 3) : b;
+// (workgroup b runs on XCD b % 8), so in unit order XCD x runs KV head
+// x mod Hkv of every request, and each request's page-table row is fetched
+// into every XCD's L2.  For unsplit units of a batch that is a multiple of
+// 8, workgroup b instead runs request 8 floor(k / Hkv) + b % 8, head
+// k % Hkv, with k = floor(b / 8): all heads of request r on XCD r % 8, the
+// requests still dealt round-robin over the XCDs, so that a batch of mixed
+// lengths stays balanced across them (contiguous blocks of requests per XCD
+// made a mixed batch of 96 requests 29% slower).  Batch 128 x 8K on
+// MI355X: verify 0.675 -> 0.666 ms, draft 48 -> 47 us, step 0.745 -> 0.738
+// ms; 256 x 4K verify 0.694 -> 0.689 ms; bitwise-identical outputs.  Split
+// grids keep unit order.
+__device__ __forceinline__ unsigned xcd_item(unsigned b, const AttnParams& p) {
+  if (p.num_chunks != 1 || (p.batch & 7) != 0) return b;
+  const unsigned H = (unsigned)p.num_kv_heads, k = b >> 3;
+  return ((b & 7u) + 8u * (k / H)) * H + k % H;
 }
 
-// QREG workgroups run at one wave per SIMD (two of them per compute unit,
-// two waves each), so their waves may use the whole register file.
 template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS, bool SPARSE = false,
           bool QREG = false>
 __global__ void __launch_bounds__(64 * NWR * NWT, QREG ? 1 : 2) attn_mfma_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const unsigned item = xcd_item(blockIdx.x, gridDim.x);
+  const unsigned item = xcd_item(blockIdx.x, p);
   if (p.skip_len >= 0 && p.seq_lens[(item / p.num_chunks) / p.num_kv_heads] <= p.skip_len)
     return;
   Item it;
