@@ -106,6 +106,14 @@ __global__ void __launch_bounds__(64 * NWR * NWT, 2)
     kind = kVerifyKind;
     c = f.maxch_v - 1 - (int)(blockIdx.x / f.nv_units);
     u = blockIdx.x % f.nv_units;
+    // within a layer of slots, all KV heads of request r on XCD r % 8 (slot
+    // b runs on XCD b % 8) with the requests dealt round-robin, as in the
+    // one-item kernels, when the verify batch is a multiple of 8 (16
+    // requests x 4K, interleaved A/B: 0.0891 -> 0.0882 ms per step)
+    if ((pv.batch & 7) == 0 && (f.nv_units & 7) == 0) {
+      const int H = pv.num_kv_heads, k = u >> 3;
+      u = ((u & 7) + 8 * (k / H)) * H + k % H;
+    }
     if (c >= verify_chunks(pv, u, f.chunk_v)) return;
   } else {
     kind = kDraftKind;
