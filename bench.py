@@ -30,6 +30,66 @@ sys.path.insert(0, ROOT)
 METRIC = "verify+draft attn tokens/s and KV HBM GB/s (% of MI355X peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0
 
+# hipEventCreateWithFlags flag: the record skips the system-scope release
+# fence (an L2 writeback and invalidate) that a default HIP event performs.
+# These events only time work on the stream; their times are read after a
+# device synchronisation, which fences by itself.
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class TimingEvent:
+    """A HIP timing event without the system fence, recorded on torch's
+    current stream (the stream the library launches on).  Used like a
+    timing torch.cuda.Event: record(), then elapsed_time(end) in ms once
+    both are complete."""
+
+    _hip = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            # the HIP runtime torch already loaded (one runtime per process)
+            with open("/proc/self/maps") as f:
+                paths = {ln.split()[-1] for ln in f if "libamdhip64.so" in ln}
+            if len(paths) != 1:
+                raise RuntimeError(f"expected one loaded HIP runtime, found {sorted(paths)}")
+            lib = ctypes.CDLL(paths.pop())
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = (ctypes, lib)
+        return cls._hip
+
+    def __init__(self):
+        import torch
+        torch.cuda.init()
+        ct, lib = self._runtime()
+        self._ct, self._lib = ct, lib
+        self._ev = ct.c_void_p()
+        rc = lib.hipEventCreateWithFlags(ct.byref(self._ev), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        import torch
+        rc = self._lib.hipEventRecord(self._ev, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        ms = self._ct.c_float()
+        rc = self._lib.hipEventElapsedTime(self._ct.byref(ms), self._ev, end._ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "_ev", None) and self._ev.value:
+            self._lib.hipEventDestroy(self._ev)
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -261,7 +321,7 @@ def run_sparse(args, wl, dev):
         step()
     torch.cuda.synchronize()
     nb = sparse_bytes(wl)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -290,7 +350,7 @@ def run_sparse(args, wl, dev):
 
     for _ in range(2):
         ungrouped()
-    eu = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    eu = [TimingEvent() for _ in range(2)]
     eu[0].record()
     for _ in range(args.steps):
         ungrouped()
@@ -370,7 +430,7 @@ def time_kv_update(wl, kv, vb, dev, steps):
     v_new = wl.v_cache[pages, :, t % P].contiguous()
     keep = torch.full((B,), n_q, dtype=torch.int32, device=dev)
     out = torch.empty_like(lens)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev = [TimingEvent() for _ in range(3)]
     for _ in range(3):
         sss.kv_write(kv, k_new, v_new, pos0)
         sss.kv_commit(lens, keep, n_q, out)
@@ -478,8 +538,8 @@ def main():
 
     # ev: events [before, after the verify (or fused) call, after Top-N,
     # after the draft]; the timed steps record only the first two (each
-    # timing event costs a few microseconds of GPU time), a separate pass
-    # records all four for the stage breakdown
+    # record is a barrier on the stream), a separate pass records all four
+    # for the stage breakdown
     def step(ev=None, stages=False):
         if args.path == "fused":
             if ev is not None:
@@ -514,7 +574,7 @@ def main():
     nbytes = algorithmic_bytes(wl, sel_d.cpu().numpy() if Bd else None,
                                cnt_d.cpu().numpy() if Bd else None)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -524,7 +584,7 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     v_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     # stage breakdown (untimed pass)
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    sev = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(sev[i], stages=True)
     torch.cuda.synchronize()
@@ -534,7 +594,7 @@ def main():
     cold = None
     if args.cold_mib > 0:
         scratch = torch.empty(args.cold_mib << 20, dtype=torch.uint8, device=dev)
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        cev = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
         for i in range(args.steps):
             scratch.fill_(i & 255)
             cev[i][0].record()
