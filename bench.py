@@ -87,6 +87,10 @@ class TimingEvent:
         return float(ms.value)
 
     def __del__(self):
+        # at interpreter exit the runtime may already be torn down; the
+        # process end releases the event then
+        if sys.is_finalizing():
+            return
         if getattr(self, "_ev", None) and self._ev.value:
             self._lib.hipEventDestroy(self._ev)
 
