@@ -544,12 +544,14 @@ def main():
     # after the draft]; the timed steps record only the first two (each
     # record is a barrier on the stream), a separate pass records all four
     # for the stage breakdown
-    def step(ev=None, stages=False):
+    def step(ev=None, stages=False, chain=False):
         if args.path == "fused":
             if ev is not None:
                 ev[0].record()
             sss.fused_step(v_step, d_step, chained=shared, ws=ws_f)
-            if ev is not None:
+            # chain: the next step's first event (or the one after the
+            # loop) closes this one
+            if ev is not None and not chain:
                 ev[1].record()
                 if stages:
                     ev[2].record()
@@ -578,11 +580,20 @@ def main():
     nbytes = algorithmic_bytes(wl, sel_d.cpu().numpy() if Bd else None,
                                cnt_d.cpu().numpy() if Bd else None)
 
-    evs = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
+    chain = args.path == "fused"
+    if chain:
+        # the fused call is the whole step: consecutive steps share their
+        # boundary event, one record per step
+        marks = [TimingEvent() for _ in range(args.steps + 1)]
+        evs = [[marks[i], marks[i + 1]] for i in range(args.steps)]
+    else:
+        evs = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], chain=chain)
+    if chain:
+        marks[-1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
