@@ -152,6 +152,34 @@ size_t sss_verify_workspace_size(const sss_paged_kv* kv, int32_t batch, int32_t 
                                  int32_t num_q_heads, int32_t block_size, int32_t max_blocks,
                                  int32_t num_splits);
 
+/* Bytes of the library's static device scratch (per GPU). */
+#define SSS_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * sss_verify_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and host
+ * checks as sss_verify_attn (the same kernels and plan run, so outputs are
+ * bitwise equal); the split partials and block log masses live in a static
+ * device array of SSS_NOALLOC_SCRATCH_BYTES (32 MiB) that every GPU the
+ * library runs on holds until the process ends.
+ *
+ * Nothing is allocated: no hipMalloc / hipFree, no allocating library call.
+ * The first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress, with the device current) and keeps its address.
+ * Arguments whose workspace (sss_verify_workspace_size) exceeds
+ * SSS_NOALLOC_SCRATCH_BYTES return SSS_ERR_WORKSPACE_TOO_SMALL and launch
+ * nothing.  The scratch holds the last call's contents; nothing in it needs
+ * to start at zero.  All calls on one GPU share the one array: calls that
+ * overlap on that GPU (other streams, other host threads) race and give
+ * wrong results -- serialise them.
+ */
+sss_status sss_verify_attn_noalloc(const sss_paged_kv* kv, const void* q, int32_t batch,
+                                   int32_t n_q, int32_t num_q_heads, float sm_scale,
+                                   int32_t block_size, int32_t score_row_start, int32_t num_splits,
+                                   void* o, float* lse, float* block_scores, int32_t max_blocks,
+                                   void* stream);
+
 /*
  * Top-N block selection (SparseSpec §4.1: Top-K over the aggregated scores).
  *

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "sss_common.h"
 
@@ -601,12 +602,16 @@ size_t sss_draft_workspace_size(const sss_paged_kv* kv, int32_t batch, int32_t n
   return pl.bytes;
 }
 
-sss_status sss_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch, int32_t n_q,
-                           int32_t num_q_heads, float sm_scale, int32_t block_size,
-                           int32_t score_row_start, int32_t num_splits, void* o, float* lse,
-                           float* block_scores, int32_t max_blocks, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  Plan pl;
+}  // extern "C"
+
+namespace {
+
+// Host checks of sss_verify_attn's arguments other than the workspace;
+// fills the plan.  SSS_OK with batch == 0 means there is nothing to do.
+sss_status verify_checks(const sss_paged_kv* kv, const void* q, int32_t batch, int32_t n_q,
+                         int32_t num_q_heads, float sm_scale, int32_t block_size,
+                         int32_t score_row_start, int32_t num_splits, void* o, float* lse,
+                         float* block_scores, int32_t max_blocks, Plan& pl) {
   sss_status st = plan_verify(kv, batch, n_q, num_q_heads, block_size, max_blocks, num_splits, pl);
   if (st != SSS_OK) return st;
   if (!std::isfinite(sm_scale)) return fail(SSS_ERR_INVALID_ARGUMENT, "sm_scale is not finite");
@@ -619,12 +624,15 @@ sss_status sss_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
     return fail(SSS_ERR_INVALID_ARGUMENT, "q and o must be 16-byte aligned");
   if (!aligned(lse, 4) || !aligned(block_scores, 4))
     return fail(SSS_ERR_INVALID_ARGUMENT, "lse and block_scores must be 4-byte aligned");
-  if (workspace_bytes < pl.bytes)
-    return fail(SSS_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace_bytes,
-                pl.bytes);
-  if (pl.bytes > 0 && (!workspace || !aligned(workspace, 256)))
-    return fail(SSS_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+  return ok();
+}
 
+// The launches of a verify call whose arguments passed verify_checks, with
+// a workspace of at least pl.bytes bytes.
+sss_status verify_launch(const sss_paged_kv* kv, const void* q, int32_t batch, int32_t n_q,
+                         int32_t num_q_heads, float sm_scale, int32_t block_size,
+                         int32_t score_row_start, void* o, float* lse, float* block_scores,
+                         int32_t max_blocks, void* workspace, const Plan& pl, void* stream) {
   char* ws = static_cast<char*>(workspace);
   AttnParams p = base_params(kv, q, batch, n_q, num_q_heads, sm_scale, pl);
   p.chunk_tokens = pl.chunk;
@@ -674,6 +682,85 @@ sss_status sss_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch,
   e = launch_finalize(f, s);
   if (e != hipSuccess) return fail(SSS_ERR_HIP, "verify finalize launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+
+// ---- allocation-free verify: the workspace is a static device array ----
+
+// Scratch of sss_verify_attn_noalloc.  In host code `scratch` names a
+// host-side shadow, not device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device (each GPU holds its own
+// copy), kept per device below.
+static __device__ __align__(256) char scratch[SSS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept until the process ends.
+sss_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SSS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SSS_ERR_UNSUPPORTED, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(SSS_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return SSS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sss_status sss_verify_attn(const sss_paged_kv* kv, const void* q, int32_t batch, int32_t n_q,
+                           int32_t num_q_heads, float sm_scale, int32_t block_size,
+                           int32_t score_row_start, int32_t num_splits, void* o, float* lse,
+                           float* block_scores, int32_t max_blocks, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  Plan pl;
+  sss_status st = verify_checks(kv, q, batch, n_q, num_q_heads, sm_scale, block_size,
+                                score_row_start, num_splits, o, lse, block_scores, max_blocks, pl);
+  if (st != SSS_OK || batch == 0) return st;
+  if (workspace_bytes < pl.bytes)
+    return fail(SSS_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace_bytes,
+                pl.bytes);
+  if (pl.bytes > 0 && (!workspace || !aligned(workspace, 256)))
+    return fail(SSS_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+  return verify_launch(kv, q, batch, n_q, num_q_heads, sm_scale, block_size, score_row_start, o,
+                       lse, block_scores, max_blocks, workspace, pl, stream);
+}
+
+sss_status sss_verify_attn_noalloc(const sss_paged_kv* kv, const void* q, int32_t batch,
+                                   int32_t n_q, int32_t num_q_heads, float sm_scale,
+                                   int32_t block_size, int32_t score_row_start, int32_t num_splits,
+                                   void* o, float* lse, float* block_scores, int32_t max_blocks,
+                                   void* stream) {
+  Plan pl;
+  sss_status st = verify_checks(kv, q, batch, n_q, num_q_heads, sm_scale, block_size,
+                                score_row_start, num_splits, o, lse, block_scores, max_blocks, pl);
+  if (st != SSS_OK || batch == 0) return st;
+  if (pl.bytes > (size_t)SSS_NOALLOC_SCRATCH_BYTES)
+    return fail(SSS_ERR_WORKSPACE_TOO_SMALL,
+                "these arguments need %zu bytes of scratch; sss_verify_attn_noalloc has %zu "
+                "(call sss_verify_attn with a workspace, or pass fewer splits or requests)",
+                pl.bytes, (size_t)SSS_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (pl.bytes > 0) {
+    st = scratch_of_current_device(&ws);
+    if (st != SSS_OK) return st;
+  }
+  return verify_launch(kv, q, batch, n_q, num_q_heads, sm_scale, block_size, score_row_start, o,
+                       lse, block_scores, max_blocks, ws, pl, stream);
 }
 
 sss_status sss_block_topk(const float* block_scores, int32_t batch, int32_t num_kv_heads,

@@ -20,6 +20,8 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 SSS_OK, SSS_ERR_INVALID_ARGUMENT, SSS_ERR_UNSUPPORTED, SSS_ERR_WORKSPACE_TOO_SMALL, SSS_ERR_HIP = range(5)
 SSS_F32, SSS_BF16 = 0, 1
+# size of the static device scratch of sss_verify_attn_noalloc (SSS_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _c_int = ctypes.c_int32
 _vp = ctypes.c_void_p
@@ -42,6 +44,10 @@ _lib.sss_verify_attn.argtypes = [ctypes.POINTER(PagedKV), _vp, _c_int, _c_int, _
 _lib.sss_verify_workspace_size.restype = ctypes.c_size_t
 _lib.sss_verify_workspace_size.argtypes = [ctypes.POINTER(PagedKV), _c_int, _c_int, _c_int,
                                            _c_int, _c_int, _c_int]
+_lib.sss_verify_attn_noalloc.restype = _c_int
+_lib.sss_verify_attn_noalloc.argtypes = [ctypes.POINTER(PagedKV), _vp, _c_int, _c_int, _c_int,
+                                         ctypes.c_float, _c_int, _c_int, _c_int, _vp, _fp, _fp,
+                                         _c_int, _vp]
 _lib.sss_block_topk.restype = _c_int
 _lib.sss_block_topk.argtypes = [_fp, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp, _vp,
                                 _c_int, _vp]
@@ -99,8 +105,8 @@ _lib.sss_last_error.argtypes = []
 _lib.sss_version.restype = _c_int
 _lib.sss_version.argtypes = []
 
-EXPORTED = ["sss_verify_attn", "sss_verify_workspace_size", "sss_block_topk", "sss_draft_attn",
-            "sss_draft_workspace_size", "sss_merge", "sss_fused_step", "sss_fused_workspace_size",
+EXPORTED = ["sss_verify_attn", "sss_verify_workspace_size", "sss_verify_attn_noalloc",
+            "sss_block_topk", "sss_draft_attn", "sss_draft_workspace_size", "sss_merge", "sss_fused_step", "sss_fused_workspace_size",
             "sss_kv_write", "sss_kv_commit", "sss_sparse_verify_attn",
             "sss_sparse_verify_workspace_size", "sss_status_string", "sss_last_error",
             "sss_version"]
@@ -242,6 +248,23 @@ def verify_attn(kv: PagedKV, q, sm_scale, block_size, max_blocks, o, lse, block_
                                 score_row_start, num_splits, _ptr(o), _ptr(lse),
                                 _ptr(block_scores), max_blocks, _ptr(ws), ws.numel(), _stream()),
            "sss_verify_attn")
+    return o, lse, block_scores
+
+
+def verify_attn_noalloc(kv: PagedKV, q, sm_scale, block_size, max_blocks, o, lse, block_scores,
+                        score_row_start=0, num_splits=0):
+    """sss_verify_attn_noalloc: verify_attn with the library's static device
+    scratch instead of a workspace (no allocation on either side)."""
+    B, n_q, hq, _ = q.shape
+    _requests(kv, B, "verify_attn_noalloc")
+    _expect(q, (B, n_q, hq, kv.head_dim), "q", _TORCH_DTYPE.get(kv.dtype))
+    _expect(o, q.shape, "o", q.dtype)
+    _expect(lse, (B, n_q, hq), "lse", torch.float32)
+    _expect(block_scores, (B, kv.num_kv_heads, max_blocks), "block_scores", torch.float32)
+    _check(_lib.sss_verify_attn_noalloc(ctypes.byref(kv), _ptr(q), B, n_q, hq, float(sm_scale),
+                                        block_size, score_row_start, num_splits, _ptr(o),
+                                        _ptr(lse), _ptr(block_scores), max_blocks, _stream()),
+           "sss_verify_attn_noalloc")
     return o, lse, block_scores
 
 

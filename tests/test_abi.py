@@ -342,3 +342,28 @@ def test_binding_checks_shapes_against_the_cache():
         sss.kv_write(kv, torch.zeros((2, 5, 4, 128), dtype=torch.bfloat16),
                      torch.zeros((2, 5, 4, 128), dtype=torch.bfloat16),
                      torch.zeros(2, dtype=torch.int32))
+
+
+def test_noalloc_verify_checks_on_the_host():
+    """sss_verify_attn_noalloc validates like sss_verify_attn and refuses,
+    before touching the device, a call whose workspace exceeds its static
+    scratch (the size the binding and the header state)."""
+    sss = _binding()
+    lib = sss.raw()
+    hdr = open(HDR).read()
+    assert re.search(r"#define SSS_NOALLOC_SCRATCH_BYTES \(\(size_t\)32 << 20\)", hdr)
+    assert sss.NOALLOC_SCRATCH_BYTES == 32 << 20
+    kv = good_kv(sss)
+    f = lib.sss_verify_attn_noalloc
+    assert f(ctypes.byref(kv), 4096, 2, 0, 8, 0.1, 16, 0, 0, 8192, 16384, 32768, 8, None) == 1
+    assert f(ctypes.byref(kv), 4096, 2, 5, 7, 0.1, 16, 0, 0, 8192, 16384, 32768, 8, None) == 1
+    assert f(ctypes.byref(good_kv(sss, head_dim=96)), 4096, 2, 5, 8, 0.1, 16, 0, 0, 8192, 16384,
+             32768, 8, None) == 2
+    assert f(ctypes.byref(kv), 4096, 0, 5, 8, 0.1, 16, 0, 0, 8192, 16384, 32768, 8, None) == 0
+    big = sss.PagedKV(k=256, v=512, dtype=sss.SSS_BF16, num_pages=16384, page_size=64,
+                      num_kv_heads=2, head_dim=128, max_pages_per_req=2048, page_table=1024,
+                      seq_lens=2048, max_seq_len=131072)
+    assert sss.verify_workspace_size(big, 8, 5, 32, 64, 2048, 64) > sss.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), 4096, 8, 5, 32, 0.088, 64, 0, 64, 8192, 16384, 32768, 2048,
+             None) == 3
+    assert b"needs" in lib.sss_last_error() or b"need" in lib.sss_last_error()
