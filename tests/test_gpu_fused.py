@@ -7,7 +7,8 @@ oracle; the selection bit-exactly against the oracle's Top-N run on the
 step's own fp32 scores; the draft against the oracle's draft over the
 step's own selection.  Mixed steps (some requests verify, the others draft
 over given selections) are checked the same way.  Small lengths force the
-work list to split units into many chunks, so the last-arrival merge runs.
+work list to split units into many chunks, so the follow-up launches that
+merge, score and select split units run.
 """
 import numpy as np
 import pytest
@@ -179,7 +180,7 @@ def test_fused_mixed(case):
 
 def test_fused_draft_only_split_lists():
     """Draft-only step with long lists: each unit's list is cut into several
-    chunks and merged by the last arriving chunk."""
+    chunks, which the follow-up merge launch combines."""
     wl = mk("qwen3_8b_layer_b16_l4096", seed=35, B=3, L=2900, sigma="one")
     db = wl.draft
     hkv = wl.shape.Hkv

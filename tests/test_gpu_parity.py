@@ -49,6 +49,13 @@ SMALL = [
      dict(B=2, L=150, page_size=8, block_size=8, Hq=8, Hkv=2, sigma="one"), [0, 2]),
     ("f32_d128", "qwen3_8b_layer_b16_l4096", dict(B=1, L=100, dtype="f32", Hq=8, Hkv=2), [0]),
     ("rows80", "longctx_b4_l128k", dict(B=1, L=3000, sigma="one"), [0, 4]),
+    # three row tiles: 96 rows, 65 rows at head dim 64 (one live row in the
+    # last tile), 80 rows with 16-token blocks
+    ("rows96", "longctx_b4_l128k", dict(B=1, L=1100, n_q=6, sigma="one"), [0, 3]),
+    ("rows65_d64", "qwen3_8b_layer_b16_l4096", dict(B=2, L=700, Hq=26, Hkv=2, d=64,
+                                                    sigma="one"), [0, 2]),
+    ("rows80_blk16", "longctx_b4_l128k", dict(B=2, L=900, block_size=16, page_size=16, budget=9,
+                                              sigma="one"), [0, 2]),
     ("rows128", "qwen3_8b_layer_b16_l4096", dict(B=1, L=400, Hq=32, Hkv=1, n_q=4), [0, 2]),
     ("rows40", "qwen3_8b_layer_b16_l4096", dict(B=2, L=333, Hq=16, Hkv=2, sigma="one"), [0, 2]),
     # single-token blocks: logits as token masses, gathered draft tiles
@@ -143,6 +150,14 @@ def test_full_size_sampled(name, n_units):
     torch.cuda.synchronize()
     units = H.sample_units(vb, hkv, n_units, seed=1)
     H.compare_verify(wl, vb, v_out, units).check(f"{name} verify")
+    # every unit's outputs were written (the harness NaN-fills them) and are
+    # finite: no row of these workloads is empty
+    o_v, lse_v = v_out[0], v_out[1]
+    assert torch.isfinite(o_v).all() and torch.isfinite(lse_v).all(), f"{name}: verify o/lse"
+    # |O| <= max |V| (a convex combination of cache rows; slack for the bf16
+    # rounding of P and of O)
+    vmax = wl.v_cache.abs().amax().float()
+    assert o_v.float().abs().max() <= vmax * (1 + 2 ** -6), f"{name}: verify |O| bound"
     # per-row mass invariant on every unit
     G = wl.shape.Hq // hkv
     tot = v_out[2].sum(-1).cpu().numpy()
@@ -158,6 +173,11 @@ def test_full_size_sampled(name, n_units):
     d_out = H.gpu_draft(wl, db, torch.from_numpy(sel).to(DEV), torch.from_numpy(cnt).to(DEV))
     torch.cuda.synchronize()
     H.compare_draft(wl, db, d_out, sel, cnt, d_units).check(f"{name} draft")
+    # every draft unit was written and is finite (a window of 64+ tokens
+    # keeps every set non-empty)
+    assert wl.shape.window > 0
+    assert torch.isfinite(d_out[0]).all() and torch.isfinite(d_out[1]).all(), f"{name}: draft"
+    assert d_out[0].float().abs().max() <= vmax * (1 + 2 ** -6), f"{name}: draft |O| bound"
 
 
 # --------------------------------------------------------------------------
@@ -261,14 +281,21 @@ def test_bitwise_determinism():
                            b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
 
 
-def test_merge_matches_oracle():
-    g = np.random.default_rng(21)
-    S, rows, d = 5, 37, 128
+# (partials, rows, head_dim): a few partials; more partials than one LDS
+# weight tile holds (1024), with rows not a multiple of the 4 rows of a
+# workgroup; a head dim that is not a multiple of 64; one row, one partial
+MERGE_CASES = [(5, 37, 128), (2500, 6, 64), (3, 10, 80), (1, 1, 128)]
+
+
+@pytest.mark.parametrize("S,rows,d", MERGE_CASES)
+def test_merge_matches_oracle(S, rows, d):
+    g = np.random.default_rng(21 + S)
     o_parts = g.normal(size=(S, rows, d)).astype(np.float32)
     lse_parts = g.normal(size=(S, rows)).astype(np.float32) * 3
-    lse_parts[1, 3] = -np.inf
-    lse_parts[:, 7] = -np.inf           # an all-empty row
-    ref_o, ref_l = oracle.merge(o_parts, lse_parts)
+    if rows > 7:
+        lse_parts[min(1, S - 1), 3] = -np.inf
+        lse_parts[:, 7] = -np.inf       # an all-empty row
+    ref_o, ref_l = oracle.merge(o_parts.astype(np.float64), lse_parts.astype(np.float64))
     for dtype, tol in ((torch.float32, 1e-5), (torch.bfloat16, 1e-2)):
         o = torch.full((rows, d), float("nan"), dtype=dtype, device=DEV)
         lse = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV)
@@ -280,7 +307,23 @@ def test_merge_matches_oracle():
         fin = np.isfinite(ref_l)
         assert np.array_equal(np.isfinite(gl), fin)
         assert np.abs(gl[fin] - ref_l[fin]).max() < 1e-5
-        assert np.all(go[7] == 0)
+        if rows > 7:
+            assert np.all(go[7] == 0)
+
+
+def test_merge_nan_partial_poisons_its_row():
+    g = np.random.default_rng(5)
+    S, rows, d = 3, 9, 128
+    o_parts = torch.from_numpy(g.normal(size=(S, rows, d)).astype(np.float32)).to(DEV)
+    lse_parts = torch.from_numpy(g.normal(size=(S, rows)).astype(np.float32)).to(DEV)
+    lse_parts[2, 4] = float("nan")
+    o = torch.zeros((rows, d), device=DEV)
+    lse = torch.zeros((rows,), device=DEV)
+    H.sss().merge(o_parts, lse_parts, o, lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[4]).all() and torch.isnan(lse[4])
+    keep = [r for r in range(rows) if r != 4]
+    assert torch.isfinite(o[keep]).all() and torch.isfinite(lse[keep]).all()
 
 
 def test_invalid_seq_len_poisons_outputs():
