@@ -125,22 +125,41 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run device copies of this size (calibrates HBM byte counters "
                          "against a transfer of known size) and exit")
+    ap.add_argument("--read-calibration-mib", type=int, default=0,
+                    help="only run the library's streaming-read probe over a buffer of this "
+                         "size (3 reads; the same 16-byte non-temporal loads as the attention "
+                         "kernels: calibrates FETCH_SIZE against a read of known size) and exit")
+    ap.add_argument("--configs", default="all",
+                    help="comma-separated workloads measured after the headline, each on its "
+                         "default path, into the 'configs' block of the JSON line "
+                         "('all': every benchmark configuration and the two extra workloads; "
+                         "'none': skip)")
+    ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
+                    help="oracle time budget of each entry of 'configs' (0 = no CPU baseline "
+                         "there)")
+    ap.add_argument("--probe-mib", type=int, default=4096,
+                    help="size of the streaming-read probe buffer for the 'achievable' block "
+                         "(0 = skip the probes)")
+    ap.add_argument("--source-hash", action="store_true",
+                    help="print the hash of the library sources (stamped into profiles/) and exit")
     return ap.parse_args()
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "verify_decode_b128_l8192_counters.json")
-KERNEL_SOURCES = ["sparse_self_speculative_sss_amd/csrc/attn_item.h",
-                  "sparse_self_speculative_sss_amd/csrc/attn_mfma.hip",
-                  "sparse_self_speculative_sss_amd/csrc/sss_common.h",
-                  "sparse_self_speculative_sss_amd/csrc/api.hip"]
+# every source the library is built from: a profile or counter summary taken
+# on another build is not quoted
+SOURCE_DIRS = ["sparse_self_speculative_sss_amd/csrc", "include"]
 
 
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for d in SOURCE_DIRS:
+        for name in sorted(os.listdir(os.path.join(ROOT, d))):
+            if name.endswith((".hip", ".h")):
+                h.update(f"{d}/{name}\n".encode())
+                with open(os.path.join(ROOT, d, name), "rb") as f:
+                    h.update(f.read())
     return h.hexdigest()
 
 
@@ -213,7 +232,6 @@ def cpu_baseline(wl, n_req, budget_s=20.0):
     seconds of oracle time are spent.  Returns query tokens/s."""
     import numpy as np
     import oracle
-    from threadpoolctl import threadpool_info
     from sparse_self_speculative_sss_amd import workload as W
     s = wl.shape
     vb, db = wl.verify, wl.draft
@@ -258,12 +276,23 @@ def cpu_baseline(wl, n_req, budget_s=20.0):
             tokens += 1
             del k, v
         nd = done
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     what = (f"{nv} of {vb.B if vb else 0} verify requests" +
             ("" if shared else f" and {nd} of {db.B if db else 0} draft requests"))
-    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": host_cores(),
+            "blas_threads": blas_threads(), "kind": "oracle",
             "sample": (f"{what} (all {s.Hkv} KV heads each): fp64 verify + block scores, Top-N "
                        f"and draft, {elapsed:.1f} s wall on the host")}
+
+
+def host_cores():
+    """Host cores this process may run on (the oracle's NumPy/BLAS calls use
+    them; its Python loops use one)."""
+    return len(os.sched_getaffinity(0))
+
+
+def blas_threads():
+    from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
 
 
 def sparse_bytes(wl):
@@ -298,9 +327,10 @@ def sparse_bytes(wl):
     return {"total": total, "kv": kv, "kv_per_position": per_pos_toks * s.d * el * 2}
 
 
-def run_sparse(args, wl, dev):
+def run_sparse(args, wl, dev, compact=False, cpu_seconds=None):
     """One step = one sss_sparse_verify_attn call over the batch (every
-    position attends to its own layout; each unit's union is loaded once)."""
+    position attends to its own layout; each unit's union is loaded once).
+    Prints the JSON line, or with compact=True returns a 'configs' entry."""
     import numpy as np
     import torch
     import oracle
@@ -334,7 +364,8 @@ def run_sparse(args, wl, dev):
         evs[i][1].record()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    k_list = [e[0].elapsed_time(e[1]) for e in evs]
+    k_ms = float(np.mean(k_list))
     gbs = nb["total"] / (k_ms * 1e-3) / 1e9
 
     # the same loads without grouping: one launch per query position, each
@@ -389,7 +420,8 @@ def run_sparse(args, wl, dev):
                      "one_launch_per_position_ms": round(u_ms, 4),
                      "speedup": round(u_ms / k_ms, 3)},
     }
-    if args.cpu_sample > 0:
+    budget = args.cpu_seconds if cpu_seconds is None else cpu_seconds
+    if args.cpu_sample > 0 and budget > 0:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         n = min(args.cpu_sample, B)
         q = W.to_numpy64(vb.q[:n])
@@ -397,7 +429,7 @@ def run_sparse(args, wl, dev):
         elapsed = 0.0
         done = 0
         for b in range(n):
-            if elapsed >= args.cpu_seconds:
+            if elapsed >= budget:
                 break
             done += 1
             k, v, table, lens = _request_copy(wl, vb, b)
@@ -405,14 +437,24 @@ def run_sparse(args, wl, dev):
             oracle.sparse_verify(q[b:b + 1], k, v, table, lens, rs[b:b + 1], rc[b:b + 1],
                                  s.block_size, s.window, wl.sm_scale)
             elapsed += time.perf_counter() - t0
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
         rec["cpu_baseline"] = {"value": done * n_q / elapsed, "unit": "tokens/s",
-                               "cores": threads, "kind": "oracle",
+                               "cores": host_cores(), "blas_threads": blas_threads(),
+                               "kind": "oracle",
                                "sample": f"{done} of {B} requests (all {s.Hkv} KV heads each): fp64 "
                                          f"sparse verify, {elapsed:.1f} s wall on the host"}
     else:
         rec["cpu_baseline"] = None
+    if compact:
+        med = float(np.median(k_list))
+        return {"workload": s.name, "path": "sparse_verify", "dtype": s.dtype,
+                "verify_requests": B, "draft_requests": 0, "query_tokens_per_step": B * n_q,
+                "ms_per_step_wall": round(ms_step, 4), "ms_per_step_median": round(med, 4),
+                "ms_per_step_p10": pct(k_list, 10), "ms_per_step_p90": pct(k_list, 90),
+                "tokens/s": round(B * n_q / (med * 1e-3), 1), "algorithmic_bytes": nb["total"],
+                "GB/s": round(nb["total"] / (med * 1e-3) / 1e9, 1),
+                "frac": round(nb["total"] / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "kv_bytes": nb["kv"], "dominant": rec["roofline"], "grouping": rec["grouping"],
+                "cpu_baseline": rec["cpu_baseline"]}
     print(json.dumps(rec), flush=True)
 
 
@@ -454,6 +496,259 @@ def time_kv_update(wl, kv, vb, dev, steps):
             "write_GB/s": round(moved / (w_ms * 1e-3) / 1e9, 1), "commit_ms": round(c_ms, 4)}
 
 
+def default_path(s):
+    """The faster path on MI355X for a workload: the fused step for mixed
+    batches and for steps of few one-row-tile units on the matrix-core path
+    (16 requests x 4K: 0.088 against 0.096 ms); the per-stage calls with
+    1024 or more units (one-wave drafts; level or faster: 0.749 against
+    0.764 ms at batch 128 x 8K), several row tiles per unit (80-row long
+    context: 0.199 against 0.201 ms), or the vector-ALU and single-token
+    paths, which the fused step does not take."""
+    shared = s.p_verify is None
+    units = s.B * s.Hkv
+    one_tile = s.n_q * (s.Hq // s.Hkv) <= 32
+    mfma = s.dtype == "bf16" and s.block_size % 16 == 0 and s.page_size % 16 == 0
+    few = units < 1024 and one_tile and mfma
+    return "fused" if (not shared or few) else "separate"
+
+
+def pct(x, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(x), q)), 4)
+
+
+def run_step_workload(args, wl, dev, path="auto", steps=20, warmup=5, cold_mib=0,
+                      verify_splits=-1, draft_splits=0):
+    """Warm-up, then `steps` timed steps of the whole path (verify, Top-N,
+    draft) with events at every step boundary and after each verify call,
+    then (untimed) a stage breakdown and, with cold_mib, each step again
+    after a scratch fill that evicts the caches.  Returns the raw results."""
+    import numpy as np
+    import torch
+    from sparse_self_speculative_sss_amd import sss
+    s = wl.shape
+    vb, db = wl.verify, wl.draft
+    shared = s.p_verify is None      # draft reads the selection this step's verify made
+    if path == "auto":
+        path = default_path(s)
+    n_q = s.n_q
+    Bv = vb.B if vb is not None else 0
+    Bd = db.B if db is not None else 0
+    vsplits = s.num_splits if verify_splits < 0 else verify_splits
+    verify_launches = 0
+    if Bv:
+        kv_v = sss.paged_kv(wl.k_cache, wl.v_cache, vb.page_table, vb.seq_lens, vb.max_seq_len)
+        o = torch.empty_like(vb.q)
+        lse = torch.empty((Bv, n_q, s.Hq), dtype=torch.float32, device=dev)
+        sc = torch.empty((Bv, s.Hkv, wl.max_blocks), dtype=torch.float32, device=dev)
+        sel = torch.empty((Bv, s.Hkv, wl.max_sel), dtype=torch.int32, device=dev)
+        cnt = torch.empty((Bv, s.Hkv), dtype=torch.int32, device=dev)
+        nws = sss.verify_workspace_size(kv_v, Bv, n_q, s.Hq, s.block_size, wl.max_blocks, vsplits)
+        ws_v = sss.workspace(nws, dev)
+        # one launch when the plan keeps every unit in one chunk: the same
+        # workspace as an explicit single split (a split plan adds partials)
+        one = sss.verify_workspace_size(kv_v, Bv, n_q, s.Hq, s.block_size, wl.max_blocks, 1)
+        verify_launches = 1 if (nws == one and s.dtype == "bf16") else 2
+    if Bd:
+        kv_d = sss.paged_kv(wl.k_cache, wl.v_cache, db.page_table, db.seq_lens, db.max_seq_len)
+        od = torch.empty_like(db.q)
+        lsed = torch.empty((Bd, 1, s.Hq), dtype=torch.float32, device=dev)
+        sel_d = sel if shared else db.sel
+        cnt_d = cnt if shared else db.sel_count
+        ws_d = sss.workspace(sss.draft_workspace_size(kv_d, Bd, s.Hq, s.block_size, wl.max_sel,
+                                                      s.window, draft_splits), dev)
+    if path == "fused":
+        v_step = d_step = None
+        if Bv:
+            v_step = sss.verify_step(kv_v, vb.q, wl.sm_scale, s.block_size, wl.max_blocks, o, lse,
+                                     sc, budget=vb.budget, window=s.window, sel=sel,
+                                     sel_count=cnt)
+        if Bd:
+            # a shared workload drafts the verify requests over this step's
+            # selection (same cache description); a mixed one its own
+            d_step = sss.draft_step(kv_v if shared else kv_d, db.q, wl.sm_scale, s.block_size,
+                                    sel_d, cnt_d, s.window, od, lsed)
+        ws_f = sss.workspace(sss.fused_workspace_size(v_step, d_step, shared), dev)
+
+    # mark: event at the start of the step; mid: after the verify call (the
+    # roofline kernel); top / end: after Top-N and the draft (stage pass only)
+    def step(mark=None, mid=None, top=None, end=None):
+        if mark is not None:
+            mark.record()
+        if path == "fused":
+            sss.fused_step(v_step, d_step, chained=shared, ws=ws_f)
+            return
+        if Bv:
+            sss.verify_attn(kv_v, vb.q, wl.sm_scale, s.block_size, wl.max_blocks, o, lse, sc,
+                            ws=ws_v, num_splits=vsplits)
+        if mid is not None:
+            mid.record()
+        if Bv:
+            sss.block_topk(sc, vb.seq_lens, s.block_size, vb.budget, s.window, sel, cnt)
+        if top is not None:
+            top.record()
+        if Bd:
+            sss.draft_attn(kv_d, db.q, wl.sm_scale, s.block_size, sel_d, cnt_d, s.window, od,
+                           lsed, ws=ws_d, num_splits=draft_splits)
+        if end is not None:
+            end.record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    nbytes = algorithmic_bytes(wl, sel_d.cpu().numpy() if Bd else None,
+                               cnt_d.cpu().numpy() if Bd else None)
+
+    # timed steps: consecutive steps share their boundary event (one record
+    # per step boundary, plus one after each verify call on the per-stage
+    # path); every record is a barrier on the stream
+    marks = [TimingEvent() for _ in range(steps + 1)]
+    mids = [TimingEvent() for _ in range(steps)] if path == "separate" else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(marks[i], mids[i] if mids else None)
+    marks[-1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
+    verify_ms = ([marks[i].elapsed_time(mids[i]) for i in range(steps)] if mids else
+                 list(step_ms))
+    # stage breakdown (untimed pass)
+    t_ms = d_ms = None
+    if path == "separate":
+        sev = [[TimingEvent() for _ in range(4)] for _ in range(steps)]
+        for i in range(steps):
+            step(*sev[i])
+        torch.cuda.synchronize()
+        t_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in sev]))
+        d_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in sev]))
+    cold = None
+    if cold_mib > 0:
+        scratch = torch.empty(cold_mib << 20, dtype=torch.uint8, device=dev)
+        cev = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            scratch.fill_(i & 255)
+            cev[i][0].record()
+            step()
+            cev[i][1].record()
+        torch.cuda.synchronize()
+        cold = [e[0].elapsed_time(e[1]) for e in cev]
+        del scratch
+    res = dict(path=path, Bv=Bv, Bd=Bd, n_q=n_q, vsplits=vsplits, draft_splits=draft_splits,
+               verify_launches=verify_launches, steps=steps, warmup=warmup,
+               ms_wall=(t1 - t0) * 1e3 / steps, step_ms=step_ms, verify_ms=verify_ms,
+               topk_ms=t_ms, draft_ms=d_ms, cold=cold, cold_mib=cold_mib, nbytes=nbytes,
+               tokens=Bv * n_q + Bd)
+    if Bv:
+        res["kv_v"] = kv_v
+    return res
+
+
+def roofline_of(res, workload):
+    """Roofline block of the dominant kernel: the verify call (one launch of
+    attn_mfma_kernel when units run unsplit), or the whole fused call."""
+    import numpy as np
+    nb = res["nbytes"]
+    v_ms = float(np.mean(res["verify_ms"]))
+    if res["path"] == "fused":
+        a = nb["total"] / (v_ms * 1e-3) / 1e9
+        return {"kernel": "sss_fused_step (its work-list launch, or for chained whole units the "
+                          "verify, Top-N and draft launches; split-merge launches included)",
+                "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes": nb["total"], "ms": round(v_ms, 4)}
+    a = nb["verify"] / (v_ms * 1e-3) / 1e9 if res["Bv"] else 0.0
+    one = res["verify_launches"] == 1
+    return {"kernel": ("attn_mfma_kernel<verify> (the one launch of sss_verify_attn: every "
+                       "unit in one chunk)" if one else
+                       "sss_verify_attn (attention launch plus the split merge / scoring launch)"),
+            "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(workload) if one else None,
+            "algorithmic_bytes": nb["verify"], "ms": round(v_ms, 4)}
+
+
+def config_record(res, wl, cpu=None):
+    """Compact per-workload record for the 'configs' block."""
+    import numpy as np
+    s = wl.shape
+    nb = res["nbytes"]
+    med = float(np.median(res["step_ms"]))
+    kv = nb["verify_kv"] + nb["draft_kv"]
+    rec = {
+        "workload": s.name, "path": res["path"], "dtype": s.dtype,
+        "verify_requests": res["Bv"], "draft_requests": res["Bd"],
+        "query_tokens_per_step": res["tokens"],
+        "ms_per_step_wall": round(res["ms_wall"], 4),
+        "ms_per_step_median": round(med, 4),
+        "ms_per_step_p10": pct(res["step_ms"], 10), "ms_per_step_p90": pct(res["step_ms"], 90),
+        "tokens/s": round(res["tokens"] / (med * 1e-3), 1),
+        "algorithmic_bytes": nb["total"],
+        "GB/s": round(nb["total"] / (med * 1e-3) / 1e9, 1),
+        "frac": round(nb["total"] / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kv_bytes": kv,
+        "kv_frac": round(kv / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "dominant": roofline_of(res, s.name),
+    }
+    if res["topk_ms"] is not None:
+        rec["topk_ms"] = round(res["topk_ms"], 4)
+        rec["draft_ms"] = round(res["draft_ms"], 4)
+    if res["cold"]:
+        c = float(np.median(res["cold"]))
+        rec["cold_ms_median"] = round(c, 4)
+        rec["cold_frac"] = round(nb["total"] / (c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
+    return rec
+
+
+def probes(dev, kv, batch, mib, reps=5):
+    """Achievable read rates from the library's probe kernels: a plain
+    streaming read of `mib` MiB, and a read of exactly the (page, head) runs
+    the verify loads (the same bytes in the permuted page order)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from sparse_self_speculative_sss_amd import sss
+    lib = sss.raw()
+    lib.sss_probe_stream_read.restype = ctypes.c_int32
+    lib.sss_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    lib.sss_probe_paged_read.restype = ctypes.c_int32
+    lib.sss_probe_paged_read.argtypes = [ctypes.POINTER(sss.PagedKV), ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    buf = torch.ones(mib << 20, dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [TimingEvent() for _ in range(reps + 1)]
+        for i in range(reps):
+            ev[i].record()
+            fn()
+        ev[-1].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+    def stream_read():
+        st = lib.sss_probe_stream_read(buf.data_ptr(), buf.numel(), sink.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError(f"sss_probe_stream_read failed ({st})")
+
+    def paged_read():
+        st = lib.sss_probe_paged_read(ctypes.byref(kv), batch, sink.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError(f"sss_probe_paged_read failed ({st})")
+
+    ts = timed(stream_read)
+    del buf
+    tp = timed(paged_read)
+    return ts, tp
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -461,6 +756,9 @@ def main():
               "(attention units shard by request and KV head with no exchange; only the one-GPU share is measured)",
               file=sys.stderr)
         sys.exit(2)
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
 
     import numpy as np
     import torch
@@ -479,189 +777,43 @@ def main():
         print(json.dumps({"copy_calibration": {"bytes_read": n * 4, "bytes_written": n * 4,
                                                "copies": 3}}), flush=True)
         return
+    if args.read_calibration_mib > 0:
+        import ctypes
+        lib = sss.raw()
+        lib.sss_probe_stream_read.restype = ctypes.c_int32
+        lib.sss_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+        n = args.read_calibration_mib << 20
+        buf = torch.ones(n, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for _ in range(3):
+            if lib.sss_probe_stream_read(buf.data_ptr(), n, sink.data_ptr(), stream) != 0:
+                raise RuntimeError("sss_probe_stream_read failed")
+        torch.cuda.synchronize()
+        print(json.dumps({"read_calibration": {"bytes_read": n, "reads": 3,
+                                               "kernel": "sss::stream_read_kernel"}}), flush=True)
+        return
     print(f"[bench] generating {args.workload} seed={args.seed}", file=sys.stderr, flush=True)
     wl = W.make(args.workload, seed=args.seed, device=dev)
     s = wl.shape
     if s.layout_shared is not None:
         run_sparse(args, wl, dev)
         return
+    res = run_step_workload(args, wl, dev, path=args.path, steps=args.steps, warmup=args.warmup,
+                            cold_mib=args.cold_mib, verify_splits=args.verify_splits,
+                            draft_splits=args.draft_splits)
     vb, db = wl.verify, wl.draft
-    shared = s.p_verify is None      # draft reads the selection this step's verify made
-    if args.path == "auto":
-        # the faster path on MI355X: the fused step for mixed batches and for
-        # steps of few one-row-tile units on the matrix-core path (16
-        # requests x 4K: 0.088 against 0.096 ms); the per-stage calls with
-        # 1024 or more units (one-wave drafts; level or faster: 0.749 against
-        # 0.764 ms at batch 128 x 8K), several row tiles per unit (80-row
-        # long context: 0.199 against 0.201 ms), or the vector-ALU and
-        # single-token paths, which the fused step does not take
-        units = s.B * s.Hkv
-        one_tile = s.n_q * (s.Hq // s.Hkv) <= 32
-        mfma = s.dtype == "bf16" and s.block_size % 16 == 0 and s.page_size % 16 == 0
-        few = units < 1024 and one_tile and mfma
-        args.path = "fused" if (not shared or few) else "separate"
-    n_q = s.n_q
-    Bv = vb.B if vb is not None else 0
-    Bd = db.B if db is not None else 0
-    vsplits = s.num_splits if args.verify_splits < 0 else args.verify_splits
-    if Bv:
-        kv_v = sss.paged_kv(wl.k_cache, wl.v_cache, vb.page_table, vb.seq_lens, vb.max_seq_len)
-        o = torch.empty_like(vb.q)
-        lse = torch.empty((Bv, n_q, s.Hq), dtype=torch.float32, device=dev)
-        sc = torch.empty((Bv, s.Hkv, wl.max_blocks), dtype=torch.float32, device=dev)
-        sel = torch.empty((Bv, s.Hkv, wl.max_sel), dtype=torch.int32, device=dev)
-        cnt = torch.empty((Bv, s.Hkv), dtype=torch.int32, device=dev)
-        ws_v = sss.workspace(sss.verify_workspace_size(kv_v, Bv, n_q, s.Hq, s.block_size,
-                                                       wl.max_blocks, vsplits), dev)
-        # the verify call is a single kernel launch when its plan leaves units unsplit
-        verify_launches = 1 if sss.verify_workspace_size(kv_v, Bv, n_q, s.Hq, s.block_size,
-                                                         wl.max_blocks, vsplits) == 0 else 2
-    else:
-        verify_launches = 0
-    if Bd:
-        kv_d = sss.paged_kv(wl.k_cache, wl.v_cache, db.page_table, db.seq_lens, db.max_seq_len)
-        od = torch.empty_like(db.q)
-        lsed = torch.empty((Bd, 1, s.Hq), dtype=torch.float32, device=dev)
-        sel_d = sel if shared else db.sel
-        cnt_d = cnt if shared else db.sel_count
-        ws_d = sss.workspace(sss.draft_workspace_size(kv_d, Bd, s.Hq, s.block_size, wl.max_sel,
-                                                      s.window, args.draft_splits), dev)
-
-    if args.path == "fused":
-        v_step = d_step = None
-        if Bv:
-            v_step = sss.verify_step(kv_v, vb.q, wl.sm_scale, s.block_size, wl.max_blocks, o, lse,
-                                     sc, budget=vb.budget, window=s.window, sel=sel,
-                                     sel_count=cnt)
-        if Bd:
-            # a shared workload drafts the verify requests over this step's
-            # selection (same cache description); a mixed one its own
-            d_step = sss.draft_step(kv_v if shared else kv_d, db.q, wl.sm_scale, s.block_size,
-                                    sel_d, cnt_d, s.window, od, lsed)
-        ws_f = sss.workspace(sss.fused_workspace_size(v_step, d_step, shared), dev)
-
-    # ev: events [before, after the verify (or fused) call, after Top-N,
-    # after the draft]; the timed steps record only the first two (each
-    # record is a barrier on the stream), a separate pass records all four
-    # for the stage breakdown
-    def step(ev=None, stages=False, chain=False):
-        if args.path == "fused":
-            if ev is not None:
-                ev[0].record()
-            sss.fused_step(v_step, d_step, chained=shared, ws=ws_f)
-            # chain: the next step's first event (or the one after the
-            # loop) closes this one
-            if ev is not None and not chain:
-                ev[1].record()
-                if stages:
-                    ev[2].record()
-                    ev[3].record()
-            return
-        if ev is not None:
-            ev[0].record()
-        if Bv:
-            sss.verify_attn(kv_v, vb.q, wl.sm_scale, s.block_size, wl.max_blocks, o, lse, sc,
-                            ws=ws_v, num_splits=vsplits)
-        if ev is not None:
-            ev[1].record()
-        if Bv:
-            sss.block_topk(sc, vb.seq_lens, s.block_size, vb.budget, s.window, sel, cnt)
-        if ev is not None and stages:
-            ev[2].record()
-        if Bd:
-            sss.draft_attn(kv_d, db.q, wl.sm_scale, s.block_size, sel_d, cnt_d, s.window, od,
-                           lsed, ws=ws_d, num_splits=args.draft_splits)
-        if ev is not None and stages:
-            ev[3].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    nbytes = algorithmic_bytes(wl, sel_d.cpu().numpy() if Bd else None,
-                               cnt_d.cpu().numpy() if Bd else None)
-
-    chain = args.path == "fused"
-    if chain:
-        # the fused call is the whole step: consecutive steps share their
-        # boundary event, one record per step
-        marks = [TimingEvent() for _ in range(args.steps + 1)]
-        evs = [[marks[i], marks[i + 1]] for i in range(args.steps)]
-    else:
-        evs = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i], chain=chain)
-    if chain:
-        marks[-1].record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    v_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    # stage breakdown (untimed pass)
-    sev = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(sev[i], stages=True)
-    torch.cuda.synchronize()
-    t_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in sev]))
-    d_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in sev]))
-    # cold pass (untimed for the headline): each step after a scratch fill
-    cold = None
-    if args.cold_mib > 0:
-        scratch = torch.empty(args.cold_mib << 20, dtype=torch.uint8, device=dev)
-        cev = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
-        for i in range(args.steps):
-            scratch.fill_(i & 255)
-            cev[i][0].record()
-            step()
-            cev[i][1].record()
-        torch.cuda.synchronize()
-        ct = np.array([e[0].elapsed_time(e[1]) for e in cev])
-        c_med = float(np.median(ct))
-        cold = {"flush_mib": args.cold_mib,
-                "ms_per_step_median": round(c_med, 4),
-                "ms_per_step_p10": round(float(np.percentile(ct, 10)), 4),
-                "ms_per_step_p90": round(float(np.percentile(ct, 90)), 4),
-                "GB/s": round(nbytes["total"] / (c_med * 1e-3) / 1e9, 1),
-                "frac": round(nbytes["total"] / (c_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "timing": "events around each step; the fill runs before the first event"}
-        del scratch
-    tokens = Bv * n_q + Bd
-    value = tokens / (ms_step / 1e3)
-
-    v_gbs = nbytes["verify"] / (v_ms * 1e-3) / 1e9 if Bv else 0.0
+    Bv, Bd, n_q = res["Bv"], res["Bd"], res["n_q"]
+    nbytes = res["nbytes"]
+    ms_step = res["ms_wall"]
+    step_ms = res["step_ms"]
+    v_ms = float(np.mean(res["verify_ms"]))
+    value = res["tokens"] / (ms_step / 1e3)
     unit_gbs = nbytes["total"] / (ms_step * 1e-3) / 1e9
-    if args.path == "fused":
-        # one call does the whole step: its bytes are the step's bytes
-        roofline = {
-            "kernel": "sss_fused_step (the fused_kernel work-list launch, or for chained whole "
-                      "units the verify and select-and-draft launches; split-merge launches "
-                      "included in the time)",
-            "bound": "hbm",
-            "achieved": round(nbytes["total"] / (v_ms * 1e-3) / 1e9, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(nbytes["total"] / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "algorithmic_bytes": nbytes["total"],
-            "ms": round(v_ms, 4),
-        }
-    else:
-        roofline = {
-            "kernel": ("attn_mfma_kernel<verify> (the one launch of sss_verify_attn when units "
-                       "run unsplit)" if verify_launches == 1 else
-                       "sss_verify_attn (attention, plus the merge / scoring launch when units "
-                       "are split)"),
-            "bound": "hbm",
-            "achieved": round(v_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(v_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(s.name) if verify_launches == 1 else None,
-            "algorithmic_bytes": nbytes["verify"],
-            "ms": round(v_ms, 4),
-        }
+    roofline = roofline_of(res, s.name)
     lens = vb.seq_lens if Bv else db.seq_lens
+    med = float(np.median(step_ms))
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -683,9 +835,18 @@ def main():
             "block": s.block_size, "page": s.page_size, "window": s.window,
             "budget_blocks": (int(vb.budget[0]) if s.budget_frac is None or s.p_verify is None
                               else f"ceil({s.budget_frac} * blocks)"),
-            "verify_splits": vsplits, "draft_splits": args.draft_splits, "path": args.path,
+            "verify_splits": res["vsplits"], "draft_splits": res["draft_splits"],
+            "path": res["path"],
         },
         "roofline": roofline,
+        "warm": {
+            "ms_per_step_median": round(med, 4),
+            "ms_per_step_p10": pct(step_ms, 10), "ms_per_step_p90": pct(step_ms, 90),
+            "verify_ms_median": round(float(np.median(res["verify_ms"])), 4),
+            "verify_ms_p10": pct(res["verify_ms"], 10), "verify_ms_p90": pct(res["verify_ms"], 90),
+            "timing": "HIP events (no system fence) at every step boundary and after each "
+                      "verify call, on the library's stream; ms_per_step is the wall-clock mean",
+        },
         "step_hbm": {
             "algorithmic_bytes": nbytes["total"],
             "GB/s": round(unit_gbs, 1),
@@ -695,21 +856,80 @@ def main():
             "kv_GB/s": round((nbytes["verify_kv"] + nbytes["draft_kv"]) / (ms_step * 1e-3) / 1e9, 1),
             "kv_frac": round((nbytes["verify_kv"] + nbytes["draft_kv"]) / (ms_step * 1e-3) / 1e9
                              / HBM_PEAK_GBS, 4),
-            "verify_ms": round(v_ms, 4), "topk_ms": round(t_ms, 4), "draft_ms": round(d_ms, 4),
+            "verify_ms": round(v_ms, 4),
+            "topk_ms": None if res["topk_ms"] is None else round(res["topk_ms"], 4),
+            "draft_ms": None if res["draft_ms"] is None else round(res["draft_ms"], 4),
             "stage_times": "verify_ms from the timed steps; topk_ms and draft_ms from a "
                            "separate untimed pass with events between the stages",
-            "draft_GB/s": (round(nbytes["draft"] / (d_ms * 1e-3) / 1e9, 1)
-                           if Bd and args.path == "separate" else None),
+            "draft_GB/s": (round(nbytes["draft"] / (res["draft_ms"] * 1e-3) / 1e9, 1)
+                           if Bd and res["draft_ms"] else None),
         },
     }
-    rec["cold"] = cold
+    if res["cold"]:
+        ct = res["cold"]
+        c_med = float(np.median(ct))
+        rec["cold"] = {"flush_mib": res["cold_mib"],
+                       "ms_per_step_median": round(c_med, 4),
+                       "ms_per_step_p10": pct(ct, 10), "ms_per_step_p90": pct(ct, 90),
+                       "GB/s": round(nbytes["total"] / (c_med * 1e-3) / 1e9, 1),
+                       "frac": round(nbytes["total"] / (c_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "timing": "events around each step; the fill runs before the first event"}
+    else:
+        rec["cold"] = None
     if args.kv_update and Bv:
-        rec["kv_update"] = time_kv_update(wl, kv_v, vb, dev, args.steps)
+        rec["kv_update"] = time_kv_update(wl, res["kv_v"], vb, dev, args.steps)
+    if args.probe_mib > 0 and Bv:
+        print("[bench] bandwidth probes", file=sys.stderr, flush=True)
+        ts, tp = probes(dev, res["kv_v"], Bv, args.probe_mib)
+        sr = (args.probe_mib << 20) / (float(np.median(ts)) * 1e-3) / 1e9
+        pr = nbytes["verify_kv"] / (float(np.median(tp)) * 1e-3) / 1e9
+        rec["achievable"] = {
+            "stream_read_GB/s": round(sr, 1), "stream_read_frac": round(sr / HBM_PEAK_GBS, 4),
+            "stream_read_bytes": args.probe_mib << 20,
+            "paged_read_GB/s": round(pr, 1), "paged_read_frac": round(pr / HBM_PEAK_GBS, 4),
+            "paged_read_bytes": nbytes["verify_kv"],
+            "verify_vs_paged_read": round(roofline["achieved"] / pr, 4) if res["path"] == "separate" else None,
+            "kernels": "sss_probe_stream_read / sss_probe_paged_read (16-byte non-temporal loads, "
+                       "nothing but reads): context for the roofline, not the peak",
+        }
     if args.cpu_sample > 0:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample, args.cpu_seconds)
     else:
         rec["cpu_baseline"] = None
+    headline = config_record(res, wl, None)
+    if rec["cpu_baseline"] is not None:
+        headline["cpu_baseline"] = rec["cpu_baseline"]
+    del wl, res
+    torch.cuda.empty_cache()
+
+    names = [] if args.configs == "none" else (
+        [n for n in W.SHAPE_ORDER] if args.configs == "all" else args.configs.split(","))
+    configs = []
+    for name in names:
+        if name == s.name:
+            configs.append(headline)
+            continue
+        print(f"[bench] config {name}", file=sys.stderr, flush=True)
+        w2 = W.make(name, seed=args.seed, device=dev)
+        if w2.shape.layout_shared is not None:
+            configs.append(run_sparse(args, w2, dev, compact=True,
+                                      cpu_seconds=args.config_cpu_seconds))
+            print(f"[bench] config {name}: {configs[-1]['ms_per_step_median']} ms",
+                  file=sys.stderr, flush=True)
+        else:
+            r2 = run_step_workload(args, w2, dev, steps=args.steps, warmup=args.warmup,
+                                   cold_mib=args.cold_mib)
+            cpu = (cpu_baseline(w2, args.cpu_sample, args.config_cpu_seconds)
+                   if args.config_cpu_seconds > 0 and args.cpu_sample > 0 else None)
+            configs.append(config_record(r2, w2, cpu))
+            print(f"[bench] config {name}: {configs[-1]['ms_per_step_median']} ms "
+                  f"({configs[-1]['frac']:.3f} of peak)", file=sys.stderr, flush=True)
+            del r2
+        del w2
+        torch.cuda.empty_cache()
+    rec["configs"] = configs
+    rec["source_sha256"] = kernel_source_hash()
     print(json.dumps(rec), flush=True)
 
 

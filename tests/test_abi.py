@@ -14,14 +14,18 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libsss.so not b
 
 
 def declared():
-    text = open(HDR).read()
+    """Every sss_* function any header in include/ declares."""
+    inc = os.path.join(ROOT, "include")
+    text = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc))
+                   if f.endswith(".h"))
     return sorted(set(re.findall(r"\b(sss_[a-z_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(LIB)
     names = declared()
-    assert {"sss_verify_attn", "sss_block_topk", "sss_draft_attn", "sss_merge"} <= set(names)
+    assert {"sss_verify_attn", "sss_block_topk", "sss_draft_attn", "sss_merge",
+            "sss_verify_attn_noalloc", "sss_probe_stream_read", "sss_probe_paged_read"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     out = os.popen(f"nm -D --defined-only {LIB}").read()
@@ -367,3 +371,23 @@ def test_noalloc_verify_checks_on_the_host():
     assert f(ctypes.byref(big), 4096, 8, 5, 32, 0.088, 64, 0, 64, 8192, 16384, 32768, 2048,
              None) == 3
     assert b"needs" in lib.sss_last_error() or b"need" in lib.sss_last_error()
+
+
+def test_probes_reject_bad_arguments():
+    sss = _binding()
+    lib = sss.raw()
+    lib.sss_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    lib.sss_probe_paged_read.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    assert lib.sss_probe_stream_read(None, 16, 256, None) == 1
+    assert lib.sss_probe_stream_read(264, 16, 256, None) == 1      # misaligned source
+    assert lib.sss_probe_stream_read(256, 17, 256, None) == 1      # not a multiple of 16 bytes
+    assert lib.sss_probe_stream_read(256, 0, 256, None) == 0       # nothing to read
+    kv = good_kv(sss)
+    assert lib.sss_probe_paged_read(ctypes.addressof(kv), -1, 256, None) == 1
+    assert lib.sss_probe_paged_read(ctypes.addressof(kv), 2, None, None) == 1
+    assert lib.sss_probe_paged_read(ctypes.addressof(good_kv(sss, dtype=7)), 2, 256, None) == 2
+    assert lib.sss_probe_paged_read(ctypes.addressof(good_kv(sss, page_size=1, head_dim=1)), 2,
+                                    256, None) == 2                 # 2-byte runs
+    assert lib.sss_probe_paged_read(ctypes.addressof(kv), 0, 256, None) == 0
