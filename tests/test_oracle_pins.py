@@ -493,6 +493,64 @@ def test_layout_union_contains_exactly_the_selected_blocks():
             assert all(t >= ws or t // 8 in picked for t in toks)
 
 
+def _union_by_mask(row_sel, row_cnt, L, bs, window):
+    """Independent construction: a boolean [positions][blocks] membership
+    matrix from torch scatter, OR-reduced over positions, restricted to the
+    blocks that start before the window start."""
+    n_q, max_sel = row_sel.shape
+    ws = L if window <= 0 else max(0, L - window)
+    nblk = -(-L // bs)
+    sel = torch.as_tensor(row_sel, dtype=torch.long)
+    cnt = torch.as_tensor(row_cnt, dtype=torch.long).clamp(0, max_sel)
+    slot_live = torch.arange(max_sel)[None, :] < cnt[:, None]          # entry within the count
+    in_range = (sel >= 0) & (sel < nblk)
+    member = torch.zeros((n_q, nblk + 1), dtype=torch.bool)
+    idx = torch.where(slot_live & in_range, sel, torch.full_like(sel, nblk))  # dead -> spare column
+    member.scatter_(1, idx, True)
+    union = member[:, :nblk].any(0) & (torch.arange(nblk) * bs < ws)
+    return torch.nonzero(union).flatten().tolist()
+
+
+def test_layout_union_equals_boolean_mask_or():
+    g = np.random.default_rng(31)
+    for trial in range(300):
+        n_q = int(g.integers(1, 9))
+        bs = int(g.choice([1, 4, 16]))
+        L = int(g.integers(1, 400))
+        window = int(g.choice([0, 1, 7, 64, 1000]))
+        max_sel = int(g.integers(1, 12))
+        nblk = -(-L // bs)
+        # entries: in range, duplicated, negative, past the request, in the window
+        row_sel = g.integers(-3, nblk + 4, (n_q, max_sel)).astype(np.int32)
+        if trial % 3 == 0:
+            row_sel[:, -1] = row_sel[:, 0]
+        row_cnt = g.integers(-2, max_sel + 3, n_q).astype(np.int32)   # clamped to [0, max_sel]
+        got = oracle.layout_union(row_sel, row_cnt, L, bs, window)
+        assert got == _union_by_mask(row_sel, row_cnt, L, bs, window), trial
+
+
+def test_layout_union_pin_rejects_planted_mistakes():
+    """A union that ignores the per-position counts, or keeps blocks inside
+    the window, differs from the mask construction on these inputs."""
+    row_sel = np.array([[2, 5, 3], [5, 8, -1]], dtype=np.int32)
+    row_cnt = np.array([2, 3], dtype=np.int32)
+    L, bs, window = 160, 16, 40          # window start 120: blocks 0..7 are candidates
+    ref = _union_by_mask(row_sel, row_cnt, L, bs, window)
+    assert ref == [2, 5]
+    assert oracle.layout_union(row_sel, row_cnt, L, bs, window) == ref
+
+    def ignore_counts(rs, rc, L_, bs_, w_):
+        ws = L_ if w_ <= 0 else max(0, L_ - w_)
+        return sorted({int(j) for j in rs.flatten() if j >= 0 and j * bs_ < ws})
+
+    def keep_window(rs, rc, L_, bs_, w_):
+        return sorted({int(j) for i in range(rs.shape[0]) for j in rs[i, :rc[i]]
+                       if 0 <= j < -(-L_ // bs_)})
+
+    assert ignore_counts(row_sel, row_cnt, L, bs, window) != ref     # picks up block 3
+    assert keep_window(row_sel, row_cnt, L, bs, window) != ref       # keeps block 8
+
+
 # --------------------------------------------------------------------------
 # merge
 # --------------------------------------------------------------------------
