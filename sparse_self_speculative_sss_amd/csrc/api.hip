@@ -1132,9 +1132,15 @@ sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* d
     // a unit's partials small enough for one workgroup: merge, score and
     // select in one launch; otherwise spread the merge, then select
     const size_t unit_partials = (size_t)fs.pl.maxch_v * fs.rows_v * fs.head_dim * 4;
+    bool drafted = false;
     if (unit_partials <= ((size_t)1 << 20)) {
-      e = launch_fused_finish(f, pv, s);
+      // a chained draft whose lists need no split runs in the finishing
+      // workgroup, right after the unit's selection
+      const bool fin_draft = chained && fs.chain_draft.num_chunks == 1 && fs.group_d <= 32;
+      const size_t lds = finish_lds(f, fs.head_dim, verify->max_blocks, fin_draft);
+      e = launch_fused_finish(f, pv, pd, fs.head_dim, lds, s);
       if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step finish launch: %s", hipGetErrorString(e));
+      drafted = fin_draft;
     } else {
       e = launch_finalize(finalize_of(pv, SSS_BF16, false, fs.pl.maxch_v, fs.pl.chunk_v,
                                       fs.pl.chunk_v), s);
@@ -1147,7 +1153,7 @@ sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* d
         if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step topk launch: %s", hipGetErrorString(e));
       }
     }
-    if (chained) {
+    if (chained && !drafted) {
       const Plan& cp = fs.chain_draft;
       AttnParams q = pd;
       q.num_chunks = cp.num_chunks;

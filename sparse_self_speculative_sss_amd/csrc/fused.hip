@@ -177,98 +177,271 @@ __global__ void __launch_bounds__(64 * kDraftWaves, 2)
                                     park ? pv.max_blocks : 0);
 }
 
-// Finishes the split verify units of a fused step, one workgroup per unit:
-// merges the chunk partials into o / lse, turns the block log masses into
-// block scores, then selects (the one-launch merge and selection kernels
-// spread this over more launches; here a unit's partials are small).
-constexpr int kFinishThreads = 1024;
-constexpr int kFinishWeights = 8192;
+// Finishes the split verify units of a fused step, one workgroup per unit
+// (eight waves, or four when it also drafts: the draft's token groups): merges the chunk partials into o / lse, turns the block
+// log masses into block scores (keys parked in LDS), selects and, with
+// f.fin_draft, drafts the unit over that selection (held in LDS).  Every
+// phase issues its loads together: the partial LSEs with one batched copy,
+// each thread's merge elements with all their partials at once, each
+// block's rows at once; the selection reads the keys from LDS instead of
+// the scores back from memory.  (One thread per output looping over
+// dependent loads, the scores re-read for the selection, and the chained
+// draft as a separate launch took 15.3 + 14.8 us for 16 requests x 8 KV
+// heads of 4K tokens in 4 chunks.)
+// waves of a finishing workgroup: eight, or four (the draft's token groups)
+// when it drafts -- the 16-request chained step took 31.6 us with an
+// eight-group draft against 25.4 us with four; the 96-request mixed batch's
+// finish 20.9 us with eight waves against 30.9 us with four
+template <bool DRAFT>
+constexpr int finish_waves() { return DRAFT ? 4 : 8; }
+constexpr int kFinishStage = 4096;  // partial LSEs staged in LDS (S * rows)
+constexpr int kFinishLoads = 16;    // 16-byte loads a thread keeps in flight
 
-__global__ void __launch_bounds__(kFinishThreads) finish_kernel(FusedParams f, AttnParams p) {
-  __shared__ float lse2[128];
-  __shared__ float wts[kFinishWeights];
-  __shared__ int topk_lds[kTopkLdsWords];
+__host__ __device__ constexpr int fin_off_stage_host() {
+  return 512 + (int)((kTopkLdsWords * 4 + 15) / 16 * 16);
+}
+__device__ __forceinline__ int fin_off_stage() { return fin_off_stage_host(); }
+
+// o = sum_s w_s o_s for elements e4 (float4 of row r = e4 / (D/4)) of the
+// unit, EB elements per thread and SB partials of each loaded at once.
+template <int NT, int D, int SB, int EB>
+__device__ void finish_merge(const AttnParams& p, const f32x4* __restrict__ op, int S,
+                             const float* lse2, const float* lpart, long long orow0, int b, int h) {
+  constexpr int d4 = D / 4;
+  const int R = p.rows, G = p.group;
+  const int n4 = R * d4;
+  bf16* o = reinterpret_cast<bf16*>(p.o);
+  for (int e0 = 0; e0 < n4; e0 += EB * NT) {
+    f32x4 acc[EB];
+#pragma unroll
+    for (int k = 0; k < EB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += SB) {
+      f32x4 v[EB][SB];
+#pragma unroll
+      for (int k = 0; k < EB; ++k) {
+        const int e4 = min(e0 + k * NT + (int)threadIdx.x, n4 - 1);
+#pragma unroll
+        for (int j = 0; j < SB; ++j)
+          v[k][j] = op[(long long)min(s0 + j, S - 1) * n4 + e4];
+      }
+#pragma unroll
+      for (int k = 0; k < EB; ++k) {
+        const int e4 = min(e0 + k * NT + (int)threadIdx.x, n4 - 1);
+        const int r = e4 / d4;
+        const float tot = lse2[r];
+        const bool live = tot == tot && tot != neg_inf();
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          const int s1 = s0 + j;
+          const float w = (live && s1 < S) ? fast_exp2(lpart[s1 * R + r] - tot) : 0.f;
+          acc[k][0] += w * v[k][j][0];
+          acc[k][1] += w * v[k][j][1];
+          acc[k][2] += w * v[k][j][2];
+          acc[k][3] += w * v[k][j][3];
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < EB; ++k) {
+      const int e4 = e0 + k * NT + (int)threadIdx.x;
+      if (e4 < n4) {
+        const int r = e4 / d4;
+        const float tot = lse2[r];
+        const long long orow = orow0 + ((long long)(r / G)) * p.num_q_heads + h * G + r % G;
+        bf16x4 w4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) w4[c] = from_f32<bf16>(tot != tot ? qnan() : acc[k][c]);
+        *reinterpret_cast<bf16x4*>(o + orow * D + 4 * (e4 % d4)) = w4;
+      }
+    }
+  }
+}
+
+// Block scores sum_r 2^(ell[j][r] - lse2[r]) over rows r0 .. r0 + 4 nq4 - 1
+// (float4s), BB blocks per thread and batch with all their loads issued
+// together; written to sc_out (0 past nblk) and, when parked, as Top-N keys.
+template <int NT, int BB, int QMAX>
+__device__ void finish_scores(const AttnParams& p, const float* ell, const float* lse2, int r0,
+                              int nq4, int nblk, int ncand, bool park, float* sc_out,
+                              uint32_t* keys) {
+  const int R = p.rows;
+  const int tid = threadIdx.x;
+  for (int j0 = 0; j0 < p.max_blocks; j0 += BB * NT) {
+    f32x4 x[BB][QMAX];
+#pragma unroll
+    for (int jb = 0; jb < BB; ++jb) {
+      const int j = min(j0 + jb * NT + tid, max(nblk - 1, 0));
+      const f32x4* e = reinterpret_cast<const f32x4*>(ell + (long long)j * R + r0);
+#pragma unroll
+      for (int q = 0; q < QMAX; ++q)
+        if (q < nq4) x[jb][q] = e[q];
+    }
+#pragma unroll
+    for (int jb = 0; jb < BB; ++jb) {
+      const int j = j0 + jb * NT + tid;
+      float sc = 0.f;
+#pragma unroll
+      for (int q = 0; q < QMAX; ++q)
+        if (q < nq4) {
+          const float* l2 = lse2 + r0 + 4 * q;
+          sc += fast_exp2(x[jb][q][0] - l2[0]) + fast_exp2(x[jb][q][1] - l2[1]) +
+                fast_exp2(x[jb][q][2] - l2[2]) + fast_exp2(x[jb][q][3] - l2[3]);
+        }
+      if (j < p.max_blocks) {
+        if (j >= nblk) sc = 0.f;
+        sc_out[j] = sc;
+        if (park && j < ncand) keys[j] = score_key(sc);
+      }
+    }
+  }
+}
+
+template <int D, bool DRAFT>
+__global__ void __launch_bounds__(64 * finish_waves<DRAFT>(), 2)
+    finish_kernel(FusedParams f, AttnParams p, AttnParams pd) {
+  constexpr int kFinishWaves = finish_waves<DRAFT>();
+  constexpr int kFinishThreads = 64 * kFinishWaves;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int u = blockIdx.x;
   const int b = u / p.num_kv_heads, h = u % p.num_kv_heads;
   const int L = p.seq_lens[b];
   // units that fit in one chunk, and invalid ones, were finished in place
   if (!unit_valid(p, L, p.n_q) || L <= f.chunk_v) return;
-  const int R = p.rows, D = p.head_dim, G = p.group;
+  const int R = p.rows;
   const int S = ceil_div(L, f.chunk_v);
+  float* lse2 = reinterpret_cast<float*>(smem);
+  int* topk_lds = reinterpret_cast<int*>(smem + 512);
+  float* lst = reinterpret_cast<float*>(smem + fin_off_stage());
+  uint32_t* keys = reinterpret_cast<uint32_t*>(smem + f.fin_off_keys);
   const float* lp = p.lse_part + (long long)u * f.maxch_v * R;
-  const float* op = p.o_part + (long long)u * f.maxch_v * R * D;
-  auto out_row = [&](int r) -> long long {
-    return ((long long)b * p.n_q + r / G) * p.num_q_heads + h * G + r % G;
-  };
-  for (int r = tid; r < R; r += kFinishThreads) {
-    float m = neg_inf();
-    bool nan = false;
-    for (int s = 0; s < S; ++s) {
-      const float x = lp[s * R + r];
-      nan |= (x != x);
-      m = fmaxf(m, x);
+  const long long orow0 = (long long)b * p.n_q * p.num_q_heads;
+
+  // partial LSEs -> LDS, then each row's LSE over `lpr` lanes
+  const bool staged = S * R <= kFinishStage;
+  if (staged) {
+    for (int i0 = 0; i0 < S * R; i0 += kFinishLoads * kFinishThreads) {
+      float x[kFinishLoads];
+#pragma unroll
+      for (int k = 0; k < kFinishLoads; ++k) x[k] = lp[min(i0 + k * kFinishThreads + tid, S * R - 1)];
+#pragma unroll
+      for (int k = 0; k < kFinishLoads; ++k)
+        if (i0 + k * kFinishThreads + tid < S * R) lst[i0 + k * kFinishThreads + tid] = x[k];
     }
-    float sum = 0.f;
-    if (!nan && m != neg_inf())
-      for (int s = 0; s < S; ++s) sum += fast_exp2(lp[s * R + r] - m);
-    const float tot = nan ? qnan() : (m == neg_inf() ? neg_inf() : m + fast_log2(sum));
-    lse2[r] = tot;
-    p.lse[out_row(r)] = tot * kLn2;
   }
   __syncthreads();
-  const bool wfit = S * R <= kFinishWeights;
-  if (wfit)
-    for (int i = tid; i < S * R; i += kFinishThreads) {
-      const float tot = lse2[i % R];
-      wts[i] = (tot == neg_inf() || tot != tot) ? 0.f : fast_exp2(lp[i] - tot);
-    }
-  __syncthreads();
-  bf16* o = reinterpret_cast<bf16*>(p.o);
-  for (int idx = tid; idx < R * D; idx += kFinishThreads) {
-    const int r = idx / D, d = idx % D;
-    const float tot = lse2[r];
-    float acc = 0.f;
-    if (tot != neg_inf())
-      for (int s = 0; s < S; ++s) {
-        const float w = wfit ? wts[s * R + r] : fast_exp2(lp[s * R + r] - tot);
-        acc += w * op[((long long)s * R + r) * D + d];
-      }
-    if (tot != tot) acc = qnan();
-    o[out_row(r) * D + d] = from_f32<bf16>(acc);
-  }
-  const int nblk = ceil_div(L, p.block_size);
-  const float* ell = p.ell + (long long)u * p.max_blocks * R;
-  const int r0 = p.score_row_start * G;
-  float* sc_out = p.block_scores + (long long)u * p.max_blocks;
-  // rows in groups of 4 with 16-byte loads when the row count allows
-  const bool vec = (R % 4) == 0 && (r0 % 4) == 0;
-  for (int j = tid; j < p.max_blocks; j += kFinishThreads) {
-    float sc = 0.f;
-    if (j < nblk) {
-      const float* e = ell + (long long)j * R;
-      if (vec) {
-        for (int r = r0; r < R; r += 4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(e + r);
-          sc += fast_exp2(x[0] - lse2[r]) + fast_exp2(x[1] - lse2[r + 1]) +
-                fast_exp2(x[2] - lse2[r + 2]) + fast_exp2(x[3] - lse2[r + 3]);
+  const float* lpart = staged ? lst : lp;
+  {
+    int lpr = 1;
+    while (lpr < 16 && 2 * lpr * R <= kFinishThreads) lpr *= 2;
+    const int q = tid % lpr;
+    for (int rb = 0; rb < R; rb += kFinishThreads / lpr) {
+      const int r = rb + tid / lpr;
+      const bool live = r < R;
+      float m = neg_inf();
+      bool nan = false;
+      if (live)
+        for (int s0 = q; s0 < S; s0 += lpr) {
+          const float x = lpart[s0 * R + r];
+          nan |= (x != x);
+          m = fmaxf(m, x);
         }
-      } else {
-        for (int r = r0; r < R; ++r) sc += fast_exp2(e[r] - lse2[r]);
+      for (int o = 1; o < lpr; o <<= 1) {
+        m = fmaxf(m, __shfl_xor(m, o));
+        nan |= __shfl_xor((int)nan, o) != 0;
+      }
+      float sum = 0.f;
+      if (live && !nan && m != neg_inf())
+        for (int s0 = q; s0 < S; s0 += lpr) sum += fast_exp2(lpart[s0 * R + r] - m);
+      for (int o = 1; o < lpr; o <<= 1) sum += __shfl_xor(sum, o);
+      if (live && q == 0) {
+        const float tot = nan ? qnan() : (m == neg_inf() ? neg_inf() : m + fast_log2(sum));
+        lse2[r] = tot;
+        const int G = p.group;
+        p.lse[orow0 + (long long)(r / G) * p.num_q_heads + h * G + r % G] = tot * kLn2;
       }
     }
-    sc_out[j] = sc;
   }
+  __syncthreads();
+
+  // merge: EB elements per thread, SB partials each, in flight together
+  const f32x4* op = reinterpret_cast<const f32x4*>(p.o_part) + (long long)u * f.maxch_v * R * (D / 4);
+  if (S <= 2)
+    finish_merge<kFinishThreads, D, 2, kFinishLoads / 2>(p, op, S, lse2, lpart, orow0, b, h);
+  else if (S <= 4)
+    finish_merge<kFinishThreads, D, 4, kFinishLoads / 4>(p, op, S, lse2, lpart, orow0, b, h);
+  else
+    finish_merge<kFinishThreads, D, 8, kFinishLoads / 8>(p, op, S, lse2, lpart, orow0, b, h);
+
+  // block scores (every row of a block loaded at once), keys parked in LDS
+  const int nblk = ceil_div(L, p.block_size);
+  int ncand, n;
+  topk_bounds(L, p.block_size, f.topk_window, p.max_blocks, f.topk ? f.budget[b] : 0, f.max_sel,
+              ncand, n);
+  const bool park = f.topk && ncand <= f.fin_keys_cap;
+  const float* ell = p.ell + (long long)u * p.max_blocks * R;
+  const int r0 = p.score_row_start * p.group;
+  float* sc_out = p.block_scores + (long long)u * p.max_blocks;
+  const bool vec = (R % 4) == 0 && (r0 % 4) == 0;
+  const int nr = R - r0;
+  // a thread scores BB blocks per batch with the float4s of all their rows
+  // loaded together; scalar rows (counts not a multiple of 4) one block at
+  // a time
+  if (vec && nr <= 4 * 4)
+    finish_scores<kFinishThreads, 4, 4>(p, ell, lse2, r0, nr / 4, nblk, ncand, park, sc_out, keys);
+  else if (vec && nr <= 4 * 8)
+    finish_scores<kFinishThreads, 2, 8>(p, ell, lse2, r0, nr / 4, nblk, ncand, park, sc_out, keys);
+  else if (vec && nr <= 4 * 16)
+    finish_scores<kFinishThreads, 1, 16>(p, ell, lse2, r0, nr / 4, nblk, ncand, park, sc_out, keys);
+  else
+    for (int j = tid; j < p.max_blocks; j += kFinishThreads) {
+      float sc = 0.f;
+      if (j < nblk) {
+        const float* e = ell + (long long)j * R + r0;
+        for (int k0 = 0; k0 < nr; k0 += kFinishLoads) {
+          float x[kFinishLoads];
+#pragma unroll
+          for (int k = 0; k < kFinishLoads; ++k) x[k] = e[min(k0 + k, nr - 1)];
+#pragma unroll
+          for (int k = 0; k < kFinishLoads; ++k)
+            if (k0 + k < nr) sc += fast_exp2(x[k] - lse2[r0 + k0 + k]);
+        }
+      }
+      sc_out[j] = sc;
+      if (park && j < ncand) keys[j] = score_key(sc);
+    }
   if (!f.topk) return;
+  if (tid == 0) f.sel_count[u] = n;
+  int32_t* sel_s = DRAFT ? reinterpret_cast<int32_t*>(smem + f.fin_off_sel) : nullptr;
+  // the scores (or their keys) of every block, written above, before any read
   __threadfence_block();
   __syncthreads();
-  int ncand, n;
-  topk_bounds(L, p.block_size, f.topk_window, p.max_blocks, f.budget[b], f.max_sel, ncand, n);
-  if (tid == 0) f.sel_count[u] = n;
-  // the merge weights are dead: their LDS parks the selection's keys
-  topk_select<kFinishThreads>(sc_out, ncand, n, f.sel + (long long)u * f.max_sel, f.max_sel,
-                              nullptr, topk_lds, reinterpret_cast<uint32_t*>(wts),
-                              kFinishWeights);
+  if (park)
+    topk_select_parked<kFinishThreads>(keys, ncand, n, f.sel + (long long)u * f.max_sel,
+                                       f.max_sel, sel_s, topk_lds);
+  else
+    topk_select<kFinishThreads>(sc_out, ncand, n, f.sel + (long long)u * f.max_sel, f.max_sel,
+                                sel_s, topk_lds);
+  if constexpr (DRAFT) {
+    // the chained draft of this unit over the selection in LDS (the LDS
+    // above is dead: the selection ended with a barrier)
+    const int Ld = pd.seq_lens[b];
+    const int nseg = unit_valid(pd, Ld, 1)
+                         ? draft_list_len_mfma(n, pd.block_size, Ld, window_start(Ld, pd.window))
+                         : 0;
+    constexpr int A = 2 * kFinishWaves;
+    Item dt;
+    dt.u = u;
+    dt.c = 0;
+    dt.chunk = max(A, (nseg + A - 1) / A * A);
+    dt.single = 1;
+    dt.part_row0 = 0;
+    dt.ell_off = 0;
+    dt.sel_off = f.fin_off_sel;
+    dt.nsel_s = n;
+    dt.list_off = 0;
+    attn_item<D, 1, kFinishWaves, true, false>(pd, dt, smem);
+  }
 }
 
 template <int D, int NWR, int NWT>
@@ -396,10 +569,40 @@ hipError_t launch_select_draft(const FusedParams& f, const AttnParams& pv, const
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fused_finish(const FusedParams& f, const AttnParams& pv, hipStream_t s) {
+size_t finish_lds(FusedParams& f, int head_dim, int max_blocks, bool draft) {
+  const size_t keys_at = (size_t)fin_off_stage_host() + (size_t)kFinishStage * 4;
+  size_t cap = (size_t)max_blocks;
+  const size_t draft_area = align_up(item_lds_bytes(head_dim, 1, finish_waves<true>()), 16);
+  const size_t sel_bytes = draft ? align_up((size_t)f.max_sel * 4, 16) : 0;
+  // keys beyond the LDS room are read back from memory by the selection
+  if (keys_at + cap * 4 + sel_bytes > kMaxLds) cap = 0;
+  f.fin_off_keys = (int32_t)keys_at;
+  f.fin_keys_cap = (int32_t)cap;
+  f.fin_draft = draft ? 1 : 0;
+  const size_t end_keys = align_up(keys_at + cap * 4, 16);
+  f.fin_off_sel = (int32_t)(draft ? std::max(draft_area, end_keys) : end_keys);
+  return (size_t)f.fin_off_sel + sel_bytes;
+}
+
+hipError_t launch_fused_finish(const FusedParams& f, const AttnParams& pv, const AttnParams& pd,
+                               int head_dim, size_t lds_bytes, hipStream_t s) {
   if (f.nv_units == 0) return hipSuccess;
-  hipLaunchKernelGGL(finish_kernel, dim3((unsigned)f.nv_units), dim3(kFinishThreads), 0, s, f, pv);
-  return hipGetLastError();
+  if (lds_bytes > kMaxLds) return hipErrorInvalidValue;
+  auto go = [&](auto kern, int waves) -> hipError_t {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)kMaxLds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3((unsigned)f.nv_units), dim3(64 * waves), lds_bytes, s, f, pv,
+                       pd);
+    return hipGetLastError();
+  };
+  const int w = f.fin_draft ? finish_waves<true>() : finish_waves<false>();
+  if (head_dim == 128)
+    return f.fin_draft ? go(finish_kernel<128, true>, w) : go(finish_kernel<128, false>, w);
+  if (head_dim == 64)
+    return f.fin_draft ? go(finish_kernel<64, true>, w) : go(finish_kernel<64, false>, w);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fused(const FusedParams& f, const AttnParams& pv, const AttnParams& pd,

@@ -131,6 +131,10 @@ struct FusedParams {
   int32_t* sel_count;
   // LDS byte offsets: block log masses of a verify chunk, the selection
   int32_t off_ell, off_sel;
+  // finish kernel of split verify units: LDS offset and capacity of the
+  // parked Top-N keys, offset of the selection its chained draft reads, and
+  // whether it drafts the unit (chained steps with short draft lists)
+  int32_t fin_off_keys, fin_keys_cap, fin_off_sel, fin_draft;
 };
 
 struct FusedPlanIn {
@@ -181,8 +185,12 @@ size_t select_draft_lds(int head_dim, int max_sel, int max_blocks, int32_t& off_
                         int32_t& off_keys);
 hipError_t launch_select_draft(const FusedParams& f, const AttnParams& pv, const AttnParams& pd,
                                int head_dim, hipStream_t s);
-// One workgroup per split verify unit: merge, scores and selection.
-hipError_t launch_fused_finish(const FusedParams& f, const AttnParams& pv, hipStream_t s);
+// One workgroup per split verify unit: merge, scores, selection and, with
+// f.fin_draft, the chained draft.  finish_lds sets the fin_* LDS fields of f
+// and returns the workgroup's LDS bytes.
+size_t finish_lds(FusedParams& f, int head_dim, int max_blocks, bool draft);
+hipError_t launch_fused_finish(const FusedParams& f, const AttnParams& pv, const AttnParams& pd,
+                               int head_dim, size_t lds_bytes, hipStream_t s);
 hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s);
 // Sparse verify (a layout per query position): LDS bytes beyond the tiles,
 // and the launch.

@@ -251,4 +251,27 @@ __device__ void topk_select(const float* sc, int ncand, int n, int32_t* __restri
   }
 }
 
+// topk_select over keys already parked in LDS (keys[0, ncand), score_key of
+// each score), e.g. by the routine that computed the scores.
+template <int NT>
+__device__ void topk_select_parked(const uint32_t* keys, int ncand, int n,
+                                   int32_t* __restrict__ out, int max_sel, int32_t* out_lds,
+                                   int* lds) {
+  static_assert(NT % 64 == 0 && NT >= 64 && NT <= 1024, "workgroup of whole waves");
+  const int tid = threadIdx.x;
+  for (int j = tid; j < max_sel; j += NT) {
+    if (n == ncand)
+      out[j] = j < n ? j : -1;
+    else if (j >= n)
+      out[j] = -1;
+  }
+  if (n == 0 || n == ncand) {
+    if (out_lds)
+      for (int j = tid; j < n; j += NT) out_lds[j] = j;
+    __syncthreads();
+    return;
+  }
+  topk_core<NT, 4>(KeySrc{keys}, ncand, n, out, out_lds, lds);
+}
+
 }  // namespace sss
