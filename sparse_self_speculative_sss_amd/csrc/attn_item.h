@@ -130,12 +130,17 @@ struct Seg {
 // Descriptor of one 16-token segment, held by one lane: 64 consecutive
 // segments of a token group live in one register set, and each tile reads
 // its two descriptors with readlane, so page-table lookups are issued a whole
-// batch ahead instead of once per tile.
+// batch ahead instead of once per tile.  Once the batch's page ids have
+// arrived, seg_resolve turns each into the cache row of the segment's first
+// token, in vector code once per batch: the tile loop then only reads the
+// row (turning a page id into an address took ~25 scalar instructions per
+// segment in every tile of every wave).
 struct SegLane {
   int t0;
   int lohi;     // (lo - t0) | ((hi - t0) << 8)
-  int pg;       // page id (0 for an empty segment)
+  int pg;       // page id as loaded from the page table
   uint32_t pm;  // sparse verify: query positions whose layout holds it
+  int row;      // after seg_resolve: cache row (page, head, slot) of token t0
 };
 
 // Segment k of a verify unit (16 tokens starting at 16k), or entry k of a
@@ -183,14 +188,28 @@ __device__ __forceinline__ SegLane seg_lane(const AttnParams& p, const int32_t* 
   return d;
 }
 
-// Descriptor idx of the current (or next) batch as uniform values.  An
-// empty segment reads page 0; a page id outside [0, num_pages) also reads
-// page 0 and sets `bad` (the unit's outputs become NaN).  PM: also read
-// the position mask.
+// The cache rows of a batch of descriptors (this lane's segment), once its
+// page ids have arrived.  An empty segment reads page 0; a page id outside
+// [0, num_pages) also reads page 0 and sets this lane's `bad` (the unit's
+// outputs become NaN once the flags are combined).
+__device__ __forceinline__ void seg_resolve(const AttnParams& p, const FastDiv& pdiv, int h,
+                                            SegLane& d, int& bad) {
+  int pg = d.pg;
+  if (d.lohi == 0) {
+    pg = 0;
+  } else if (pg < 0 || pg >= p.num_pages) {
+    bad = 1;
+    pg = 0;
+  }
+  // rows of the pool number < 2^31 (checked on the host)
+  d.row = (pg * p.num_kv_heads + h) * p.page_size + pdiv.mod(d.t0);
+}
+
+// Descriptor idx of the current (or next) batch as uniform values, from
+// resolved batches.  PM: also read the position mask.
 template <bool PM = false>
-__device__ __forceinline__ Seg seg_of(const AttnParams& p, const FastDiv& pdiv, int h,
-                                      const SegLane& cur, const SegLane& nxt, bool use_nxt,
-                                      int idx, int& bad) {
+__device__ __forceinline__ Seg seg_of(const AttnParams& p, const SegLane& cur, const SegLane& nxt,
+                                      bool use_nxt, int idx) {
   Seg s;
   s.pm = 0xffffffffu;
   if (PM) {
@@ -202,22 +221,13 @@ __device__ __forceinline__ Seg seg_of(const AttnParams& p, const FastDiv& pdiv, 
   const int t0n = __builtin_amdgcn_readlane(nxt.t0, idx);
   const int lhc = __builtin_amdgcn_readlane(cur.lohi, idx);
   const int lhn = __builtin_amdgcn_readlane(nxt.lohi, idx);
-  const int pgc = __builtin_amdgcn_readlane(cur.pg, idx);
-  const int pgn = __builtin_amdgcn_readlane(nxt.pg, idx);
+  const int rowc = __builtin_amdgcn_readlane(cur.row, idx);
+  const int rown = __builtin_amdgcn_readlane(nxt.row, idx);
   s.t0 = use_nxt ? t0n : t0c;
   const int lh = use_nxt ? lhn : lhc;
-  int pg = use_nxt ? pgn : pgc;
-  if (lh == 0) {
-    pg = 0;
-  } else if (pg < 0 || pg >= p.num_pages) {
-    bad = 1;
-    pg = 0;
-  }
   s.lo = s.t0 + (lh & 255);
   s.hi = s.t0 + (lh >> 8);
-  // cache row of token t0 (rows of the pool number < 2^31; checked on the host)
-  const int row = (pg * p.num_kv_heads + h) * p.page_size + pdiv.mod(s.t0);
-  s.base = (long long)row * p.head_dim;
+  s.base = (long long)(use_nxt ? rown : rowc) * p.head_dim;
   return s;
 }
 
@@ -724,6 +734,12 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   float* const tok_stage = NWR == 1 ? reinterpret_cast<float*>(grp)
                                     : reinterpret_cast<float*>(smem + it.list_off) + w * 32 * 32;
 
+  // the first two batches' page ids, loaded while Q was staged (resolving
+  // them before the Q loads made every unit wait one more round trip)
+  if constexpr (!GATHER) {
+    seg_resolve(p, pdiv, h, cur, bad);
+    seg_resolve(p, pdiv, h, nxt, bad);
+  }
   TileRegs<D, NWR> regs[PD];
   Seg sa[PD], sb[PD];
   uint32_t vm[PD];
@@ -733,8 +749,8 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       vm[q] = gather_mask(rows_s, g_rel + 32 * q, g_len - 32 * q);
       load_tile_gather<D, NWR>(regs[q], kc, vc, rows_s, g_rel + 32 * q, vm[q], lig);
     } else {
-      sa[q] = seg_of<SPARSE>(p, pdiv, h, cur, nxt, false, 2 * q, bad);
-      sb[q] = seg_of<SPARSE>(p, pdiv, h, cur, nxt, false, 2 * q + 1, bad);
+      sa[q] = seg_of<SPARSE>(p, cur, nxt, false, 2 * q);
+      sb[q] = seg_of<SPARSE>(p, cur, nxt, false, 2 * q + 1);
       load_tile<D, NWR>(regs[q], kc, vc, sa[q], sb[q], lig);
     }
   }
@@ -764,6 +780,9 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       nxt = seg_lane<LIST>(p, sel_s, b, h, g_lo + 64 * (cur_batch + 1) + lane, g_hi, nsel, L, ws,
                            umsk);
     }
+    // the next batch's page ids were fetched 16 tiles ago: resolve them
+    // before the first prefetch that reads that batch (its last tiles)
+    if (!GATHER && (rel0 & 63) == 32) seg_resolve(p, pdiv, h, nxt, bad);
     group_sync<NWR>();
     if (SCORES && !ell_lds) {
       if (ell_at >= 0) ell_u[ell_at] = ell_val;
@@ -777,8 +796,8 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
         load_tile_gather<D, NWR>(regs[q], kc, vc, rows_s, g_rel + rn, vm[q], lig);
       } else {
         const int ra = rel0 + 2 * PD, rb = ra + 1;
-        sa[q] = seg_of<SPARSE>(p, pdiv, h, cur, nxt, (ra >> 6) != cur_batch, ra & 63, bad);
-        sb[q] = seg_of<SPARSE>(p, pdiv, h, cur, nxt, (rb >> 6) != cur_batch, rb & 63, bad);
+        sa[q] = seg_of<SPARSE>(p, cur, nxt, (ra >> 6) != cur_batch, ra & 63);
+        sb[q] = seg_of<SPARSE>(p, cur, nxt, (rb >> 6) != cur_batch, rb & 63);
         load_tile<D, NWR>(regs[q], kc, vc, sa[q], sb[q], lig);
       }
     }

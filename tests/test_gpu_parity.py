@@ -361,3 +361,38 @@ def test_negative_and_zero_scale(scale):
     out = H.gpu_draft(wl, db, torch.from_numpy(sel).to(DEV), torch.from_numpy(cnt).to(DEV))
     torch.cuda.synchronize()
     H.compare_draft(wl, db, out, sel, cnt, units).check(f"draft scale={scale}")
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("bad_id", [-3, 10 ** 6])
+def test_invalid_page_id_poisons_its_request(splits, bad_id):
+    """A page id outside [0, num_pages) in one request's table reads nothing
+    out of bounds: that request's outputs (every KV head reads the page) are
+    NaN, and the other request's match the oracle."""
+    wl = mk("qwen3_8b_layer_b16_l4096", seed=17, B=2, L=300, sigma="one")
+    vb, db = wl.verify, wl.draft
+    table = vb.page_table.clone()
+    table[1, 5] = bad_id                 # tokens 80..95 of request 1
+    bad = W.Batch(q=vb.q, page_table=table, seq_lens=vb.seq_lens, budget=vb.budget,
+                  req_ids=vb.req_ids)
+    out = H.gpu_verify(wl, bad, num_splits=splits)
+    torch.cuda.synchronize()
+    o, lse, sc = out
+    assert torch.isnan(o[1].float()).all() and torch.isnan(lse[1]).all() and torch.isnan(sc[1]).all()
+    H.compare_verify(wl, vb, out, [(0, h) for h in range(wl.shape.Hkv)]).check(
+        f"bad page {bad_id} splits={splits}")
+    # the draft reads the bad page only if it selects block 5 or the window
+    # reaches it: select block 5 for every head of request 1
+    Hkv = wl.shape.Hkv
+    sel = torch.full((2, Hkv, 4), -1, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros((2, Hkv), dtype=torch.int32, device=DEV)
+    sel[:, :, 0] = 5
+    sel[:, :, 1] = 9
+    cnt[:] = 2
+    dbad = W.Batch(q=db.q, page_table=table, seq_lens=db.seq_lens, budget=db.budget,
+                   req_ids=db.req_ids)
+    od, lsed = H.gpu_draft(wl, dbad, sel, cnt, num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.isnan(od[1].float()).all() and torch.isnan(lsed[1]).all()
+    H.compare_draft(wl, db, (od, lsed), sel.cpu().numpy(), cnt.cpu().numpy(),
+                    [(0, h) for h in range(Hkv)]).check(f"bad page draft {bad_id}")
