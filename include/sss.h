@@ -403,6 +403,36 @@ size_t sss_fused_workspace_size(const sss_verify_step* verify, const sss_draft_s
                                 int32_t chained);
 
 /*
+ * Which launch form sss_fused_step takes for these arguments (host query; no
+ * device memory is read and nothing is launched):
+ *   SSS_FUSED_PERSISTENT  a chained step of at least two units per compute
+ *                         unit (512) whose verify units fit one workgroup
+ *                         each: one persistent launch whose workgroups loop
+ *                         over units, drafting the unit each verified before
+ *                         while the other workgroup on the compute unit
+ *                         streams (SparseSpec §4.2, persistent-style fused
+ *                         attention).  Verify outputs, scores and selections
+ *                         are bitwise those of sss_verify_attn +
+ *                         sss_block_topk; the draft splits its list over two
+ *                         token groups and equals sss_draft_attn up to
+ *                         summation order;
+ *   SSS_FUSED_TWO_LAUNCH  other chained steps of whole units: the unsplit
+ *                         verify launch, then selection and draft launches;
+ *   SSS_FUSED_WORK_LIST   everything else: the work-list launch plus the
+ *                         merge / selection / draft launches of split units.
+ * Returns -1 when sss_fused_step would reject the arguments (and 0 when
+ * both halves are empty).
+ */
+enum {
+  SSS_FUSED_NOTHING = 0,
+  SSS_FUSED_PERSISTENT = 1,
+  SSS_FUSED_TWO_LAUNCH = 2,
+  SSS_FUSED_WORK_LIST = 3
+};
+int32_t sss_fused_step_form(const sss_verify_step* verify, const sss_draft_step* draft,
+                            int32_t chained);
+
+/*
  * KV write for new token positions (SpecSA, 核心创新 / 刷新/复用NSA内核融合:
  * the KV of the speculative positions is written before verification and
  * refreshed -- overwritten -- when it is recomputed; the KV of accepted

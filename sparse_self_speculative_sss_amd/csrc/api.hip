@@ -48,6 +48,23 @@ long long lcm_ll(long long a, long long b) {
 // figures so that the workspace query and the call always agree.
 constexpr long long kTargetWaves = 256 * 8;
 constexpr int kMinChunkTokens = 256;
+// units from which a chained step of whole units runs persistently: two
+// per compute unit
+constexpr long long kPersistMinUnits = 256 * 2;
+
+// Compute units of the current device (the persistent step's grid); the
+// planning figures above stay fixed.
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
 
 sss_status check_kv(const sss_paged_kv* kv, int batch) {
   if (!kv) return fail(SSS_ERR_INVALID_ARGUMENT, "kv is NULL");
@@ -363,6 +380,8 @@ struct FusedSetup {
   // chain_draft
   bool select_then_draft_launches = false;
   Plan vplan = {};
+  // chained step of whole units run as one persistent launch (persist.hip)
+  bool persist = false;
 };
 
 sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int chained,
@@ -504,6 +523,25 @@ sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int ch
         }
       }
     }
+  }
+  if (fs.two_launch) {
+    // At least two units per compute unit whose unsplit verify runs as
+    // two-token-group workgroups (Q in registers, the unit's block masses in
+    // LDS, two workgroups per CU), draft lists of at most 64 segments per
+    // token group: one persistent launch verifies, scores, selects and
+    // drafts every unit (persist.hip), the drafts overlapping the verify
+    // stream instead of following it.  The workspace stays that of the
+    // two-launch form, so the size query never depends on this choice.
+    const int D = fs.head_dim;
+    const long long ellf = fs.vplan.ell_lds_floats;
+    const bool two_per_cu = fs.rows_v <= 32 && v->block_size != 1 &&
+                            mfma_smem_bytes(D, 1, 4, ellf) > kMaxLds / 2 &&
+                            mfma_smem_bytes(D, 1, 2, ellf, true) <= kMaxLds / 2;
+    int32_t o1, o2, o3, o4;
+    const size_t lds =
+        persist_lds(D, fs.rows_v, fs.group_d, v->max_blocks, v->max_sel, o1, o2, o3, o4);
+    fs.persist = two_per_cu && lds > 0 && lds <= kMaxLds / 2 && fs.group_d <= 32 &&
+                 list_max_d <= 2 * 64 && fs.nv >= kPersistMinUnits;
   }
   if (chained && fs.split_v) {
     // split units draft after their selection, with the one-launch kernels
@@ -1014,6 +1052,16 @@ size_t sss_fused_workspace_size(const sss_verify_step* verify, const sss_draft_s
   return fs.bytes;
 }
 
+int32_t sss_fused_step_form(const sss_verify_step* verify, const sss_draft_step* draft,
+                            int32_t chained) {
+  FusedSetup fs;
+  if (setup_fused(verify, draft, chained, fs) != SSS_OK) return -1;
+  if (!fs.has_v && !fs.has_d) return SSS_FUSED_NOTHING;
+  if (fs.persist) return SSS_FUSED_PERSISTENT;
+  if (fs.two_launch) return SSS_FUSED_TWO_LAUNCH;
+  return SSS_FUSED_WORK_LIST;
+}
+
 sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* draft,
                           int32_t chained, void* workspace, size_t workspace_bytes, void* stream) {
   FusedSetup fs;
@@ -1085,6 +1133,24 @@ sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* d
   f.chained = chained ? 1 : 0;
   f.off_ell = fs.pl.off_ell;
   f.off_sel = fs.pl.off_sel;
+  if (fs.persist) {
+    const sss_verify_step* v = verify;
+    AttnParams p = base_params(&v->kv, v->q, v->batch, v->n_q, v->num_q_heads, v->sm_scale, fs.vplan);
+    p.o = v->o;
+    p.lse = v->lse;
+    p.block_size = v->block_size;
+    p.max_blocks = v->max_blocks;
+    p.score_row_start = v->score_row_start;
+    p.block_scores = v->block_scores;
+    // two workgroups per compute unit, a multiple of 8 (the XCD-aware unit
+    // order assumes slot i runs on XCD i % 8)
+    const int grid = std::max(8, 2 * device_cus() / 8 * 8);
+    hipError_t e = launch_persist_step(p, pd, v->max_sel, v->window, v->budget, v->sel,
+                                       v->sel_count, grid, s);
+    if (e != hipSuccess)
+      return fail(SSS_ERR_HIP, "fused step persistent launch: %s", hipGetErrorString(e));
+    return ok();
+  }
   if (fs.two_launch) {
     const sss_verify_step* v = verify;
     const Plan& vp = fs.vplan;

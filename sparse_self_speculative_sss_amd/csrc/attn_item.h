@@ -151,8 +151,8 @@ struct SegLane {
 // The page id is loaded for every lane (the table index is clamped into the
 // request's row) and only checked when a tile reads the descriptor, so the
 // load is never waited for here.
-template <bool LIST>
-__device__ __forceinline__ SegLane seg_lane(const AttnParams& p, const int32_t* sel_s, int b,
+template <bool LIST, class P>
+__device__ __forceinline__ SegLane seg_lane(const P& p, const int32_t* sel_s, int b,
                                             int h, int k, int k_end, int nsel, int L, int ws,
                                             const uint32_t* pm_s = nullptr) {
   int t0 = 0, lo = 0, hi = 0;
@@ -192,7 +192,8 @@ __device__ __forceinline__ SegLane seg_lane(const AttnParams& p, const int32_t* 
 // page ids have arrived.  An empty segment reads page 0; a page id outside
 // [0, num_pages) also reads page 0 and sets this lane's `bad` (the unit's
 // outputs become NaN once the flags are combined).
-__device__ __forceinline__ void seg_resolve(const AttnParams& p, const FastDiv& pdiv, int h,
+template <class P>
+__device__ __forceinline__ void seg_resolve(const P& p, const FastDiv& pdiv, int h,
                                             SegLane& d, int& bad) {
   int pg = d.pg;
   if (d.lohi == 0) {
@@ -207,8 +208,8 @@ __device__ __forceinline__ void seg_resolve(const AttnParams& p, const FastDiv& 
 
 // Descriptor idx of the current (or next) batch as uniform values, from
 // resolved batches.  PM: also read the position mask.
-template <bool PM = false>
-__device__ __forceinline__ Seg seg_of(const AttnParams& p, const SegLane& cur, const SegLane& nxt,
+template <bool PM = false, class P>
+__device__ __forceinline__ Seg seg_of(const P& p, const SegLane& cur, const SegLane& nxt,
                                       bool use_nxt, int idx) {
   Seg s;
   s.pm = 0xffffffffu;

@@ -1,0 +1,740 @@
+// Persistent decode step (SparseSpec §4.2: one persistent-style fused kernel
+// serves the full attention of the verifying requests and the sparse
+// attention of the drafting ones; §4.1 PillarAttn: the verify pass yields
+// the block scores whose Top-K is the pattern the following draft steps
+// use; SpecAttn, technical framework: the critical KV entries are a
+// by-product of verification and the draft loads only those).
+//
+// One launch runs, for every (request, KV head) unit of a chained step:
+// the verify (k+1 positions x G heads over the whole paged cache, block log
+// masses kept in LDS), the block scores, the Top-N selection and the draft
+// over that selection.  A workgroup is two waves (two token groups that
+// split each unit's tokens) and two workgroups share a compute unit.
+// Workgroup w loops over the units w, w + grid, w + 2 grid, ... (in the
+// XCD-aware order of the one-item kernels).  For each unit it first drafts
+// the unit it verified before -- that unit's selection and draft query are
+// still in its LDS -- and then verifies the new unit; the draft's last tile
+// prefetches the verify's first.  The short, latency-bound dependent chain
+// of draft tiles therefore runs while the other workgroup on the compute
+// unit keeps streaming the cache, instead of in launches after the whole
+// verify.  The next unit's Q and page ids are loaded before the epilogue
+// (token-group merge, outputs, block scores, selection), so they arrive
+// while it runs.  Only the last unit of each workgroup is drafted at the
+// end.  No workgroup waits for another: every dependency (block masses ->
+// scores -> selection -> draft) stays inside one workgroup.
+//
+// The verify arithmetic is that of the one-item kernel with two token
+// groups (attn_item with Q in registers): the same tile partition, order
+// and merge, so outputs, scores and selections are bitwise equal to
+// sss_verify_attn + sss_block_topk on the same inputs.  The draft splits
+// its list over the two token groups (the stand-alone draft of this many
+// units runs one wave per unit), so it agrees with sss_draft_attn up to
+// summation order.
+#include <algorithm>
+
+#include "attn_item.h"
+#include "topk_dev.h"
+
+namespace sss {
+namespace {
+
+constexpr int kPersistWaves = 2;  // token groups (waves) per workgroup
+constexpr int kPersistThreads = 64 * kPersistWaves;
+constexpr int kTopkLdsBytes = (kTopkLdsWords * 4 + 127) / 128 * 128;
+
+// Everything the persistent step reads: one paged cache serves both halves
+// (a chained step drafts the requests it verifies), so the draft half adds
+// only its query, outputs, scale and window.  Field names follow
+// AttnParams where they mean the same (the segment helpers take either).
+struct PersistParams {
+  const bf16* k;
+  const bf16* v;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int32_t num_pages, page_size, num_kv_heads, head_dim, max_pages, max_seq_len;
+  int32_t block_size, max_blocks, score_row_start;
+  // verify: q [B][n_q][Hq][d], o like q, lse [B][n_q][Hq], block_scores
+  // [B][Hkv][max_blocks]; rows = n_q * group per unit
+  const bf16* q;
+  bf16* o;
+  float* lse;
+  float* block_scores;
+  int32_t batch, n_q, num_q_heads, group, rows;
+  float scale_log2;
+  // selection: budget [B], sel [B][Hkv][max_sel], sel_count [B][Hkv]
+  int32_t max_sel, topk_window;
+  const int32_t* budget;
+  int32_t* sel;
+  int32_t* sel_count;
+  // draft: q [B][1][Hq][d], o like it, lse [B][1][Hq]
+  const bf16* dq;
+  bf16* dout;
+  float* dlse;
+  float dscale_log2;
+  int32_t window;
+  int32_t units;  // batch x KV heads
+  // LDS byte offsets: the unit's block log masses (or the next unit's Q
+  // rows parked there), the row log2-LSEs, the selection the next draft
+  // reads, the draft query rows
+  int32_t off_ell, off_lse, off_sel, off_dq;
+};
+
+// Unit run by the i-th workgroup slot: all KV heads of request r on XCD r % 8
+// when the batch is a multiple of 8 (slot i runs on XCD i % 8 as long as the
+// grid is a multiple of 8), the requests dealt round-robin over the XCDs.
+__device__ __forceinline__ int persist_unit(int i, int batch, int H) {
+  if ((batch & 7) != 0) return i;
+  const int k = i >> 3;
+  return ((i & 7) + 8 * (k / H)) * H + k % H;
+}
+
+template <int D>
+struct Acc {
+  f32x16 o[Geo<D>::MT];
+  float m, l;
+};
+
+template <int D>
+__device__ __forceinline__ void acc_init(Acc<D>& a) {
+#pragma unroll
+  for (int mt = 0; mt < Geo<D>::MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a.o[mt][i] = 0.f;
+  a.m = neg_inf();
+  a.l = 0.f;
+}
+
+// The Q^T operand of one row tile, read from global memory: lane (rl, hl)
+// holds 16-byte chunk 2 ks + hl of its row (the layout the first MFMA of a
+// tile reads).  `row` points at the row's head_dim elements; rows without
+// one are zero.  A negative scale is folded in as an exact sign flip.
+template <int D>
+__device__ __forceinline__ void load_qreg(bf16x8 (&q)[Geo<D>::KS], const bf16* row, bool neg) {
+  const int hl = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < Geo<D>::KS; ++ks) {
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (row) v = *reinterpret_cast<const uint4*>(row + 16 * ks + 8 * hl);
+    if (neg) {
+      v.x ^= 0x80008000u;
+      v.y ^= 0x80008000u;
+      v.z ^= 0x80008000u;
+      v.w ^= 0x80008000u;
+    }
+    q[ks] = *reinterpret_cast<const bf16x8*>(&v);
+  }
+}
+
+// Masked logits of a tile (S^T in `sacc`) for a row at position pos_r:
+// interior tiles need no mask.  Returns the row's (lane-local) max.
+__device__ __forceinline__ float mask_logits(const f32x16& sacc, float (&s)[16], const Seg& ca,
+                                             const Seg& cb, bool interior, int pos_r, int hl) {
+  float mx = neg_inf();
+  if (interior) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = sacc[i];
+      mx = fmaxf(mx, s[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = (i >> 2) * 8 + 4 * hl + (i & 3);
+      const Seg& sg = (m < kSeg) ? ca : cb;
+      const int tok = sg.t0 + (m % kSeg);
+      const bool ok = tok >= sg.lo && tok < sg.hi && tok <= pos_r;
+      s[i] = ok ? sacc[i] : neg_inf();
+      mx = fmaxf(mx, s[i]);
+    }
+  }
+  return mx;
+}
+
+// Online softmax of a tile's masked logits into `a` (lazy rescaling as in
+// attn_item: the reference max moves only past kRescaleSlack), then
+// O^T += V^T P^T from the tile's V^T in LDS.  `extra` is rescaled with the
+// running sums (a block's partial mass).  Returns the frame m_use of pr[].
+template <int D>
+__device__ __forceinline__ float softmax_pv(Acc<D>& a, const float (&s)[16], float mx, float scl,
+                                            const char* vt, float (&pr)[16], float& psum,
+                                            float& extra, int rl, int hl) {
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * scl;
+  const float m_new = fmaxf(a.m, mx);
+  const bool move = (a.m == neg_inf()) || (m_new > a.m + kRescaleSlack);
+  if (__builtin_amdgcn_ballot_w64(move)) {
+    const float m_tgt = move ? m_new : a.m;
+    const float alpha = (m_tgt == neg_inf()) ? 1.f : fast_exp2(a.m - m_tgt);
+    a.l *= alpha;
+    extra *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < Geo<D>::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a.o[mt][i] *= alpha;
+    a.m = m_tgt;
+  }
+  const float m_use = (a.m == neg_inf()) ? 0.f : a.m;
+  psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    pr[i] = fast_exp2(fmaf(s[i], scl, -m_use));
+    psum += pr[i];
+  }
+  a.l += psum;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    bf16x8 pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pb[j] = static_cast<bf16>(pr[8 * kk + j]);
+    const int qd = 2 * kk + hl;
+#pragma unroll
+    for (int mt = 0; mt < Geo<D>::MT; ++mt) {
+      const int d = 32 * mt + rl;
+      const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + vrow(d) * 64 + 16 * (qd ^ vq_swz(d)));
+      a.o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, a.o[mt], 0, 0, 0);
+    }
+  }
+  return m_use;
+}
+
+// S^T = K Q^T of the tile in LDS at gt.
+template <int D>
+__device__ __forceinline__ f32x16 qk_tile(const char* gt, const bf16x8 (&q)[Geo<D>::KS], int rl,
+                                          int hl) {
+  f32x16 sacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < Geo<D>::KS; ++ks) {
+    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(gt + rl * Geo<D>::K_STRIDE + 32 * ks + 16 * hl);
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, q[ks], sacc, 0, 0, 0);
+  }
+  return sacc;
+}
+
+// S^T = K Q^T with the Q rows read from LDS (row stride K_STRIDE, as the
+// K rows); rows >= nrows are zero.
+template <int D>
+__device__ __forceinline__ f32x16 qk_tile_lds(const char* gt, const char* qt, int nrows, int rl,
+                                              int hl) {
+  f32x16 sacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < Geo<D>::KS; ++ks) {
+    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(gt + rl * Geo<D>::K_STRIDE + 32 * ks + 16 * hl);
+    const bf16x8 z = {};
+    const bf16x8 qb =
+        rl < nrows ? *reinterpret_cast<const bf16x8*>(qt + rl * Geo<D>::K_STRIDE + 32 * ks + 16 * hl) : z;
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb, sacc, 0, 0, 0);
+  }
+  return sacc;
+}
+
+// Combines the two token groups' (m, l, O) of one row tile through LDS at
+// `red` (tg 1 writes, tg 0 reads after the barrier; rows < nrows) and
+// leaves the result in token group 0's `a`.  Same arithmetic and order as
+// attn_item's token-group merge.  All threads call it; it has one barrier.
+template <int D>
+__device__ __forceinline__ void merge_groups(Acc<D>& a, float* red, int tg, int rl, int hl,
+                                             int nrows) {
+  float* ml = red + 32 * D;  // [2][32] max, then [2][32] sum
+  if (hl == 0) {
+    ml[tg * 32 + rl] = a.m;
+    ml[2 * 32 + tg * 32 + rl] = a.l;
+  }
+  if (tg == 1 && rl < nrows) {
+    float* dst = red + rl * D;
+#pragma unroll
+    for (int mt = 0; mt < Geo<D>::MT; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = a.o[mt][4 * q4 + e];
+        *reinterpret_cast<f32x4*>(dst + 32 * mt + 8 * q4 + 4 * hl) = v4;
+      }
+  }
+  __syncthreads();
+  if (tg == 0) {
+    float mg = fmaxf(a.m, ml[32 + rl]);
+    const float mu = (mg == neg_inf()) ? 0.f : mg;
+    const float a0 = fast_exp2(a.m - mu);
+    float lsum = a.l * a0;
+#pragma unroll
+    for (int mt = 0; mt < Geo<D>::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a.o[mt][i] *= a0;
+    const float ag = fast_exp2(ml[32 + rl] - mu);
+    lsum += ag * ml[2 * 32 + 32 + rl];
+    if (rl < nrows) {
+      const float* src = red + rl * D;
+#pragma unroll
+      for (int mt = 0; mt < Geo<D>::MT; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(src + 32 * mt + 8 * q4 + 4 * hl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a.o[mt][4 * q4 + e] += ag * v4[e];
+        }
+    }
+    a.m = mg;
+    a.l = lsum;
+  }
+}
+
+// Normalised O (bf16) and LSE (natural log) of row `orow`; bad poisons.
+template <int D>
+__device__ __forceinline__ float write_row(const Acc<D>& a, bf16* o, float* lse, long long orow,
+                                           bool bad, int hl) {
+  const bool empty = !(a.l > 0.f);
+  const float inv = empty ? 0.f : 1.f / a.l;
+  const float lse2 = bad ? qnan() : (empty ? neg_inf() : a.m + fast_log2(a.l));
+  const float poison = bad ? qnan() : 1.f;
+#pragma unroll
+  for (int mt = 0; mt < Geo<D>::MT; ++mt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = from_f32<bf16>(a.o[mt][4 * q4 + e] * inv * poison);
+      *reinterpret_cast<bf16x4*>(o + orow * D + 32 * mt + 8 * q4 + 4 * hl) = v4;
+    }
+  if (hl == 0) lse[orow] = lse2 * kLn2;
+  return lse2;
+}
+
+// The draft of unit du (request bd, head hd) over its selection sel_s[0, nsel)
+// (LDS) plus the window, with the draft query rows staged at dq; the list's
+// segments are split over the two token groups (at most 64 each).  On
+// return the outputs are written.  When `vnext` is set, the last tile
+// prefetches the first verify tile (segments vs0, vs1) into `regs`.
+template <int D>
+__device__ __forceinline__ void run_draft(const PersistParams& pd, int du, const int32_t* sel_s,
+                                          int nsel, const char* dq, char* smem,
+                                          TileRegs<D, 1>& regs, bool vnext, const Seg& vs0,
+                                          const Seg& vs1, const FastDiv& pdiv) {
+  typedef Geo<D> G;
+  const int lane = threadIdx.x & 63;
+  const int tg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = lane >> 5, rl = lane & 31;
+  const int Gd = pd.group;
+  const int bd = du / pd.num_kv_heads, hd = du % pd.num_kv_heads;
+  const bf16* __restrict__ kc = pd.k;
+  const bf16* __restrict__ vc = pd.v;
+  char* const grp = smem + tg * G::GROUP_BYTES;
+
+  const int L = pd.seq_lens[bd];
+  const bool valid =
+      L >= 1 && L <= pd.max_seq_len && (long long)L <= (long long)pd.max_pages * pd.page_size;
+  int bad = valid ? 0 : 1;
+  const int ws = valid ? window_start(L, pd.window) : 0;
+  const int nseg = valid ? draft_list_len_mfma(nsel, pd.block_size, L, ws) : 0;
+  const int per_group = ceil_div(ceil_div(nseg, kPersistWaves), 2) * 2;
+  const int g_lo = min(tg * per_group, nseg), g_hi = min(g_lo + per_group, nseg);
+  const int n_tiles = ceil_div(min(per_group, nseg), 2);
+  const int pos_r = L - 1;
+  const float scl = fmaxf(fabsf(pd.dscale_log2), 1e-30f);
+
+  SegLane dl = seg_lane<true>(pd, sel_s, bd, hd, g_lo + lane, g_hi, nsel, L, ws);
+  seg_resolve(pd, pdiv, hd, dl, bad);
+
+  Acc<D> a;
+  acc_init(a);
+  float dummy = 0.f;
+  Seg sa = {}, sb = {};
+  if (n_tiles > 0) {
+    sa = seg_of(pd, dl, dl, false, 0);
+    sb = seg_of(pd, dl, dl, false, 1);
+    load_tile<D, 1>(regs, kc, vc, sa, sb, lane);
+  } else if (vnext) {
+    load_tile<D, 1>(regs, kc, vc, vs0, vs1, lane);
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    const int rel0 = 2 * t;
+    const bool live = g_lo + rel0 < g_hi;
+    const Seg ca = sa, cb = sb;
+    const bool full = seg_full(ca) && seg_full(cb);
+    store_tile<D, 1>(regs, grp, lane, ca, cb, full);
+    group_sync<1>();
+    if (t + 1 < n_tiles) {
+      sa = seg_of(pd, dl, dl, false, rel0 + 2);
+      sb = seg_of(pd, dl, dl, false, rel0 + 3);
+      load_tile<D, 1>(regs, kc, vc, sa, sb, lane);
+    } else if (vnext) {
+      load_tile<D, 1>(regs, kc, vc, vs0, vs1, lane);
+    }
+    if (live) {
+      const f32x16 sacc = qk_tile_lds<D>(grp, dq, Gd, rl, hl);
+      float s[16], pr[16], psum;
+      const bool interior = full && cb.t0 + kSeg - 1 <= pos_r;
+      const float mx = mask_logits(sacc, s, ca, cb, interior, pos_r, hl);
+      softmax_pv<D>(a, s, mx, scl, grp + G::K_BYTES, pr, psum, dummy, rl, hl);
+    }
+    group_sync<1>();
+  }
+  a.l += __shfl_xor(a.l, 32);
+  bad = __syncthreads_or(bad);  // both groups are done with their tile buffers
+  merge_groups<D>(a, reinterpret_cast<float*>(smem), tg, rl, hl, Gd);
+  if (tg == 0 && rl < Gd) {
+    const long long orow = (long long)bd * pd.num_q_heads + hd * Gd + rl;
+    write_row<D>(a, pd.dout, pd.dlse, orow, bad != 0, hl);
+  }
+  // token group 0 reads the merge scratch (its own tile buffer) before it
+  // stores its next tile there: program order within the wave suffices
+}
+
+// Segments [g_lo, g_hi) of token group tg for a verify unit of L tokens, and
+// the tile count of the loop (group 0's share), as attn_item splits them.
+__device__ __forceinline__ void verify_range(int L, int bs, int tg, int& g_lo, int& g_hi,
+                                             int& n_tiles) {
+  const int seg_hi = ceil_div(L, kSeg);
+  const int galign = bs < 2 * kSeg ? 2 : bs / kSeg;
+  const int per_group = ceil_div(ceil_div(seg_hi, kPersistWaves), galign) * galign;
+  g_lo = min(tg * per_group, seg_hi);
+  g_hi = min(g_lo + per_group, seg_hi);
+  n_tiles = ceil_div(min(per_group, seg_hi), 2);
+}
+
+__device__ __forceinline__ bool verify_unit_ok(const PersistParams& p, int L) {
+  return L >= p.n_q && L <= p.max_seq_len && (long long)L <= (long long)p.max_pages * p.page_size;
+}
+
+// The first two descriptor batches of unit u's token group (page ids in
+// flight).
+__device__ __forceinline__ void verify_segs(const PersistParams& p, int u, int tg, SegLane& cur,
+                                            SegLane& nxt) {
+  const int lane = threadIdx.x & 63;
+  const int b = u / p.num_kv_heads, h = u % p.num_kv_heads;
+  const int L = p.seq_lens[b];
+  int g_lo = 0, g_hi = 0, nt = 0;
+  if (verify_unit_ok(p, L)) verify_range(L, p.block_size, tg, g_lo, g_hi, nt);
+  cur = seg_lane<false>(p, nullptr, b, h, g_lo + lane, g_hi, 0, L, L);
+  nxt = seg_lane<false>(p, nullptr, b, h, g_lo + 64 + lane, g_hi, 0, L, L);
+}
+
+// Unit u's Q rows as 16-byte chunks, chunk e = row * CPT + column for
+// e = threadIdx.x + 128 j; rows >= rows are zero, a negative scale folded in.
+template <int D, int NQ>
+__device__ __forceinline__ void verify_q_chunks(const PersistParams& p, int u, uint4 (&qc)[NQ]) {
+  const int b = u / p.num_kv_heads, h = u % p.num_kv_heads;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int e = (int)threadIdx.x + kPersistThreads * j;
+    const int row = e / Geo<D>::CPT, cc = e % Geo<D>::CPT;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (row < p.rows) {
+      const int iq = row / p.group, hq = h * p.group + row % p.group;
+      v = *reinterpret_cast<const uint4*>(p.q + (((long long)b * p.n_q + iq) * p.num_q_heads + hq) * D +
+                                          8 * cc);
+      if (p.scale_log2 < 0.f) {
+        v.x ^= 0x80008000u;
+        v.y ^= 0x80008000u;
+        v.z ^= 0x80008000u;
+        v.w ^= 0x80008000u;
+      }
+    }
+    qc[j] = v;
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kPersistThreads, 1) persist_step_kernel(PersistParams p) {
+  typedef Geo<D> G;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int tg = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, rl = lane & 31;
+  const int r = rl;
+  const bool row_ok = r < p.rows;
+  char* const grp = smem + tg * G::GROUP_BYTES;
+  const int grid = gridDim.x;
+  const int nmine = p.units > (int)blockIdx.x ? (p.units - (int)blockIdx.x + grid - 1) / grid : 0;
+  // the next unit's Q rows: loaded into qpre before an epilogue, parked in
+  // the dead block-mass area at its end, read into the Q^T operand after
+  // the next draft (no Q registers are held across the draft's tiles)
+  constexpr int kQChunks = (32 * G::CPT + kPersistThreads - 1) / kPersistThreads;
+  uint4 qpre[kQChunks];
+  bf16x8 qreg[G::KS];
+  SegLane vcur = {}, vnxt = {};
+  const FastDiv pdiv(p.page_size);
+
+  int du = -1, dn = 0;  // unit whose draft is pending, its selection's length
+  if (nmine > 0) {
+    const int u0 = persist_unit(blockIdx.x, p.batch, p.num_kv_heads);
+    const int b0 = u0 / p.num_kv_heads, h0 = u0 % p.num_kv_heads;
+    const bf16* row = nullptr;
+    if (row_ok)
+      row = p.q + (((long long)b0 * p.n_q + r / p.group) * p.num_q_heads + h0 * p.group + r % p.group) * D;
+    load_qreg<D>(qreg, row, p.scale_log2 < 0.f);
+    verify_segs(p, u0, tg, vcur, vnxt);
+  }
+
+  for (int k = 0; k < nmine; ++k) {
+    const int u = persist_unit(blockIdx.x + k * grid, p.batch, p.num_kv_heads);
+    const int b = u / p.num_kv_heads, h = u % p.num_kv_heads;
+    const int L = p.seq_lens[b];
+    const bool unit_ok = verify_unit_ok(p, L);
+    int g_lo = 0, g_hi = 0, n_tiles = 0;
+    if (unit_ok) verify_range(L, p.block_size, tg, g_lo, g_hi, n_tiles);
+    int bad = unit_ok ? 0 : 1;
+    // the first two descriptor batches (page ids fetched before the last
+    // epilogue): cache rows
+    seg_resolve(p, pdiv, h, vcur, bad);
+    seg_resolve(p, pdiv, h, vnxt, bad);
+    Seg sa = {}, sb = {};
+    if (n_tiles > 0) {
+      sa = seg_of(p, vcur, vnxt, false, 0);
+      sb = seg_of(p, vcur, vnxt, false, 1);
+    }
+    TileRegs<D, 1> regs;
+    if (du >= 0) {
+      // the previous unit's draft; its last tile prefetches this verify's first
+      run_draft<D>(p, du, reinterpret_cast<const int32_t*>(smem + p.off_sel), dn, smem + p.off_dq,
+                   smem, regs, n_tiles > 0, sa, sb, pdiv);
+      // this unit's Q operand from where the last epilogue parked it; every
+      // wave holds it before any block mass overwrites it
+      const char* qpark = smem + p.off_ell;
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) {
+        const bf16x8 z = {};
+        qreg[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(qpark + rl * G::K_STRIDE + 32 * ks + 16 * hl)
+                          : z;
+      }
+      __syncthreads();
+    } else if (n_tiles > 0) {
+      load_tile<D, 1>(regs, p.k, p.v, sa, sb, lane);
+    }
+
+    // ---- verify of unit u: this token group's tiles ----
+    {
+      float* const ell_s = reinterpret_cast<float*>(smem + p.off_ell);
+      const FastDiv bdiv(p.block_size);
+      const int bs = p.block_size;
+      const int R = p.rows;
+      const float scl = fmaxf(fabsf(p.scale_log2), 1e-30f);
+      const int pos_r = L - p.n_q + (row_ok ? r / p.group : 0);
+      const int pos_min = L - p.n_q;
+      Acc<D> a;
+      acc_init(a);
+      float blk_run = 0.f;
+      int cur_batch = 0;
+      for (int t = 0; t < n_tiles; ++t) {
+        const int rel0 = 2 * t;
+        const bool tile_live = g_lo + rel0 < g_hi;
+        const Seg ca = sa, cb = sb;
+        const bool full = seg_full(ca) && seg_full(cb);
+        store_tile<D, 1>(regs, grp, lane, ca, cb, full);
+        if (rel0 > 0 && (rel0 & 63) == 0) {
+          vcur = vnxt;
+          ++cur_batch;
+          vnxt = seg_lane<false>(p, nullptr, b, h, g_lo + 64 * (cur_batch + 1) + lane, g_hi, 0, L, L);
+        }
+        if ((rel0 & 63) == 32) seg_resolve(p, pdiv, h, vnxt, bad);
+        group_sync<1>();
+        if (t + 1 < n_tiles) {
+          const int ra = rel0 + 2, rb = ra + 1;
+          sa = seg_of(p, vcur, vnxt, (ra >> 6) != cur_batch, ra & 63);
+          sb = seg_of(p, vcur, vnxt, (rb >> 6) != cur_batch, rb & 63);
+          load_tile<D, 1>(regs, p.k, p.v, sa, sb, lane);
+        }
+        if (tile_live) {
+          const f32x16 sacc = qk_tile<D>(grp, qreg, rl, hl);
+          float s[16], pr[16], psum;
+          const bool interior = full && cb.t0 + kSeg - 1 <= pos_min;
+          const float mx = mask_logits(sacc, s, ca, cb, interior, pos_r, hl);
+          const float m_use = softmax_pv<D>(a, s, mx, scl, grp + G::K_BYTES, pr, psum, blk_run, rl, hl);
+          // per-block log mass of this row, frame m_use
+          if (bs == kSeg) {
+            float x = 0.f, y = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x += pr[i];
+#pragma unroll
+            for (int i = 8; i < 16; ++i) y += pr[i];
+            x += __shfl_xor(x, 32);
+            y += __shfl_xor(y, 32);
+            const Seg& mine = hl ? cb : ca;
+            if (row_ok && mine.lo < mine.hi)
+              ell_s[(mine.t0 / kSeg) * R + r] = m_use + fast_log2(hl ? y : x);
+          } else {
+            blk_run += psum;
+            const bool last = (bdiv.mod(ca.t0 + 2 * kSeg) == 0) || (g_lo + rel0 + 2 >= g_hi);
+            if (last) {
+              const float tot = blk_run + __shfl_xor(blk_run, 32);
+              if (row_ok && hl == 0) ell_s[bdiv.div(ca.t0) * R + r] = m_use + fast_log2(tot);
+              blk_run = 0.f;
+            }
+          }
+        }
+        group_sync<1>();
+      }
+
+      // ---- the next unit's Q rows and page ids, and this unit's draft
+      // query rows, in flight during the epilogue ----
+      const bool more = k + 1 < nmine;
+      if (more) {
+        const int un = persist_unit(blockIdx.x + (k + 1) * grid, p.batch, p.num_kv_heads);
+        verify_q_chunks<D>(p, un, qpre);
+        verify_segs(p, un, tg, vcur, vnxt);
+      }
+      {
+        char* const dq = smem + p.off_dq;
+        const int Gd = p.group;
+        for (int e = tid; e < Gd * G::CPT; e += kPersistThreads) {
+          const int row = e / G::CPT, cc = e % G::CPT;
+          uint4 v = *reinterpret_cast<const uint4*>(
+              p.dq + ((long long)b * p.num_q_heads + h * Gd + row) * D + 8 * cc);
+          if (p.dscale_log2 < 0.f) {
+            v.x ^= 0x80008000u;
+            v.y ^= 0x80008000u;
+            v.z ^= 0x80008000u;
+            v.w ^= 0x80008000u;
+          }
+          *reinterpret_cast<uint4*>(dq + row * G::K_STRIDE + 16 * cc) = v;
+        }
+      }
+
+      // ---- epilogue: token groups merged, outputs, block scores, selection ----
+      float* const lse2s = reinterpret_cast<float*>(smem + p.off_lse);
+      a.l += __shfl_xor(a.l, 32);
+      bad = __syncthreads_or(bad);
+      merge_groups<D>(a, reinterpret_cast<float*>(smem), tg, rl, hl, 32);
+      if (tg == 0 && row_ok) {
+        const long long orow =
+            ((long long)b * p.n_q + r / p.group) * p.num_q_heads + h * p.group + r % p.group;
+        const float lse2 = write_row<D>(a, p.o, p.lse, orow, bad != 0, hl);
+        if (hl == 0) lse2s[r] = lse2;
+      }
+      __threadfence_block();
+      __syncthreads();
+      uint32_t* const keys = reinterpret_cast<uint32_t*>(smem);
+      int ncand, n;
+      topk_bounds(L, bs, p.topk_window, p.max_blocks, p.budget[b], p.max_sel, ncand, n);
+      {
+        const int nblk = unit_ok ? ceil_div(L, bs) : 0;
+        const int r0 = p.score_row_start * p.group;
+        float* scores = p.block_scores + (long long)u * p.max_blocks;
+        for (int j = tid; j < p.max_blocks; j += kPersistThreads) {
+          float sc = 0.f;
+          if (j < nblk) {
+            const float* e = ell_s + (long long)j * R;
+            for (int rr = r0; rr < R; ++rr) sc += fast_exp2(e[rr] - lse2s[rr]);
+          }
+          sc = bad ? qnan() : sc;
+          scores[j] = sc;
+          if (j < ncand) keys[j] = score_key(sc);
+        }
+      }
+      if (tid == 0) p.sel_count[u] = n;
+      __syncthreads();
+      // the block masses are dead: park the next unit's Q rows there
+      if (more) {
+        char* const qpark = smem + p.off_ell;
+#pragma unroll
+        for (int j = 0; j < kQChunks; ++j) {
+          const int e = tid + kPersistThreads * j;
+          const int row = e / G::CPT, cc = e % G::CPT;
+          if (row < 32) *reinterpret_cast<uint4*>(qpark + row * G::K_STRIDE + 16 * cc) = qpre[j];
+        }
+      }
+      topk_select_parked<kPersistThreads>(
+          keys, ncand, n, p.sel + (long long)u * p.max_sel, p.max_sel,
+          reinterpret_cast<int32_t*>(smem + p.off_sel),
+          reinterpret_cast<int*>(smem + 2 * G::GROUP_BYTES - kTopkLdsBytes));
+      dn = n;
+    }
+    du = u;
+  }
+
+  // the last unit's draft
+  if (du >= 0) {
+    TileRegs<D, 1> regs;
+    const Seg z = {};
+    run_draft<D>(p, du, reinterpret_cast<const int32_t*>(smem + p.off_sel), dn, smem + p.off_dq,
+                 smem, regs, false, z, z, pdiv);
+  }
+}
+
+}  // namespace
+
+// LDS layout of the persistent step workgroup: two tile buffers (also the
+// token-group merge scratch, the Top-N keys and the selection scratch), the
+// unit's block log masses, row log2-LSEs, the selection, the draft rows.
+// Returns the bytes, or 0 when the step does not fit (keys or scratch).
+size_t persist_lds(int head_dim, int rows, int group, int max_blocks, int max_sel, int32_t& off_ell,
+                   int32_t& off_lse, int32_t& off_sel, int32_t& off_dq) {
+  const size_t group_bytes = (size_t)32 * (head_dim * 2 + 16) + (size_t)head_dim * 64;
+  const size_t tiles = 2 * group_bytes;
+  if ((size_t)max_blocks * 4 + kTopkLdsBytes > tiles) return 0;
+  size_t off = tiles;
+  off_ell = (int32_t)off;
+  // the block masses, or the next unit's Q rows parked there
+  off += align_up(std::max((size_t)max_blocks * rows * 4, (size_t)32 * (head_dim * 2 + 16)), 16);
+  off_lse = (int32_t)off;
+  off += align_up((size_t)rows * 4, 16);
+  off_sel = (int32_t)off;
+  off += align_up((size_t)max_sel * 4, 16);
+  off_dq = (int32_t)off;
+  off += (size_t)group * (head_dim * 2 + 16);
+  return off;
+}
+
+hipError_t launch_persist_step(const AttnParams& pv, const AttnParams& pd, int max_sel,
+                               int topk_window, const int32_t* budget, int32_t* sel,
+                               int32_t* sel_count, int grid, hipStream_t s) {
+  PersistParams p = {};
+  p.k = reinterpret_cast<const bf16*>(pv.k);
+  p.v = reinterpret_cast<const bf16*>(pv.v);
+  p.page_table = pv.page_table;
+  p.seq_lens = pv.seq_lens;
+  p.num_pages = pv.num_pages;
+  p.page_size = pv.page_size;
+  p.num_kv_heads = pv.num_kv_heads;
+  p.head_dim = pv.head_dim;
+  p.max_pages = pv.max_pages;
+  p.max_seq_len = pv.max_seq_len;
+  p.block_size = pv.block_size;
+  p.max_blocks = pv.max_blocks;
+  p.score_row_start = pv.score_row_start;
+  p.q = reinterpret_cast<const bf16*>(pv.q);
+  p.o = reinterpret_cast<bf16*>(pv.o);
+  p.lse = pv.lse;
+  p.block_scores = pv.block_scores;
+  p.batch = pv.batch;
+  p.n_q = pv.n_q;
+  p.num_q_heads = pv.num_q_heads;
+  p.group = pv.group;
+  p.rows = pv.rows;
+  p.scale_log2 = pv.scale_log2;
+  p.max_sel = max_sel;
+  p.topk_window = topk_window;
+  p.budget = budget;
+  p.sel = sel;
+  p.sel_count = sel_count;
+  p.dq = reinterpret_cast<const bf16*>(pd.q);
+  p.dout = reinterpret_cast<bf16*>(pd.o);
+  p.dlse = pd.lse;
+  p.dscale_log2 = pd.scale_log2;
+  p.window = pd.window;
+  p.units = pv.batch * pv.num_kv_heads;
+  if (pd.rows != pv.group || pd.num_q_heads != pv.num_q_heads || pd.block_size != pv.block_size)
+    return hipErrorInvalidValue;
+  const size_t lds = persist_lds(pv.head_dim, pv.rows, pv.group, pv.max_blocks, max_sel, p.off_ell,
+                                 p.off_lse, p.off_sel, p.off_dq);
+  if (lds == 0 || lds > kMaxLds) return hipErrorInvalidValue;
+  if (p.units <= 0) return hipSuccess;
+  if (grid > p.units) grid = p.units;
+  auto go = [&](auto kern) -> hipError_t {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)kMaxLds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kPersistThreads), lds, s, p);
+    return hipGetLastError();
+  };
+  if (pv.head_dim == 128) return go(persist_step_kernel<128>);
+  if (pv.head_dim == 64) return go(persist_step_kernel<64>);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sss

@@ -192,6 +192,14 @@ size_t finish_lds(FusedParams& f, int head_dim, int max_blocks, bool draft);
 hipError_t launch_fused_finish(const FusedParams& f, const AttnParams& pv, const AttnParams& pd,
                                int head_dim, size_t lds_bytes, hipStream_t s);
 hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s);
+// Persistent chained step (persist.hip): LDS bytes and offsets of its
+// workgroup (0: the step does not fit), and the launch over `grid`
+// workgroups that loop over the units.
+size_t persist_lds(int head_dim, int rows, int group, int max_blocks, int max_sel, int32_t& off_ell,
+                   int32_t& off_lse, int32_t& off_sel, int32_t& off_dq);
+hipError_t launch_persist_step(const AttnParams& pv, const AttnParams& pd, int max_sel,
+                               int topk_window, const int32_t* budget, int32_t* sel,
+                               int32_t* sel_count, int grid, hipStream_t s);
 // Sparse verify (a layout per query position): LDS bytes beyond the tiles,
 // and the launch.
 size_t sparse_union_lds_bytes(int max_blocks, int n_q, int max_sel);

@@ -91,6 +91,8 @@ class DraftStep(ctypes.Structure):
 _lib.sss_fused_step.restype = _c_int
 _lib.sss_fused_step.argtypes = [ctypes.POINTER(VerifyStep), ctypes.POINTER(DraftStep), _c_int,
                                 _vp, ctypes.c_size_t, _vp]
+_lib.sss_fused_step_form.restype = _c_int
+_lib.sss_fused_step_form.argtypes = [ctypes.POINTER(VerifyStep), ctypes.POINTER(DraftStep), _c_int]
 _lib.sss_fused_workspace_size.restype = ctypes.c_size_t
 _lib.sss_fused_workspace_size.argtypes = [ctypes.POINTER(VerifyStep), ctypes.POINTER(DraftStep),
                                           _c_int]
@@ -106,7 +108,7 @@ _lib.sss_version.restype = _c_int
 _lib.sss_version.argtypes = []
 
 EXPORTED = ["sss_verify_attn", "sss_verify_workspace_size", "sss_verify_attn_noalloc",
-            "sss_block_topk", "sss_draft_attn", "sss_draft_workspace_size", "sss_merge", "sss_fused_step", "sss_fused_workspace_size",
+            "sss_block_topk", "sss_draft_attn", "sss_draft_workspace_size", "sss_merge", "sss_fused_step", "sss_fused_workspace_size", "sss_fused_step_form",
             "sss_kv_write", "sss_kv_commit", "sss_sparse_verify_attn",
             "sss_sparse_verify_workspace_size", "sss_status_string", "sss_last_error",
             "sss_version"]
@@ -388,6 +390,19 @@ def fused_workspace_size(verify=None, draft=None, chained=False) -> int:
     if n == 0 and _lib.sss_last_error():
         raise SSSError(SSS_ERR_INVALID_ARGUMENT, "sss_fused_workspace_size")
     return n
+
+
+FUSED_FORMS = {0: "nothing", 1: "persistent", 2: "two_launch", 3: "work_list"}
+
+
+def fused_step_form(verify=None, draft=None, chained=False) -> str:
+    """sss_fused_step_form: the launch form sss_fused_step takes for these
+    arguments ('persistent', 'two_launch', 'work_list' or 'nothing')."""
+    f = _lib.sss_fused_step_form(_byref_or_null(verify, VerifyStep),
+                                 _byref_or_null(draft, DraftStep), 1 if chained else 0)
+    if f < 0:
+        raise SSSError(SSS_ERR_INVALID_ARGUMENT, "sss_fused_step_form")
+    return FUSED_FORMS[f]
 
 
 def fused_step(verify=None, draft=None, chained=False, ws=None, device=None):

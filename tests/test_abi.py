@@ -391,3 +391,33 @@ def test_probes_reject_bad_arguments():
     assert lib.sss_probe_paged_read(ctypes.addressof(good_kv(sss, page_size=1, head_dim=1)), 2,
                                     256, None) == 2                 # 2-byte runs
     assert lib.sss_probe_paged_read(ctypes.addressof(kv), 0, 256, None) == 0
+
+
+def test_fused_step_form():
+    """The launch form sss_fused_step takes (host query, nothing launched):
+    chained decode steps of >= 512 whole units whose verify runs two
+    workgroups per compute unit are persistent."""
+    sss = _binding()
+
+    def form(batch, L, chained=True, **vkw):
+        kv = dict(num_kv_heads=8, max_seq_len=L, max_pages_per_req=-(-L // 16),
+                  num_pages=batch * -(-L // 16))
+        nblk = -(-L // 16)
+        v, d = fused_args(sss, dict(batch=batch, num_q_heads=32, max_blocks=nblk, max_sel=26,
+                                    **vkw),
+                          dict(batch=batch, num_q_heads=32, max_sel=26), kv)
+        if not chained:
+            d.sel, d.sel_count = 1 << 23, 1 << 24
+        return sss.fused_step_form(v, d, chained)
+
+    assert form(128, 8192) == "persistent"         # the batch-128 x 8K decode step
+    assert form(64, 8192) == "persistent"          # 512 units
+    assert form(128, 1500) == "persistent"
+    assert form(63, 8192) == "work_list"           # 504 units: split to fill the GPU
+    assert form(128, 512) == "two_launch"          # four-group verify fits twice per CU
+    assert form(128, 8192, chained=False) == "work_list"
+    assert form(16, 4096) == "work_list"
+    v, d = fused_args(sss)
+    assert sss.fused_step_form(None, None, False) == "nothing"
+    with pytest.raises(sss.SSSError):
+        sss.fused_step_form(v, None, True)         # chained without a draft half

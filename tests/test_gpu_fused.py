@@ -8,7 +8,9 @@ step's own fp32 scores; the draft against the oracle's draft over the
 step's own selection.  Mixed steps (some requests verify, the others draft
 over given selections) are checked the same way.  Small lengths force the
 work list to split units into many chunks, so the follow-up launches that
-merge, score and select split units run.
+merge, score and select split units run; batches of at least 512 whole
+units run the persistent step kernel (its verify, scores and selection are
+also checked bitwise against the one-stage-at-a-time calls).
 """
 import numpy as np
 import pytest
@@ -98,15 +100,36 @@ def test_fused_chained(case):
         f"fused {cid} draft")
 
 
-@pytest.mark.parametrize("L", [512, 1500])
-def test_fused_chained_matches_separate_calls(L):
-    """A chained step of whole units runs the one-launch-per-stage verify
-    kernel itself: verify outputs, scores and selection are bitwise equal.
-    (A batch of 1024 units keeps every unit in one chunk; smaller batches are
+def step_form(wl, chained=True):
+    s = H.sss()
+    vb, db = wl.verify, wl.draft
+    o, lse, sc, sel, cnt = verify_outputs(wl, vb)
+    kv = H.kv_of(wl, vb)
+    v = s.verify_step(kv, vb.q, wl.sm_scale, wl.shape.block_size, wl.max_blocks, o, lse, sc,
+                      budget=vb.budget, window=wl.shape.window, sel=sel, sel_count=cnt)
+    d = s.draft_step(kv, db.q, wl.sm_scale, wl.shape.block_size, sel, cnt, wl.shape.window,
+                     torch.empty_like(db.q), torch.empty(db.q.shape[:3], device=DEV))
+    return s.fused_step_form(v, d, chained)
+
+
+def nan_equal(a, b):
+    if a.dtype == torch.bfloat16:
+        return torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    return bool(((a == b) | (torch.isnan(a) & torch.isnan(b))).all())
+
+
+@pytest.mark.parametrize("L,form", [(512, "two_launch"), (1500, "persistent")])
+def test_fused_chained_matches_separate_calls(L, form):
+    """A chained step of whole units runs the one-launch-per-stage verify's
+    arithmetic: verify outputs, scores and selection are bitwise equal.  (A
+    batch of 1024 units keeps every unit in one chunk; smaller batches are
     split to fill the GPU.  At 1500 tokens the block masses make the verify
-    run as two-token-group workgroups, two per compute unit.)"""
+    run as two-token-group workgroups, two per compute unit, and the step
+    runs persistently: its draft splits each list over two token groups, so
+    it equals the separate draft up to summation order.)"""
     wl = mk("decode_b128_l8192", seed=32, B=128, L=L)
     vb = wl.verify
+    assert step_form(wl) == form
     v_out, (sel, cnt), d_out = run_chained(wl)
     o, lse, sc = H.gpu_verify(wl, vb, num_splits=1)
     sel2, cnt2 = H.gpu_topk(wl, vb, sc)
@@ -115,11 +138,106 @@ def test_fused_chained_matches_separate_calls(L):
     assert torch.equal(v_out[1], lse)
     assert torch.equal(v_out[2], sc)
     assert torch.equal(sel, sel2) and torch.equal(cnt, cnt2)
-    # 1024 units: the step drafts with the separate draft kernel itself
     od, lsed = H.gpu_draft(wl, wl.draft, sel2, cnt2)
     torch.cuda.synchronize()
-    assert torch.equal(d_out[0].view(torch.uint8), od.view(torch.uint8))
-    assert torch.equal(d_out[1], lsed)
+    if form == "two_launch":
+        # 1024 units: the step drafts with the separate draft kernel itself
+        assert torch.equal(d_out[0].view(torch.uint8), od.view(torch.uint8))
+        assert torch.equal(d_out[1], lsed)
+    else:
+        assert torch.isfinite(d_out[0].float()).all() and torch.isfinite(d_out[1]).all()
+        assert (d_out[0].float() - od.float()).abs().max().item() <= H.O_MAX_ABS
+        assert (d_out[1] - lsed).abs().max().item() <= H.LSE_ABS
+        H.compare_draft(wl, wl.draft, d_out, sel.cpu().numpy(), cnt.cpu().numpy(),
+                        H.sample_units(wl.draft, wl.shape.Hkv, 24, seed=3)).check(
+            "persistent draft")
+
+
+# Chained steps the persistent kernel runs (at least 512 whole units whose
+# verify takes two workgroups per compute unit): ragged lengths, a batch
+# that is not a multiple of 8 (no XCD-aware order, units not a multiple of
+# the grid), blocks of 32 tokens (block masses summed over two segments),
+# head dim 64.  Oracle units: "all", or a seeded sample of that many.
+PERSIST = [
+    ("ragged_b128", "decode_b128_l8192", dict(B=128, L=(1000, 2000), sigma="one"), "all"),
+    ("b100_not_mult8", "decode_b128_l8192", dict(B=100, L=1500, sigma="one"), 48),
+    ("blk32_b64", "qwen3_8b_layer_b16_l4096", dict(B=64, L=3000, block_size=32, sigma="one"), 32),
+    ("d64_b64", "decode_b128_l8192", dict(B=64, L=8400, d=64, sigma="one"), 16),
+    ("nq1_b128", "decode_b128_l8192", dict(B=128, L=(5000, 6000), n_q=1, sigma="one"), 32),
+]
+
+
+@pytest.mark.parametrize("case", PERSIST, ids=[c[0] for c in PERSIST])
+def test_fused_persistent(case):
+    cid, name, kw, nunits = case
+    wl = mk(name, seed=41, **kw)
+    vb, db = wl.verify, wl.draft
+    hkv = wl.shape.Hkv
+    print(f"[fused persistent] {cid}", flush=True)
+    assert step_form(wl) == "persistent"
+    v_out, (sel, cnt), d_out = run_chained(wl)
+    # verify arithmetic, scores and selection: bitwise those of the
+    # one-launch-per-stage calls
+    o, lse, sc = H.gpu_verify(wl, vb, num_splits=1)
+    sel2, cnt2 = H.gpu_topk(wl, vb, sc)
+    torch.cuda.synchronize()
+    assert torch.equal(v_out[0].view(torch.uint8), o.view(torch.uint8))
+    assert torch.equal(v_out[1], lse) and torch.equal(v_out[2], sc)
+    assert torch.equal(sel, sel2) and torch.equal(cnt, cnt2)
+    # every unit's outputs written and finite
+    for t in (*v_out, *d_out):
+        assert torch.isfinite(t.float()).all()
+    units = H.all_units(vb, hkv) if nunits == "all" else H.sample_units(vb, hkv, nunits, seed=4)
+    H.compare_verify(wl, vb, v_out, units).check(f"persistent {cid} verify")
+    sel_np, cnt_np = check_selection(wl, vb, v_out[2], sel, cnt)
+    H.compare_draft(wl, db, d_out, sel_np, cnt_np, units).check(f"persistent {cid} draft")
+    # the draft against the separate draft kernel on the same selection, all units
+    od, lsed = H.gpu_draft(wl, db, sel2, cnt2)
+    torch.cuda.synchronize()
+    assert (d_out[0].float() - od.float()).abs().max().item() <= H.O_MAX_ABS
+    assert (d_out[1] - lsed).abs().max().item() <= H.LSE_ABS
+
+
+def test_fused_persistent_poisoned_requests():
+    """A request longer than max_seq_len and one with an out-of-range page id
+    poison only their own units, as in the separate calls."""
+    wl = mk("decode_b128_l8192", seed=42, B=64, L=1500)
+    vb, db = wl.verify, wl.draft
+    assert step_form(wl) == "persistent"
+    s = H.sss()
+    lens = vb.seq_lens.clone()
+    lens[3] = 100000
+    table = vb.page_table.clone()
+    table[5, 7] = -3
+    kv = s.paged_kv(wl.k_cache, wl.v_cache, table, lens, 1500)
+    o, lse, sc, sel, cnt = verify_outputs(wl, vb)
+    od = torch.full_like(db.q, 7.0)
+    lsed = torch.full(db.q.shape[:3], 7.0, device=DEV)
+    v = s.verify_step(kv, vb.q, wl.sm_scale, 16, wl.max_blocks, o, lse, sc, budget=vb.budget,
+                      window=wl.shape.window, sel=sel, sel_count=cnt)
+    d = s.draft_step(kv, db.q, wl.sm_scale, 16, sel, cnt, wl.shape.window, od, lsed)
+    assert s.fused_step_form(v, d, True) == "persistent"
+    s.fused_step(v, d, chained=True)
+    # the same calls one stage at a time
+    o2, lse2, sc2 = (torch.empty_like(t) for t in (o, lse, sc))
+    s.verify_attn(kv, vb.q, wl.sm_scale, 16, wl.max_blocks, o2, lse2, sc2, num_splits=1)
+    sel2, cnt2 = torch.empty_like(sel), torch.empty_like(cnt)
+    s.block_topk(sc2, lens, 16, vb.budget, wl.shape.window, sel2, cnt2)
+    od2, lsed2 = torch.empty_like(od), torch.empty_like(lsed)
+    s.draft_attn(kv, db.q, wl.sm_scale, 16, sel2, cnt2, wl.shape.window, od2, lsed2)
+    torch.cuda.synchronize()
+    for b in (3, 5):
+        for t in (o[b].float(), lse[b], sc[b]):
+            assert torch.isnan(t).all()
+    assert torch.isnan(od[3].float()).all() and torch.isnan(lsed[3]).all()
+    good = [b for b in range(vb.B) if b not in (3, 5)]
+    for t in (o[good].float(), lse[good], sc[good], od[good].float(), lsed[good]):
+        assert torch.isfinite(t).all()
+    assert nan_equal(o, o2) and nan_equal(lse, lse2) and nan_equal(sc, sc2)
+    assert torch.equal(sel, sel2) and torch.equal(cnt, cnt2)
+    assert torch.equal(torch.isnan(lsed), torch.isnan(lsed2))
+    fin = torch.isfinite(lsed)
+    assert (lsed[fin] - lsed2[fin]).abs().max().item() <= H.LSE_ABS
 
 
 def test_fused_score_row_start_one():
