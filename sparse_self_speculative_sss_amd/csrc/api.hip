@@ -537,9 +537,8 @@ sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int ch
     const bool two_per_cu = fs.rows_v <= 32 && v->block_size != 1 &&
                             mfma_smem_bytes(D, 1, 4, ellf) > kMaxLds / 2 &&
                             mfma_smem_bytes(D, 1, 2, ellf, true) <= kMaxLds / 2;
-    int32_t o1, o2, o3, o4;
-    const size_t lds =
-        persist_lds(D, fs.rows_v, fs.group_d, v->max_blocks, v->max_sel, o1, o2, o3, o4);
+    int32_t offs[5];
+    const size_t lds = persist_lds(D, fs.rows_v, fs.group_d, v->max_blocks, v->max_sel, offs);
     fs.persist = two_per_cu && lds > 0 && lds <= kMaxLds / 2 && fs.group_d <= 32 &&
                  list_max_d <= 2 * 64 && fs.nv >= kPersistMinUnits;
   }

@@ -13,13 +13,11 @@
 // Workgroup w loops over the units w, w + grid, w + 2 grid, ... (in the
 // XCD-aware order of the one-item kernels).  For each unit it first drafts
 // the unit it verified before -- that unit's selection and draft query are
-// still in its LDS -- and then verifies the new unit; the draft's last tile
-// prefetches the verify's first.  The short, latency-bound dependent chain
+// still in its LDS -- and then verifies the new unit.  The short, latency-bound dependent chain
 // of draft tiles therefore runs while the other workgroup on the compute
 // unit keeps streaming the cache, instead of in launches after the whole
-// verify.  The next unit's Q and page ids are loaded before the epilogue
-// (token-group merge, outputs, block scores, selection), so they arrive
-// while it runs.  Only the last unit of each workgroup is drafted at the
+// verify.  The next unit's Q and page ids are loaded during the selection,
+// so they arrive while it runs.  Only the last unit of each workgroup is drafted at the
 // end.  No workgroup waits for another: every dependency (block masses ->
 // scores -> selection -> draft) stays inside one workgroup.
 //
@@ -41,6 +39,7 @@ namespace {
 constexpr int kPersistWaves = 2;  // token groups (waves) per workgroup
 constexpr int kPersistThreads = 64 * kPersistWaves;
 constexpr int kTopkLdsBytes = (kTopkLdsWords * 4 + 127) / 128 * 128;
+constexpr int kWaveTopkKeys = 16;  // keys per lane of the one-wave selection (1024 candidates)
 
 // Everything the persistent step reads: one paged cache serves both halves
 // (a chained step drafts the requests it verifies), so the draft half adds
@@ -74,9 +73,9 @@ struct PersistParams {
   int32_t window;
   int32_t units;  // batch x KV heads
   // LDS byte offsets: the unit's block log masses (or the next unit's Q
-  // rows parked there), the row log2-LSEs, the selection the next draft
-  // reads, the draft query rows
-  int32_t off_ell, off_lse, off_sel, off_dq;
+  // rows parked there), the row log2-LSEs, two flags, the selection the
+  // next draft reads and its draft query rows
+  int32_t off_ell, off_lse, off_flags, off_sel, off_dq;
 };
 
 // Unit run by the i-th workgroup slot: all KV heads of request r on XCD r % 8
@@ -233,7 +232,8 @@ __device__ __forceinline__ f32x16 qk_tile_lds(const char* gt, const char* qt, in
 // Combines the two token groups' (m, l, O) of one row tile through LDS at
 // `red` (tg 1 writes, tg 0 reads after the barrier; rows < nrows) and
 // leaves the result in token group 0's `a`.  Same arithmetic and order as
-// attn_item's token-group merge.  All threads call it; it has one barrier.
+// attn_item's token-group merge.  All threads call it; it has one (LDS-only)
+// barrier.
 template <int D>
 __device__ __forceinline__ void merge_groups(Acc<D>& a, float* red, int tg, int rl, int hl,
                                              int nrows) {
@@ -254,7 +254,7 @@ __device__ __forceinline__ void merge_groups(Acc<D>& a, float* red, int tg, int 
         *reinterpret_cast<f32x4*>(dst + 32 * mt + 8 * q4 + 4 * hl) = v4;
       }
   }
-  __syncthreads();
+  lds_barrier();
   if (tg == 0) {
     float mg = fmaxf(a.m, ml[32 + rl]);
     const float mu = (mg == neg_inf()) ? 0.f : mg;
@@ -280,6 +280,15 @@ __device__ __forceinline__ void merge_groups(Acc<D>& a, float* red, int tg, int 
     a.m = mg;
     a.l = lsum;
   }
+}
+
+// OR of v over the workgroup's two waves through LDS slots `flags` (two
+// ints), at an LDS-only barrier.
+__device__ __forceinline__ int lds_barrier_or(int v, int* flags) {
+  const bool any = __builtin_amdgcn_ballot_w64(v != 0) != 0;
+  if ((threadIdx.x & 63) == 0) flags[threadIdx.x >> 6] = any ? 1 : 0;
+  lds_barrier();
+  return flags[0] | flags[1];
 }
 
 // Normalised O (bf16) and LSE (natural log) of row `orow`; bad poisons.
@@ -310,7 +319,7 @@ __device__ __forceinline__ float write_row(const Acc<D>& a, bf16* o, float* lse,
 // prefetches the first verify tile (segments vs0, vs1) into `regs`.
 template <int D>
 __device__ __forceinline__ void run_draft(const PersistParams& pd, int du, const int32_t* sel_s,
-                                          int nsel, const char* dq, char* smem,
+                                          int nsel, const char* dq, char* smem, int* flags,
                                           TileRegs<D, 1>& regs, bool vnext, const Seg& vs0,
                                           const Seg& vs1, const FastDiv& pdiv) {
   typedef Geo<D> G;
@@ -373,7 +382,7 @@ __device__ __forceinline__ void run_draft(const PersistParams& pd, int du, const
     group_sync<1>();
   }
   a.l += __shfl_xor(a.l, 32);
-  bad = __syncthreads_or(bad);  // both groups are done with their tile buffers
+  bad = lds_barrier_or(bad, flags);  // both groups are done with their tile buffers
   merge_groups<D>(a, reinterpret_cast<float*>(smem), tg, rl, hl, Gd);
   if (tg == 0 && rl < Gd) {
     const long long orow = (long long)bd * pd.num_q_heads + hd * Gd + rl;
@@ -413,27 +422,89 @@ __device__ __forceinline__ void verify_segs(const PersistParams& p, int u, int t
 }
 
 // Unit u's Q rows as 16-byte chunks, chunk e = row * CPT + column for
-// e = threadIdx.x + 128 j; rows >= rows are zero, a negative scale folded in.
+// e = threadIdx.x + 128 j (rows < 32), loaded unconditionally (a row past
+// the unit's reads row 0; it is zeroed when parked).  The loads are left in
+// flight: park_q_chunks consumes them later.
 template <int D, int NQ>
 __device__ __forceinline__ void verify_q_chunks(const PersistParams& p, int u, uint4 (&qc)[NQ]) {
   const int b = u / p.num_kv_heads, h = u % p.num_kv_heads;
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     const int e = (int)threadIdx.x + kPersistThreads * j;
+    const int row0 = e / Geo<D>::CPT, cc = e % Geo<D>::CPT;
+    const int row = row0 < p.rows ? row0 : 0;
+    const int iq = row / p.group, hq = h * p.group + row % p.group;
+    qc[j] = *reinterpret_cast<const uint4*>(p.q + (((long long)b * p.n_q + iq) * p.num_q_heads + hq) * D +
+                                            8 * cc);
+  }
+}
+
+// The chunks of verify_q_chunks into LDS at qpark (row stride K_STRIDE):
+// rows past the unit's zeroed, a negative scale folded in (exact sign flip).
+template <int D, int NQ>
+__device__ __forceinline__ void park_q_chunks(const PersistParams& p, const uint4 (&qc)[NQ],
+                                              char* qpark) {
+  const uint32_t flip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int e = (int)threadIdx.x + kPersistThreads * j;
     const int row = e / Geo<D>::CPT, cc = e % Geo<D>::CPT;
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (row < p.rows) {
-      const int iq = row / p.group, hq = h * p.group + row % p.group;
-      v = *reinterpret_cast<const uint4*>(p.q + (((long long)b * p.n_q + iq) * p.num_q_heads + hq) * D +
-                                          8 * cc);
-      if (p.scale_log2 < 0.f) {
-        v.x ^= 0x80008000u;
-        v.y ^= 0x80008000u;
-        v.z ^= 0x80008000u;
-        v.w ^= 0x80008000u;
-      }
+    if (row < 32) {
+      uint4 v = qc[j];
+      v.x ^= flip;
+      v.y ^= flip;
+      v.z ^= flip;
+      v.w ^= flip;
+      if (row >= p.rows) v = uint4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<uint4*>(qpark + row * Geo<D>::K_STRIDE + 16 * cc) = v;
     }
-    qc[j] = v;
+  }
+}
+
+// Block scores of a unit from its block log masses: sc_j = sum over rows
+// r0 <= r < R of 2^(ell[j][r] - lse2[r]), rows summed in order (as attn_item
+// does, so the scores are bitwise equal); written to `scores` (0 past nblk,
+// NaN if bad) and, for j < ncand, parked as Top-N keys.  Rows are read as
+// float4 when they allow it, all of a block's at once.
+__device__ __forceinline__ void unit_scores(const float* ell, const float* lse2, int R, int r0,
+                                            int nblk, int max_blocks, bool bad, int ncand,
+                                            float* scores, uint32_t* keys) {
+  const int tid = threadIdx.x;
+  if ((R & 3) == 0 && (r0 & 3) == 0 && R - r0 <= 32) {
+    const int nq4 = (R - r0) >> 2;
+    for (int j = tid; j < max_blocks; j += kPersistThreads) {
+      float sc = 0.f;
+      if (j < nblk) {
+        const f32x4* e = reinterpret_cast<const f32x4*>(ell + (long long)j * R + r0);
+        f32x4 x[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (q < nq4) x[q] = e[q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (q < nq4) {
+            const float* l2 = lse2 + r0 + 4 * q;
+            sc += fast_exp2(x[q][0] - l2[0]);
+            sc += fast_exp2(x[q][1] - l2[1]);
+            sc += fast_exp2(x[q][2] - l2[2]);
+            sc += fast_exp2(x[q][3] - l2[3]);
+          }
+      }
+      sc = bad ? qnan() : sc;
+      scores[j] = sc;
+      if (j < ncand) keys[j] = score_key(sc);
+    }
+  } else {
+    for (int j = tid; j < max_blocks; j += kPersistThreads) {
+      float sc = 0.f;
+      if (j < nblk) {
+        const float* e = ell + (long long)j * R;
+        for (int rr = r0; rr < R; ++rr) sc += fast_exp2(e[rr] - lse2[rr]);
+      }
+      sc = bad ? qnan() : sc;
+      scores[j] = sc;
+      if (j < ncand) keys[j] = score_key(sc);
+    }
   }
 }
 
@@ -448,6 +519,7 @@ __global__ void __launch_bounds__(kPersistThreads, 1) persist_step_kernel(Persis
   const int r = rl;
   const bool row_ok = r < p.rows;
   char* const grp = smem + tg * G::GROUP_BYTES;
+  int* const flags = reinterpret_cast<int*>(smem + p.off_flags);
   const int grid = gridDim.x;
   const int nmine = p.units > (int)blockIdx.x ? (p.units - (int)blockIdx.x + grid - 1) / grid : 0;
   // the next unit's Q rows: loaded into qpre before an epilogue, parked in
@@ -459,7 +531,7 @@ __global__ void __launch_bounds__(kPersistThreads, 1) persist_step_kernel(Persis
   SegLane vcur = {}, vnxt = {};
   const FastDiv pdiv(p.page_size);
 
-  int du = -1, dn = 0;  // unit whose draft is pending, its selection's length
+  int du = -1, dn = 0;  // the unit verified last (its draft is pending), its selection's length
   if (nmine > 0) {
     const int u0 = persist_unit(blockIdx.x, p.batch, p.num_kv_heads);
     const int b0 = u0 / p.num_kv_heads, h0 = u0 % p.num_kv_heads;
@@ -475,6 +547,7 @@ __global__ void __launch_bounds__(kPersistThreads, 1) persist_step_kernel(Persis
     const int b = u / p.num_kv_heads, h = u % p.num_kv_heads;
     const int L = p.seq_lens[b];
     const bool unit_ok = verify_unit_ok(p, L);
+    const int budget = p.budget[b];
     int g_lo = 0, g_hi = 0, n_tiles = 0;
     if (unit_ok) verify_range(L, p.block_size, tg, g_lo, g_hi, n_tiles);
     int bad = unit_ok ? 0 : 1;
@@ -489,9 +562,17 @@ __global__ void __launch_bounds__(kPersistThreads, 1) persist_step_kernel(Persis
     }
     TileRegs<D, 1> regs;
     if (du >= 0) {
-      // the previous unit's draft; its last tile prefetches this verify's first
+      // the last unit's draft (handing its last tile's prefetch over to this
+      // verify keeps the verify's first segments live through the draft, and
+      // the two then overflow the register file)
+      const Seg z = {};
       run_draft<D>(p, du, reinterpret_cast<const int32_t*>(smem + p.off_sel), dn, smem + p.off_dq,
-                   smem, regs, n_tiles > 0, sa, sb, pdiv);
+                   smem, flags, regs, false, z, z, pdiv);
+    }
+    if (n_tiles > 0) {
+      load_tile<D, 1>(regs, p.k, p.v, sa, sb, lane);
+    }
+    if (k > 0) {
       // this unit's Q operand from where the last epilogue parked it; every
       // wave holds it before any block mass overwrites it
       const char* qpark = smem + p.off_ell;
@@ -501,9 +582,7 @@ __global__ void __launch_bounds__(kPersistThreads, 1) persist_step_kernel(Persis
         qreg[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(qpark + rl * G::K_STRIDE + 32 * ks + 16 * hl)
                           : z;
       }
-      __syncthreads();
-    } else if (n_tiles > 0) {
-      load_tile<D, 1>(regs, p.k, p.v, sa, sb, lane);
+      lds_barrier();
     }
 
     // ---- verify of unit u: this token group's tiles ----
@@ -569,35 +648,14 @@ __global__ void __launch_bounds__(kPersistThreads, 1) persist_step_kernel(Persis
         group_sync<1>();
       }
 
-      // ---- the next unit's Q rows and page ids, and this unit's draft
-      // query rows, in flight during the epilogue ----
       const bool more = k + 1 < nmine;
-      if (more) {
-        const int un = persist_unit(blockIdx.x + (k + 1) * grid, p.batch, p.num_kv_heads);
-        verify_q_chunks<D>(p, un, qpre);
-        verify_segs(p, un, tg, vcur, vnxt);
-      }
-      {
-        char* const dq = smem + p.off_dq;
-        const int Gd = p.group;
-        for (int e = tid; e < Gd * G::CPT; e += kPersistThreads) {
-          const int row = e / G::CPT, cc = e % G::CPT;
-          uint4 v = *reinterpret_cast<const uint4*>(
-              p.dq + ((long long)b * p.num_q_heads + h * Gd + row) * D + 8 * cc);
-          if (p.dscale_log2 < 0.f) {
-            v.x ^= 0x80008000u;
-            v.y ^= 0x80008000u;
-            v.z ^= 0x80008000u;
-            v.w ^= 0x80008000u;
-          }
-          *reinterpret_cast<uint4*>(dq + row * G::K_STRIDE + 16 * cc) = v;
-        }
-      }
 
-      // ---- epilogue: token groups merged, outputs, block scores, selection ----
+      // ---- epilogue: token groups merged, outputs, block scores, selection
+      // (every exchange through LDS, so the barriers wait for no memory
+      // operation in flight) ----
       float* const lse2s = reinterpret_cast<float*>(smem + p.off_lse);
       a.l += __shfl_xor(a.l, 32);
-      bad = __syncthreads_or(bad);
+      bad = lds_barrier_or(bad, flags);
       merge_groups<D>(a, reinterpret_cast<float*>(smem), tg, rl, hl, 32);
       if (tg == 0 && row_ok) {
         const long long orow =
@@ -605,45 +663,64 @@ __global__ void __launch_bounds__(kPersistThreads, 1) persist_step_kernel(Persis
         const float lse2 = write_row<D>(a, p.o, p.lse, orow, bad != 0, hl);
         if (hl == 0) lse2s[r] = lse2;
       }
-      __threadfence_block();
-      __syncthreads();
+      lds_barrier();
       uint32_t* const keys = reinterpret_cast<uint32_t*>(smem);
       int ncand, n;
-      topk_bounds(L, bs, p.topk_window, p.max_blocks, p.budget[b], p.max_sel, ncand, n);
-      {
-        const int nblk = unit_ok ? ceil_div(L, bs) : 0;
-        const int r0 = p.score_row_start * p.group;
-        float* scores = p.block_scores + (long long)u * p.max_blocks;
-        for (int j = tid; j < p.max_blocks; j += kPersistThreads) {
-          float sc = 0.f;
-          if (j < nblk) {
-            const float* e = ell_s + (long long)j * R;
-            for (int rr = r0; rr < R; ++rr) sc += fast_exp2(e[rr] - lse2s[rr]);
-          }
-          sc = bad ? qnan() : sc;
-          scores[j] = sc;
-          if (j < ncand) keys[j] = score_key(sc);
-        }
-      }
+      topk_bounds(L, bs, p.topk_window, p.max_blocks, budget, p.max_sel, ncand, n);
+      unit_scores(ell_s, lse2s, R, p.score_row_start * p.group, unit_ok ? ceil_div(L, bs) : 0,
+                  p.max_blocks, bad != 0, ncand, p.block_scores + (long long)u * p.max_blocks, keys);
       if (tid == 0) p.sel_count[u] = n;
-      __syncthreads();
-      // the block masses are dead: park the next unit's Q rows there
+      lds_barrier();
+      // in flight during the selection: the next unit's Q rows and page ids,
+      // this unit's draft query rows (consumed after it, so no load is waited
+      // for inside the latency-bound phases)
       if (more) {
-        char* const qpark = smem + p.off_ell;
+        const int un = persist_unit(blockIdx.x + (k + 1) * grid, p.batch, p.num_kv_heads);
+        verify_q_chunks<D>(p, un, qpre);
+        verify_segs(p, un, tg, vcur, vnxt);
+      }
+      const int Gd = p.group;
+      const bool dq_mine = tid < Gd * G::CPT;  // group <= 32: at most 512 chunks
+      uint4 dqc[kQChunks];
+#pragma unroll
+      for (int j = 0; j < kQChunks; ++j) {
+        const int e = min(tid + kPersistThreads * j, Gd * G::CPT - 1);
+        dqc[j] = *reinterpret_cast<const uint4*>(
+            p.dq + ((long long)b * p.num_q_heads + h * Gd + e / G::CPT) * D + 8 * (e % G::CPT));
+      }
+      // token group 0 selects (one-wave radix select) while group 1 parks
+      // the next Q rows; larger candidate sets take the workgroup routine
+      int* const topk_lds = reinterpret_cast<int*>(smem + 2 * G::GROUP_BYTES - kTopkLdsBytes);
+      int32_t* const sel_out = p.sel + (long long)u * p.max_sel;
+      int32_t* const sel_s = reinterpret_cast<int32_t*>(smem + p.off_sel);
+      if (p.max_blocks <= 64 * kWaveTopkKeys) {
+        if (tg == 0) topk_wave<kWaveTopkKeys>(KeySrc{keys}, ncand, n, sel_out, p.max_sel, sel_s, topk_lds);
+      } else {
+        topk_select_parked<kPersistThreads>(keys, ncand, n, sel_out, p.max_sel, sel_s, topk_lds);
+      }
+      // the block masses are dead: park the next unit's Q rows there; the
+      // draft query rows of this unit into its slot
+      if (more) park_q_chunks<D>(p, qpre, smem + p.off_ell);
+      if (dq_mine) {
+        const uint32_t flip = p.dscale_log2 < 0.f ? 0x80008000u : 0u;
+        char* const dq = smem + p.off_dq;
 #pragma unroll
         for (int j = 0; j < kQChunks; ++j) {
           const int e = tid + kPersistThreads * j;
-          const int row = e / G::CPT, cc = e % G::CPT;
-          if (row < 32) *reinterpret_cast<uint4*>(qpark + row * G::K_STRIDE + 16 * cc) = qpre[j];
+          if (e < Gd * G::CPT) {
+            uint4 v = dqc[j];
+            v.x ^= flip;
+            v.y ^= flip;
+            v.z ^= flip;
+            v.w ^= flip;
+            *reinterpret_cast<uint4*>(dq + (e / G::CPT) * G::K_STRIDE + 16 * (e % G::CPT)) = v;
+          }
         }
       }
-      topk_select_parked<kPersistThreads>(
-          keys, ncand, n, p.sel + (long long)u * p.max_sel, p.max_sel,
-          reinterpret_cast<int32_t*>(smem + p.off_sel),
-          reinterpret_cast<int*>(smem + 2 * G::GROUP_BYTES - kTopkLdsBytes));
+      lds_barrier();
+      du = u;
       dn = n;
     }
-    du = u;
   }
 
   // the last unit's draft
@@ -651,7 +728,7 @@ __global__ void __launch_bounds__(kPersistThreads, 1) persist_step_kernel(Persis
     TileRegs<D, 1> regs;
     const Seg z = {};
     run_draft<D>(p, du, reinterpret_cast<const int32_t*>(smem + p.off_sel), dn, smem + p.off_dq,
-                 smem, regs, false, z, z, pdiv);
+                 smem, flags, regs, false, z, z, pdiv);
   }
 }
 
@@ -659,23 +736,25 @@ __global__ void __launch_bounds__(kPersistThreads, 1) persist_step_kernel(Persis
 
 // LDS layout of the persistent step workgroup: two tile buffers (also the
 // token-group merge scratch, the Top-N keys and the selection scratch), the
-// unit's block log masses, row log2-LSEs, the selection, the draft rows.
-// Returns the bytes, or 0 when the step does not fit (keys or scratch).
-size_t persist_lds(int head_dim, int rows, int group, int max_blocks, int max_sel, int32_t& off_ell,
-                   int32_t& off_lse, int32_t& off_sel, int32_t& off_dq) {
+// unit's block log masses (or the next unit's Q rows), row log2-LSEs, two
+// flags, the selection the next draft reads and its draft query rows.
+// Returns the bytes (0 when the keys and scratch do not fit in the tiles).
+size_t persist_lds(int head_dim, int rows, int group, int max_blocks, int max_sel,
+                   int32_t* offs /* [5] */) {
   const size_t group_bytes = (size_t)32 * (head_dim * 2 + 16) + (size_t)head_dim * 64;
   const size_t tiles = 2 * group_bytes;
   if ((size_t)max_blocks * 4 + kTopkLdsBytes > tiles) return 0;
   size_t off = tiles;
-  off_ell = (int32_t)off;
-  // the block masses, or the next unit's Q rows parked there
-  off += align_up(std::max((size_t)max_blocks * rows * 4, (size_t)32 * (head_dim * 2 + 16)), 16);
-  off_lse = (int32_t)off;
-  off += align_up((size_t)rows * 4, 16);
-  off_sel = (int32_t)off;
-  off += align_up((size_t)max_sel * 4, 16);
-  off_dq = (int32_t)off;
-  off += (size_t)group * (head_dim * 2 + 16);
+  auto take = [&](size_t n) {
+    const int32_t at = (int32_t)off;
+    off += align_up(n, 16);
+    return at;
+  };
+  offs[0] = take(std::max((size_t)max_blocks * rows * 4, (size_t)32 * (head_dim * 2 + 16)));
+  offs[1] = take((size_t)rows * 4);
+  offs[2] = take(2 * 4);
+  offs[3] = take((size_t)max_sel * 4);
+  offs[4] = take((size_t)group * (head_dim * 2 + 16));
   return off;
 }
 
@@ -719,8 +798,13 @@ hipError_t launch_persist_step(const AttnParams& pv, const AttnParams& pd, int m
   p.units = pv.batch * pv.num_kv_heads;
   if (pd.rows != pv.group || pd.num_q_heads != pv.num_q_heads || pd.block_size != pv.block_size)
     return hipErrorInvalidValue;
-  const size_t lds = persist_lds(pv.head_dim, pv.rows, pv.group, pv.max_blocks, max_sel, p.off_ell,
-                                 p.off_lse, p.off_sel, p.off_dq);
+  int32_t offs[5];
+  const size_t lds = persist_lds(pv.head_dim, pv.rows, pv.group, pv.max_blocks, max_sel, offs);
+  p.off_ell = offs[0];
+  p.off_lse = offs[1];
+  p.off_flags = offs[2];
+  p.off_sel = offs[3];
+  p.off_dq = offs[4];
   if (lds == 0 || lds > kMaxLds) return hipErrorInvalidValue;
   if (p.units <= 0) return hipSuccess;
   if (grid > p.units) grid = p.units;

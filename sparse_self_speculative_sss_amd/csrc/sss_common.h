@@ -34,6 +34,27 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
 
+// Workgroup barrier that orders LDS accesses only: each wave's LDS
+// operations complete before it meets the others, but global loads and
+// stores in flight are not waited for (the workgroup-scope fence of
+// __syncthreads waits for all of them, which makes every barrier of a
+// latency-bound phase cost a memory round trip).  For exchanges through LDS
+// only.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Orders LDS accesses among the lanes of one wave (LDS operations of a wave
+// complete in issue order; the fences keep the compiler from moving them
+// across this point).  No instruction is emitted.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float qnan() { return __builtin_nanf(""); }
 
@@ -195,8 +216,8 @@ hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s);
 // Persistent chained step (persist.hip): LDS bytes and offsets of its
 // workgroup (0: the step does not fit), and the launch over `grid`
 // workgroups that loop over the units.
-size_t persist_lds(int head_dim, int rows, int group, int max_blocks, int max_sel, int32_t& off_ell,
-                   int32_t& off_lse, int32_t& off_sel, int32_t& off_dq);
+size_t persist_lds(int head_dim, int rows, int group, int max_blocks, int max_sel,
+                   int32_t* offs /* [5] */);
 hipError_t launch_persist_step(const AttnParams& pv, const AttnParams& pd, int max_sel,
                                int topk_window, const int32_t* budget, int32_t* sel,
                                int32_t* sel_count, int grid, hipStream_t s);

@@ -28,6 +28,27 @@ __global__ void __launch_bounds__(NT)
                   max_sel, nullptr, lds, keys, max_blocks <= kTopkMaxKeys ? max_blocks : 0);
 }
 
+// One wave per unit for units of at most 64 * KPL candidates (topk_wave:
+// no workgroup barrier), four units per workgroup.
+template <int KPL>
+__global__ void __launch_bounds__(256)
+    topk_wave_kernel(const float* __restrict__ scores, int units, int hkv, int max_blocks,
+                     const int32_t* __restrict__ seq_lens, int bs,
+                     const int32_t* __restrict__ budget, int window, int32_t* __restrict__ sel,
+                     int32_t* __restrict__ sel_count, int max_sel, int skip_len) {
+  __shared__ __attribute__((aligned(16))) int hist[4][kTopkBins];
+  const int w = threadIdx.x >> 6;
+  const int u = blockIdx.x * 4 + w;
+  if (u >= units) return;
+  const int b = u / hkv;
+  if (skip_len >= 0 && seq_lens[b] <= skip_len) return;
+  int ncand, n;
+  topk_bounds(seq_lens[b], bs, window, max_blocks, budget[b], max_sel, ncand, n);
+  if ((threadIdx.x & 63) == 0) sel_count[u] = n;
+  topk_wave<KPL>(ScoreSrc{scores + (long long)u * max_blocks}, ncand, n, sel + (long long)u * max_sel,
+                 max_sel, nullptr, hist[w]);
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float* scores, int batch, int hkv, int max_blocks,
@@ -51,6 +72,15 @@ hipError_t launch_topk(const float* scores, int batch, int hkv, int max_blocks,
                        block_size, budget, window, sel, sel_count, max_sel, skip_len);
     return hipGetLastError();
   };
+  // many units of at most 1024 candidates: one wave per unit, no barrier
+  // (batch 128 x 8 heads, 508 candidates: see DESIGN)
+  if (max_blocks <= 1024 && grid > 256) {
+    const unsigned wgrid = (grid + 3) / 4;
+    auto wkern = max_blocks <= 512 ? topk_wave_kernel<8> : topk_wave_kernel<16>;
+    hipLaunchKernelGGL(wkern, dim3(wgrid), dim3(256), 0, s, scores, (int)grid, hkv, max_blocks,
+                       seq_lens, block_size, budget, window, sel, sel_count, max_sel, skip_len);
+    return hipGetLastError();
+  }
   if (grid <= 256 && max_blocks >= 1024) return go(topk_kernel<1024>, 1024);
   // many units of thousands of candidates (single-token selection): 512
   // threads (1024 units of 8128 tokens: 43 us against 49 us with 256)

@@ -2,6 +2,10 @@
 // device routine (SparseSpec §4.1: Top-K over the aggregated block scores).
 // Used by the stand-alone selection kernel and by the fused step kernel.
 //
+// Every exchange between threads goes through LDS, so the routines meet at
+// LDS-only barriers (a selection's global reads and writes in flight are
+// never waited for at a barrier).
+//
 // Exact radix select on 32-bit order-preserving keys of the fp32 scores:
 // four 8-bit MSB-first histogram passes find the N-th largest key T; the
 // blocks with key > T are taken, plus the lowest-index blocks with key == T
@@ -60,7 +64,7 @@ __device__ __forceinline__ int wg_exclusive_sum(int v, int* scratch, int& total)
     if (lane >= off) incl += y;
   }
   if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   int before = 0;
   total = 0;
 #pragma unroll
@@ -69,7 +73,7 @@ __device__ __forceinline__ int wg_exclusive_sum(int v, int* scratch, int& total)
     if (w < wave) before += c;
     total += c;
   }
-  __syncthreads();
+  lds_barrier();
   return before + incl - v;
 }
 
@@ -123,7 +127,7 @@ __device__ void topk_core(Src key, int ncand, int n, int32_t* __restrict__ out, 
     const int shift = 24 - 8 * pass;
     const uint32_t dmask = 255u;
     for (int i = tid; i < kTopkBins; i += NT) hist[i] = 0;
-    __syncthreads();
+    lds_barrier();
     // indices past the end re-read the last key and count nothing
     for (int j0 = tid; j0 < ncand; j0 += B * NT) {
       uint32_t k[B];
@@ -133,7 +137,7 @@ __device__ void topk_core(Src key, int ncand, int n, int32_t* __restrict__ out, 
       for (int e = 0; e < B; ++e)
         hist_count(hist, j0 + e * NT < ncand && (k[e] & pmask) == prefix, (k[e] >> shift) & dmask);
     }
-    __syncthreads();
+    lds_barrier();
     // the digit holding the rem-th largest key: bins in descending order,
     // PT consecutive ones per thread
     int c[PT], local = 0;
@@ -157,11 +161,11 @@ __device__ void topk_core(Src key, int ncand, int n, int32_t* __restrict__ out, 
         cum += c[i];
       }
     }
-    __syncthreads();
+    lds_barrier();
     prefix |= (uint32_t)*s_digit << shift;
     pmask |= dmask << shift;
     rem = *s_rem;
-    __syncthreads();
+    lds_barrier();
   }
   const uint32_t T = prefix;
   const int need_eq = rem;
@@ -205,7 +209,7 @@ __device__ void topk_core(Src key, int ncand, int n, int32_t* __restrict__ out, 
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // The n largest of sc[0, ncand) (ties to the lower index), ascending, into
@@ -232,7 +236,7 @@ __device__ void topk_select(const float* sc, int ncand, int n, int32_t* __restri
   if (n == 0 || n == ncand) {
     if (out_lds)
       for (int j = tid; j < n; j += NT) out_lds[j] = j;
-    __syncthreads();
+    lds_barrier();
     return;
   }
   if (keys && ncand <= keys_cap) {
@@ -244,7 +248,7 @@ __device__ void topk_select(const float* sc, int ncand, int n, int32_t* __restri
       for (int e = 0; e < kTopkBatch; ++e)
         if (j0 + e * NT < ncand) keys[j0 + e * NT] = score_key(x[e]);
     }
-    __syncthreads();
+    lds_barrier();
     topk_core<NT, 4>(KeySrc{keys}, ncand, n, out, out_lds, lds);
   } else {
     topk_core<NT, kTopkBatch>(ScoreSrc{sc}, ncand, n, out, out_lds, lds);
@@ -268,10 +272,146 @@ __device__ void topk_select_parked(const uint32_t* keys, int ncand, int n,
   if (n == 0 || n == ncand) {
     if (out_lds)
       for (int j = tid; j < n; j += NT) out_lds[j] = j;
-    __syncthreads();
+    lds_barrier();
     return;
   }
   topk_core<NT, 4>(KeySrc{keys}, ncand, n, out, out_lds, lds);
+}
+
+// ---- one-wave selection ----
+//
+// The same selection as topk_select (the n largest keys, lowest index first
+// among equal ones, emitted ascending) made by a single wave with no
+// workgroup barrier: for units of at most 64 * KPL candidates the
+// workgroup version's ~25 barriers and their dependent LDS round trips set
+// its latency, which a persistent workgroup pays per unit.  Lane l owns
+// candidates [l * KPL, (l + 1) * KPL) in registers.  Radix passes over
+// 8-bit digits (MSB first) count the keys still matching the prefix in a
+// 256-bin LDS histogram (LDS operations of one wave complete in issue
+// order), a wave scan over the bins in descending order finds the digit of
+// the rem-th largest key, and the search stops as soon as that digit's bin
+// is taken whole.  Emission compares masked keys with the prefix: greater
+// ones are taken, and the first `rem` equal ones (by index).
+
+// Inclusive scan of v over the wave's lanes in lane order.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
+
+// The n largest of key(0 .. ncand-1) (0 < n < ncand <= 64 * KPL; `key` as
+// for topk_core), ascending into out[0, n) and, if given, out_lds[0, n).
+// `hist` is 256 ints of LDS (16-byte aligned) owned by this wave.  Called
+// by one whole wave.
+template <int KPL, typename Src>
+__device__ __forceinline__ void topk_wave_core(Src key, int ncand, int n, int32_t* __restrict__ out,
+                               int32_t* out_lds, int* hist) {
+  const int lane = threadIdx.x & 63;
+  const int j0 = lane * KPL;
+  uint32_t k[KPL];
+#pragma unroll
+  for (int e = 0; e < KPL; ++e) k[e] = key(min(j0 + e, ncand - 1));
+  bool live[KPL];
+#pragma unroll
+  for (int e = 0; e < KPL; ++e) live[e] = j0 + e < ncand;
+
+  uint32_t prefix = 0, pmask = 0;
+  int rem = n;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    *reinterpret_cast<int4*>(hist + 4 * lane) = int4{0, 0, 0, 0};
+    wave_lds_sync();
+#pragma unroll
+    for (int e = 0; e < KPL; ++e)
+      if (live[e] && (k[e] & pmask) == prefix) atomicAdd(&hist[(k[e] >> shift) & 255u], 1);
+    wave_lds_sync();
+    // lane l holds bins 255 - 4l .. 252 - 4l (descending)
+    const int4 h4 = *reinterpret_cast<const int4*>(hist + 252 - 4 * lane);
+    const int c0 = h4.w, c1 = h4.z, c2 = h4.y, c3 = h4.x;
+    const int local = c0 + c1 + c2 + c3;
+    const int incl = wave_inclusive_sum(local);
+    const int excl = incl - local;
+    // the lane whose bins hold the rem-th largest
+    const bool here = excl < rem && rem <= incl;
+    const unsigned long long hm = __ballot(here);
+    const int src = __builtin_ctzll(hm);
+    int cum = excl, digit = 0, cnt = 0;
+    if (cum + c0 >= rem) {
+      digit = 255 - 4 * lane;
+      cnt = c0;
+    } else if ((cum += c0) + c1 >= rem) {
+      digit = 254 - 4 * lane;
+      cnt = c1;
+    } else if ((cum += c1) + c2 >= rem) {
+      digit = 253 - 4 * lane;
+      cnt = c2;
+    } else {
+      cum += c2;
+      digit = 252 - 4 * lane;
+      cnt = c3;
+    }
+    const int d = __builtin_amdgcn_readlane(digit, src);
+    const int r = rem - __builtin_amdgcn_readlane(cum, src);
+    const int c = __builtin_amdgcn_readlane(cnt, src);
+    prefix |= (uint32_t)d << shift;
+    pmask |= 255u << shift;
+    rem = r;
+    wave_lds_sync();  // every lane has read the bins before the next pass clears them
+    if (c == r) break;  // every key of this bin is taken
+  }
+  // ---- ascending emission ----
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int e = 0; e < KPL; ++e)
+    if (live[e]) {
+      const uint32_t m = k[e] & pmask;
+      n_gt += m > prefix;
+      n_eq += m == prefix;
+    }
+  const int eq_incl = wave_inclusive_sum(n_eq);
+  const int eq_take = min(max(rem - (eq_incl - n_eq), 0), n_eq);
+  const int take = n_gt + eq_take;
+  int pos = wave_inclusive_sum(take) - take;
+  int eq_seen = 0;
+#pragma unroll
+  for (int e = 0; e < KPL; ++e)
+    if (live[e]) {
+      const uint32_t m = k[e] & pmask;
+      bool t = m > prefix;
+      if (m == prefix) t = eq_seen++ < eq_take;
+      if (t) {
+        out[pos] = j0 + e;
+        if (out_lds) out_lds[pos] = j0 + e;
+        ++pos;
+      }
+    }
+  wave_lds_sync();
+}
+
+// topk_select for one wave (ncand <= 64 * KPL candidates; keys from `key`):
+// out[0, n) ascending, out[n, max_sel) = -1, out_lds[0, n) if given.
+template <int KPL, typename Src>
+__device__ __forceinline__ void topk_wave(Src key, int ncand, int n, int32_t* __restrict__ out, int max_sel,
+                          int32_t* out_lds, int* hist) {
+  const int lane = threadIdx.x & 63;
+  for (int j = lane; j < max_sel; j += 64) {
+    if (n == ncand)
+      out[j] = j < n ? j : -1;
+    else if (j >= n)
+      out[j] = -1;
+  }
+  if (n == 0 || n == ncand) {
+    if (out_lds)
+      for (int j = lane; j < n; j += 64) out_lds[j] = j;
+    wave_lds_sync();
+    return;
+  }
+  topk_wave_core<KPL>(key, ncand, n, out, out_lds, hist);
 }
 
 }  // namespace sss

@@ -197,6 +197,13 @@ TOPK_CASES = [
     (1, 2, 20000, (19000, 20000), 1, 64, (500, 1500), 1500, 0),
     # more than 256 units of thousands of candidates (512-thread workgroups)
     (40, 8, 4096, (3900, 4096), 1, 64, (150, 220), 220, 30),
+    # more than 256 units of at most 1024 candidates: one wave per unit (8
+    # and 16 keys per lane), heavy ties, continuous scores, every candidate
+    # kept, no window
+    (64, 8, 512, (100, 8192), 16, 64, (0, 40), 30, 3),
+    (48, 8, 1000, (5000, 16000), 16, 64, (0, 60), 64, 0),
+    (33, 8, 700, (1, 11200), 16, 0, (1, 700), 700, 2),
+    (40, 8, 512, (1, 8192), 16, 64, (26, 26), 26, 7),
 ]
 
 
