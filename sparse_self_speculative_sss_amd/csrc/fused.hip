@@ -317,6 +317,43 @@ __global__ void __launch_bounds__(64 * finish_waves<DRAFT>(), 2)
   const float* lp = p.lse_part + (long long)u * f.maxch_v * R;
   const long long orow0 = (long long)b * p.n_q * p.num_q_heads;
 
+  // When a thread's merge elements (all partials of each) or its blocks
+  // (all rows of each) make one batch, their loads are issued here, before
+  // the partial LSEs are reduced, so that the unit's partials arrive in one
+  // memory round trip instead of three.  Only in the drafting (four-wave)
+  // form: the registers would halve the eight-wave form's occupancy.
+  constexpr int PEB = 4, PSB = 4;  // merge: elements per thread, partials
+  constexpr int PBB = 2, PQ = 8;   // scores: blocks per thread, float4 rows
+  const f32x4* op = reinterpret_cast<const f32x4*>(p.o_part) + (long long)u * f.maxch_v * R * (D / 4);
+  const int n4 = R * (D / 4);
+  const bool merge_pre = DRAFT && S <= PSB && n4 <= PEB * kFinishThreads;
+  f32x4 mv[PEB][PSB];
+  if (DRAFT && merge_pre) {
+#pragma unroll
+    for (int k = 0; k < PEB; ++k) {
+      const int e4 = min(k * kFinishThreads + tid, n4 - 1);
+#pragma unroll
+      for (int j = 0; j < PSB; ++j) mv[k][j] = op[(long long)min(j, S - 1) * n4 + e4];
+    }
+  }
+  const int nblk = ceil_div(L, p.block_size);
+  const float* ell = p.ell + (long long)u * p.max_blocks * R;
+  const int r0 = p.score_row_start * p.group;
+  const bool vec = (R % 4) == 0 && (r0 % 4) == 0;
+  const int nr = R - r0;
+  const bool score_pre = DRAFT && vec && nr <= 4 * PQ && p.max_blocks <= PBB * kFinishThreads;
+  f32x4 sx[PBB][PQ];
+  if (DRAFT && score_pre) {
+#pragma unroll
+    for (int jb = 0; jb < PBB; ++jb) {
+      const int j = min(jb * kFinishThreads + tid, max(nblk - 1, 0));
+      const f32x4* e = reinterpret_cast<const f32x4*>(ell + (long long)j * R + r0);
+#pragma unroll
+      for (int q = 0; q < PQ; ++q)
+        if (q < nr / 4) sx[jb][q] = e[q];
+    }
+  }
+
   // partial LSEs -> LDS, then each row's LSE over `lpr` lanes
   const bool staged = S * R <= kFinishStage;
   if (staged) {
@@ -329,7 +366,7 @@ __global__ void __launch_bounds__(64 * finish_waves<DRAFT>(), 2)
         if (i0 + k * kFinishThreads + tid < S * R) lst[i0 + k * kFinishThreads + tid] = x[k];
     }
   }
-  __syncthreads();
+  lds_barrier();
   const float* lpart = staged ? lst : lp;
   {
     int lpr = 1;
@@ -362,11 +399,36 @@ __global__ void __launch_bounds__(64 * finish_waves<DRAFT>(), 2)
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // merge: EB elements per thread, SB partials each, in flight together
-  const f32x4* op = reinterpret_cast<const f32x4*>(p.o_part) + (long long)u * f.maxch_v * R * (D / 4);
-  if (S <= 2)
+  if (DRAFT && merge_pre) {
+    bf16* o = reinterpret_cast<bf16*>(p.o);
+    const int G = p.group;
+#pragma unroll
+    for (int k = 0; k < PEB; ++k) {
+      const int e4 = k * kFinishThreads + tid;
+      if (e4 < n4) {
+        const int r = e4 / (D / 4);
+        const float tot = lse2[r];
+        const bool live = tot == tot && tot != neg_inf();
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < PSB; ++j) {
+          const float w = (live && j < S) ? fast_exp2(lpart[j * R + r] - tot) : 0.f;
+          acc[0] += w * mv[k][j][0];
+          acc[1] += w * mv[k][j][1];
+          acc[2] += w * mv[k][j][2];
+          acc[3] += w * mv[k][j][3];
+        }
+        const long long orow = orow0 + ((long long)(r / G)) * p.num_q_heads + h * G + r % G;
+        bf16x4 w4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) w4[c] = from_f32<bf16>(tot != tot ? qnan() : acc[c]);
+        *reinterpret_cast<bf16x4*>(o + orow * D + 4 * (e4 % (D / 4))) = w4;
+      }
+    }
+  } else if (S <= 2)
     finish_merge<kFinishThreads, D, 2, kFinishLoads / 2>(p, op, S, lse2, lpart, orow0, b, h);
   else if (S <= 4)
     finish_merge<kFinishThreads, D, 4, kFinishLoads / 4>(p, op, S, lse2, lpart, orow0, b, h);
@@ -374,20 +436,33 @@ __global__ void __launch_bounds__(64 * finish_waves<DRAFT>(), 2)
     finish_merge<kFinishThreads, D, 8, kFinishLoads / 8>(p, op, S, lse2, lpart, orow0, b, h);
 
   // block scores (every row of a block loaded at once), keys parked in LDS
-  const int nblk = ceil_div(L, p.block_size);
   int ncand, n;
   topk_bounds(L, p.block_size, f.topk_window, p.max_blocks, f.topk ? f.budget[b] : 0, f.max_sel,
               ncand, n);
   const bool park = f.topk && ncand <= f.fin_keys_cap;
-  const float* ell = p.ell + (long long)u * p.max_blocks * R;
-  const int r0 = p.score_row_start * p.group;
   float* sc_out = p.block_scores + (long long)u * p.max_blocks;
-  const bool vec = (R % 4) == 0 && (r0 % 4) == 0;
-  const int nr = R - r0;
   // a thread scores BB blocks per batch with the float4s of all their rows
   // loaded together; scalar rows (counts not a multiple of 4) one block at
   // a time
-  if (vec && nr <= 4 * 4)
+  if (DRAFT && score_pre) {
+#pragma unroll
+    for (int jb = 0; jb < PBB; ++jb) {
+      const int j = jb * kFinishThreads + tid;
+      float sc = 0.f;
+#pragma unroll
+      for (int q = 0; q < PQ; ++q)
+        if (q < nr / 4) {
+          const float* l2 = lse2 + r0 + 4 * q;
+          sc += fast_exp2(sx[jb][q][0] - l2[0]) + fast_exp2(sx[jb][q][1] - l2[1]) +
+                fast_exp2(sx[jb][q][2] - l2[2]) + fast_exp2(sx[jb][q][3] - l2[3]);
+        }
+      if (j < p.max_blocks) {
+        if (j >= nblk) sc = 0.f;
+        sc_out[j] = sc;
+        if (park && j < ncand) keys[j] = score_key(sc);
+      }
+    }
+  } else if (vec && nr <= 4 * 4)
     finish_scores<kFinishThreads, 4, 4>(p, ell, lse2, r0, nr / 4, nblk, ncand, park, sc_out, keys);
   else if (vec && nr <= 4 * 8)
     finish_scores<kFinishThreads, 2, 8>(p, ell, lse2, r0, nr / 4, nblk, ncand, park, sc_out, keys);
@@ -413,15 +488,28 @@ __global__ void __launch_bounds__(64 * finish_waves<DRAFT>(), 2)
   if (!f.topk) return;
   if (tid == 0) f.sel_count[u] = n;
   int32_t* sel_s = DRAFT ? reinterpret_cast<int32_t*>(smem + f.fin_off_sel) : nullptr;
-  // the scores (or their keys) of every block, written above, before any read
-  __threadfence_block();
-  __syncthreads();
-  if (park)
-    topk_select_parked<kFinishThreads>(keys, ncand, n, f.sel + (long long)u * f.max_sel,
-                                       f.max_sel, sel_s, topk_lds);
-  else
-    topk_select<kFinishThreads>(sc_out, ncand, n, f.sel + (long long)u * f.max_sel, f.max_sel,
-                                sel_s, topk_lds);
+  int32_t* const sel_out = f.sel + (long long)u * f.max_sel;
+  if (park) {
+    // the keys of every block, parked above, before any read; up to 1024
+    // candidates one wave selects (no workgroup barrier in the selection)
+    lds_barrier();
+    if (ncand <= 64 * 16) {
+      if (tid < 64) {
+        if (ncand <= 64 * 8)
+          topk_wave<8>(KeySrc{keys}, ncand, n, sel_out, f.max_sel, sel_s, topk_lds);
+        else
+          topk_wave<16>(KeySrc{keys}, ncand, n, sel_out, f.max_sel, sel_s, topk_lds);
+      }
+      lds_barrier();
+    } else {
+      topk_select_parked<kFinishThreads>(keys, ncand, n, sel_out, f.max_sel, sel_s, topk_lds);
+    }
+  } else {
+    // the scores of every block, written to memory above, before any read
+    __threadfence_block();
+    __syncthreads();
+    topk_select<kFinishThreads>(sc_out, ncand, n, sel_out, f.max_sel, sel_s, topk_lds);
+  }
   if constexpr (DRAFT) {
     // the chained draft of this unit over the selection in LDS (the LDS
     // above is dead: the selection ended with a barrier)
