@@ -569,6 +569,7 @@ def run_step_workload(args, wl, dev, path="auto", steps=20, warmup=5, cold_mib=0
             d_step = sss.draft_step(kv_v if shared else kv_d, db.q, wl.sm_scale, s.block_size,
                                     sel_d, cnt_d, s.window, od, lsed)
         ws_f = sss.workspace(sss.fused_workspace_size(v_step, d_step, shared), dev)
+        form = sss.fused_step_form(v_step, d_step, shared)
 
     # mark: event at the start of the step; mid: after the verify call (the
     # roofline kernel); top / end: after Top-N and the draft (stage pass only)
@@ -635,7 +636,8 @@ def run_step_workload(args, wl, dev, path="auto", steps=20, warmup=5, cold_mib=0
         torch.cuda.synchronize()
         cold = [e[0].elapsed_time(e[1]) for e in cev]
         del scratch
-    res = dict(path=path, Bv=Bv, Bd=Bd, n_q=n_q, vsplits=vsplits, draft_splits=draft_splits,
+    res = dict(path=path, form=form if path == "fused" else None, Bv=Bv, Bd=Bd, n_q=n_q,
+               vsplits=vsplits, draft_splits=draft_splits,
                verify_launches=verify_launches, steps=steps, warmup=warmup,
                ms_wall=(t1 - t0) * 1e3 / steps, step_ms=step_ms, verify_ms=verify_ms,
                topk_ms=t_ms, draft_ms=d_ms, cold=cold, cold_mib=cold_mib, nbytes=nbytes,
@@ -653,8 +655,15 @@ def roofline_of(res, workload):
     v_ms = float(np.mean(res["verify_ms"]))
     if res["path"] == "fused":
         a = nb["total"] / (v_ms * 1e-3) / 1e9
-        return {"kernel": "sss_fused_step (its work-list launch, or for chained whole units the "
-                          "verify, Top-N and draft launches; split-merge launches included)",
+        kernels = {
+            "persistent": "sss_fused_step (one persistent launch: verify, scores, Top-N and "
+                          "draft of every unit)",
+            "two_launch": "sss_fused_step (the unsplit verify launch, then the Top-N and draft "
+                          "launches)",
+        }
+        return {"kernel": kernels.get(res.get("form"),
+                                      "sss_fused_step (its work-list launch plus the merge, "
+                                      "selection and draft launches of split units)"),
                 "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None,
                 "algorithmic_bytes": nb["total"], "ms": round(v_ms, 4)}
@@ -678,6 +687,7 @@ def config_record(res, wl, cpu=None):
     kv = nb["verify_kv"] + nb["draft_kv"]
     rec = {
         "workload": s.name, "path": res["path"], "dtype": s.dtype,
+        **({"form": res["form"]} if res.get("form") else {}),
         "verify_requests": res["Bv"], "draft_requests": res["Bd"],
         "query_tokens_per_step": res["tokens"],
         "ms_per_step_wall": round(res["ms_wall"], 4),
@@ -900,6 +910,19 @@ def main():
     headline = config_record(res, wl, None)
     if rec["cpu_baseline"] is not None:
         headline["cpu_baseline"] = rec["cpu_baseline"]
+    # the headline workload on the other path too, when its fused step runs
+    # as the persistent kernel (the per-stage calls are the headline path)
+    alt = None
+    if args.configs != "none" and res["path"] == "separate" and s.p_verify is None:
+        print(f"[bench] config {s.name} (fused step)", file=sys.stderr, flush=True)
+        r_alt = run_step_workload(args, wl, dev, path="fused", steps=args.steps,
+                                  warmup=args.warmup, cold_mib=args.cold_mib)
+        if r_alt["form"] == "persistent":
+            alt = config_record(r_alt, wl, None)
+            print(f"[bench] config {s.name} (persistent fused step): "
+                  f"{alt['ms_per_step_median']} ms ({alt['frac']:.3f} of peak)",
+                  file=sys.stderr, flush=True)
+        del r_alt
     del wl, res
     torch.cuda.empty_cache()
 
@@ -909,6 +932,8 @@ def main():
     for name in names:
         if name == s.name:
             configs.append(headline)
+            if alt is not None:
+                configs.append(alt)
             continue
         print(f"[bench] config {name}", file=sys.stderr, flush=True)
         w2 = W.make(name, seed=args.seed, device=dev)
