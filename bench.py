@@ -79,6 +79,11 @@ class TimingEvent:
         if rc != 0:
             raise RuntimeError(f"hipEventRecord failed ({rc})")
 
+    @property
+    def handle(self):
+        """The hipEvent_t, for a library call that records it itself."""
+        return self._ev
+
     def elapsed_time(self, end: "TimingEvent") -> float:
         ms = self._ct.c_float()
         rc = self._lib.hipEventElapsedTime(self._ct.byref(ms), self._ev, end._ev)
@@ -498,18 +503,16 @@ def time_kv_update(wl, kv, vb, dev, steps):
 
 def default_path(s):
     """The faster path on MI355X for a workload: the fused step for mixed
-    batches and for steps of few one-row-tile units on the matrix-core path
-    (16 requests x 4K: 0.088 against 0.096 ms); the per-stage calls with
-    1024 or more units (one-wave drafts; level or faster: 0.749 against
-    0.764 ms at batch 128 x 8K), several row tiles per unit (80-row long
-    context: 0.199 against 0.201 ms), or the vector-ALU and single-token
-    paths, which the fused step does not take."""
+    batches and for chained steps of one-row-tile units on the matrix-core
+    path (16 requests x 4K: 0.076 against 0.096 ms; batch 128 x 8K, where
+    one wave per unit selects and drafts after the verify launch: 0.723
+    against 0.728 ms); the per-stage calls with several row tiles per unit
+    (80-row long context: 0.199 against 0.201 ms), or on the vector-ALU and
+    single-token paths, which the fused step does not take."""
     shared = s.p_verify is None
-    units = s.B * s.Hkv
     one_tile = s.n_q * (s.Hq // s.Hkv) <= 32
     mfma = s.dtype == "bf16" and s.block_size % 16 == 0 and s.page_size % 16 == 0
-    few = units < 1024 and one_tile and mfma
-    return "fused" if (not shared or few) else "separate"
+    return "fused" if (not shared or (one_tile and mfma)) else "separate"
 
 
 def pct(x, q):
@@ -577,7 +580,8 @@ def run_step_workload(args, wl, dev, path="auto", steps=20, warmup=5, cold_mib=0
         if mark is not None:
             mark.record()
         if path == "fused":
-            sss.fused_step(v_step, d_step, chained=shared, ws=ws_f)
+            sss.fused_step(v_step, d_step, chained=shared, ws=ws_f,
+                           verify_done=None if mid is None else mid.handle)
             return
         if Bv:
             sss.verify_attn(kv_v, vb.q, wl.sm_scale, s.block_size, wl.max_blocks, o, lse, sc,
@@ -602,9 +606,11 @@ def run_step_workload(args, wl, dev, path="auto", steps=20, warmup=5, cold_mib=0
 
     # timed steps: consecutive steps share their boundary event (one record
     # per step boundary, plus one after each verify call on the per-stage
-    # path); every record is a barrier on the stream
+    # path, or after the verify launch inside the fused step's two-launch
+    # form); every record is a barrier on the stream
     marks = [TimingEvent() for _ in range(steps + 1)]
-    mids = [TimingEvent() for _ in range(steps)] if path == "separate" else None
+    timed_mid = path == "separate" or (path == "fused" and form == "two_launch")
+    mids = [TimingEvent() for _ in range(steps)] if timed_mid else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -615,8 +621,11 @@ def run_step_workload(args, wl, dev, path="auto", steps=20, warmup=5, cold_mib=0
     step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
     verify_ms = ([marks[i].elapsed_time(mids[i]) for i in range(steps)] if mids else
                  list(step_ms))
-    # stage breakdown (untimed pass)
-    t_ms = d_ms = None
+    # stage breakdown (untimed pass; the fused two-launch form's selection
+    # and draft launch is the rest of each timed step)
+    t_ms = d_ms = sd_ms = None
+    if path == "fused" and mids:
+        sd_ms = float(np.mean([a - b for a, b in zip(step_ms, verify_ms)]))
     if path == "separate":
         sev = [[TimingEvent() for _ in range(4)] for _ in range(steps)]
         for i in range(steps):
@@ -640,7 +649,8 @@ def run_step_workload(args, wl, dev, path="auto", steps=20, warmup=5, cold_mib=0
                vsplits=vsplits, draft_splits=draft_splits,
                verify_launches=verify_launches, steps=steps, warmup=warmup,
                ms_wall=(t1 - t0) * 1e3 / steps, step_ms=step_ms, verify_ms=verify_ms,
-               topk_ms=t_ms, draft_ms=d_ms, cold=cold, cold_mib=cold_mib, nbytes=nbytes,
+               topk_ms=t_ms, draft_ms=d_ms, select_draft_ms=sd_ms, cold=cold,
+               cold_mib=cold_mib, nbytes=nbytes,
                tokens=Bv * n_q + Bd)
     if Bv:
         res["kv_v"] = kv_v
@@ -653,13 +663,20 @@ def roofline_of(res, workload):
     import numpy as np
     nb = res["nbytes"]
     v_ms = float(np.mean(res["verify_ms"]))
+    if res["path"] == "fused" and res.get("form") == "two_launch":
+        # the verify launch inside the step, timed by the event the step
+        # records after it (the same kernel as the per-stage verify call)
+        a = nb["verify"] / (v_ms * 1e-3) / 1e9
+        return {"kernel": "attn_mfma_kernel<verify> (the first launch of sss_fused_step's "
+                          "two-launch form: every unit in one chunk)",
+                "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": measured_traffic(workload),
+                "algorithmic_bytes": nb["verify"], "ms": round(v_ms, 4)}
     if res["path"] == "fused":
         a = nb["total"] / (v_ms * 1e-3) / 1e9
         kernels = {
             "persistent": "sss_fused_step (one persistent launch: verify, scores, Top-N and "
                           "draft of every unit)",
-            "two_launch": "sss_fused_step (the unsplit verify launch, then the Top-N and draft "
-                          "launches)",
         }
         return {"kernel": kernels.get(res.get("form"),
                                       "sss_fused_step (its work-list launch plus the merge, "
@@ -847,6 +864,7 @@ def main():
                               else f"ceil({s.budget_frac} * blocks)"),
             "verify_splits": res["vsplits"], "draft_splits": res["draft_splits"],
             "path": res["path"],
+            **({"form": res["form"]} if res.get("form") else {}),
         },
         "roofline": roofline,
         "warm": {
@@ -869,8 +887,12 @@ def main():
             "verify_ms": round(v_ms, 4),
             "topk_ms": None if res["topk_ms"] is None else round(res["topk_ms"], 4),
             "draft_ms": None if res["draft_ms"] is None else round(res["draft_ms"], 4),
-            "stage_times": "verify_ms from the timed steps; topk_ms and draft_ms from a "
-                           "separate untimed pass with events between the stages",
+            **({"select_draft_ms": round(res["select_draft_ms"], 4),
+                "stage_times": "verify_ms from the timed steps (an event the fused step records "
+                               "after its verify launch); select_draft_ms = step - verify"}
+               if res.get("select_draft_ms") is not None else
+               {"stage_times": "verify_ms from the timed steps; topk_ms and draft_ms from a "
+                               "separate untimed pass with events between the stages"}),
             "draft_GB/s": (round(nbytes["draft"] / (res["draft_ms"] * 1e-3) / 1e9, 1)
                            if Bd and res["draft_ms"] else None),
         },
@@ -898,7 +920,9 @@ def main():
             "stream_read_bytes": args.probe_mib << 20,
             "paged_read_GB/s": round(pr, 1), "paged_read_frac": round(pr / HBM_PEAK_GBS, 4),
             "paged_read_bytes": nbytes["verify_kv"],
-            "verify_vs_paged_read": round(roofline["achieved"] / pr, 4) if res["path"] == "separate" else None,
+            "verify_vs_paged_read": (round(roofline["achieved"] / pr, 4)
+                                     if roofline["algorithmic_bytes"] == nbytes["verify"]
+                                     else None),
             "kernels": "sss_probe_stream_read / sss_probe_paged_read (16-byte non-temporal loads, "
                        "nothing but reads): context for the roofline, not the peak",
         }
@@ -910,18 +934,18 @@ def main():
     headline = config_record(res, wl, None)
     if rec["cpu_baseline"] is not None:
         headline["cpu_baseline"] = rec["cpu_baseline"]
-    # the headline workload on the other path too, when its fused step runs
-    # as the persistent kernel (the per-stage calls are the headline path)
+    # a chained headline workload on the other path too (per-stage calls
+    # beside the fused step, or the other way round), for comparison
     alt = None
-    if args.configs != "none" and res["path"] == "separate" and s.p_verify is None:
-        print(f"[bench] config {s.name} (fused step)", file=sys.stderr, flush=True)
-        r_alt = run_step_workload(args, wl, dev, path="fused", steps=args.steps,
+    if args.configs != "none" and s.p_verify is None:
+        other = "separate" if res["path"] == "fused" else "fused"
+        print(f"[bench] config {s.name} ({other} path)", file=sys.stderr, flush=True)
+        r_alt = run_step_workload(args, wl, dev, path=other, steps=args.steps,
                                   warmup=args.warmup, cold_mib=args.cold_mib)
-        if r_alt["form"] == "persistent":
-            alt = config_record(r_alt, wl, None)
-            print(f"[bench] config {s.name} (persistent fused step): "
-                  f"{alt['ms_per_step_median']} ms ({alt['frac']:.3f} of peak)",
-                  file=sys.stderr, flush=True)
+        alt = config_record(r_alt, wl, None)
+        print(f"[bench] config {s.name} ({other} path): "
+              f"{alt['ms_per_step_median']} ms ({alt['frac']:.3f} of peak)",
+              file=sys.stderr, flush=True)
         del r_alt
     del wl, res
     torch.cuda.empty_cache()

@@ -21,7 +21,8 @@
  *   sss_merge        log-sum-exp merge of split-KV partials;
  *   sss_fused_step   all of the above for a (mixed or chained) batch in one
  *                    work-list launch (or, for a chained step of whole
- *                    units, a verify launch and a select-and-draft launch);
+ *                    units, one persistent launch, or a verify launch and a
+ *                    select-and-draft launch);
  *   sss_sparse_verify_attn  verify rows over a block layout per query
  *                    position, the union of a request's layouts loaded once;
  *   sss_kv_write     K/V of new token positions into the paged cache;
@@ -344,8 +345,10 @@ sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_p
  * whose verify units all fit in one chunk, with no separate draft half,
  * runs as two launches instead: the one-launch verify kernel, then one
  * workgroup per unit that selects and drafts over the selection held in
- * LDS -- or, with 1024 or more units, as the verify, Top-N and draft
- * kernels of the separate entry points (one-wave draft workgroups).
+ * LDS -- with 1024 or more units of at most 1024 candidates and draft lists
+ * in one chunk, one wave per unit (the draft the separate entry point runs
+ * for that many units); with 1024 or more units otherwise, the Top-N and
+ * draft kernels of the separate entry points.
  *
  * Requirements beyond those of the separate entry points: both halves use
  * the matrix-core path (BF16 cache, page_size a multiple of 16, block_size
@@ -398,6 +401,23 @@ typedef struct {
 sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* draft,
                           int32_t chained, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sss_fused_step that also records the caller's HIP event `verify_done`
+ * (a hipEvent_t passed as void*; NULL: none) on `stream` right after the
+ * launch that produces the verify outputs: in the two-launch form after the
+ * verify kernel, in the persistent form after its one launch, in the
+ * work-list form after the work-list launch (before the launches that
+ * finish split units).  Events recorded around the call then time the
+ * verify kernel inside a step.  The record is a stream barrier like any
+ * event record; an event created without hipEventDisableSystemFence also
+ * writes back the caches when it completes.  Same arguments, results and
+ * errors as sss_fused_step, plus SSS_ERR_HIP if the record fails.  Not a
+ * step of the method: a measurement hook.
+ */
+sss_status sss_fused_step_marked(const sss_verify_step* verify, const sss_draft_step* draft,
+                                 int32_t chained, void* workspace, size_t workspace_bytes,
+                                 void* stream, void* verify_done);
+
 /* Workspace bytes sss_fused_step needs (0 on invalid arguments). */
 size_t sss_fused_workspace_size(const sss_verify_step* verify, const sss_draft_step* draft,
                                 int32_t chained);
@@ -407,7 +427,10 @@ size_t sss_fused_workspace_size(const sss_verify_step* verify, const sss_draft_s
  * device memory is read and nothing is launched):
  *   SSS_FUSED_PERSISTENT  a chained step of at least two units per compute
  *                         unit (512) whose verify units fit one workgroup
- *                         each: one persistent launch whose workgroups loop
+ *                         each, unless the two-launch form selects and
+ *                         drafts with one wave per unit (1024 or more units
+ *                         of at most 1024 candidates, which is faster):
+ *                         one persistent launch whose workgroups loop
  *                         over units, drafting the unit each verified before
  *                         while the other workgroup on the compute unit
  *                         streams (SparseSpec §4.2, persistent-style fused
@@ -417,7 +440,9 @@ size_t sss_fused_workspace_size(const sss_verify_step* verify, const sss_draft_s
  *                         token groups and equals sss_draft_attn up to
  *                         summation order;
  *   SSS_FUSED_TWO_LAUNCH  other chained steps of whole units: the unsplit
- *                         verify launch, then selection and draft launches;
+ *                         verify launch, then selection and draft launches
+ *                         (one launch of one wave per unit for 1024 or more
+ *                         units of at most 1024 candidates);
  *   SSS_FUSED_WORK_LIST   everything else: the work-list launch plus the
  *                         merge / selection / draft launches of split units.
  * Returns -1 when sss_fused_step would reject the arguments (and 0 when

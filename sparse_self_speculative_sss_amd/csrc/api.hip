@@ -379,6 +379,9 @@ struct FusedSetup {
   // the Top-N kernel, then the draft kernel (one wave per unit) over
   // chain_draft
   bool select_then_draft_launches = false;
+  // ... or one launch of one wave per unit that selects and drafts (units
+  // of at most 1024 candidates, one-chunk draft lists)
+  bool select_draft_wave = false;
   Plan vplan = {};
   // chained step of whole units run as one persistent launch (persist.hip)
   bool persist = false;
@@ -520,6 +523,9 @@ sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int ch
                                      d->window, 0, fs.chain_draft);
           if (st != SSS_OK) return st;
           fs.select_then_draft_launches = true;
+          int32_t off;
+          fs.select_draft_wave = v->max_blocks <= 1024 && fs.chain_draft.num_chunks == 1 &&
+                                 select_draft_wave_lds(fs.head_dim, v->max_sel, off) <= kMaxLds / 2;
         }
       }
     }
@@ -530,8 +536,12 @@ sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int ch
     // LDS, two workgroups per CU), draft lists of at most 64 segments per
     // token group: one persistent launch verifies, scores, selects and
     // drafts every unit (persist.hip), the drafts overlapping the verify
-    // stream instead of following it.  The workspace stays that of the
-    // two-launch form, so the size query never depends on this choice.
+    // stream instead of following it.  Not when one wave per unit selects
+    // and drafts after the verify launch: that form is faster (batch 128 x
+    // 8 heads, 8K tokens on MI355X, interleaved: 0.723 ms per step against
+    // 0.735 persistent and 0.728 for the separate entry points).  The
+    // workspace stays that of the two-launch form, so the size query never
+    // depends on this choice.
     const int D = fs.head_dim;
     const long long ellf = fs.vplan.ell_lds_floats;
     const bool two_per_cu = fs.rows_v <= 32 && v->block_size != 1 &&
@@ -539,7 +549,8 @@ sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int ch
                             mfma_smem_bytes(D, 1, 2, ellf, true) <= kMaxLds / 2;
     int32_t offs[5];
     const size_t lds = persist_lds(D, fs.rows_v, fs.group_d, v->max_blocks, v->max_sel, offs);
-    fs.persist = two_per_cu && lds > 0 && lds <= kMaxLds / 2 && fs.group_d <= 32 &&
+    fs.persist = !fs.select_draft_wave && two_per_cu && lds > 0 && lds <= kMaxLds / 2 &&
+                 fs.group_d <= 32 &&
                  list_max_d <= 2 * 64 && fs.nv >= kPersistMinUnits;
   }
   if (chained && fs.split_v) {
@@ -1061,12 +1072,24 @@ int32_t sss_fused_step_form(const sss_verify_step* verify, const sss_draft_step*
   return SSS_FUSED_WORK_LIST;
 }
 
-sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* draft,
-                          int32_t chained, void* workspace, size_t workspace_bytes, void* stream) {
+// The fused step; `mark`, when given, is recorded on the stream once the
+// launch that produces the verify outputs is enqueued (two-launch form:
+// after the verify kernel; persistent form: after its one launch; work
+// list: after the work-list launch, before the launches of split units).
+static sss_status fused_step_impl(const sss_verify_step* verify, const sss_draft_step* draft,
+                                  int32_t chained, void* workspace, size_t workspace_bytes,
+                                  void* stream, hipEvent_t mark) {
   FusedSetup fs;
   sss_status st = setup_fused(verify, draft, chained, fs);
   if (st != SSS_OK) return st;
-  if (!fs.has_v && !fs.has_d) return ok();
+  auto record_mark = [&]() -> hipError_t {
+    return mark ? hipEventRecord(mark, reinterpret_cast<hipStream_t>(stream)) : hipSuccess;
+  };
+  if (!fs.has_v && !fs.has_d) {
+    const hipError_t e = record_mark();
+    if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step mark: %s", hipGetErrorString(e));
+    return ok();
+  }
   if (workspace_bytes < fs.bytes)
     return fail(SSS_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace_bytes,
                 fs.bytes);
@@ -1146,6 +1169,7 @@ sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* d
     const int grid = std::max(8, 2 * device_cus() / 8 * 8);
     hipError_t e = launch_persist_step(p, pd, v->max_sel, v->window, v->budget, v->sel,
                                        v->sel_count, grid, s);
+    if (e == hipSuccess) e = record_mark();
     if (e != hipSuccess)
       return fail(SSS_ERR_HIP, "fused step persistent launch: %s", hipGetErrorString(e));
     return ok();
@@ -1164,7 +1188,20 @@ sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* d
     p.ell_in_lds = 1;
     p.ell_lds_floats = (int32_t)vp.ell_lds_floats;
     hipError_t e = launch_verify_mfma(p, s);
+    if (e == hipSuccess) e = record_mark();
     if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step verify launch: %s", hipGetErrorString(e));
+    if (fs.select_draft_wave) {
+      select_draft_wave_lds(fs.head_dim, f.max_sel, f.off_sel);
+      AttnParams q = pd;
+      q.num_chunks = 1;
+      q.chunk_tokens = 0;
+      q.chunk_items = fs.chain_draft.chunk;
+      q.skip_len = -1;
+      e = launch_select_draft_wave(f, pv, q, fs.head_dim, s);
+      if (e != hipSuccess)
+        return fail(SSS_ERR_HIP, "fused step select + draft launch: %s", hipGetErrorString(e));
+      return ok();
+    }
     if (fs.select_then_draft_launches) {
       e = launch_topk(v->block_scores, v->batch, v->kv.num_kv_heads, v->max_blocks, v->kv.seq_lens,
                       v->block_size, v->budget, v->window, v->sel, v->sel_count, v->max_sel, -1, s);
@@ -1190,6 +1227,7 @@ sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* d
     return ok();
   }
   hipError_t e = launch_fused(f, pv, pd, fs.pl, fs.head_dim, s);
+  if (e == hipSuccess) e = record_mark();
   if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step launch: %s", hipGetErrorString(e));
 
   // units split over several chunks: merge and score, select, then draft
@@ -1239,6 +1277,18 @@ sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* d
     if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step merge launch: %s", hipGetErrorString(e));
   }
   return ok();
+}
+
+sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* draft,
+                          int32_t chained, void* workspace, size_t workspace_bytes, void* stream) {
+  return fused_step_impl(verify, draft, chained, workspace, workspace_bytes, stream, nullptr);
+}
+
+sss_status sss_fused_step_marked(const sss_verify_step* verify, const sss_draft_step* draft,
+                                 int32_t chained, void* workspace, size_t workspace_bytes,
+                                 void* stream, void* verify_done) {
+  return fused_step_impl(verify, draft, chained, workspace, workspace_bytes, stream,
+                         reinterpret_cast<hipEvent_t>(verify_done));
 }
 
 }  // extern "C"

@@ -177,6 +177,51 @@ __global__ void __launch_bounds__(64 * kDraftWaves, 2)
                                     park ? pv.max_blocks : 0);
 }
 
+// Selection and chained draft of whole verify units, one wave per unit, for
+// batches whose drafts run one wave per unit anyway (at least four units
+// per compute unit) and units of at most 64 * KPL candidates: the wave
+// selects with topk_wave (no workgroup barrier; the histogram borrows the
+// tile area, which the draft overwrites afterwards), keeps the selection in
+// LDS and drafts over it.  This replaces the Top-N launch and the draft
+// launch of such steps by one launch.  Units are taken in the XCD-aware
+// order of the one-item kernels (all heads of request r on XCD r % 8 when
+// the batch is a multiple of 8), so each wave reads the scores its unit's
+// verify wrote on the same XCD.
+template <int D, int KPL>
+__global__ void __launch_bounds__(64, 2)
+    select_draft_wave_kernel(FusedParams f, AttnParams pv, AttnParams pd) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int u = blockIdx.x;
+  if ((pv.batch & 7) == 0) {
+    const int H = pv.num_kv_heads, k = u >> 3;
+    u = ((u & 7) + 8 * (k / H)) * H + k % H;
+  }
+  const int b = u / pv.num_kv_heads;
+  int ncand, n;
+  topk_bounds(pv.seq_lens[b], pv.block_size, f.topk_window, pv.max_blocks, f.budget[b], f.max_sel,
+              ncand, n);
+  if (threadIdx.x == 0) f.sel_count[u] = n;
+  int32_t* sel_s = reinterpret_cast<int32_t*>(smem + f.off_sel);
+  static_assert(kTopkBins * 4 <= Geo<D>::GROUP_BYTES, "histogram must fit in the tile area");
+  topk_wave<KPL>(ScoreSrc{pv.block_scores + (long long)u * pv.max_blocks}, ncand, n,
+                 f.sel + (long long)u * f.max_sel, f.max_sel, sel_s, reinterpret_cast<int*>(smem));
+  const int Ld = pd.seq_lens[b];
+  const int nseg =
+      unit_valid(pd, Ld, 1) ? draft_list_len_mfma(n, pd.block_size, Ld, window_start(Ld, pd.window))
+                            : 0;
+  Item dt;
+  dt.u = u;
+  dt.c = 0;
+  dt.chunk = max(2, (nseg + 1) / 2 * 2);
+  dt.single = 1;
+  dt.part_row0 = 0;
+  dt.ell_off = 0;
+  dt.sel_off = f.off_sel;
+  dt.nsel_s = n;
+  dt.list_off = 0;
+  attn_item<D, 1, 1, true, false>(pd, dt, smem);
+}
+
 // Finishes the split verify units of a fused step, one workgroup per unit
 // (eight waves, or four when it also drafts: the draft's token groups): merges the chunk partials into o / lse, turns the block
 // log masses into block scores (keys parked in LDS), selects and, with
@@ -654,6 +699,33 @@ hipError_t launch_select_draft(const FusedParams& f, const AttnParams& pv, const
   };
   if (head_dim == 128) return go(select_draft_kernel<128>);
   if (head_dim == 64) return go(select_draft_kernel<64>);
+  return hipErrorInvalidValue;
+}
+
+size_t select_draft_wave_lds(int head_dim, int max_sel, int32_t& off_sel) {
+  off_sel = (int32_t)align_up(item_lds_bytes(head_dim, 1, 1), 16);
+  return (size_t)off_sel + align_up((size_t)max_sel * 4, 16);
+}
+
+hipError_t launch_select_draft_wave(const FusedParams& f, const AttnParams& pv,
+                                    const AttnParams& pd, int head_dim, hipStream_t s) {
+  if (f.nv_units == 0) return hipSuccess;
+  int32_t off_sel;
+  const size_t smem = select_draft_wave_lds(head_dim, f.max_sel, off_sel);
+  if (smem > kMaxLds || off_sel != f.off_sel || pv.max_blocks > 1024) return hipErrorInvalidValue;
+  auto go = [&](auto kern) -> hipError_t {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)kMaxLds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3((unsigned)f.nv_units), dim3(64), smem, s, f, pv, pd);
+    return hipGetLastError();
+  };
+  const bool small = pv.max_blocks <= 512;
+  if (head_dim == 128)
+    return small ? go(select_draft_wave_kernel<128, 8>) : go(select_draft_wave_kernel<128, 16>);
+  if (head_dim == 64)
+    return small ? go(select_draft_wave_kernel<64, 8>) : go(select_draft_wave_kernel<64, 16>);
   return hipErrorInvalidValue;
 }
 

@@ -206,6 +206,12 @@ size_t select_draft_lds(int head_dim, int max_sel, int max_blocks, int32_t& off_
                         int32_t& off_keys);
 hipError_t launch_select_draft(const FusedParams& f, const AttnParams& pv, const AttnParams& pd,
                                int head_dim, hipStream_t s);
+// The same, one wave per unit (units of at most 1024 candidates whose
+// drafts run one wave per unit): select_draft_wave_lds gives the LDS bytes
+// and the selection's offset (FusedParams::off_sel).
+size_t select_draft_wave_lds(int head_dim, int max_sel, int32_t& off_sel);
+hipError_t launch_select_draft_wave(const FusedParams& f, const AttnParams& pv,
+                                    const AttnParams& pd, int head_dim, hipStream_t s);
 // One workgroup per split verify unit: merge, scores, selection and, with
 // f.fin_draft, the chained draft.  finish_lds sets the fin_* LDS fields of f
 // and returns the workgroup's LDS bytes.

@@ -91,6 +91,9 @@ class DraftStep(ctypes.Structure):
 _lib.sss_fused_step.restype = _c_int
 _lib.sss_fused_step.argtypes = [ctypes.POINTER(VerifyStep), ctypes.POINTER(DraftStep), _c_int,
                                 _vp, ctypes.c_size_t, _vp]
+_lib.sss_fused_step_marked.restype = _c_int
+_lib.sss_fused_step_marked.argtypes = [ctypes.POINTER(VerifyStep), ctypes.POINTER(DraftStep),
+                                       _c_int, _vp, ctypes.c_size_t, _vp, _vp]
 _lib.sss_fused_step_form.restype = _c_int
 _lib.sss_fused_step_form.argtypes = [ctypes.POINTER(VerifyStep), ctypes.POINTER(DraftStep), _c_int]
 _lib.sss_fused_workspace_size.restype = ctypes.c_size_t
@@ -108,7 +111,9 @@ _lib.sss_version.restype = _c_int
 _lib.sss_version.argtypes = []
 
 EXPORTED = ["sss_verify_attn", "sss_verify_workspace_size", "sss_verify_attn_noalloc",
-            "sss_block_topk", "sss_draft_attn", "sss_draft_workspace_size", "sss_merge", "sss_fused_step", "sss_fused_workspace_size", "sss_fused_step_form",
+            "sss_block_topk", "sss_draft_attn", "sss_draft_workspace_size", "sss_merge",
+            "sss_fused_step", "sss_fused_step_marked", "sss_fused_workspace_size",
+            "sss_fused_step_form",
             "sss_kv_write", "sss_kv_commit", "sss_sparse_verify_attn",
             "sss_sparse_verify_workspace_size", "sss_status_string", "sss_last_error",
             "sss_version"]
@@ -405,15 +410,24 @@ def fused_step_form(verify=None, draft=None, chained=False) -> str:
     return FUSED_FORMS[f]
 
 
-def fused_step(verify=None, draft=None, chained=False, ws=None, device=None):
-    """sss_fused_step: one work-list launch for a verify half and a draft
-    half (chained: the draft half drafts the verify requests over the
-    selection this call makes)."""
+def fused_step(verify=None, draft=None, chained=False, ws=None, device=None, verify_done=None):
+    """sss_fused_step: the verify half and the draft half of a step (chained:
+    the draft half drafts the verify requests over the selection this call
+    makes).  verify_done: a hipEvent_t handle (int or ctypes.c_void_p) that
+    sss_fused_step_marked records after the launch producing the verify
+    outputs."""
     if ws is None:
         ws = workspace(fused_workspace_size(verify, draft, chained), device or "cuda")
-    _check(_lib.sss_fused_step(_byref_or_null(verify, VerifyStep), _byref_or_null(draft, DraftStep),
-                               int(bool(chained)), _ptr(ws), ws.numel(), _stream()),
-           "sss_fused_step")
+    if verify_done is None:
+        _check(_lib.sss_fused_step(_byref_or_null(verify, VerifyStep),
+                                   _byref_or_null(draft, DraftStep), int(bool(chained)), _ptr(ws),
+                                   ws.numel(), _stream()),
+               "sss_fused_step")
+    else:
+        _check(_lib.sss_fused_step_marked(_byref_or_null(verify, VerifyStep),
+                                          _byref_or_null(draft, DraftStep), int(bool(chained)),
+                                          _ptr(ws), ws.numel(), _stream(), verify_done),
+               "sss_fused_step_marked")
 
 
 def kv_write(kv: PagedKV, k_new, v_new, pos0):

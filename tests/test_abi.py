@@ -396,7 +396,9 @@ def test_probes_reject_bad_arguments():
 def test_fused_step_form():
     """The launch form sss_fused_step takes (host query, nothing launched):
     chained decode steps of >= 512 whole units whose verify runs two
-    workgroups per compute unit are persistent."""
+    workgroups per compute unit are persistent, unless there are >= 1024
+    units of <= 1024 candidates (then one wave per unit selects and drafts
+    after the verify launch: two launches)."""
     sss = _binding()
 
     def form(batch, L, chained=True, **vkw):
@@ -410,9 +412,11 @@ def test_fused_step_form():
             d.sel, d.sel_count = 1 << 23, 1 << 24
         return sss.fused_step_form(v, d, chained)
 
-    assert form(128, 8192) == "persistent"         # the batch-128 x 8K decode step
+    assert form(128, 8192) == "two_launch"         # the batch-128 x 8K decode step
     assert form(64, 8192) == "persistent"          # 512 units
-    assert form(128, 1500) == "persistent"
+    assert form(96, 1500) == "persistent"          # 768 units
+    assert form(128, 1500) == "two_launch"
+    assert form(128, 16384) == "two_launch"        # 1024 candidates per unit
     assert form(63, 8192) == "work_list"           # 504 units: split to fill the GPU
     assert form(128, 512) == "two_launch"          # four-group verify fits twice per CU
     assert form(128, 8192, chained=False) == "work_list"

@@ -118,16 +118,18 @@ def nan_equal(a, b):
     return bool(((a == b) | (torch.isnan(a) & torch.isnan(b))).all())
 
 
-@pytest.mark.parametrize("L,form", [(512, "two_launch"), (1500, "persistent")])
-def test_fused_chained_matches_separate_calls(L, form):
+@pytest.mark.parametrize("B,L,form", [(128, 512, "two_launch"), (128, 1500, "two_launch"),
+                                      (96, 1500, "persistent")])
+def test_fused_chained_matches_separate_calls(B, L, form):
     """A chained step of whole units runs the one-launch-per-stage verify's
     arithmetic: verify outputs, scores and selection are bitwise equal.  (A
-    batch of 1024 units keeps every unit in one chunk; smaller batches are
-    split to fill the GPU.  At 1500 tokens the block masses make the verify
-    run as two-token-group workgroups, two per compute unit, and the step
-    runs persistently: its draft splits each list over two token groups, so
-    it equals the separate draft up to summation order.)"""
-    wl = mk("decode_b128_l8192", seed=32, B=128, L=L)
+    batch of 1024 units keeps every unit in one chunk, and its draft runs
+    one wave per unit as the separate draft does; smaller batches are split
+    to fill the GPU.  At 1500 tokens the block masses make the verify run as
+    two-token-group workgroups, two per compute unit; with 768 units the
+    step runs persistently: its draft splits each list over two token
+    groups, so it equals the separate draft up to summation order.)"""
+    wl = mk("decode_b128_l8192", seed=32, B=B, L=L)
     vb = wl.verify
     assert step_form(wl) == form
     v_out, (sel, cnt), d_out = run_chained(wl)
@@ -141,7 +143,7 @@ def test_fused_chained_matches_separate_calls(L, form):
     od, lsed = H.gpu_draft(wl, wl.draft, sel2, cnt2)
     torch.cuda.synchronize()
     if form == "two_launch":
-        # 1024 units: the step drafts with the separate draft kernel itself
+        # 1024 units: the step drafts with the separate draft kernel's arithmetic
         assert torch.equal(d_out[0].view(torch.uint8), od.view(torch.uint8))
         assert torch.equal(d_out[1], lsed)
     else:
@@ -153,18 +155,60 @@ def test_fused_chained_matches_separate_calls(L, form):
             "persistent draft")
 
 
-# Chained steps the persistent kernel runs (at least 512 whole units whose
+# Chained steps the persistent kernel runs (512 to 1023 whole units whose
 # verify takes two workgroups per compute unit): ragged lengths, a batch
 # that is not a multiple of 8 (no XCD-aware order, units not a multiple of
 # the grid), blocks of 32 tokens (block masses summed over two segments),
 # head dim 64.  Oracle units: "all", or a seeded sample of that many.
 PERSIST = [
-    ("ragged_b128", "decode_b128_l8192", dict(B=128, L=(1000, 2000), sigma="one"), "all"),
+    ("ragged_b96", "decode_b128_l8192", dict(B=96, L=(1000, 2000), sigma="one"), "all"),
     ("b100_not_mult8", "decode_b128_l8192", dict(B=100, L=1500, sigma="one"), 48),
     ("blk32_b64", "qwen3_8b_layer_b16_l4096", dict(B=64, L=3000, block_size=32, sigma="one"), 32),
     ("d64_b64", "decode_b128_l8192", dict(B=64, L=8400, d=64, sigma="one"), 16),
-    ("nq1_b128", "decode_b128_l8192", dict(B=128, L=(5000, 6000), n_q=1, sigma="one"), 32),
+    ("nq1_b96", "decode_b128_l8192", dict(B=96, L=(5000, 6000), n_q=1, sigma="one"), 32),
 ]
+
+# Chained steps of 1024 or more whole units of at most 1024 candidates: the
+# verify launch, then one wave per unit that selects and drafts over the
+# selection it keeps in LDS.  The same shapes as above at 1024+ units, and
+# units of exactly 1024 candidates (the largest the one-wave selection takes).
+WAVE = [
+    ("ragged_b128", "decode_b128_l8192", dict(B=128, L=(1000, 2000), sigma="one"), "all"),
+    ("b132_not_mult8", "decode_b128_l8192", dict(B=132, L=1500, sigma="one"), 48),
+    ("blk32_b128", "qwen3_8b_layer_b16_l4096", dict(B=128, L=3000, block_size=32, sigma="one"), 32),
+    ("d64_b128", "decode_b128_l8192", dict(B=128, L=4100, d=64, sigma="one"), 16),
+    ("nq1_b128", "decode_b128_l8192", dict(B=128, L=(5000, 6000), n_q=1, sigma="one"), 32),
+    ("cand1024_b128", "decode_b128_l8192", dict(B=128, L=16384, sigma="one"), 8),
+]
+
+
+@pytest.mark.parametrize("case", WAVE, ids=[c[0] for c in WAVE])
+def test_fused_select_draft_wave(case):
+    cid, name, kw, nunits = case
+    wl = mk(name, seed=43, **kw)
+    vb, db = wl.verify, wl.draft
+    hkv = wl.shape.Hkv
+    print(f"[fused select+draft wave] {cid}", flush=True)
+    assert step_form(wl) == "two_launch"
+    v_out, (sel, cnt), d_out = run_chained(wl)
+    # verify, scores, selection and draft: bitwise those of the
+    # one-launch-per-stage calls (the separate draft of 1024+ units runs
+    # one wave per unit too)
+    o, lse, sc = H.gpu_verify(wl, vb, num_splits=1)
+    sel2, cnt2 = H.gpu_topk(wl, vb, sc)
+    od, lsed = H.gpu_draft(wl, db, sel2, cnt2)
+    torch.cuda.synchronize()
+    assert torch.equal(v_out[0].view(torch.uint8), o.view(torch.uint8))
+    assert torch.equal(v_out[1], lse) and torch.equal(v_out[2], sc)
+    assert torch.equal(sel, sel2) and torch.equal(cnt, cnt2)
+    assert torch.equal(d_out[0].view(torch.uint8), od.view(torch.uint8))
+    assert torch.equal(d_out[1], lsed)
+    for t in (*v_out, *d_out):
+        assert torch.isfinite(t.float()).all()
+    units = H.all_units(vb, hkv) if nunits == "all" else H.sample_units(vb, hkv, nunits, seed=4)
+    H.compare_verify(wl, vb, v_out, units).check(f"wave {cid} verify")
+    sel_np, cnt_np = check_selection(wl, vb, v_out[2], sel, cnt)
+    H.compare_draft(wl, db, d_out, sel_np, cnt_np, units).check(f"wave {cid} draft")
 
 
 @pytest.mark.parametrize("case", PERSIST, ids=[c[0] for c in PERSIST])
@@ -198,12 +242,14 @@ def test_fused_persistent(case):
     assert (d_out[1] - lsed).abs().max().item() <= H.LSE_ABS
 
 
-def test_fused_persistent_poisoned_requests():
+@pytest.mark.parametrize("B,form", [(64, "persistent"), (128, "two_launch")])
+def test_fused_chained_poisoned_requests(B, form):
     """A request longer than max_seq_len and one with an out-of-range page id
-    poison only their own units, as in the separate calls."""
-    wl = mk("decode_b128_l8192", seed=42, B=64, L=1500)
+    poison only their own units, as in the separate calls (persistent form,
+    and the two-launch form with one select-and-draft wave per unit)."""
+    wl = mk("decode_b128_l8192", seed=42, B=B, L=1500)
     vb, db = wl.verify, wl.draft
-    assert step_form(wl) == "persistent"
+    assert step_form(wl) == form
     s = H.sss()
     lens = vb.seq_lens.clone()
     lens[3] = 100000
@@ -216,7 +262,7 @@ def test_fused_persistent_poisoned_requests():
     v = s.verify_step(kv, vb.q, wl.sm_scale, 16, wl.max_blocks, o, lse, sc, budget=vb.budget,
                       window=wl.shape.window, sel=sel, sel_count=cnt)
     d = s.draft_step(kv, db.q, wl.sm_scale, 16, sel, cnt, wl.shape.window, od, lsed)
-    assert s.fused_step_form(v, d, True) == "persistent"
+    assert s.fused_step_form(v, d, True) == form
     s.fused_step(v, d, chained=True)
     # the same calls one stage at a time
     o2, lse2, sc2 = (torch.empty_like(t) for t in (o, lse, sc))
@@ -387,3 +433,38 @@ def test_fused_full_size_sampled():
         assert np.abs(tot - wl.shape.n_q * G).max() < 5e-3
         d_units = H.sample_units(db, hkv, 6, seed=2)
         H.compare_draft(wl, db, d_out, sel_np, cnt_np, d_units).check(f"fused {name} draft")
+
+
+@pytest.mark.parametrize("name,kw,form", [
+    ("decode_b128_l8192", dict(B=128, L=1500), "two_launch"),
+    ("decode_b128_l8192", dict(B=64, L=1500), "persistent"),
+    ("qwen3_8b_layer_b16_l4096", dict(B=16, L=2000), "work_list"),
+])
+def test_fused_step_marked(name, kw, form):
+    """sss_fused_step_marked records the caller's event between the step's
+    start and end (after the launch producing the verify outputs) and
+    computes exactly what sss_fused_step computes."""
+    wl = mk(name, seed=44, **kw)
+    assert step_form(wl) == form
+    ref_v, ref_sel, ref_d = run_chained(wl)
+    s = H.sss()
+    vb, db = wl.verify, wl.draft
+    o, lse, sc, sel, cnt = verify_outputs(wl, vb)
+    od = torch.full_like(db.q, float("nan"))
+    lsed = torch.full(db.q.shape[:3], float("nan"), device=DEV)
+    kv = H.kv_of(wl, vb)
+    v = s.verify_step(kv, vb.q, wl.sm_scale, wl.shape.block_size, wl.max_blocks, o, lse, sc,
+                      budget=vb.budget, window=wl.shape.window, sel=sel, sel_count=cnt)
+    d = s.draft_step(kv, db.q, wl.sm_scale, wl.shape.block_size, sel, cnt, wl.shape.window, od,
+                     lsed)
+    start, mid, end = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    mid.record()  # creates the event the library records again
+    torch.cuda.synchronize()
+    start.record()
+    s.fused_step(v, d, chained=True, verify_done=mid._as_parameter_)
+    end.record()
+    torch.cuda.synchronize()
+    assert start.elapsed_time(mid) > 0 and mid.elapsed_time(end) >= 0
+    for a, b in zip((o, lse, sc, sel, cnt, od, lsed), (*ref_v, *ref_sel, *ref_d)):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
