@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG_DIR, "libsss.so")
 SOURCES = ["api.hip", "attn_mfma.hip", "attn_simple.hip", "finalize.hip", "fused.hip",
-           "kv_update.hip", "persist.hip", "probe.hip", "topk.hip"]
+           "kv_update.hip", "persist.hip", "probe.hip", "topk.hip", "verify_rows.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

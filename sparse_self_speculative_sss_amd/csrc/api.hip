@@ -181,6 +181,22 @@ sss_status plan_verify(const sss_paged_kv* kv, int batch, int n_q, int hq, int b
   if (S < 1) S = 1;
   long long chunk = (Lmax + S - 1) / S;
   chunk = (chunk + align - 1) / align * align;
+  if (num_splits == 0 && pl.mfma && block_size != 1 && nwr == 3 && units > 0) {
+    // three row tiles run as four-wave workgroups (three compute waves and
+    // a load wave, verify_rows.hip) when a chunk's block masses fit in LDS:
+    // split so that the grid is two of them per compute unit (8 units of
+    // 80 rows x 128K tokens: 64 chunks; the plan above gave 86, so 688
+    // workgroups ran in 1.34 rounds of 512)
+    const long long wgs = kTargetWaves / kVerifyRowsWaves;
+    long long Sr = (wgs + units - 1) / units;
+    const long long cap = (Lmax + kMinChunkTokens - 1) / kMinChunkTokens;
+    if (Sr > cap) Sr = cap;
+    long long cr = (Lmax + Sr - 1) / Sr;
+    cr = (cr + align - 1) / align * align;
+    if (cr <= (1LL << 30) && verify_rows_fits_shape(kv->head_dim, pl.rows, block_size, kv->page_size,
+                                            (int)cr))
+      chunk = cr;
+  }
   if (chunk > (1LL << 30)) return fail(SSS_ERR_UNSUPPORTED, "chunk too large");
   pl.chunk = (int)chunk;
   pl.num_chunks = (int)((Lmax + chunk - 1) / chunk);

@@ -6,24 +6,6 @@
 namespace sss {
 namespace {
 
-// The dispatcher deals workgroups round-robin over the eight XCDs
-// (workgroup b runs on XCD b % 8), so in unit order XCD x runs KV head
-// x mod Hkv of every request, and each request's page-table row is fetched
-// into every XCD's L2.  For unsplit units of a batch that is a multiple of
-// 8, workgroup b instead runs request 8 floor(k / Hkv) + b % 8, head
-// k % Hkv, with k = floor(b / 8): all heads of request r on XCD r % 8, the
-// requests still dealt round-robin over the XCDs, so that a batch of mixed
-// lengths stays balanced across them (contiguous blocks of requests per XCD
-// made a mixed batch of 96 requests 29% slower).  Batch 128 x 8K on
-// MI355X: verify 0.675 -> 0.666 ms, draft 48 -> 47 us, step 0.745 -> 0.738
-// ms; 256 x 4K verify 0.694 -> 0.689 ms; bitwise-identical outputs.  Split
-// grids keep unit order.
-__device__ __forceinline__ unsigned xcd_item(unsigned b, const AttnParams& p) {
-  if (p.num_chunks != 1 || (p.batch & 7) != 0) return b;
-  const unsigned H = (unsigned)p.num_kv_heads, k = b >> 3;
-  return ((b & 7u) + 8u * (k / H)) * H + k % H;
-}
-
 template <int D, int NWR, int NWT, bool DRAFT, bool ELL_LDS, bool TOKENS, bool SPARSE = false,
           bool QREG = false>
 __global__ void __launch_bounds__(64 * NWR * NWT, QREG ? 1 : 2) attn_mfma_kernel(AttnParams p) {
@@ -145,6 +127,7 @@ template <bool DRAFT>
 hipError_t dispatch(const AttnParams& p, hipStream_t s) {
   const int nwr = ceil_div(p.rows, 32);
   if (!DRAFT) {
+    if (p.block_size != 1 && verify_rows_fits(p)) return launch_verify_rows(p, s);
     if (p.head_dim == 128 && verify_two_per_cu<128>(p)) return launch_verify_two_per_cu<128>(p, s);
     if (p.head_dim == 64 && verify_two_per_cu<64>(p)) return launch_verify_two_per_cu<64>(p, s);
   } else if (nwr == 1 && draft_token_groups((long long)p.batch * p.num_kv_heads) == 1) {

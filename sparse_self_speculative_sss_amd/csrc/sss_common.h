@@ -219,6 +219,14 @@ size_t finish_lds(FusedParams& f, int head_dim, int max_blocks, bool draft);
 hipError_t launch_fused_finish(const FusedParams& f, const AttnParams& pv, const AttnParams& pd,
                                int head_dim, size_t lds_bytes, hipStream_t s);
 hipError_t launch_verify_mfma(const AttnParams& p, hipStream_t s);
+// Verify of units with three 32-row tiles: three compute waves and a load
+// wave per workgroup (verify_rows.hip), when a chunk's block log masses fit
+// in LDS with two workgroups per compute unit (verify_rows_fits).
+bool verify_rows_fits(const AttnParams& p);
+bool verify_rows_fits_shape(int head_dim, int rows, int block_size, int page_size,
+                            int chunk_tokens);
+constexpr int kVerifyRowsWaves = 4;  // waves of a verify_rows workgroup
+hipError_t launch_verify_rows(const AttnParams& p, hipStream_t s);
 // Persistent chained step (persist.hip): LDS bytes and offsets of its
 // workgroup (0: the step does not fit), and the launch over `grid`
 // workgroups that loop over the units.
