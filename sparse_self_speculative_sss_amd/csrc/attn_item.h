@@ -543,6 +543,10 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   constexpr bool LIST = DRAFT || SPARSE;     // segments come from a block list
   constexpr bool SCORES = !DRAFT && !SPARSE;  // block importance is computed
   static_assert(!GATHER || NWR == 1, "token lists serve one-row-tile drafts");
+  // tiles in flight per token group: two with several row waves, one
+  // otherwise (two for the Q-in-registers verify and the one-wave draft,
+  // each then one wave per SIMD, made the batch-128 x 8K step slower on
+  // MI355X: 0.731 against 0.720 ms)
   constexpr int PD = NWR >= 2 ? 2 : 1;
   constexpr int NT = 64 * NWR * NWT;
   typedef Geo<D> G;
@@ -774,23 +778,32 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
     }
   }
 
+  // With PD > 1 every trip runs all PD slots and issues each slot's next
+  // loads unconditionally (past the group's tiles they read empty segments
+  // of page 0): the compiler's count of the loads issued after a slot's is
+  // then the same on every path.  With a break or a conditional load in the
+  // trip it merged in paths on which fewer loads followed and waited for
+  // the other slot's loads as well before every store, keeping one tile in
+  // flight instead of PD.
   for (int t0 = 0; t0 < n_tiles; t0 += PD)
 #pragma unroll
   for (int q = 0; q < PD; ++q) {
     const int t = t0 + q;
-    if (t >= n_tiles) break;
+    const bool live = PD == 1 || t < n_tiles;  // uniform
     const int rel0 = kTileEntries * t;
-    const bool tile_live = g_lo + rel0 < g_hi;
+    const bool tile_live = live && g_lo + rel0 < g_hi;
     const Seg ca = sa[q], cb = sb[q];
     char* const gt = DB ? smem + (t & 1) * G::GROUP_BYTES : grp;
     const uint32_t vmq = GATHER ? vm[q] : 0u;
-    bool full;
-    if constexpr (GATHER) {
-      full = vmq == 0xffffffffu;
-      store_tile_gather<D, NWR>(regs[q], gt, lig, vmq);
-    } else {
-      full = seg_full(ca) && seg_full(cb);
-      store_tile<D, NWR>(regs[q], gt, lig, ca, cb, full);
+    bool full = false;
+    if (live) {
+      if constexpr (GATHER) {
+        full = vmq == 0xffffffffu;
+        store_tile_gather<D, NWR>(regs[q], gt, lig, vmq);
+      } else {
+        full = seg_full(ca) && seg_full(cb);
+        store_tile<D, NWR>(regs[q], gt, lig, ca, cb, full);
+      }
     }
     if (!GATHER && rel0 > 0 && (rel0 & 63) == 0) {
       // move to the next batch of descriptors; fetch the one after it
@@ -802,13 +815,13 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
     // the next batch's page ids were fetched 16 tiles ago: resolve them
     // before the first prefetch that reads that batch (its last tiles)
     if (!GATHER && (rel0 & 63) == 32) seg_resolve(p, pdiv, h, nxt, bad);
-    group_sync<NWR>();
+    if (live) group_sync<NWR>();
     if (SCORES && !ell_lds) {
       if (ell_at >= 0) ell_u[ell_at] = ell_val;
       ell_at = -1;
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (t + PD < n_tiles) {
+    if (PD > 1 || t + PD < n_tiles) {
       if constexpr (GATHER) {
         const int rn = rel0 + 32 * PD;
         vm[q] = gather_mask(rows_s, g_rel + rn, g_len - rn);
@@ -990,7 +1003,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
     // a double-buffered tile needs no second barrier: the next tile goes to
     // the other buffer, and the waves meet at the next tile's barrier before
     // the buffer after it is written
-    if (!DB) group_sync<NWR>();
+    if (!DB && live) group_sync<NWR>();
   }
 
   if (SCORES && ell_at >= 0) ell_u[ell_at] = ell_val;
