@@ -23,13 +23,18 @@
 // ring 107 us -- the load wave still kept one tile in flight, because the
 // compiler's wait counts were conservative (see the load loop) -- and with
 // three tiles really in flight and no page-table reads in the loop,
-// 91-101 us.
+// 91-101 us; with the 16-row last tile on 16x16x32 MFMAs and the wave
+// roles below, 2% less again (verify call 0.113 against 0.115 ms in an
+// interleaved A/B).  One workgroup per compute unit (each wave alone on its
+// SIMD, five tiles in the load wave's registers) took 0.166 ms: the two
+// workgroups' compute chains need to overlap.
 
-// The arithmetic is attn_item's for the same item (one token group, the
-// same tiles in the same order, the same masking, lazy rescaling and block
-// log masses), so the results, split partials and block log masses equal
-// that routine's; split chunks keep their block log masses in LDS and copy
-// them to the workspace in one burst at the end.
+// The arithmetic of the 32-row tiles is attn_item's for the same item (one
+// token group, the same tiles in the same order, the same masking, lazy
+// rescaling and block log masses); a 16-row last tile sums its rows' terms
+// in another order, so it agrees with that routine up to rounding.  Split
+// chunks keep their block log masses in LDS and copy them to the workspace
+// in one burst at the end.
 #include "attn_item.h"
 #include "attn_tile.h"
 
@@ -86,6 +91,25 @@ __device__ __forceinline__ LanePair lane_pair(float x) {
   return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
+// The same for lane i ^ 16 (v_permlane16_swap).
+__device__ __forceinline__ LanePair lane_pair16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// Sum and max over the four lanes i, i ^ 16, i ^ 32, i ^ 48 (the lanes of
+// one row in the 16-row tile); every one of them gets the same value.
+__device__ __forceinline__ float quad_sum(float x) {
+  const LanePair a = lane_pair16(x);
+  const LanePair b = lane_pair(a.a + a.b);
+  return b.a + b.b;
+}
+__device__ __forceinline__ float quad_max(float x) {
+  const LanePair a = lane_pair16(x);
+  const LanePair b = lane_pair(fmaxf(a.a, a.b));
+  return fmaxf(b.a, b.b);
+}
+
 // The workgroup's counters: raised by one wave, waited on by others.
 __device__ __forceinline__ int counter_peek(int* c) {
   return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -103,7 +127,16 @@ __device__ __forceinline__ bool counter_wait(int* c, int v) {
   return false;
 }
 
-template <int D>
+// HALF: the last row tile holds at most 16 rows (65 to 80 rows in all) and
+// runs on 16x16x32 MFMAs (half the matrix work and softmax of a padded
+// 32-row tile).  Wave roles: wave 1 loads, waves 0, 2 and 3 compute row
+// tiles 0, 1 and 2.  The dispatcher puts the four waves of a workgroup on
+// the four SIMDs of a compute unit and the second workgroup on the same
+// SIMDs shifted by one wave (MI355X, read from the hardware ids), so SIMD
+// k holds wave k of one workgroup and wave k - 1 of the other: this order
+// gives each SIMD at most one full and one half row tile, or a row tile and
+// a load wave (with the load wave last, two SIMDs carried two full tiles).
+template <int D, bool HALF>
 __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams p, int nb) {
   typedef Geo<D> G;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -113,10 +146,15 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
   if (p.skip_len >= 0 && p.seq_lens[b] <= p.skip_len) return;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool loader = w == kRowWaves;
+  const bool loader = w == 1;
+  const int rt = w == 0 ? 0 : (w == 2 ? 1 : 2);  // row tile of a compute wave
+  const bool half = HALF && rt == 2;
   const int hl = lane >> 5, rl = lane & 31;
   const int R = p.rows;
-  const int r = w * 32 + rl;  // this lane's row (compute waves)
+  // this lane's row: two lanes per row in a 32-row tile (hl), four in the
+  // 16-row tile (lane >> 4)
+  const int r = half ? 64 + (lane & 15) : rt * 32 + rl;
+  const int rsub = half ? (lane >> 4) : hl, rstep = half ? 4 : 2;
   const bool row_ok = !loader && r < R;
   const int iq = row_ok ? r / p.group : 0;
   const int hq = h * p.group + (row_ok ? r % p.group : 0);
@@ -131,8 +169,8 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
     if (row_ok) {
       bf16* o = reinterpret_cast<bf16*>(p.o);
       const long long orow = ((long long)b * p.n_q + iq) * p.num_q_heads + hq;
-      for (int d = hl; d < D; d += 2) o[orow * D + d] = from_f32<bf16>(qnan());
-      if (hl == 0) p.lse[orow] = qnan();
+      for (int d = rsub; d < D; d += rstep) o[orow * D + d] = from_f32<bf16>(qnan());
+      if (rsub == 0) p.lse[orow] = qnan();
     }
     for (int j = threadIdx.x; j < p.max_blocks; j += kRowsThreads)
       p.block_scores[(long long)u * p.max_blocks + j] = qnan();
@@ -263,8 +301,196 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
     if (lane == 0 && __builtin_amdgcn_ballot_w64(bad != 0) != 0ull) sync[kSyncBad] = 1;
     // (the compute waves' matching barrier follows their tile loop)
     fail = __syncthreads_or(fail);
+  } else if (half) {
+    // ---- the 16-row tile (rows 64 .. R - 1), 16x16x32 MFMAs: lane group
+    // g = lane >> 4 holds tokens 4g .. 4g + 3 of each 16-token segment of
+    // row 64 + (lane & 15) in S^T, and d rows 4g .. 4g + 3 of each 16-row
+    // tile of O^T ----
+    const int g = lane >> 4, jr = lane & 15;
+    constexpr int KS2 = D / 32;  // k-steps of S^T = K Q^T
+    constexpr int DT = D / 16;   // 16-row tiles of O^T
+    // Q^T operand: row jr, d [32 ks + 8 g, 32 ks + 8 g + 8); a negative
+    // scale is folded in as an exact sign flip
+    bf16x8 q16[KS2];
+    {
+      const bf16* qrow = row_ok ? reinterpret_cast<const bf16*>(p.q) +
+                                      (((long long)b * p.n_q + iq) * p.num_q_heads + hq) * D
+                                : nullptr;
+      const bool neg = p.scale_log2 < 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS2; ++ks) {
+        uint4 v = {0u, 0u, 0u, 0u};
+        if (qrow) v = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
+        if (neg) {
+          v.x ^= 0x80008000u;
+          v.y ^= 0x80008000u;
+          v.z ^= 0x80008000u;
+          v.w ^= 0x80008000u;
+        }
+        q16[ks] = *reinterpret_cast<const bf16x8*>(&v);
+      }
+    }
+    const int pos_r = L - p.n_q + iq;
+    const int pos_min = L - p.n_q;
+    const float scl = fmaxf(fabsf(p.scale_log2), 1e-30f);
+    const FastDiv bdiv(p.block_size);
+    // V^T position groups of this lane's token groups g and 4 + g
+    const int pg0 = tau_group(g), pg1 = 4 + tau_group(g);
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = neg_inf(), l_run = 0.f, blk_run = 0.f;
+    int buf = 0;
+    for (int t = 0; t < n_tiles; ++t) {
+      if (!counter_wait(&sync[kSyncReady], t + 1)) fail = 1;
+      const char* gt = smem + buf * G::GROUP_BYTES;
+      buf = buf + 1 == nb ? 0 : buf + 1;
+      const int ka = seg_lo + 2 * t;
+      const Seg ca = plain_seg(ka, seg_hi, L), cb = plain_seg(ka + 1, seg_hi, L);
+      const bool interior = seg_full(ca) && seg_full(cb) && cb.t0 + kSeg - 1 <= pos_min;
+      // S^T of the tile's two 16-token segments
+      bf16x8 kf[2][KS2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int ks = 0; ks < KS2; ++ks)
+          kf[hh][ks] = *reinterpret_cast<const bf16x8*>(gt + (16 * hh + jr) * G::K_STRIDE +
+                                                         64 * ks + 16 * g);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 sv[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        sv[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS2; ++ks)
+          sv[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[hh][ks], q16[ks], sv[hh], 0, 0, 0);
+      }
+      if (!interior) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const Seg& sg = hh ? cb : ca;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tok = sg.t0 + 4 * g + e;
+            if (!(tok >= sg.lo && tok < sg.hi && tok <= pos_r)) sv[hh][e] = neg_inf();
+          }
+        }
+      }
+      float mx = neg_inf();
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sv[hh][e]);
+      mx = quad_max(mx) * scl;
+      const float m_new = fmaxf(m_run, mx);
+      const bool move = (m_run == neg_inf()) || (m_new > m_run + kRescaleSlack);
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float m_tgt = move ? m_new : m_run;
+        const float alpha = (m_tgt == neg_inf()) ? 1.f : fast_exp2(m_run - m_tgt);
+        l_run *= alpha;
+        blk_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[dt][e] *= alpha;
+        m_run = m_tgt;
+      }
+      const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
+      // V^T operand of O^T tile dt: d row 16 dt + jr, the positions of token
+      // groups g and 4 + g (tokens 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3,
+      // the k order of this lane's probabilities)
+      const char* vt = gt + G::K_BYTES;
+      bf16x8 vf[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + jr;
+        const char* vr = vt + vrow(d) * 64;
+        const int sw = vq_swz(d);
+        const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(vr + 16 * ((pg0 >> 1) ^ sw) + 8 * (pg0 & 1));
+        const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(vr + 16 * ((pg1 >> 1) ^ sw) + 8 * (pg1 & 1));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf[dt][e] = lo4[e];
+          vf[dt][4 + e] = hi4[e];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float pr[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pr[4 * hh + e] = fast_exp2(fmaf(sv[hh][e], scl, -m_use));
+          psum += pr[4 * hh + e];
+        }
+      l_run += psum;
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = static_cast<bf16>(pr[e]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pb, o[dt], 0, 0, 0);
+      // the tile's LDS reads are complete: its buffer may be refilled
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      if (lane == 0)
+        __hip_atomic_fetch_add(&sync[kSyncDone], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // per-block log mass of this row, frame m_use
+      if (p.block_size == kSeg) {
+        const float sa0 = quad_sum(pr[0] + pr[1] + pr[2] + pr[3]);
+        const float sb0 = quad_sum(pr[4] + pr[5] + pr[6] + pr[7]);
+        if (row_ok && g == 0 && ca.lo < ca.hi)
+          ell_s[(ca.t0 / kSeg) * R + r] = m_use + fast_log2(sa0);
+        if (row_ok && g == 1 && cb.lo < cb.hi)
+          ell_s[(cb.t0 / kSeg) * R + r] = m_use + fast_log2(sb0);
+      } else {
+        blk_run += psum;
+        const int tile_end = ca.t0 + 2 * kSeg;
+        if (bdiv.mod(tile_end) == 0 || ka + 2 >= seg_hi) {
+          const float tot = quad_sum(blk_run);
+          if (row_ok && g == 0) ell_s[bdiv.div(ca.t0) * R + r] = m_use + fast_log2(tot);
+          blk_run = 0.f;
+        }
+      }
+    }
+    l_run = quad_sum(l_run);
+    // (the load wave's matching barrier follows its tile loop)
+    fail = __syncthreads_or(fail);
+    bad = fail || sync[kSyncBad] != 0;
+    if (row_ok) {
+      const bool empty = !(l_run > 0.f);
+      const float inv = empty ? 0.f : 1.f / l_run;
+      const float lse2 = bad ? qnan() : (empty ? neg_inf() : m_run + fast_log2(l_run));
+      const float poison = bad ? qnan() : 1.f;
+      if (final_out) {
+        const long long orow = ((long long)b * p.n_q + iq) * p.num_q_heads + hq;
+        bf16* out = reinterpret_cast<bf16*>(p.o) + orow * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          bf16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = from_f32<bf16>(o[dt][e] * inv * poison);
+          *reinterpret_cast<bf16x4*>(out + 16 * dt + 4 * g) = v4;
+        }
+        if (g == 0) {
+          p.lse[orow] = lse2 * kLn2;
+          lse2s[r] = lse2;
+        }
+      } else {
+        const long long prow = (long long)u * p.num_chunks * R + (long long)c * R + r;
+        float* op = p.o_part + prow * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = o[dt][e] * inv * poison;
+          *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * g) = v4;
+        }
+        if (g == 0) p.lse_part[prow] = lse2;
+      }
+    }
   } else {
-    // ---- compute waves: row tile w, Q rows in registers ----
+    // ---- compute waves of 32-row tiles: row tile rt, Q rows in registers ----
     bf16x8 qreg[G::KS];
     load_qreg<D>(qreg,
                  row_ok ? reinterpret_cast<const bf16*>(p.q) +
@@ -487,7 +713,10 @@ hipError_t launch_verify_rows(const AttnParams& p, hipStream_t s) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kRowsThreads), smem, s, p, nb);
     return hipGetLastError();
   };
-  return p.head_dim == 128 ? go(verify_rows_kernel<128>) : go(verify_rows_kernel<64>);
+  // at most 16 rows in the last row tile: the 16x16x32 form of that tile
+  if (p.rows <= 2 * 32 + 16)
+    return p.head_dim == 128 ? go(verify_rows_kernel<128, true>) : go(verify_rows_kernel<64, true>);
+  return p.head_dim == 128 ? go(verify_rows_kernel<128, false>) : go(verify_rows_kernel<64, false>);
 }
 
 }  // namespace sss
