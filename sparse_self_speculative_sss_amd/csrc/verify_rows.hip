@@ -47,16 +47,16 @@ constexpr int kLoadSlots = 3;                    // tiles the load wave holds in
 constexpr int kMaxTileBufs = 4;                  // tiles the load wave may hold in LDS
 constexpr int kSpinCap = 1 << 22;                // polls before a counter wait gives up
 
-// LDS: nb tile buffers, the final row log2-LSEs, four counters (page-check
-// flag, tiles stored, tiles finished, wait failures), the chunk's block log
-// masses, then the chunk's page ids.
+// LDS: nb tile buffers, the final row log2-LSEs, eight counters (page-check
+// flag, tiles stored, two unused, then tiles finished by each compute wave),
+// the chunk's block log masses, then the chunk's page ids.
 template <int D>
 __host__ __device__ constexpr int rows_off_lse(int nb) { return nb * Geo<D>::GROUP_BYTES; }
 template <int D>
 __host__ __device__ constexpr int rows_off_sync(int nb) { return rows_off_lse<D>(nb) + Geo<D>::LSE_BYTES; }
 template <int D>
-__host__ __device__ constexpr int rows_off_ell(int nb) { return rows_off_sync<D>(nb) + 16; }
-enum { kSyncBad = 0, kSyncReady = 1, kSyncDone = 2, kSyncFail = 3 };
+__host__ __device__ constexpr int rows_off_ell(int nb) { return rows_off_sync<D>(nb) + 32; }
+enum { kSyncBad = 0, kSyncReady = 1, kSyncDone = 4 };  // kSyncDone + row tile
 
 // Segment k of a verify item whose token range ends at segment k_end:
 // tokens [16 k, min(16 k + 16, L)), empty at and past k_end (the segment
@@ -190,14 +190,16 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
   float* const ell_s = reinterpret_cast<float*>(smem + rows_off_ell<D>(nb)) - (ptrdiff_t)blk0 * R;
   int* const pages_s = reinterpret_cast<int*>(
       smem + rows_off_ell<D>(nb) + ((chunk / p.block_size) * R * 4 + 15) / 16 * 16);
-  if (threadIdx.x < 4) sync[threadIdx.x] = 0;
+  if (threadIdx.x < 8) sync[threadIdx.x] = 0;
   __syncthreads();
 
-  // Tile j goes through LDS buffer j % nb.  The load wave stores it once the
-  // compute waves have finished tile j - nb (counter kSyncDone: three per
-  // tile) and then raises kSyncReady to j + 1; a compute wave starts tile j
-  // once kSyncReady > j and raises kSyncDone when its LDS reads of the tile
-  // are complete.  The load wave thus runs up to nb tiles ahead of the
+  // Tile j goes through LDS buffer j % nb.  The load wave stores it once
+  // every compute wave has finished tile j - nb (each wave counts its own
+  // finished tiles: the waves run at different speeds, and a shared count
+  // would let two waves that are ahead stand in for one still reading the
+  // buffer) and then raises kSyncReady to j + 1; a compute wave starts tile
+  // j once kSyncReady > j and raises its counter when its LDS reads of the
+  // tile are complete.  The load wave thus runs up to nb tiles ahead of the
   // slowest compute wave (plus the kLoadSlots tiles in its registers), and
   // no wave waits at a per-tile barrier for the others.
   int fail = 0;
@@ -284,7 +286,11 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
               __hip_atomic_store(&sync[kSyncReady], j, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_WORKGROUP);
           }
-          if (j >= nb && !counter_wait(&sync[kSyncDone], kRowWaves * (j - nb + 1))) fail = 1;
+          if (j >= nb) {
+#pragma unroll
+            for (int k = 0; k < kRowWaves; ++k)
+              if (!counter_wait(&sync[kSyncDone + k], j - nb + 1)) fail = 1;
+          }
           store_tile<D, 1>(regs[q], smem + buf * G::GROUP_BYTES, lane, sa[q], sb[q],
                            seg_full(sa[q]) && seg_full(sb[q]));
           buf = buf + 1 == nb ? 0 : buf + 1;
@@ -434,7 +440,7 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
       // the tile's LDS reads are complete: its buffer may be refilled
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
       if (lane == 0)
-        __hip_atomic_fetch_add(&sync[kSyncDone], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&sync[kSyncDone + rt], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       // per-block log mass of this row, frame m_use
       if (p.block_size == kSeg) {
         const float sa0 = quad_sum(pr[0] + pr[1] + pr[2] + pr[3]);
@@ -588,7 +594,7 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
       // the tile's LDS reads are complete: its buffer may be refilled
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
       if (lane == 0)
-        __hip_atomic_fetch_add(&sync[kSyncDone], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&sync[kSyncDone + rt], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       // per-block log mass of this row, frame m_use
       if (p.block_size == kSeg) {
         float sa0 = 0.f, sb0 = 0.f;

@@ -32,7 +32,9 @@ SMALL = [
     ("mha_nq3", "qwen3_8b_layer_b16_l4096", dict(B=2, L=130, Hq=8, Hkv=8, n_q=3, sigma="one"), [0]),
     ("decode_nq1", "qwen3_8b_layer_b16_l4096", dict(B=3, L=77, n_q=1, sigma="one"), [0, 2]),
     ("L_eq_nq", "qwen3_8b_layer_b16_l4096", dict(B=2, L=5, window=0, sigma="one"), [0]),
-    ("page64_blk64", "longctx_b4_l128k", dict(B=1, L=2000, sigma="one"), [0, 3]),
+    # 80 rows (load-wave verify): split counts from one chunk of 2000 tokens
+    # (many tiles through a ring of LDS buffers) to short chunks
+    ("page64_blk64", "longctx_b4_l128k", dict(B=1, L=2000, sigma="one"), [0, 1, 2, 3, 4]),
     ("page32_blk16", "qwen3_8b_layer_b16_l4096", dict(B=2, L=700, page_size=32, sigma="one"), [0]),
     ("page16_blk64", "qwen3_8b_layer_b16_l4096", dict(B=2, L=700, block_size=64, sigma="one"), [0, 2]),
     ("page16_blk128", "qwen3_8b_layer_b16_l4096", dict(B=2, L=900, block_size=128, budget=3,
@@ -48,7 +50,7 @@ SMALL = [
     ("bf16_page8_simple", "qwen3_8b_layer_b16_l4096",
      dict(B=2, L=150, page_size=8, block_size=8, Hq=8, Hkv=2, sigma="one"), [0, 2]),
     ("f32_d128", "qwen3_8b_layer_b16_l4096", dict(B=1, L=100, dtype="f32", Hq=8, Hkv=2), [0]),
-    ("rows80", "longctx_b4_l128k", dict(B=1, L=3000, sigma="one"), [0, 4]),
+    ("rows80", "longctx_b4_l128k", dict(B=1, L=3000, sigma="one"), [0, 1, 2, 3, 4, 6, 8]),
     # three row tiles: 96 rows, 65 rows at head dim 64 (one live row in the
     # last tile), 80 rows with 16-token blocks
     ("rows96", "longctx_b4_l128k", dict(B=1, L=1100, n_q=6, sigma="one"), [0, 3]),
@@ -286,6 +288,23 @@ def test_bitwise_determinism():
     for a, b in zip(*runs):
         assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+def test_bitwise_determinism_load_wave_verify():
+    # the 65-96-row verify runs its compute waves at different speeds through
+    # a ring of LDS tile buffers: repeated runs must agree to the bit
+    wl = mk("longctx_b4_l128k", seed=7, B=2, L=3000, sigma="one")
+    vb = wl.verify
+    for ns in [1, 2, 3]:
+        print(f"[determinism] rows80 num_splits={ns}", flush=True)
+        runs = []
+        for _ in range(3):
+            o, lse, sc = H.gpu_verify(wl, vb, num_splits=ns)
+            torch.cuda.synchronize()
+            runs.append((o.view(torch.uint8).cpu(), lse.cpu(), sc.cpu()))
+        for r in runs[1:]:
+            for a, b in zip(runs[0], r):
+                assert torch.equal(a, b), f"splits={ns}"
 
 
 # (partials, rows, head_dim): a few partials; more partials than one LDS
