@@ -47,11 +47,87 @@ constexpr int kLoadSlots = 3;                    // tiles the load wave holds in
 constexpr int kMaxTileBufs = 4;                  // tiles the load wave may hold in LDS
 constexpr int kSpinCap = 1 << 22;                // polls before a counter wait gives up
 
+// A tile in LDS: K rows as loaded (row stride 2 D + 16 bytes), then V rows
+// as loaded (stride 2 D + 32: the transposing reads below take four rows
+// of one 8-byte column group per lane quad, and this stride spreads them
+// over distinct banks).  The compute waves read V^T with
+// ds_read_b64_tr_b16, so the load wave stores V untransposed.
+template <int D>
+struct RowsTile {
+  static constexpr int K_STRIDE = 2 * D + 16;
+  static constexpr int V_STRIDE = 2 * D + 32;
+  static constexpr int K_BYTES = 32 * K_STRIDE;
+  static constexpr int BYTES = K_BYTES + 32 * V_STRIDE;
+  static constexpr int CHUNKS = 32 * D / 8;  // 16-byte chunks of K (and of V)
+};
+
+// A tile's K and V, 16-byte chunk ci = lane + 64 j of each: token ci / (D / 8),
+// column chunk ci % (D / 8), as loaded.
+template <int D>
+struct RowRegs {
+  static constexpr int J = RowsTile<D>::CHUNKS / 64;
+  bf16x8 k[J];
+  bf16x8 v[J];
+};
+
+// Loads a tile (the two 16-token segments sa, sb); every load is issued.
+template <int D>
+__device__ __forceinline__ void load_rows(RowRegs<D>& r, const bf16* __restrict__ kc,
+                                          const bf16* __restrict__ vc, const Seg& sa,
+                                          const Seg& sb, int lane) {
+  constexpr int CPT = D / 8;
+#pragma unroll
+  for (int j = 0; j < RowRegs<D>::J; ++j) {
+    const int ci = lane + 64 * j;
+    const int m = ci / CPT, c = ci % CPT;
+    const long long at = (m < kSeg ? sa.base : sb.base) + (long long)(m % kSeg) * D + 8 * c;
+    r.k[j] = stream_load(reinterpret_cast<const bf16x8*>(kc + at));
+    r.v[j] = stream_load(reinterpret_cast<const bf16x8*>(vc + at));
+  }
+}
+
+// Stores a tile to LDS at t; unless both segments are full, V rows of
+// tokens outside their segment's [lo, hi) are zeroed (their probabilities
+// are 0, but the cache slots may hold non-finite values).
+template <int D>
+__device__ __forceinline__ void store_rows(RowRegs<D>& r, char* t, const Seg& sa, const Seg& sb,
+                                           bool full, int lane) {
+  typedef RowsTile<D> T;
+  constexpr int CPT = D / 8;
+#pragma unroll
+  for (int j = 0; j < RowRegs<D>::J; ++j) {
+    const int ci = lane + 64 * j;
+    const int m = ci / CPT, c = ci % CPT;
+    *reinterpret_cast<bf16x8*>(t + m * T::K_STRIDE + 16 * c) = r.k[j];
+    if (!full) {
+      const Seg& sg = m < kSeg ? sa : sb;
+      const int tok = sg.t0 + m % kSeg;
+      if (tok < sg.lo || tok >= sg.hi) r.v[j] = bf16x8{};
+    }
+    *reinterpret_cast<bf16x8*>(t + T::K_BYTES + m * T::V_STRIDE + 16 * c) = r.v[j];
+  }
+}
+
+// Four consecutive V rows r0 .. r0 + 3 of column c0 + (lane & 15) for every
+// lane of a 16-lane group, from a V tile stored row by row: source lane j
+// of the group addresses row r0 + j / 4, columns c0 + 4 (j % 4) .. + 3, and
+// the transposing read hands lane i element i % 4 of source lanes
+// 4 k + i / 4, k = 0 .. 3.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+template <int D>
+__device__ __forceinline__ bf16x4 v_col4(const char* vbase, int r0, int c0, int lane) {
+  const int j = lane & 15;
+  const char* a = vbase + (r0 + (j >> 2)) * RowsTile<D>::V_STRIDE + 2 * (c0 + 4 * (j & 3));
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(a));
+  return *reinterpret_cast<const bf16x4*>(&v);
+}
+
 // LDS: nb tile buffers, the final row log2-LSEs, eight counters (page-check
 // flag, tiles stored, two unused, then tiles finished by each compute wave),
 // the chunk's block log masses, then the chunk's page ids.
 template <int D>
-__host__ __device__ constexpr int rows_off_lse(int nb) { return nb * Geo<D>::GROUP_BYTES; }
+__host__ __device__ constexpr int rows_off_lse(int nb) { return nb * RowsTile<D>::BYTES; }
 template <int D>
 __host__ __device__ constexpr int rows_off_sync(int nb) { return rows_off_lse<D>(nb) + Geo<D>::LSE_BYTES; }
 template <int D>
@@ -247,7 +323,7 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
     SegLane cur = lane_seg(seg_lo + lane);
     SegLane nxt = lane_seg(seg_lo + 64 + lane);
     int cur_batch = 0;
-    TileRegs<D, 1> regs[kLoadSlots];
+    RowRegs<D> regs[kLoadSlots];
     Seg sa[kLoadSlots], sb[kLoadSlots];
     // tile j in register slot j % kLoadSlots; empty segments past the item
     // read page 0 (every load is issued)
@@ -255,7 +331,7 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
     for (int q = 0; q < kLoadSlots; ++q) {
       sa[q] = seg_of(p, cur, nxt, false, 2 * q);
       sb[q] = seg_of(p, cur, nxt, false, 2 * q + 1);
-      load_tile<D, 1>(regs[q], kc, vc, sa[q], sb[q], lane);
+      load_rows<D>(regs[q], kc, vc, sa[q], sb[q], lane);
     }
     // Every trip handles all kLoadSlots slots, and each slot's next loads are
     // issued unconditionally (past the item they read an empty segment of
@@ -291,14 +367,14 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
             for (int k = 0; k < kRowWaves; ++k)
               if (!counter_wait(&sync[kSyncDone + k], j - nb + 1)) fail = 1;
           }
-          store_tile<D, 1>(regs[q], smem + buf * G::GROUP_BYTES, lane, sa[q], sb[q],
-                           seg_full(sa[q]) && seg_full(sb[q]));
+          store_rows<D>(regs[q], smem + buf * RowsTile<D>::BYTES, sa[q], sb[q],
+                        seg_full(sa[q]) && seg_full(sb[q]), lane);
           buf = buf + 1 == nb ? 0 : buf + 1;
         }
         const int ra = 2 * (j + kLoadSlots), rb = ra + 1;
         sa[q] = seg_of(p, cur, nxt, (ra >> 6) != cur_batch, ra & 63);
         sb[q] = seg_of(p, cur, nxt, (rb >> 6) != cur_batch, rb & 63);
-        load_tile<D, 1>(regs[q], kc, vc, sa[q], sb[q], lane);
+        load_rows<D>(regs[q], kc, vc, sa[q], sb[q], lane);
       }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0)
@@ -340,8 +416,6 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
     const int pos_min = L - p.n_q;
     const float scl = fmaxf(fabsf(p.scale_log2), 1e-30f);
     const FastDiv bdiv(p.block_size);
-    // V^T position groups of this lane's token groups g and 4 + g
-    const int pg0 = tau_group(g), pg1 = 4 + tau_group(g);
     f32x4 o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -349,7 +423,7 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
     int buf = 0;
     for (int t = 0; t < n_tiles; ++t) {
       if (!counter_wait(&sync[kSyncReady], t + 1)) fail = 1;
-      const char* gt = smem + buf * G::GROUP_BYTES;
+      const char* gt = smem + buf * RowsTile<D>::BYTES;
       buf = buf + 1 == nb ? 0 : buf + 1;
       const int ka = seg_lo + 2 * t;
       const Seg ca = plain_seg(ka, seg_hi, L), cb = plain_seg(ka + 1, seg_hi, L);
@@ -402,18 +476,14 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
         m_run = m_tgt;
       }
       const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
-      // V^T operand of O^T tile dt: d row 16 dt + jr, the positions of token
-      // groups g and 4 + g (tokens 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3,
-      // the k order of this lane's probabilities)
-      const char* vt = gt + G::K_BYTES;
+      // V^T operand of O^T tile dt: d row 16 dt + jr, tokens 4g .. 4g + 3 and
+      // 16 + 4g .. 16 + 4g + 3 (the k order of this lane's probabilities)
+      const char* vt = gt + RowsTile<D>::K_BYTES;
       bf16x8 vf[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int d = 16 * dt + jr;
-        const char* vr = vt + vrow(d) * 64;
-        const int sw = vq_swz(d);
-        const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(vr + 16 * ((pg0 >> 1) ^ sw) + 8 * (pg0 & 1));
-        const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(vr + 16 * ((pg1 >> 1) ^ sw) + 8 * (pg1 & 1));
+        const bf16x4 lo4 = v_col4<D>(vt, 4 * g, 16 * dt, lane);
+        const bf16x4 hi4 = v_col4<D>(vt, 16 + 4 * g, 16 * dt, lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           vf[dt][e] = lo4[e];
@@ -513,7 +583,7 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
     int buf = 0;
     for (int t = 0; t < n_tiles; ++t) {
       if (!counter_wait(&sync[kSyncReady], t + 1)) fail = 1;
-      const char* gt = smem + buf * G::GROUP_BYTES;
+      const char* gt = smem + buf * RowsTile<D>::BYTES;
       buf = buf + 1 == nb ? 0 : buf + 1;
       const int ka = seg_lo + 2 * t;
       const Seg ca = plain_seg(ka, seg_hi, L), cb = plain_seg(ka + 1, seg_hi, L);
@@ -563,15 +633,22 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
       }
       const float m_use = (a.m == neg_inf()) ? 0.f : a.m;
       // the tile's V^T fragments read before the PV MFMAs
-      const char* vt = gt + G::K_BYTES;
+      // (lane (rl, hl), k-step kk: d row 32 mt + rl, tokens 16 kk + 4 hl ..
+      // + 3 and 16 kk + 8 + 4 hl .. + 3, the k order of pr[8 kk ..])
+      const char* vt = gt + RowsTile<D>::K_BYTES;
       bf16x8 vf[2][G::MT];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt) {
-          const int d = 32 * mt + rl;
-          vf[kk][mt] = *reinterpret_cast<const bf16x8*>(vt + vrow(d) * 64 +
-                                                         16 * ((2 * kk + hl) ^ vq_swz(d)));
+          const int c0 = 32 * mt + 16 * ((lane >> 4) & 1);
+          const bf16x4 lo4 = v_col4<D>(vt, 16 * kk + 4 * hl, c0, lane);
+          const bf16x4 hi4 = v_col4<D>(vt, 16 * kk + 8 + 4 * hl, c0, lane);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vf[kk][mt][e] = lo4[e];
+            vf[kk][mt][4 + e] = hi4[e];
+          }
         }
       __builtin_amdgcn_sched_barrier(0);
       float pr[16];
@@ -672,13 +749,13 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
 
 }  // namespace
 
-// LDS tile buffers of a workgroup: as many as fit (up to kMaxTileBufs) with
-// two workgroups per compute unit; 0 when not even two fit.
 // LDS bytes after the tile buffers' part: block log masses and page ids of
 // a chunk
 size_t rows_tail_bytes(long long ell_floats, int chunk_tokens, int page_size) {
   return (size_t)(ell_floats * 4 + 15) / 16 * 16 + ((size_t)chunk_tokens / page_size + 2) * 4;
 }
+// LDS tile buffers of a workgroup: as many as fit (up to kMaxTileBufs) with
+// two workgroups per compute unit; 0 when not even two fit.
 int verify_rows_bufs(int head_dim, long long ell_floats, int chunk_tokens, int page_size) {
   for (int nb = kMaxTileBufs; nb >= 2; --nb) {
     const size_t off = head_dim == 64 ? (size_t)rows_off_ell<64>(nb) : (size_t)rows_off_ell<128>(nb);
