@@ -10,7 +10,8 @@
 // one load wave.  The load wave streams the chunk's 32-token K/V tiles from
 // the paged cache (three tiles in flight in its registers; the chunk's page
 // ids staged in LDS first) and writes each into a ring of up to four LDS
-// tile buffers (K rows as loaded, V transposed).  LDS counters, not
+// tile buffers (K and V rows as loaded; the compute waves read V^T with
+// transposing LDS reads).  LDS counters, not
 // barriers, order the ring, so the load wave runs ahead while the compute
 // waves work.  The compute waves hold their Q rows in registers and only
 // read LDS and issue matrix-core and softmax instructions.
@@ -379,8 +380,10 @@ __global__ void __launch_bounds__(kRowsThreads, 2) verify_rows_kernel(AttnParams
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0)
       __hip_atomic_store(&sync[kSyncReady], n_tiles, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    // every page id of the item has been checked
-    if (lane == 0 && __builtin_amdgcn_ballot_w64(bad != 0) != 0ull) sync[kSyncBad] = 1;
+    // every page id of the item has been checked (the vote over all lanes
+    // first: a ballot inside the lane-0 branch would see lane 0 only)
+    const bool any_bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0ull;
+    if (lane == 0 && any_bad) sync[kSyncBad] = 1;
     // (the compute waves' matching barrier follows their tile loop)
     fail = __syncthreads_or(fail);
   } else if (half) {

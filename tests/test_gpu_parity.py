@@ -391,6 +391,25 @@ def test_negative_and_zero_scale(scale):
 
 @pytest.mark.parametrize("splits", [0, 1, 3])
 @pytest.mark.parametrize("bad_id", [-3, 10 ** 6])
+def test_invalid_page_id_poisons_its_request_rows80(splits, bad_id):
+    """The same for 80-row units (load-wave verify): the bad page's segments
+    are looked up by lanes other than the first of the load wave."""
+    wl = mk("longctx_b4_l128k", seed=18, B=2, L=2000, sigma="one")
+    vb = wl.verify
+    table = vb.page_table.clone()
+    table[1, 5] = bad_id                 # tokens 320..383 of request 1
+    bad = W.Batch(q=vb.q, page_table=table, seq_lens=vb.seq_lens, budget=vb.budget,
+                  req_ids=vb.req_ids)
+    print(f"[bad page rows80] id={bad_id} splits={splits}", flush=True)
+    o, lse, sc = H.gpu_verify(wl, bad, num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[1].float()).all() and torch.isnan(lse[1]).all() and torch.isnan(sc[1]).all()
+    H.compare_verify(wl, vb, (o, lse, sc), [(0, h) for h in range(wl.shape.Hkv)]).check(
+        f"bad page rows80 {bad_id} splits={splits}")
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("bad_id", [-3, 10 ** 6])
 def test_invalid_page_id_poisons_its_request(splits, bad_id):
     """A page id outside [0, num_pages) in one request's table reads nothing
     out of bounds: that request's outputs (every KV head reads the page) are
