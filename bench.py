@@ -506,9 +506,12 @@ def default_path(s):
     batches and for chained steps of one-row-tile units on the matrix-core
     path (16 requests x 4K: 0.076 against 0.096 ms; batch 128 x 8K, where
     one wave per unit selects and drafts after the verify launch: 0.723
-    against 0.728 ms); the per-stage calls with several row tiles per unit
-    (80-row long context: 0.199 against 0.201 ms), or on the vector-ALU and
-    single-token paths, which the fused step does not take."""
+    against 0.728 ms); the per-stage calls with several row tiles per unit,
+    or on the vector-ALU and single-token paths, which the fused step does
+    not take.  (run_step_workload then switches chained steps of split
+    three-row-tile units to the fused step when it takes its rows-split
+    form: the per-stage kernels without the Top-N launch, 0.144-0.146
+    against 0.144-0.145 ms on the 80-row long context.)"""
     shared = s.p_verify is None
     one_tile = s.n_q * (s.Hq // s.Hkv) <= 32
     mfma = s.dtype == "bf16" and s.block_size % 16 == 0 and s.page_size % 16 == 0
@@ -532,7 +535,8 @@ def run_step_workload(args, wl, dev, path="auto", steps=20, warmup=5, cold_mib=0
     s = wl.shape
     vb, db = wl.verify, wl.draft
     shared = s.p_verify is None      # draft reads the selection this step's verify made
-    if path == "auto":
+    auto = path == "auto"
+    if auto:
         path = default_path(s)
     n_q = s.n_q
     Bv = vb.B if vb is not None else 0
@@ -560,6 +564,14 @@ def run_step_workload(args, wl, dev, path="auto", steps=20, warmup=5, cold_mib=0
         cnt_d = cnt if shared else db.sel_count
         ws_d = sss.workspace(sss.draft_workspace_size(kv_d, Bd, s.Hq, s.block_size, wl.max_sel,
                                                       s.window, draft_splits), dev)
+    if auto and path == "separate" and shared and Bv and Bd:
+        # chained split units of three row tiles: the fused step's rows-split
+        # form (the per-stage calls without the Top-N launch) when it applies
+        v_try = sss.verify_step(kv_v, vb.q, wl.sm_scale, s.block_size, wl.max_blocks, o, lse, sc,
+                                budget=vb.budget, window=s.window, sel=sel, sel_count=cnt)
+        d_try = sss.draft_step(kv_v, db.q, wl.sm_scale, s.block_size, sel, cnt, s.window, od, lsed)
+        if sss.fused_step_form(v_try, d_try, True) == "rows_split":
+            path = "fused"
     if path == "fused":
         v_step = d_step = None
         if Bv:
@@ -609,7 +621,7 @@ def run_step_workload(args, wl, dev, path="auto", steps=20, warmup=5, cold_mib=0
     # path, or after the verify launch inside the fused step's two-launch
     # form); every record is a barrier on the stream
     marks = [TimingEvent() for _ in range(steps + 1)]
-    timed_mid = path == "separate" or (path == "fused" and form == "two_launch")
+    timed_mid = path == "separate" or (path == "fused" and form in ("two_launch", "rows_split"))
     mids = [TimingEvent() for _ in range(steps)] if timed_mid else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -671,6 +683,15 @@ def roofline_of(res, workload):
                           "two-launch form: every unit in one chunk)",
                 "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(a / HBM_PEAK_GBS, 4), "traffic": measured_traffic(workload),
+                "algorithmic_bytes": nb["verify"], "ms": round(v_ms, 4)}
+    if res["path"] == "fused" and res.get("form") == "rows_split":
+        # the verify and merge launches inside the step, timed by the event
+        # the step records after the merge
+        a = nb["verify"] / (v_ms * 1e-3) / 1e9
+        return {"kernel": "verify_rows_kernel + finalize_kernel (the verify and merge launches "
+                          "of sss_fused_step's rows-split form)",
+                "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None,
                 "algorithmic_bytes": nb["verify"], "ms": round(v_ms, 4)}
     if res["path"] == "fused":
         a = nb["total"] / (v_ms * 1e-3) / 1e9

@@ -406,6 +406,7 @@ sss_status sss_fused_step(const sss_verify_step* verify, const sss_draft_step* d
  * (a hipEvent_t passed as void*; NULL: none) on `stream` right after the
  * launch that produces the verify outputs: in the two-launch form after the
  * verify kernel, in the persistent form after its one launch, in the
+ * rows-split form after the verify's merge launch, in the
  * work-list form after the work-list launch (before the launches that
  * finish split units).  Events recorded around the call then time the
  * verify kernel inside a step.  The record is a stream barrier like any
@@ -443,6 +444,18 @@ size_t sss_fused_workspace_size(const sss_verify_step* verify, const sss_draft_s
  *                         verify launch, then selection and draft launches
  *                         (one launch of one wave per unit for 1024 or more
  *                         units of at most 1024 candidates);
+ *   SSS_FUSED_ROWS_SPLIT  a chained step of split units of 65 to 96 rows
+ *                         (k+1 positions x G heads) whose verify chunks run
+ *                         as load-wave workgroups, with fewer than 1024
+ *                         units and a draft of at most 32 heads per KV
+ *                         head: the verify and merge launches of
+ *                         sss_verify_attn, one launch in which each draft
+ *                         chunk's workgroup selects its unit's Top-N and
+ *                         drafts the chunk over it, and the draft merge of
+ *                         sss_draft_attn.  Every output, score and
+ *                         selection is bitwise that of sss_verify_attn +
+ *                         sss_block_topk + sss_draft_attn with their
+ *                         default splits;
  *   SSS_FUSED_WORK_LIST   everything else: the work-list launch plus the
  *                         merge / selection / draft launches of split units.
  * Returns -1 when sss_fused_step would reject the arguments (and 0 when
@@ -452,7 +465,8 @@ enum {
   SSS_FUSED_NOTHING = 0,
   SSS_FUSED_PERSISTENT = 1,
   SSS_FUSED_TWO_LAUNCH = 2,
-  SSS_FUSED_WORK_LIST = 3
+  SSS_FUSED_WORK_LIST = 3,
+  SSS_FUSED_ROWS_SPLIT = 4
 };
 int32_t sss_fused_step_form(const sss_verify_step* verify, const sss_draft_step* draft,
                             int32_t chained);

@@ -401,6 +401,13 @@ struct FusedSetup {
   Plan vplan = {};
   // chained step of whole units run as one persistent launch (persist.hip)
   bool persist = false;
+  // chained step of split units of three row tiles: the load-wave verify
+  // and its merge (plan fs.vplan), then one workgroup per draft chunk that
+  // selects and drafts (plan rs_draft), then the draft merge; workspace
+  // regions of the two plans
+  bool rows_split = false;
+  Plan rs_draft = {};
+  size_t rs_v_off = 0, rs_d_off = 0;
 };
 
 sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int chained,
@@ -576,6 +583,43 @@ sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int ch
     if (st != SSS_OK) return st;
   }
 
+  // Chained split units of three row tiles (65-96 rows) whose verify runs
+  // as load-wave workgroups (verify_rows.hip), with a draft of one row tile
+  // and four token groups per chunk (fewer than 1024 units): the verify and
+  // merge of sss_verify_attn, then one launch in which each draft chunk's
+  // workgroup selects its unit's Top-N and drafts its chunk, then the merge
+  // of sss_draft_attn -- the per-stage calls without the Top-N launch (8
+  // units of 80 rows x 128K tokens: the work list's three-row-wave verify is
+  // slower than the load-wave kernel).  Its workspace is counted whenever
+  // the shapes qualify.
+  size_t rs_bytes = 0;
+  if (chained && fs.has_v && fs.has_d && fs.nd == 0 && !fs.two_launch) {
+    Plan vp, dp;
+    if (plan_verify(&v->kv, v->batch, v->n_q, v->num_q_heads, v->block_size, v->max_blocks, 0,
+                    vp) == SSS_OK &&
+        plan_draft(&d->kv, d->batch, d->num_q_heads, d->block_size, d->max_sel, d->window, 0,
+                   dp) == SSS_OK &&
+        vp.mfma && dp.mfma && vp.num_chunks > 1 && ceil_div(vp.rows, 32) == 3 &&
+        v->block_size != 1 && dp.rows <= 32 &&
+        mfma_token_groups(dp.rows, true, fs.nv) == 4 &&
+        verify_rows_fits_shape(v->kv.head_dim, vp.rows, v->block_size, v->kv.page_size,
+                               vp.chunk)) {
+      int32_t off_sel, cap;
+      if (select_draft_split_lds(fs.head_dim, v->max_sel, v->max_blocks, off_sel, cap) <=
+          kMaxLds) {
+        size_t o = 0;
+        fs.rs_v_off = o;
+        o += align_up(vp.bytes, 256);
+        fs.rs_d_off = o;
+        o += align_up(dp.bytes, 256);
+        rs_bytes = o;
+        fs.rows_split = true;
+        fs.vplan = vp;
+        fs.rs_draft = dp;
+      }
+    }
+  }
+
   const int D = fs.head_dim;
   size_t off = 0;
   auto take = [&](size_t n) {
@@ -589,7 +633,7 @@ sss_status setup_fused(const sss_verify_step* v, const sss_draft_step* d, int ch
   fs.opd_off = take(fs.split_d ? (size_t)fs.nd * fs.pl.maxch_d * fs.group_d * D * 4 : 0);
   fs.lpd_off = take(fs.split_d ? (size_t)fs.nd * fs.pl.maxch_d * fs.group_d * 4 : 0);
   fs.chain_off = take(fs.chain_draft.bytes);
-  fs.bytes = off;
+  fs.bytes = std::max(off, rs_bytes);
   return ok();
 }
 
@@ -1084,6 +1128,7 @@ int32_t sss_fused_step_form(const sss_verify_step* verify, const sss_draft_step*
   if (setup_fused(verify, draft, chained, fs) != SSS_OK) return -1;
   if (!fs.has_v && !fs.has_d) return SSS_FUSED_NOTHING;
   if (fs.persist) return SSS_FUSED_PERSISTENT;
+  if (fs.rows_split) return SSS_FUSED_ROWS_SPLIT;
   if (fs.two_launch) return SSS_FUSED_TWO_LAUNCH;
   return SSS_FUSED_WORK_LIST;
 }
@@ -1188,6 +1233,46 @@ static sss_status fused_step_impl(const sss_verify_step* verify, const sss_draft
     if (e == hipSuccess) e = record_mark();
     if (e != hipSuccess)
       return fail(SSS_ERR_HIP, "fused step persistent launch: %s", hipGetErrorString(e));
+    return ok();
+  }
+  if (fs.rows_split) {
+    const sss_verify_step* v = verify;
+    const Plan& vp = fs.vplan;
+    const Plan& dp = fs.rs_draft;
+    // the verify and merge of sss_verify_attn
+    char* wv = ws + fs.rs_v_off;
+    AttnParams p = base_params(&v->kv, v->q, v->batch, v->n_q, v->num_q_heads, v->sm_scale, vp);
+    p.chunk_tokens = vp.chunk;
+    p.o_part = reinterpret_cast<float*>(wv + vp.opart_off);
+    p.lse_part = reinterpret_cast<float*>(wv + vp.lpart_off);
+    p.o = v->o;
+    p.lse = v->lse;
+    p.block_size = v->block_size;
+    p.max_blocks = v->max_blocks;
+    p.score_row_start = v->score_row_start;
+    p.ell = reinterpret_cast<float*>(wv + vp.ell_off);
+    p.block_scores = v->block_scores;
+    p.ell_in_lds = vp.ell_in_lds ? 1 : 0;
+    p.ell_lds_floats = (int32_t)vp.ell_lds_floats;
+    hipError_t e = launch_verify_mfma(p, s);
+    if (e == hipSuccess)
+      e = launch_finalize(finalize_of(p, SSS_BF16, false, vp.num_chunks, vp.chunk, -1), s);
+    if (e == hipSuccess) e = record_mark();
+    if (e != hipSuccess) return fail(SSS_ERR_HIP, "fused step verify launch: %s", hipGetErrorString(e));
+    // selection and draft per draft chunk, then the merge of sss_draft_attn
+    AttnParams q = pd;
+    q.num_chunks = dp.num_chunks;
+    q.chunk_tokens = 0;
+    q.chunk_items = dp.chunk;
+    q.o_part = reinterpret_cast<float*>(ws + fs.rs_d_off + dp.opart_off);
+    q.lse_part = reinterpret_cast<float*>(ws + fs.rs_d_off + dp.lpart_off);
+    q.skip_len = -1;
+    select_draft_split_lds(fs.head_dim, f.max_sel, v->max_blocks, f.off_sel, f.fin_keys_cap);
+    e = launch_select_draft_split(f, p, q, fs.head_dim, s);
+    if (e == hipSuccess && dp.num_chunks > 1)
+      e = launch_finalize(finalize_of(q, SSS_BF16, true, dp.num_chunks, dp.chunk, -1), s);
+    if (e != hipSuccess)
+      return fail(SSS_ERR_HIP, "fused step select + draft launch: %s", hipGetErrorString(e));
     return ok();
   }
   if (fs.two_launch) {

@@ -177,6 +177,56 @@ __global__ void __launch_bounds__(64 * kDraftWaves, 2)
                                     park ? pv.max_blocks : 0);
 }
 
+// Selection and chained draft of split verify units whose block scores a
+// merge launch wrote, one workgroup per draft chunk (the chunking of
+// sss_draft_attn: one row tile of draft rows, kDraftWaves token groups,
+// partials merged by the merge launch that follows): every workgroup of a
+// unit selects the unit's Top-N itself -- the same selection, held in LDS
+// -- and chunk 0 writes it out; then each drafts its chunk of the list.
+// The selection costs each workgroup one read of the unit's scores and the
+// radix passes, in place of a Top-N launch between the merge and the draft
+// (8 units of 2046 candidates: 10-11 us plus a 4-5 us gap).
+template <int D>
+__global__ void __launch_bounds__(64 * kDraftWaves, 2)
+    select_draft_split_kernel(FusedParams f, AttnParams pv, AttnParams pd) {
+  constexpr int NT = 64 * kDraftWaves;
+  constexpr int kTopkBytes = (kTopkLdsWords * 4 + 127) / 128 * 128;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int u = (int)(blockIdx.x / (unsigned)pd.num_chunks);
+  const int c = (int)(blockIdx.x % (unsigned)pd.num_chunks);
+  const int b = u / pv.num_kv_heads;
+  const int L = pv.seq_lens[b];
+  int ncand, n;
+  topk_bounds(L, pv.block_size, f.topk_window, pv.max_blocks, f.budget[b], f.max_sel, ncand, n);
+  // chunks past the unit's draft list have nothing to do (as in attn_item;
+  // chunk 0 always runs: it owns the unit's outputs and its selection)
+  const int Ld = pd.seq_lens[b];
+  const int nseg = unit_valid(pd, Ld, 1)
+                       ? draft_list_len_mfma(n, pd.block_size, Ld, window_start(Ld, pd.window))
+                       : 0;
+  if (c > 0 && c * pd.chunk_items >= nseg) return;
+  if (c == 0 && threadIdx.x == 0) f.sel_count[u] = n;
+  int32_t* const sel_s = reinterpret_cast<int32_t*>(smem + f.off_sel);
+  // the radix scratch and the parked keys borrow the draft's tile area
+  const bool park = ncand <= f.fin_keys_cap;
+  topk_select<NT>(pv.block_scores + (long long)u * pv.max_blocks, ncand, n,
+                  c == 0 ? f.sel + (long long)u * f.max_sel : nullptr, f.max_sel, sel_s,
+                  reinterpret_cast<int*>(smem),
+                  park ? reinterpret_cast<uint32_t*>(smem + kTopkBytes) : nullptr,
+                  park ? f.fin_keys_cap : 0);
+  Item it;
+  it.u = u;
+  it.c = c;
+  it.chunk = pd.chunk_items;
+  it.single = pd.num_chunks == 1;
+  it.part_row0 = (long long)u * pd.num_chunks * pd.rows;
+  it.ell_off = 0;
+  it.sel_off = f.off_sel;
+  it.nsel_s = n;
+  it.list_off = (int)item_lds_bytes(D, 1, kDraftWaves);
+  attn_item<D, 1, kDraftWaves, true, false>(pd, it, smem);
+}
+
 // Selection and chained draft of whole verify units, one wave per unit, for
 // batches whose drafts run one wave per unit anyway (at least four units
 // per compute unit) and units of at most 64 * KPL candidates: the wave
@@ -699,6 +749,35 @@ hipError_t launch_select_draft(const FusedParams& f, const AttnParams& pv, const
   };
   if (head_dim == 128) return go(select_draft_kernel<128>);
   if (head_dim == 64) return go(select_draft_kernel<64>);
+  return hipErrorInvalidValue;
+}
+
+size_t select_draft_split_lds(int head_dim, int max_sel, int max_blocks, int32_t& off_sel,
+                              int32_t& keys_cap) {
+  const size_t area = item_lds_bytes(head_dim, 1, kDraftWaves);
+  off_sel = (int32_t)align_up(area, 16);
+  const size_t topk = (size_t)(kTopkLdsWords * 4 + 127) / 128 * 128;
+  keys_cap = (int32_t)std::min<size_t>((size_t)max_blocks, (area - topk) / 4);
+  return (size_t)off_sel + align_up((size_t)max_sel * 4, 16);
+}
+
+hipError_t launch_select_draft_split(const FusedParams& f, const AttnParams& pv,
+                                     const AttnParams& pd, int head_dim, hipStream_t s) {
+  const unsigned grid = (unsigned)((long long)f.nv_units * pd.num_chunks);
+  if (grid == 0) return hipSuccess;
+  int32_t off_sel, cap;
+  const size_t smem = select_draft_split_lds(head_dim, f.max_sel, pv.max_blocks, off_sel, cap);
+  if (smem > kMaxLds || off_sel != f.off_sel || cap != f.fin_keys_cap) return hipErrorInvalidValue;
+  auto go = [&](auto kern) -> hipError_t {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)kMaxLds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kDraftWaves), smem, s, f, pv, pd);
+    return hipGetLastError();
+  };
+  if (head_dim == 128) return go(select_draft_split_kernel<128>);
+  if (head_dim == 64) return go(select_draft_split_kernel<64>);
   return hipErrorInvalidValue;
 }
 

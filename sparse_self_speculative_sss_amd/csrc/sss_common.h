@@ -212,6 +212,15 @@ hipError_t launch_select_draft(const FusedParams& f, const AttnParams& pv, const
 size_t select_draft_wave_lds(int head_dim, int max_sel, int32_t& off_sel);
 hipError_t launch_select_draft_wave(const FusedParams& f, const AttnParams& pv,
                                     const AttnParams& pd, int head_dim, hipStream_t s);
+// Selection and chained draft of split verify units after their merge
+// launch, one workgroup per draft chunk (pd.num_chunks per unit), each
+// selecting the unit itself: select_draft_split_lds gives the LDS bytes,
+// the selection's offset (FusedParams::off_sel) and the parked keys'
+// capacity (FusedParams::fin_keys_cap).
+size_t select_draft_split_lds(int head_dim, int max_sel, int max_blocks, int32_t& off_sel,
+                              int32_t& keys_cap);
+hipError_t launch_select_draft_split(const FusedParams& f, const AttnParams& pv,
+                                     const AttnParams& pd, int head_dim, hipStream_t s);
 // One workgroup per split verify unit: merge, scores, selection and, with
 // f.fin_draft, the chained draft.  finish_lds sets the fin_* LDS fields of f
 // and returns the workgroup's LDS bytes.

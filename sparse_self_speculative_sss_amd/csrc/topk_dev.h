@@ -203,7 +203,7 @@ __device__ void topk_core(Src key, int ncand, int n, int32_t* __restrict__ out, 
       bool take = k[e] > T;
       if (k[e] == T) take = eq_seen++ < eq_take;
       if (take) {
-        out[pos] = j;
+        if (out) out[pos] = j;
         if (out_lds) out_lds[pos] = j;
         ++pos;
       }
@@ -213,8 +213,8 @@ __device__ void topk_core(Src key, int ncand, int n, int32_t* __restrict__ out, 
 }
 
 // The n largest of sc[0, ncand) (ties to the lower index), ascending, into
-// out[0, n); out[n, max_sel) = -1.  When out_lds is given, out_lds[0, n)
-// receives the same list.  `lds` holds kTopkLdsWords ints.  With `keys`
+// out[0, n); out[n, max_sel) = -1 (out may be null).  When out_lds is
+// given, out_lds[0, n) receives the same list.  `lds` holds kTopkLdsWords ints.  With `keys`
 // (LDS room for keys_cap words) and ncand <= keys_cap, the keys are read
 // from global memory once and parked there for the passes.  All NT threads
 // of the workgroup call it; it ends with a barrier.
@@ -226,8 +226,8 @@ __device__ void topk_select(const float* sc, int ncand, int n, int32_t* __restri
   const int tid = threadIdx.x;
 
   // every candidate kept, or none: the list is 0..n-1; otherwise positions
-  // [0, n) are written by the emission
-  for (int j = tid; j < max_sel; j += NT) {
+  // [0, n) are written by the emission (out == null: the LDS copy only)
+  for (int j = tid; out && j < max_sel; j += NT) {
     if (n == ncand)
       out[j] = j < n ? j : -1;
     else if (j >= n)

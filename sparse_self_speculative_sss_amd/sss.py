@@ -397,7 +397,8 @@ def fused_workspace_size(verify=None, draft=None, chained=False) -> int:
     return n
 
 
-FUSED_FORMS = {0: "nothing", 1: "persistent", 2: "two_launch", 3: "work_list"}
+FUSED_FORMS = {0: "nothing", 1: "persistent", 2: "two_launch", 3: "work_list",
+               4: "rows_split"}
 
 
 def fused_step_form(verify=None, draft=None, chained=False) -> str:

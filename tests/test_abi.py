@@ -208,6 +208,34 @@ def test_fused_rejects_bad_arguments(vkw, dkw, kvkw, chained, status):
     assert sss.raw().sss_last_error()
 
 
+def test_fused_rows_split_form():
+    """Chained steps of split 65-96-row units (fewer than 1024) take the
+    rows-split form; its workspace covers the verify and draft partials."""
+    sss = _binding()
+
+    def form(batch, L, n_q=5, hq=32, chained=True):
+        kv = dict(num_kv_heads=2, max_seq_len=L, max_pages_per_req=-(-L // 64),
+                  num_pages=batch * -(-L // 64), page_size=64)
+        nblk = -(-L // 64)
+        v, d = fused_args(sss, dict(batch=batch, num_q_heads=hq, n_q=n_q, block_size=64,
+                                    max_blocks=nblk, max_sel=16, window=128),
+                          dict(batch=batch, num_q_heads=hq, block_size=64, max_sel=16,
+                               window=128), kv)
+        if not chained:
+            d.sel, d.sel_count = 1 << 23, 1 << 24
+        return sss.fused_step_form(v, d, chained), sss.fused_workspace_size(v, d, chained)
+
+    f, ws = form(4, 131072)                       # 8 units x 64 chunks of 80 rows
+    assert f == "rows_split"
+    # verify partials (fp32 O and LSE) and block masses dominate the workspace
+    assert ws >= 8 * 64 * 80 * (128 + 1) * 4 + 8 * 2048 * 80 * 4
+    assert form(2, 3000)[0] == "rows_split"
+    assert form(2, 3000, n_q=6)[0] == "rows_split"  # 96 rows
+    assert form(1, 2000)[0] == "rows_split"        # 10 draft chunks, 8 verify chunks
+    assert form(2, 3000, n_q=2)[0] == "work_list"  # 32 rows: one row tile
+    assert form(4, 131072, chained=False)[0] == "work_list"
+
+
 def test_fused_workspace_query_and_size_check():
     sss = _binding()
     # short requests: every unit fits in one chunk, nothing to stage

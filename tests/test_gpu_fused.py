@@ -211,6 +211,119 @@ def test_fused_select_draft_wave(case):
     H.compare_draft(wl, db, d_out, sel_np, cnt_np, units).check(f"wave {cid} draft")
 
 
+# Chained steps of split units of three row tiles whose verify runs as
+# load-wave workgroups: the verify and merge launches, then one workgroup
+# per draft chunk that selects its unit's Top-N and drafts the chunk, then
+# the draft merge.  80 rows (16-row last tile), ragged lengths (units
+# with fewer verify chunks than draft chunks, and units that fit in one
+# chunk), 96 rows, 65 rows at head dim 64 with an unsplit draft.
+ROWS_SPLIT = [
+    ("rows80", "longctx_b4_l128k", dict(B=2, L=3000, sigma="one"), {}),
+    ("rows80_ragged", "longctx_b4_l128k", dict(B=3, L=(300, 4000)), {}),
+    # requests of 200 and 5 tokens: units in one chunk (finished by their
+    # verify workgroup, which then selects)
+    ("rows80_short_units", "longctx_b4_l128k", dict(B=4, L=3000, sigma="one"), {1: 200, 3: 5}),
+    ("rows96", "longctx_b4_l128k", dict(B=2, L=3000, n_q=6, sigma="one"), {}),
+    ("rows65_d64", "qwen3_8b_layer_b16_l4096", dict(B=2, L=3000, Hq=26, Hkv=2, d=64,
+                                                    sigma="one"), {}),
+]
+
+
+def separate_calls(wl, kv=None, lens=None):
+    """The per-stage calls with their default splits: verify, Top-N, draft."""
+    s = H.sss()
+    vb, db = wl.verify, wl.draft
+    kv = H.kv_of(wl, vb) if kv is None else kv
+    lens = vb.seq_lens if lens is None else lens
+    bs = wl.shape.block_size
+    o, lse, sc, sel, cnt = verify_outputs(wl, vb)
+    s.verify_attn(kv, vb.q, wl.sm_scale, bs, wl.max_blocks, o, lse, sc, num_splits=0)
+    s.block_topk(sc, lens, bs, vb.budget, wl.shape.window, sel, cnt)
+    od = torch.full_like(db.q, float("nan"))
+    lsed = torch.full(db.q.shape[:3], float("nan"), device=DEV)
+    s.draft_attn(kv, db.q, wl.sm_scale, bs, sel, cnt, wl.shape.window, od, lsed, num_splits=0)
+    torch.cuda.synchronize()
+    return (o, lse, sc), (sel, cnt), (od, lsed)
+
+
+@pytest.mark.parametrize("case", ROWS_SPLIT, ids=[c[0] for c in ROWS_SPLIT])
+def test_fused_rows_split(case):
+    cid, name, kw, short = case
+    wl = mk(name, seed=44, **kw)
+    vb, db = wl.verify, wl.draft
+    for b, n in short.items():
+        vb.seq_lens[b] = n
+        db.seq_lens[b] = n
+    hkv = wl.shape.Hkv
+    print(f"[fused rows split] {cid}", flush=True)
+    assert step_form(wl) == "rows_split"
+    v_out, (sel, cnt), d_out = run_chained(wl)
+    # every output bitwise that of the per-stage calls
+    v2, (sel2, cnt2), d2 = separate_calls(wl)
+    for a, b in zip((*v_out, *d_out), (*v2, *d2)):
+        assert nan_equal(a, b)
+    assert torch.equal(sel, sel2) and torch.equal(cnt, cnt2)
+    for t in (*v_out, *d_out):
+        assert torch.isfinite(t.float()).all()
+    # a second and third step on the same workspace
+    ws = H.sss().workspace(H.sss().fused_workspace_size(*step_args(wl), True), DEV)
+    for _ in range(2):
+        v3, (sel3, cnt3), d3 = run_chained(wl, ws=ws)
+        for a, b in zip((*v3, *d3), (*v2, *d2)):
+            assert nan_equal(a, b)
+        assert torch.equal(sel3, sel2) and torch.equal(cnt3, cnt2)
+    units = H.all_units(vb, hkv)
+    H.compare_verify(wl, vb, v_out, units).check(f"rows split {cid} verify")
+    sel_np, cnt_np = check_selection(wl, vb, v_out[2], sel, cnt)
+    H.compare_draft(wl, db, d_out, sel_np, cnt_np, H.all_units(db, hkv)).check(
+        f"rows split {cid} draft")
+
+
+def step_args(wl):
+    s = H.sss()
+    vb, db = wl.verify, wl.draft
+    o, lse, sc, sel, cnt = verify_outputs(wl, vb)
+    kv = H.kv_of(wl, vb)
+    v = s.verify_step(kv, vb.q, wl.sm_scale, wl.shape.block_size, wl.max_blocks, o, lse, sc,
+                      budget=vb.budget, window=wl.shape.window, sel=sel, sel_count=cnt)
+    d = s.draft_step(kv, db.q, wl.sm_scale, wl.shape.block_size, sel, cnt, wl.shape.window,
+                     torch.empty_like(db.q), torch.empty(db.q.shape[:3], device=DEV))
+    return v, d
+
+
+def test_fused_rows_split_poisoned_requests():
+    """A request longer than max_seq_len and one with an out-of-range page id
+    poison only their own units, bitwise as in the per-stage calls."""
+    wl = mk("longctx_b4_l128k", seed=45, B=3, L=3000, sigma="one")
+    vb, db = wl.verify, wl.draft
+    s = H.sss()
+    lens = vb.seq_lens.clone()
+    lens[1] = 100000
+    table = vb.page_table.clone()
+    table[2, 5] = -3
+    kv = s.paged_kv(wl.k_cache, wl.v_cache, table, lens, 3000)
+    bs = wl.shape.block_size
+    o, lse, sc, sel, cnt = verify_outputs(wl, vb)
+    od = torch.full_like(db.q, 7.0)
+    lsed = torch.full(db.q.shape[:3], 7.0, device=DEV)
+    v = s.verify_step(kv, vb.q, wl.sm_scale, bs, wl.max_blocks, o, lse, sc, budget=vb.budget,
+                      window=wl.shape.window, sel=sel, sel_count=cnt)
+    d = s.draft_step(kv, db.q, wl.sm_scale, bs, sel, cnt, wl.shape.window, od, lsed)
+    assert s.fused_step_form(v, d, True) == "rows_split"
+    s.fused_step(v, d, chained=True)
+    torch.cuda.synchronize()
+    v2, (sel2, cnt2), d2 = separate_calls(wl, kv, lens)
+    for b in (1, 2):
+        for t in (o[b].float(), lse[b], sc[b]):
+            assert torch.isnan(t).all()
+    assert torch.isnan(od[1].float()).all() and torch.isnan(lsed[1]).all()
+    for t in (o[0].float(), lse[0], sc[0], od[0].float(), lsed[0]):
+        assert torch.isfinite(t).all()
+    for a, b in zip((o, lse, sc, od, lsed), (*v2, *d2)):
+        assert nan_equal(a, b)
+    assert torch.equal(sel, sel2) and torch.equal(cnt, cnt2)
+
+
 @pytest.mark.parametrize("case", PERSIST, ids=[c[0] for c in PERSIST])
 def test_fused_persistent(case):
     cid, name, kw, nunits = case
