@@ -508,10 +508,9 @@ def default_path(s):
     one wave per unit selects and drafts after the verify launch: 0.723
     against 0.728 ms); the per-stage calls with several row tiles per unit,
     or on the vector-ALU and single-token paths, which the fused step does
-    not take.  (run_step_workload then switches chained steps of split
-    three-row-tile units to the fused step when it takes its rows-split
-    form: the per-stage kernels without the Top-N launch, 0.144-0.146
-    against 0.144-0.145 ms on the 80-row long context.)"""
+    not take.  (On the 80-row long context the fused step takes its
+    rows-split form, the per-stage kernels without the Top-N launch:
+    0.145-0.146 against 0.144-0.145 ms for the per-stage calls.)"""
     shared = s.p_verify is None
     one_tile = s.n_q * (s.Hq // s.Hkv) <= 32
     mfma = s.dtype == "bf16" and s.block_size % 16 == 0 and s.page_size % 16 == 0
@@ -535,8 +534,7 @@ def run_step_workload(args, wl, dev, path="auto", steps=20, warmup=5, cold_mib=0
     s = wl.shape
     vb, db = wl.verify, wl.draft
     shared = s.p_verify is None      # draft reads the selection this step's verify made
-    auto = path == "auto"
-    if auto:
+    if path == "auto":
         path = default_path(s)
     n_q = s.n_q
     Bv = vb.B if vb is not None else 0
@@ -564,14 +562,6 @@ def run_step_workload(args, wl, dev, path="auto", steps=20, warmup=5, cold_mib=0
         cnt_d = cnt if shared else db.sel_count
         ws_d = sss.workspace(sss.draft_workspace_size(kv_d, Bd, s.Hq, s.block_size, wl.max_sel,
                                                       s.window, draft_splits), dev)
-    if auto and path == "separate" and shared and Bv and Bd:
-        # chained split units of three row tiles: the fused step's rows-split
-        # form (the per-stage calls without the Top-N launch) when it applies
-        v_try = sss.verify_step(kv_v, vb.q, wl.sm_scale, s.block_size, wl.max_blocks, o, lse, sc,
-                                budget=vb.budget, window=s.window, sel=sel, sel_count=cnt)
-        d_try = sss.draft_step(kv_v, db.q, wl.sm_scale, s.block_size, sel, cnt, s.window, od, lsed)
-        if sss.fused_step_form(v_try, d_try, True) == "rows_split":
-            path = "fused"
     if path == "fused":
         v_step = d_step = None
         if Bv:

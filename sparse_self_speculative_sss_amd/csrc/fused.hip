@@ -209,11 +209,15 @@ __global__ void __launch_bounds__(64 * kDraftWaves, 2)
   int32_t* const sel_s = reinterpret_cast<int32_t*>(smem + f.off_sel);
   // the radix scratch and the parked keys borrow the draft's tile area
   const bool park = ncand <= f.fin_keys_cap;
-  topk_select<NT>(pv.block_scores + (long long)u * pv.max_blocks, ncand, n,
-                  c == 0 ? f.sel + (long long)u * f.max_sel : nullptr, f.max_sel, sel_s,
-                  reinterpret_cast<int*>(smem),
-                  park ? reinterpret_cast<uint32_t*>(smem + kTopkBytes) : nullptr,
-                  park ? f.fin_keys_cap : 0);
+  const float* const sc = pv.block_scores + (long long)u * pv.max_blocks;
+  uint32_t* const keys = park ? reinterpret_cast<uint32_t*>(smem + kTopkBytes) : nullptr;
+  const int cap = park ? f.fin_keys_cap : 0;
+  if (c == 0)
+    topk_select<NT>(sc, ncand, n, f.sel + (long long)u * f.max_sel, f.max_sel, sel_s,
+                    reinterpret_cast<int*>(smem), keys, cap);
+  else
+    topk_select<NT, false>(sc, ncand, n, nullptr, f.max_sel, sel_s, reinterpret_cast<int*>(smem),
+                           keys, cap);
   Item it;
   it.u = u;
   it.c = c;

@@ -110,7 +110,7 @@ struct KeySrc {
 
 // Radix select and ascending emission over keys key(0 .. ncand-1), with
 // 0 < n < ncand.  `B` keys are read per thread before they are used.
-template <int NT, int B, typename Src>
+template <int NT, int B, typename Src, bool OUT = true>
 __device__ void topk_core(Src key, int ncand, int n, int32_t* __restrict__ out, int32_t* out_lds,
                           int* lds) {
   int* hist = lds;
@@ -203,7 +203,7 @@ __device__ void topk_core(Src key, int ncand, int n, int32_t* __restrict__ out, 
       bool take = k[e] > T;
       if (k[e] == T) take = eq_seen++ < eq_take;
       if (take) {
-        if (out) out[pos] = j;
+        if constexpr (OUT) out[pos] = j;
         if (out_lds) out_lds[pos] = j;
         ++pos;
       }
@@ -213,12 +213,13 @@ __device__ void topk_core(Src key, int ncand, int n, int32_t* __restrict__ out, 
 }
 
 // The n largest of sc[0, ncand) (ties to the lower index), ascending, into
-// out[0, n); out[n, max_sel) = -1 (out may be null).  When out_lds is
-// given, out_lds[0, n) receives the same list.  `lds` holds kTopkLdsWords ints.  With `keys`
+// out[0, n); out[n, max_sel) = -1 (OUT = false: no global output, out is
+// not touched).  When out_lds is given, out_lds[0, n) receives the same
+// list.  `lds` holds kTopkLdsWords ints.  With `keys`
 // (LDS room for keys_cap words) and ncand <= keys_cap, the keys are read
 // from global memory once and parked there for the passes.  All NT threads
 // of the workgroup call it; it ends with a barrier.
-template <int NT>
+template <int NT, bool OUT = true>
 __device__ void topk_select(const float* sc, int ncand, int n, int32_t* __restrict__ out,
                             int max_sel, int32_t* out_lds, int* lds, uint32_t* keys = nullptr,
                             int keys_cap = 0) {
@@ -226,8 +227,8 @@ __device__ void topk_select(const float* sc, int ncand, int n, int32_t* __restri
   const int tid = threadIdx.x;
 
   // every candidate kept, or none: the list is 0..n-1; otherwise positions
-  // [0, n) are written by the emission (out == null: the LDS copy only)
-  for (int j = tid; out && j < max_sel; j += NT) {
+  // [0, n) are written by the emission
+  for (int j = tid; OUT && j < max_sel; j += NT) {
     if (n == ncand)
       out[j] = j < n ? j : -1;
     else if (j >= n)
@@ -249,9 +250,9 @@ __device__ void topk_select(const float* sc, int ncand, int n, int32_t* __restri
         if (j0 + e * NT < ncand) keys[j0 + e * NT] = score_key(x[e]);
     }
     lds_barrier();
-    topk_core<NT, 4>(KeySrc{keys}, ncand, n, out, out_lds, lds);
+    topk_core<NT, 4, KeySrc, OUT>(KeySrc{keys}, ncand, n, out, out_lds, lds);
   } else {
-    topk_core<NT, kTopkBatch>(ScoreSrc{sc}, ncand, n, out, out_lds, lds);
+    topk_core<NT, kTopkBatch, ScoreSrc, OUT>(ScoreSrc{sc}, ncand, n, out, out_lds, lds);
   }
 }
 
