@@ -399,6 +399,33 @@ def test_fused_chained_poisoned_requests(B, form):
     assert (lsed[fin] - lsed2[fin]).abs().max().item() <= H.LSE_ABS
 
 
+# Each fused form repeated on the same inputs and workspace: outputs, scores
+# and selections must agree to the bit (the persistent and work-list
+# kernels order their waves through LDS, the work list also splits units).
+REPEAT = [
+    ("two_launch", "decode_b128_l8192", dict(B=128, L=1500, sigma="one")),
+    ("persistent", "decode_b128_l8192", dict(B=96, L=(1000, 2000), sigma="one")),
+    ("work_list", "qwen3_8b_layer_b16_l4096", dict(B=16, L=(1000, 4096))),
+    ("rows_split", "longctx_b4_l128k", dict(B=2, L=3000, sigma="one")),
+]
+
+
+@pytest.mark.parametrize("case", REPEAT, ids=[c[0] for c in REPEAT])
+def test_fused_forms_bitwise_repeatable(case):
+    form, name, kw = case
+    wl = mk(name, seed=46, **kw)
+    print(f"[fused repeat] {form}", flush=True)
+    assert step_form(wl) == form
+    ws = H.sss().workspace(H.sss().fused_workspace_size(*step_args(wl), True), DEV)
+    runs = []
+    for _ in range(3):
+        v_out, (sel, cnt), d_out = run_chained(wl, ws=ws)
+        runs.append([t.clone() for t in (*v_out, sel, cnt, *d_out)])
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert nan_equal(a, b)
+
+
 def test_fused_score_row_start_one():
     wl = mk("qwen3_8b_layer_b16_l4096", seed=33, B=2, L=260, sigma="one")
     vb = wl.verify
