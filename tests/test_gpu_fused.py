@@ -291,6 +291,22 @@ def step_args(wl):
     return v, d
 
 
+def test_fused_rows_split_full_size():
+    """The long-context workload at full size (4 requests x 128K tokens, 80
+    rows per unit, 64 chunks): every output of the rows-split step bitwise
+    that of the per-stage calls (which the full-size parity test checks
+    against the oracle on sampled units), all finite."""
+    wl = mk("longctx_b4_l128k", seed=47)
+    print("[fused rows split] full size", flush=True)
+    assert step_form(wl) == "rows_split"
+    v_out, (sel, cnt), d_out = run_chained(wl)
+    v2, (sel2, cnt2), d2 = separate_calls(wl)
+    for a, b in zip((*v_out, *d_out), (*v2, *d2)):
+        assert nan_equal(a, b)
+        assert torch.isfinite(a.float()).all()
+    assert torch.equal(sel, sel2) and torch.equal(cnt, cnt2)
+
+
 def test_fused_rows_split_poisoned_requests():
     """A request longer than max_seq_len and one with an out-of-range page id
     poison only their own units, bitwise as in the per-stage calls."""
