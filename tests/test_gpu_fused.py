@@ -226,6 +226,12 @@ ROWS_SPLIT = [
     ("rows96", "longctx_b4_l128k", dict(B=2, L=3000, n_q=6, sigma="one"), {}),
     ("rows65_d64", "qwen3_8b_layer_b16_l4096", dict(B=2, L=3000, Hq=26, Hkv=2, d=64,
                                                     sigma="one"), {}),
+    # no recent window (every block a candidate, the list only selected
+    # blocks); one block selected; every candidate selected (the selection
+    # routine's early return, draft lists of about 190 segments)
+    ("rows80_window0", "longctx_b4_l128k", dict(B=2, L=3000, window=0, sigma="one"), {}),
+    ("rows80_budget1", "longctx_b4_l128k", dict(B=2, L=3000, budget=1, sigma="one"), {}),
+    ("rows80_budget_all", "longctx_b4_l128k", dict(B=2, L=3000, budget=1000, sigma="one"), {}),
 ]
 
 
