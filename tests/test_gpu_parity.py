@@ -130,12 +130,24 @@ def test_draft_small(case):
                 f"draft {cid} splits={ns} W={window}")
 
 
-def test_score_row_start_one():
-    wl = mk("qwen3_8b_layer_b16_l4096", seed=3, B=2, L=260, sigma="one")
+# 20 rows (one row tile) and 80 rows (the load-wave verify), unsplit and split
+ROW_SHAPES = [
+    ("rows20", "qwen3_8b_layer_b16_l4096", dict(B=2, L=260, sigma="one"), [None]),
+    ("rows80", "longctx_b4_l128k", dict(B=1, L=1500, sigma="one"), [0, 2]),
+]
+
+
+@pytest.mark.parametrize("shape", ROW_SHAPES, ids=[c[0] for c in ROW_SHAPES])
+def test_score_row_start_one(shape):
+    sid, name, kw, splits = shape
+    wl = mk(name, seed=3, **kw)
     vb = wl.verify
-    out = H.gpu_verify(wl, vb, score_row_start=1)
-    torch.cuda.synchronize()
-    H.compare_verify(wl, vb, out, H.all_units(vb, wl.shape.Hkv), score_row_start=1).check("r0=1")
+    for ns in splits:
+        print(f"[r0=1] {sid} num_splits={ns}", flush=True)
+        out = H.gpu_verify(wl, vb, num_splits=ns, score_row_start=1)
+        torch.cuda.synchronize()
+        H.compare_verify(wl, vb, out, H.all_units(vb, wl.shape.Hkv), score_row_start=1).check(
+            f"r0=1 {sid} splits={ns}")
     G = wl.shape.Hq // wl.shape.Hkv
     assert np.allclose(out[2].cpu().numpy().sum(-1), (wl.shape.n_q - 1) * G, atol=1e-3)
 
@@ -373,12 +385,16 @@ def test_invalid_seq_len_poisons_outputs():
     assert torch.isfinite(o[0].float()).all() and torch.isfinite(lse[0]).all()
 
 
+@pytest.mark.parametrize("shape", [("rows20", "qwen3_8b_layer_b16_l4096", dict(B=2, L=300)),
+                                   ("rows80", "longctx_b4_l128k", dict(B=1, L=1500))],
+                         ids=["rows20", "rows80"])
 @pytest.mark.parametrize("scale", [-0.06, 0.0])
-def test_negative_and_zero_scale(scale):
+def test_negative_and_zero_scale(scale, shape):
     """The tile loop scales by |scale| with a negative scale folded into Q: a
     negative and a zero softmax scale still match the oracle (verify with
-    scores, split and unsplit, and the draft)."""
-    wl = mk("qwen3_8b_layer_b16_l4096", seed=21, B=2, L=300, sigma="one")
+    scores, split and unsplit, and the draft), for one row tile and for the
+    80-row load-wave verify."""
+    wl = mk(shape[1], seed=21, sigma="one", **shape[2])
     wl.sm_scale = scale
     vb, db = wl.verify, wl.draft
     units = H.all_units(vb, wl.shape.Hkv)
