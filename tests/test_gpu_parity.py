@@ -62,6 +62,9 @@ SMALL = [
     # tile buffers in the load-wave ring; 96 rows at head dim 64 (three full
     # 32-row tiles)
     ("rows80_ring2", "longctx_b4_l128k", dict(B=1, L=8000, sigma="one"), [1]),
+    # 128-token blocks: a block's mass spans four tiles of the load-wave verify
+    ("rows80_blk128", "longctx_b4_l128k", dict(B=1, L=2000, block_size=128, budget=4,
+                                               sigma="one"), [0, 1, 2]),
     ("rows96_d64", "longctx_b4_l128k", dict(B=1, L=2000, n_q=6, d=64, sigma="one"), [0, 1, 3]),
     ("rows128", "qwen3_8b_layer_b16_l4096", dict(B=1, L=400, Hq=32, Hkv=1, n_q=4), [0, 2]),
     ("rows40", "qwen3_8b_layer_b16_l4096", dict(B=2, L=333, Hq=16, Hkv=2, sigma="one"), [0, 2]),
