@@ -348,7 +348,12 @@ sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_p
  * LDS -- with 1024 or more units of at most 1024 candidates and draft lists
  * in one chunk, one wave per unit (the draft the separate entry point runs
  * for that many units); with 1024 or more units otherwise, the Top-N and
- * draft kernels of the separate entry points.
+ * draft kernels of the separate entry points.  A chained step of split
+ * units of 65 to 96 rows whose verify runs as load-wave workgroups (fewer
+ * than 1024 units) takes no work list either: the verify and merge
+ * launches of sss_verify_attn, one launch with a workgroup per draft chunk
+ * that selects its unit's Top-N and drafts the chunk, then the draft merge
+ * of sss_draft_attn (SSS_FUSED_ROWS_SPLIT below).
  *
  * Requirements beyond those of the separate entry points: both halves use
  * the matrix-core path (BF16 cache, page_size a multiple of 16, block_size
@@ -366,7 +371,8 @@ sss_status sss_merge(const float* o_parts, const float* lse_parts, int32_t num_p
  * chunk uses the separate verify kernel itself, so its verify outputs,
  * scores and selection are bitwise those of sss_verify_attn followed by
  * sss_block_topk (and, with 1024 or more units, its draft bitwise that of
- * sss_draft_attn over that selection).
+ * sss_draft_attn over that selection); a step in the rows-split form
+ * equals all three entry points bitwise.
  */
 typedef struct {
   sss_paged_kv kv;
