@@ -517,6 +517,91 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // before the reference moves: terms stay <= 256, exact in fp32 and bf16 range.
 constexpr float kRescaleSlack = 8.f;
 
+// A single-token verify tile's logits are stored one tile later, ahead of
+// the next tile's loads: stores count in the same in-order counter as loads,
+// so a store issued after the loads would lengthen the wait for them.  They
+// stay in the wave's LDS parking area (4 KiB, 32 tokens x 32 rows), which
+// survives until then when it is a slot of its own (several row tiles); a
+// single row tile parks in its K tile, which the next tile overwrites, so
+// there the logits are read back token-major into registers first (REGS: 4
+// chunks of 4 rows when the row count is a multiple of 4, else 16 single
+// rows).  t0 = the tile's first token, -1 = nothing held (wave-uniform).
+// Empty for every other kernel, whose code it leaves untouched.
+template <bool ON, bool REGS>
+struct TokPark {
+  float v[REGS ? 16 : 1];
+  int t0 = -1, n = 0;
+};
+template <bool REGS>
+struct TokPark<false, REGS> {};
+
+// The logits of a parked tile, the lane's share: for a row count that is a
+// multiple of 4, chunk i (4 rows from 4q) of token m = lane / 8 + 8 i; else
+// row rr of token m = lane / 32 + 2 i.  Indexes past the tile's tokens or the
+// wave's rows repeat the last valid one (with its value), so every lane
+// issues the same fixed number of stores.
+__device__ __forceinline__ int tok_q(int lane, int rw) { return min(lane & 7, (rw >> 2) - 1); }
+__device__ __forceinline__ int tok_m4(int lane, int i, int n) { return min((lane >> 3) + 8 * i, n - 1); }
+__device__ __forceinline__ int tok_rr(int lane, int rw) { return min(lane & 31, rw - 1); }
+__device__ __forceinline__ int tok_m1(int lane, int i, int n) { return min((lane >> 5) + 2 * i, n - 1); }
+
+template <bool REGS>
+__device__ __forceinline__ void tok_park(TokPark<true, REGS>& tp, const float* stage, int t0,
+                                         int n, int R, int rt, int lane) {
+  if constexpr (REGS) {
+    const int rw = min(32, R - rt * 32);
+    if ((rw & 3) == 0 && (R & 3) == 0) {
+      const int q = tok_q(lane, rw);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stage + tok_m4(lane, i, n) * 32 + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tp.v[4 * i + e] = v[e];
+      }
+    } else {
+      const int rr = tok_rr(lane, rw);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tp.v[i] = stage[tok_m1(lane, i, n) * 32 + rr];
+    }
+  }
+  tp.t0 = t0;
+  tp.n = n;
+}
+
+// Stores what tp holds: token t0 + m, row r of the unit at ell_u[(t0 + m) *
+// R + r], this wave's rows rt * 32 .. rt * 32 + 31.  (Offsets stay 32-bit:
+// 64-bit addresses held across the tile loop cost more registers than exist.)
+template <bool REGS>
+__device__ __forceinline__ void tok_flush(TokPark<true, REGS>& tp, const float* stage,
+                                          float* ell_u, int R, int rt, int lane) {
+  if (tp.t0 < 0) return;
+  const int rw = min(32, R - rt * 32);
+  float* const dst = ell_u + (long long)tp.t0 * R + rt * 32;
+  if ((rw & 3) == 0 && (R & 3) == 0) {
+    const int q = tok_q(lane, rw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = tok_m4(lane, i, tp.n);
+      f32x4 v;
+      if constexpr (REGS) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = tp.v[4 * i + e];
+      } else {
+        v = *reinterpret_cast<const f32x4*>(stage + m * 32 + 4 * q);
+      }
+      *reinterpret_cast<f32x4*>(dst + (m * R + 4 * q)) = v;
+    }
+  } else {
+    const int rr = tok_rr(lane, rw);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = tok_m1(lane, i, tp.n);
+      dst[m * R + rr] = REGS ? tp.v[REGS ? i : 0] : stage[m * 32 + rr];
+    }
+  }
+  tp.t0 = -1;
+}
+
 // Runs one item with all 64 * NWR * NWT threads of the workgroup over the
 // LDS area `smem` (item_lds_bytes(D, NWR, NWT) bytes; with ELL_LDS, also
 // the chunk's block log masses, chunk-blocks x rows floats at byte offset
@@ -756,6 +841,8 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   // single-token verify: this wave's logit parking area
   float* const tok_stage = NWR == 1 ? reinterpret_cast<float*>(grp)
                                     : reinterpret_cast<float*>(smem + it.list_off) + w * 32 * 32;
+  // ... and the last live tile's logits, held until the next tile's loads
+  TokPark<SCORES && TOKENS, NWR == 1> tpark;
 
   // the first two batches' page ids, loaded while Q was staged (resolving
   // them before the Q loads made every unit wait one more round trip)
@@ -819,6 +906,10 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
     if (SCORES && !ell_lds) {
       if (ell_at >= 0) ell_u[ell_at] = ell_val;
       ell_at = -1;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (SCORES && TOKENS) {
+      tok_flush(tpark, tok_stage, ell_u, R, rt, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (PD > 1 || t + PD < n_tiles) {
@@ -938,30 +1029,13 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
       if (SCORES) {
         // per-block log mass of this row, frame m_use
         const int bs = p.block_size;
-        if (TOKENS) {
-          // the parked logits, token-major: token ca.t0 + m, row r at
-          // ell_u[(ca.t0 + m) * R + r], for the tokens of the request only;
-          // each token's run of rows with 16-byte stores, 8 lanes per token
+        if constexpr (SCORES && TOKENS) {
+          // the tile's logits, held for the next tile (tok_flush): token
+          // ca.t0 + m, for the tokens of the request only
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          const int n_tok = min(32, L - ca.t0);
-          const int rw = min(32, R - rt * 32);  // rows of this wave
-          float* dst = ell_u + (long long)ca.t0 * R + rt * 32;
-          // (offsets stay 32-bit and are formed in the loop: hoisting 64-bit
-          // addresses out of the tile loop costs more registers than exist)
-          if ((rw & 3) == 0 && (R & 3) == 0) {
-            const int q = lane & 7;
-            if (4 * q < rw) {
-#pragma unroll 1
-              for (int m = lane >> 3; m < n_tok; m += 8)
-                *reinterpret_cast<f32x4*>(dst + (m * R + 4 * q)) =
-                    *reinterpret_cast<const f32x4*>(tok_stage + m * 32 + 4 * q);
-            }
-          } else if (rl < rw) {
-#pragma unroll 1
-            for (int m = hl; m < n_tok; m += 2) dst[m * R + rl] = tok_stage[m * 32 + rl];
-          }
+          tok_park(tpark, tok_stage, ca.t0, min(32, L - ca.t0), R, rt, lane);
         } else if (bs == kSeg) {
           float a = 0.f, bb = 0.f;
 #pragma unroll
@@ -1007,6 +1081,7 @@ __device__ int attn_item(const AttnParams& p, const Item& it, char* smem) {
   }
 
   if (SCORES && ell_at >= 0) ell_u[ell_at] = ell_val;
+  if constexpr (SCORES && TOKENS) tok_flush(tpark, tok_stage, ell_u, R, rt, lane);
 
   // ---- combine the lane pair, then the token groups ----
   l_run += __shfl_xor(l_run, 32);
